@@ -1,0 +1,120 @@
+"""Test-only spherical harmonics and Wigner-D matrices (part of the oracle).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Both are written from their textbook closed forms and carried to the real basis
+with the oracle's change-of-basis matrix A_l (``oracle.real_basis``):
+
+  * complex SH with the Condon-Shortley phase,
+        Y_l^m = (-1)^m sqrt((2l+1)/(4 pi) (l-m)!/(l+m)!) P_l^m(cos t) e^{i m p},  m >= 0,
+        Y_l^{-m} = (-1)^m conj(Y_l^m),
+    P_l^m the associated Legendre function without the phase, obtained by
+    differentiating the Legendre polynomial m times; real, component-normalised
+    SH are sqrt(4 pi) A_l Y_l.
+  * Wigner's small-d formula and D^l_{m'm}(a,b,c) = e^{-i m' a} d^l_{m'm}(b) e^{-i m c}
+    for the rotation R = Rz(a) Ry(b) Rz(c); the real matrix acting on real SH
+    is A_l conj(D^l) A_l^H, the variant for which Y(R n) = D(R) Y(n).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+from numpy.polynomial import legendre as _leg
+from numpy.polynomial import polynomial as _poly
+
+from . import real_basis
+
+
+def assoc_legendre(l: int, m: int, t: np.ndarray) -> np.ndarray:
+    c = np.zeros(l + 1)
+    c[l] = 1.0
+    p = _leg.leg2poly(c)
+    dp = _poly.polyder(p, m) if m > 0 else p
+    return (1.0 - t * t) ** (m / 2.0) * _poly.polyval(t, dp)
+
+
+def sh_complex(l: int, vec: np.ndarray) -> np.ndarray:
+    x, y, z = vec[:, 0], vec[:, 1], vec[:, 2]
+    theta = np.arccos(np.clip(z, -1.0, 1.0))
+    phi = np.arctan2(y, x)
+    out = np.zeros((len(vec), 2 * l + 1), dtype=complex)
+    for m in range(0, l + 1):
+        n = math.sqrt((2 * l + 1) / (4 * math.pi) * math.factorial(l - m) / math.factorial(l + m))
+        v = n * (-1) ** m * assoc_legendre(l, m, np.cos(theta)) * np.exp(1j * m * phi)
+        out[:, m + l] = v
+        if m > 0:
+            out[:, -m + l] = (-1) ** m * np.conj(v)
+    return out
+
+
+def sh_real(L: int, vec: np.ndarray) -> np.ndarray:
+    """[E, (L+1)^2] real component-normalised SH, degrees 0..L, m = -l..l."""
+    cols = []
+    for l in range(L + 1):
+        yl = math.sqrt(4 * math.pi) * (sh_complex(l, vec) @ real_basis(l).T)
+        assert np.abs(yl.imag).max(initial=0.0) < 1e-12
+        cols.append(yl.real)
+    return np.concatenate(cols, axis=1)
+
+
+def small_d(l: int, mp: int, m: int, beta: float) -> float:
+    s = 0.0
+    cb, sb = math.cos(beta / 2), math.sin(beta / 2)
+    for k in range(0, 2 * l + 1):
+        a = (l + m - k, k, l - k - mp, k - m + mp)
+        if min(a) < 0:
+            continue
+        num = math.sqrt(math.factorial(l + mp) * math.factorial(l - mp) *
+                        math.factorial(l + m) * math.factorial(l - m))
+        den = (math.factorial(a[0]) * math.factorial(a[1]) * math.factorial(a[2]) *
+               math.factorial(a[3]))
+        s += (-1) ** (k - m + mp) * num / den * cb ** (2 * l - 2 * k + m - mp) * \
+            sb ** (2 * k - m + mp)
+    return s
+
+
+def wigner_d_complex(l: int, a: float, b: float, c: float) -> np.ndarray:
+    D = np.zeros((2 * l + 1, 2 * l + 1), dtype=complex)
+    for mp in range(-l, l + 1):
+        for m in range(-l, l + 1):
+            D[mp + l, m + l] = np.exp(-1j * mp * a) * small_d(l, mp, m, b) * np.exp(-1j * m * c)
+    return D
+
+
+def wigner_d_real(l: int, a: float, b: float, c: float) -> np.ndarray:
+    A = real_basis(l)
+    D = A @ wigner_d_complex(l, a, b, c).conj() @ A.conj().T
+    assert np.abs(D.imag).max() < 1e-12
+    return D.real
+
+
+def rot_z(t: float) -> np.ndarray:
+    c, s = math.cos(t), math.sin(t)
+    return np.array([[c, -s, 0.0], [s, c, 0.0], [0.0, 0.0, 1.0]])
+
+
+def rot_y(t: float) -> np.ndarray:
+    c, s = math.cos(t), math.sin(t)
+    return np.array([[c, 0.0, s], [0.0, 1.0, 0.0], [-s, 0.0, c]])
+
+
+def rotation(a: float, b: float, c: float) -> np.ndarray:
+    return rot_z(a) @ rot_y(b) @ rot_z(c)
+
+
+def block_diag_irreps(blocks, a, b, c):
+    """Real Wigner-D acting on a feature row laid out as blocks [(U, l), ...],
+    each block u-major (element u*(2l+1)+m)."""
+    mats = []
+    for U, l in blocks:
+        D = wigner_d_real(l, a, b, c)
+        mats.append(np.kron(np.eye(U), D))
+    n = sum(m.shape[0] for m in mats)
+    out = np.zeros((n, n))
+    o = 0
+    for m in mats:
+        k = m.shape[0]
+        out[o:o + k, o:o + k] = m
+        o += k
+    return out

@@ -1,0 +1,333 @@
+"""Pins of the oracle's convolution, its VJP and its double backward.
+
+Independent checks only: a dense einsum with one-hot incidence matrices (no CSR
+code, no sparse tables), scipy.sparse for the scalar path, rotation and
+inversion equivariance, the adjoint identities of a trilinear map, and exact
+five-point finite differences (every quantity below is a polynomial of degree
+<= 3 along a line, for which the five-point stencil is exact).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import sphere
+
+
+def _dense_fwd(d, rowptr, src, x, Y, W):
+    """out = A_recv^T msg, msg[e] = sum_p C_p(x[src[e]], Y[e]) W[e,p] (dense)."""
+    N, E = len(rowptr) - 1, len(src)
+    recv = np.repeat(np.arange(N), np.diff(rowptr))
+    A_send = np.zeros((E, N)); A_send[np.arange(E), src] = 1
+    A_recv = np.zeros((E, N)); A_recv[np.arange(E), recv] = 1
+    xs = A_send @ x
+    xoff = np.cumsum([0] + [d.U * (2 * l + 1) for l in d.xl])
+    ooff = np.cumsum([0] + [d.U * (2 * l + 1) for l in d.out_l])
+    out = np.zeros((N, d.out_dim))
+    for p, (i1, l2, l3, ob) in enumerate(d.paths):
+        l1 = d.xl[i1]
+        C = oracle.cg_real(l1, l2, l3)
+        xb = xs[:, xoff[i1]:xoff[i1 + 1]].reshape(E, d.U, 2 * l1 + 1)
+        yb = Y[:, l2 * l2:(l2 + 1) ** 2]
+        msg = np.einsum("eua,eb,abc,eu->euc", xb, yb, C, W[:, p, :])
+        out[:, ooff[ob]:ooff[ob + 1]] += A_recv.T @ msg.reshape(E, -1)
+    return out
+
+
+def _tiny_graph(rng, N=9, with_dups=True):
+    deg = rng.integers(0, 6, size=N)
+    deg[2] = 0                                    # an empty row
+    rowptr = np.concatenate([[0], np.cumsum(deg)]).astype(np.int32)
+    src = rng.integers(0, N, size=rowptr[-1]).astype(np.int32)   # self-loops, duplicates
+    if with_dups and len(src) > 1:
+        src[1] = src[0]
+    return rowptr, src
+
+
+def _tiny_inputs(d, rowptr, src, rng):
+    N, E = len(rowptr) - 1, len(src)
+    x = rng.standard_normal((N, d.x_dim))
+    Y = synth.real_sh_cartesian(d.L, synth.unit_vectors(E, rng))
+    W = rng.standard_normal((E, d.P, d.U))
+    g = rng.standard_normal((N, d.out_dim))
+    return x, Y, W, g
+
+
+DESCS = [
+    dict(x_irreps=((3, 0, 1), (3, 1, -1)), y_lmax=2, l3_max=1),
+    dict(x_irreps=((2, 0, 1), (2, 1, -1), (2, 2, 1)), y_lmax=3, l3_max=3),
+    dict(x_irreps=((2, 3, -1), (2, 1, 1)), y_lmax=3, l3_max=3),
+]
+
+
+def test_path_enumeration_counts_and_order():
+    got = {k: oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max).P
+           for k, wl in synth.WORKLOADS.items()}
+    assert got == {"tiny_fp64": 6, "mace_medium_fp32": 13, "mace_medium_fp64": 13,
+                   "mace_large_fp32": 24, "wide_proxy_fp32": 24}
+    en = oracle.enumerate_paths(synth.WORKLOADS["tiny_fp64"].x_irreps, 2, 1)
+    # 0e x 0e -> 0e, 0e x 1o -> 1o, 1o x 0e -> 1o, 1o x 1o -> 0e, 1o x 1o -> 1e, 1o x 2e -> 1o
+    assert en == [(0, 0, 0, 1), (0, 1, 1, -1), (1, 0, 1, -1), (1, 1, 0, 1), (1, 1, 1, 1),
+                  (1, 2, 1, -1)]
+
+
+def test_sparse_table_sizes():
+    d = oracle.Desc(synth.WORKLOADS["mace_medium_fp32"].x_irreps, 3, 3)
+    nnz = sum(np.count_nonzero(oracle.cg_real(d.xl[i1], l2, l3)) for i1, l2, l3, _ in d.paths)
+    assert nnz == 134
+    assert d.out_dim // d.U == 55
+    d = oracle.Desc(synth.WORKLOADS["mace_large_fp32"].x_irreps, 3, 3)
+    nnz = sum(np.count_nonzero(oracle.cg_real(d.xl[i1], l2, l3)) for i1, l2, l3, _ in d.paths)
+    assert nnz == 351
+    assert d.out_dim // d.U == 106
+
+
+@pytest.mark.parametrize("k", range(len(DESCS)))
+def test_fwd_matches_dense_einsum(k):
+    rng = np.random.default_rng(10 + k)
+    d = oracle.Desc(**DESCS[k])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, _ = _tiny_inputs(d, rowptr, src, rng)
+    ref = _dense_fwd(d, rowptr, src, x, Y, W)
+    got = oracle.fwd(d, rowptr, src, x, Y, W)
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+    assert not got[2].any()                      # empty receiver row
+
+
+def test_fwd_shared_output_block_sums_paths():
+    """Two paths pointed at one output block are summed into it."""
+    rng = np.random.default_rng(20)
+    xi = ((2, 1, -1),)
+    d_sep = oracle.Desc(xi, 2, paths=[(0, 0, 1, 0), (0, 2, 1, 1)], out_l=[1, 1])
+    d_sum = oracle.Desc(xi, 2, paths=[(0, 0, 1, 0), (0, 2, 1, 0)], out_l=[1])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, _ = _tiny_inputs(d_sep, rowptr, src, rng)
+    a = oracle.fwd(d_sep, rowptr, src, x, Y, W)
+    b = oracle.fwd(d_sum, rowptr, src, x, Y, W)
+    assert np.allclose(b, a[:, :6] + a[:, 6:], atol=1e-13)
+    assert np.allclose(b, _dense_fwd(d_sum, rowptr, src, x, Y, W), atol=1e-13)
+
+
+def test_fwd_scalar_path_is_weighted_spmm():
+    import scipy.sparse as sp
+    rng = np.random.default_rng(30)
+    U = 5
+    d = oracle.Desc(((U, 0, 1),), 0, 0)
+    assert d.paths == [(0, 0, 0, 0)]
+    rowptr, src = _tiny_graph(rng, N=12)
+    N, E = len(rowptr) - 1, len(src)
+    x = rng.standard_normal((N, U))
+    Y = rng.standard_normal((E, 1))
+    W = rng.standard_normal((E, 1, U))
+    got = oracle.fwd(d, rowptr, src, x, Y, W)
+    for u in range(U):
+        A = sp.csr_matrix((Y[:, 0] * W[:, 0, u], src, rowptr), shape=(N, N))
+        assert np.allclose(got[:, u], A @ x[:, u], atol=1e-13)
+
+
+def test_fwd_rows_subset():
+    rng = np.random.default_rng(40)
+    d = oracle.Desc(**DESCS[1])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, _ = _tiny_inputs(d, rowptr, src, rng)
+    full = oracle.fwd(d, rowptr, src, x, Y, W)
+    rows = np.array([5, 0, 2])
+    assert np.array_equal(oracle.fwd(d, rowptr, src, x, Y, W, rows=rows), full[rows])
+
+
+@pytest.mark.parametrize("k", range(len(DESCS)))
+def test_fwd_rotation_equivariance(k):
+    rng = np.random.default_rng(50 + k)
+    d = oracle.Desc(**DESCS[k])
+    rowptr, src = _tiny_graph(rng)
+    N, E = len(rowptr) - 1, len(src)
+    vec = synth.unit_vectors(E, rng)
+    x = rng.standard_normal((N, d.x_dim))
+    W = rng.standard_normal((E, d.P, d.U))
+    ang = tuple(rng.uniform(0.1, 3.0, 3))
+    R = sphere.rotation(*ang)
+    Dx = sphere.block_diag_irreps([(d.U, l) for l in d.xl], *ang)
+    Do = sphere.block_diag_irreps([(d.U, l) for l in d.out_l], *ang)
+    Y = synth.real_sh_cartesian(d.L, vec)
+    YR = synth.real_sh_cartesian(d.L, vec @ R.T)          # rotated edge vectors
+    out = oracle.fwd(d, rowptr, src, x, Y, W)
+    outR = oracle.fwd(d, rowptr, src, x @ Dx.T, YR, W)
+    assert np.abs(outR - out @ Do.T).max() < 1e-11 * np.abs(out).max()
+
+
+@pytest.mark.parametrize("k", range(len(DESCS)))
+def test_fwd_inversion_parity(k):
+    rng = np.random.default_rng(60 + k)
+    d = oracle.Desc(**DESCS[k])
+    rowptr, src = _tiny_graph(rng)
+    E = len(src)
+    x, _, W, _ = _tiny_inputs(d, rowptr, src, rng)
+    vec = synth.unit_vectors(E, rng)
+    Y, Yinv = synth.real_sh_cartesian(d.L, vec), synth.real_sh_cartesian(d.L, -vec)
+    px = np.concatenate([np.full(d.U * (2 * l + 1), p) for (_, l, p) in d.x_irreps])
+    en = oracle.enumerate_paths(d.x_irreps, d.L, DESCS[k]["l3_max"])
+    po = np.concatenate([np.full(d.U * (2 * l3 + 1), p3) for (_, _, l3, p3) in en])
+    out = oracle.fwd(d, rowptr, src, x, Y, W)
+    outI = oracle.fwd(d, rowptr, src, x * px, Yinv, W)
+    assert np.allclose(outI, out * po, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# VJP
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", range(len(DESCS)))
+def test_vjp_adjoint_identities(k):
+    rng = np.random.default_rng(70 + k)
+    d = oracle.Desc(**DESCS[k])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, g = _tiny_inputs(d, rowptr, src, rng)
+    f = oracle.fwd(d, rowptr, src, x, Y, W)
+    gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
+    L = np.vdot(g, f)
+    for grad, arg in ((gx, x), (gY, Y), (gW, W)):
+        assert np.vdot(grad, arg) == pytest.approx(L, rel=1e-12, abs=1e-12)
+
+
+def _five_point(fn, h=0.5):
+    return (8 * (fn(h) - fn(-h)) - (fn(2 * h) - fn(-2 * h))) / (12 * h)
+
+
+@pytest.mark.parametrize("k", range(len(DESCS)))
+def test_vjp_is_gradient_along_mixed_direction(k):
+    rng = np.random.default_rng(80 + k)
+    d = oracle.Desc(**DESCS[k])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, g = _tiny_inputs(d, rowptr, src, rng)
+    dx, dY, dW = (rng.standard_normal(a.shape) for a in (x, Y, W))
+
+    def loss(t):
+        return np.vdot(g, oracle.fwd(d, rowptr, src, x + t * dx, Y + t * dY, W + t * dW))
+
+    gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
+    pred = np.vdot(gx, dx) + np.vdot(gY, dY) + np.vdot(gW, dW)
+    assert _five_point(loss) == pytest.approx(pred, rel=1e-10)
+    # each argument alone: the loss is linear in it, so a one-sided difference is exact
+    for grad, arg, dd, which in ((gx, x, dx, 0), (gY, Y, dY, 1), (gW, W, dW, 2)):
+        args = [x, Y, W]
+        args[which] = arg + dd
+        delta = np.vdot(g, oracle.fwd(d, rowptr, src, *args)) - np.vdot(
+            g, oracle.fwd(d, rowptr, src, x, Y, W))
+        assert delta == pytest.approx(np.vdot(grad, dd), rel=1e-10)
+
+
+def test_vjp_subsets_match_full():
+    rng = np.random.default_rng(90)
+    d = oracle.Desc(**DESCS[1])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, g = _tiny_inputs(d, rowptr, src, rng)
+    gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
+    e = np.array([3, 0, len(src) - 1])
+    sW, sY = oracle.bwd_edges(d, rowptr, src, x, Y, W, g, edges=e)
+    assert np.array_equal(sW, gW[e]) and np.array_equal(sY, gY[e])
+    s = np.array([4, 1])
+    assert np.array_equal(oracle.bwd_gx(d, rowptr, src, Y, W, g, senders=s), gx[s])
+
+
+def test_vjp_gradient_rotation_equivariance():
+    """gx rotates like x and gY like Y when g rotates like the output."""
+    rng = np.random.default_rng(95)
+    d = oracle.Desc(**DESCS[1])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, g = _tiny_inputs(d, rowptr, src, rng)
+    ang = (0.3, 2.1, -0.8)
+    Dx = sphere.block_diag_irreps([(d.U, l) for l in d.xl], *ang)
+    Do = sphere.block_diag_irreps([(d.U, l) for l in d.out_l], *ang)
+    DY = sphere.block_diag_irreps([(1, l) for l in range(d.L + 1)], *ang)
+    gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
+    gx2, gY2, gW2 = oracle.bwd(d, rowptr, src, x @ Dx.T, Y @ DY.T, W, g @ Do.T)
+    assert np.allclose(gx2, gx @ Dx.T, atol=1e-11)
+    assert np.allclose(gY2, gY @ DY.T, atol=1e-11)
+    assert np.allclose(gW2, gW, atol=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# Double backward
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("k", range(len(DESCS)))
+def test_dbwd_matches_finite_differences_of_vjp(k):
+    rng = np.random.default_rng(100 + k)
+    d = oracle.Desc(**DESCS[k])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, g = _tiny_inputs(d, rowptr, src, rng)
+    ggx, ggY, ggW = (rng.standard_normal(a.shape) for a in (x, Y, W))
+    res = oracle.dbwd(d, rowptr, src, x, Y, W, g, ggx, ggY, ggW)
+
+    def S(xx, YY, WW, gg):
+        gx, gY, gW = oracle.bwd(d, rowptr, src, xx, YY, WW, gg)
+        return np.vdot(ggx, gx) + np.vdot(ggY, gY) + np.vdot(ggW, gW)
+
+    base = (x, Y, W, g)
+    names = ("dx", "dY", "dW", "dg")
+    dirs = [rng.standard_normal(a.shape) for a in base]
+    # each argument separately
+    for i, name in enumerate(names):
+        def line(t, i=i):
+            a = list(base)
+            a[i] = base[i] + t * dirs[i]
+            return S(*a)
+        assert _five_point(line) == pytest.approx(np.vdot(res[name], dirs[i]), rel=1e-9, abs=1e-9)
+    # all at once
+    def line_all(t):
+        return S(*(b + t * v for b, v in zip(base, dirs)))
+    pred = sum(np.vdot(res[n], v) for n, v in zip(names, dirs))
+    assert _five_point(line_all) == pytest.approx(pred, rel=1e-9)
+
+
+def test_hvp_tangent_on_x_only():
+    """With only ggx set: dx is exactly zero, dg = f(v, Y, W)."""
+    rng = np.random.default_rng(110)
+    d = oracle.Desc(**DESCS[1])
+    rowptr, src = _tiny_graph(rng)
+    x, Y, W, g = _tiny_inputs(d, rowptr, src, rng)
+    v = rng.standard_normal(x.shape)
+    res = oracle.dbwd(d, rowptr, src, x, Y, W, g, ggx=v)
+    assert not res["dx"].any()
+    assert np.array_equal(res["dg"], oracle.fwd(d, rowptr, src, v, Y, W))
+    rows, edges, senders = np.array([1, 7]), np.array([0, 4]), np.array([3])
+    sub = oracle.dbwd(d, rowptr, src, x, Y, W, g, ggx=v, rows=rows, edges=edges, senders=senders)
+    assert np.array_equal(sub["dg"], res["dg"][rows])
+    assert np.array_equal(sub["dY"], res["dY"][edges])
+    assert np.array_equal(sub["dW"], res["dW"][edges])
+
+
+# ---------------------------------------------------------------------------
+# Sender CSR
+# ---------------------------------------------------------------------------
+
+def test_sender_csr_is_stable_counting_sort():
+    rng = np.random.default_rng(120)
+    N = 50
+    src = rng.integers(0, N, size=700).astype(np.int32)
+    src[src == 7] = 8                                   # a sender with no edges
+    srowptr, sperm = oracle.sender_csr(N, src)
+    assert np.array_equal(sperm, np.argsort(src, kind="stable"))
+    assert np.array_equal(srowptr, np.concatenate([[0], np.cumsum(np.bincount(src, minlength=N))]))
+    assert srowptr[7] == srowptr[8]
+    assert np.all(np.diff(src[sperm]) >= 0)
+    assert np.array_equal(np.sort(sperm), np.arange(len(src)))
+    e0, e1 = oracle.sender_csr(0, np.zeros(0, dtype=np.int32))
+    assert e0.tolist() == [0] and len(e1) == 0
+
+
+def test_generator_graph_properties():
+    wl = synth.WORKLOADS["tiny_fp64"]
+    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    inp = synth.generate(wl, d.P, d.out_dim)
+    rowptr, src = inp["rowptr"], inp["src"]
+    assert rowptr[0] == 0 and rowptr[-1] == wl.n_edges == 1024
+    assert np.all(np.diff(rowptr) == 16)
+    for r in range(wl.n_nodes):
+        row = src[rowptr[r]:rowptr[r + 1]]
+        assert np.all(np.diff(row) > 0) and r not in row
+    assert inp["W"].shape == (1024, 6, 8) and inp["x"].dtype == np.float64
+    again = synth.generate(wl, d.P, d.out_dim)
+    assert np.array_equal(again["W"], inp["W"]) and np.array_equal(again["src"], src)
