@@ -1,0 +1,188 @@
+#!/usr/bin/env python3
+"""Throughput of the fused UVU CG tensor-product convolution on one MI355X.
+
+One step = one forward plus one full VJP (x, Y and W gradients) over the
+5,000-node / 280,000-edge receiver-sorted synthetic graph of degree 56 with node
+irreps 128x0e+128x1o, Y of degrees 0..3 and all 13 paths with l3 <= 3, in fp32
+(the workload of "Receiver-streaming convolutions for channel-wise UVU tensor
+products", benchmark paragraph).  Inputs are resident in device memory before
+the timed region; graph construction and planning are outside it.
+
+Prints one JSON line: edges/s for the step, the step's algorithmic HBM GB/s, a
+roofline entry for the dominant kernel (its average duration from HIP events on
+the stream it runs on) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def algorithmic_bytes(wl, P, out_dim, E):
+    """Bytes the method must move once: inputs read and outputs written.
+    Re-reads of x and grad_out rows from cache are not counted."""
+    s = 8 if wl.dtype == "f64" else 4
+    N = wl.n_nodes
+    W = E * P * wl.U * s
+    Y = E * wl.y_dim * s
+    x = N * wl.x_dim * s
+    o = N * out_dim * s
+    csr = (N + 1) * 4 + E * 4
+    fwd = W + Y + x + o + csr
+    vjp = (W + Y + x + o + csr) + (W + Y + x)       # read W,Y,x,g,CSR; write gW,gY,gx
+    hvp = (W + Y + x + o + csr) + (W + Y + o)       # read W,Y,v,g,CSR; write dW,dY,dg
+    return {"fwd": fwd, "vjp": vjp, "hvp": hvp}
+
+
+def cpu_baseline(wl, d, inp, target_s=12.0):
+    """The oracle (fp64 loops, OpenMP over independent rows) on a bounded sample
+    of receivers: their forward rows, the W and Y gradients of their edges and
+    the x gradients of as many senders.  Reported as edges/s of fwd + VJP."""
+    import oracle
+    from synth import edges_of_rows, subgraph
+
+    def run(nrows):
+        rows = np.arange(nrows)
+        e = edges_of_rows(inp["rowptr"], rows)
+        rp, sr, _ = subgraph(inp["rowptr"], inp["src"], e)
+        Ys, Ws = inp["Y"][e], inp["W"][e]
+        t = time.perf_counter()
+        oracle.fwd(d, rp, sr, inp["x"], Ys, Ws, rows=rows)
+        oracle.bwd_edges(d, rp, sr, inp["x"], Ys, Ws, inp["g"])
+        senders = np.unique(sr)[:nrows]
+        oracle.bwd_gx(d, rp, sr, Ys, Ws, inp["g"], senders=senders)
+        return time.perf_counter() - t, len(e)
+
+    t1, e1 = run(4)
+    per_edge = t1 / max(e1, 1)
+    deg = max(1, inp["E"] // max(wl.n_nodes, 1))
+    nrows = int(max(4, min(wl.n_nodes, target_s / max(per_edge, 1e-9) / deg)))
+    t, e = run(nrows)
+    return {"value": e / t, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"fwd rows, W/Y gradients of their edges and x gradients of up to as many senders "
+                      f"for the first {nrows} receivers ({e} edges) of the workload; {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mace_medium_fp32")
+    ap.add_argument("--mode", default="atomic", choices=["atomic", "deterministic"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON file with measured HBM bytes per launch of the dominant kernel")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the path runs on a single MI355X "
+              "(see the sharding paragraph of the design notes); --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import cg_tensor_product_amd as oeq
+    import oracle
+    import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    inp = synth.generate(wl, d.P, d.out_dim, want=("x", "Y", "W", "g"))
+    E, N = inp["E"], wl.n_nodes
+    torch.cuda.set_device(0)
+    plan = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    dev = {k: torch.from_numpy(inp[k]).cuda() for k in ("rowptr", "src", "x", "Y", "W", "g")}
+    dt = plan.torch_dtype()
+    out = torch.empty(N, plan.out_dim, dtype=dt, device="cuda")
+    grads = (torch.empty(N, plan.x_dim, dtype=dt, device="cuda"),
+             torch.empty(E, plan.y_dim, dtype=dt, device="cuda"),
+             torch.empty(E, plan.n_paths, plan.U, dtype=dt, device="cuda"))
+    ws = None
+    nbytes = oeq.oeq_workspace_size(plan, N, E, args.mode)
+    if nbytes:
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 256
+        ws = raw[off:off + nbytes]
+
+    def fwd():
+        oeq.oeq_tp_conv_fwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], out=out)
+
+    def vjp():
+        oeq.oeq_tp_conv_bwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                            mode=args.mode, out=grads, workspace=ws)
+
+    for _ in range(args.warmup):
+        fwd()
+        vjp()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b, c in ev:
+        a.record(stream)
+        fwd()
+        b.record(stream)
+        vjp()
+        c.record(stream)
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    vjp_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+
+    ab = algorithmic_bytes(wl, d.P, d.out_dim, E)
+    ms_step = total / args.steps * 1e3
+    step_bytes = ab["fwd"] + ab["vjp"]
+    dom, dom_ms, dom_bytes = ("vjp", vjp_ms, ab["vjp"]) if vjp_ms >= fwd_ms else ("fwd", fwd_ms, ab["fwd"])
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get(dom)
+    kname = {"fwd": "oeq_fwd", "vjp": "oeq_bwd_atomic" if args.mode == "atomic" else "oeq_bwd_rows"}[dom]
+    res = {
+        "metric": "edges/s and achieved HBM GB/s, fused CG-TP conv fwd+VJP, 5k nodes/280k edges",
+        "value": E / (ms_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "nodes": N, "edges": E, "degree": wl.degree,
+                   "x_irreps": "+".join(f"{m}x{l}{'e' if p > 0 else 'o'}" for m, l, p in wl.x_irreps),
+                   "y_lmax": wl.y_lmax, "paths": d.P, "step": f"forward + VJP ({args.mode} x-gradient)"},
+        "achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+        "kernels": {
+            "fwd": {"ms": fwd_ms, "GBps": ab["fwd"] / (fwd_ms * 1e-3) / 1e9, "bytes": ab["fwd"],
+                    "edges_per_s": E / (fwd_ms * 1e-3)},
+            "vjp": {"ms": vjp_ms, "GBps": ab["vjp"] / (vjp_ms * 1e-3) / 1e9, "bytes": ab["vjp"],
+                    "edges_per_s": E / (vjp_ms * 1e-3)},
+        },
+        "roofline": {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wl, d, inp)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

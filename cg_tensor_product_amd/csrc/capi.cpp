@@ -1,0 +1,326 @@
+// C ABI entry points: argument checks (host only, no device reads, no
+// synchronisation), workspace carving and stream-ordered kernel launches.
+#include <cstring>
+#include <limits>
+#include <string>
+
+#include "csr.hpp"
+#include "planner.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+oeq_status fail(oeq_status st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t esize(const oeq_plan *p) { return p->dtype == OEQ_F64 ? 8 : 4; }
+
+oeq_status check_graph(const oeq_plan *p, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src) {
+    if (!p) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (N < 0 || E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative node or edge count");
+    if (N >= std::numeric_limits<int32_t>::max() || E >= std::numeric_limits<int32_t>::max())
+        return fail(OEQ_ERR_UNSUPPORTED, "node and edge counts must fit the int32 CSR");
+    if (N == 0 && E != 0) return fail(OEQ_ERR_INVALID_ARG, "edges without nodes");
+    if (N * p->uch * 64 >= (int64_t(1) << 32)) return fail(OEQ_ERR_UNSUPPORTED, "too many nodes for one launch");
+    if (N > 0 && !rowptr) return fail(OEQ_ERR_INVALID_ARG, "rowptr is NULL");
+    if (E > 0 && !src) return fail(OEQ_ERR_INVALID_ARG, "src is NULL");
+    return OEQ_OK;
+}
+
+oeq_status launch(oeq_plan *p, const char *name, unsigned grid, unsigned block, hipStream_t stream, void **args) {
+    if (grid == 0) return OEQ_OK;
+    hipFunction_t fn = nullptr;
+    std::string why;
+    oeq_status st = oeq::get_kernel(*p, name, &fn, &why);
+    if (st != OEQ_OK) return fail(st, why);
+    const hipError_t e = hipModuleLaunchKernel(fn, grid, 1, 1, block, 1, 1, 0, stream, args, nullptr);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("launch ") + name + ": " + hipGetErrorString(e));
+    return OEQ_OK;
+}
+
+oeq_status fill_zero(oeq_plan *p, void *ptr, int64_t n, hipStream_t stream) {
+    if (n <= 0) return OEQ_OK;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    void *args[] = {&ptr, &n};
+    return launch(p, "oeq_fill_zero", static_cast<unsigned>(blocks), 256, stream, args);
+}
+
+struct DetWorkspace {
+    void *h = nullptr;
+    int32_t *srowptr = nullptr, *sperm = nullptr;
+    void *csr_scratch = nullptr;
+    size_t bytes = 0;
+};
+
+oeq_status det_layout(const oeq_plan *p, int64_t N, int64_t E, char *base, DetWorkspace *w) {
+    size_t csr_bytes = 0;
+    const hipError_t e = oeq::sender_csr_workspace(N, E, &csr_bytes);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR workspace: ") + hipGetErrorString(e));
+    size_t off = 0;
+    w->h = base + off;
+    off += up(static_cast<size_t>(E) * static_cast<size_t>(p->XD) * esize(p));
+    w->srowptr = reinterpret_cast<int32_t *>(base + off);
+    off += up(sizeof(int32_t) * static_cast<size_t>(N + 1));
+    w->sperm = reinterpret_cast<int32_t *>(base + off);
+    off += up(sizeof(int32_t) * static_cast<size_t>(E > 0 ? E : 1));
+    w->csr_scratch = base + off;
+    off += up(csr_bytes);
+    w->bytes = off;
+    return OEQ_OK;
+}
+
+// x-gradient by per-edge rows (already written to w.h) summed per sender.
+oeq_status det_prepare(oeq_plan *p, int64_t N, int64_t E, const int32_t *src, void *workspace, size_t ws_bytes,
+                       hipStream_t stream, DetWorkspace *w) {
+    if (!workspace) return fail(OEQ_ERR_WORKSPACE, "deterministic mode needs a workspace");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+        return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    oeq_status st = det_layout(p, N, E, static_cast<char *>(workspace), w);
+    if (st != OEQ_OK) return st;
+    if (ws_bytes < w->bytes) return fail(OEQ_ERR_WORKSPACE, "workspace smaller than oeq_workspace_size");
+    const hipError_t e = oeq::sender_csr(N, E, src, w->srowptr, w->sperm, w->csr_scratch, stream);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR: ") + hipGetErrorString(e));
+    return OEQ_OK;
+}
+
+oeq_status det_finish(oeq_plan *p, int64_t N, const DetWorkspace &w, void *gx, hipStream_t stream) {
+    void *h = w.h;
+    int32_t *srp = w.srowptr, *spm = w.sperm;
+    int n = static_cast<int>(N);
+    void *args[] = {&srp, &spm, &h, &gx, &n};
+    return launch(p, "oeq_sender_sum", static_cast<unsigned>(N), 256, stream, args);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *oeq_status_string(oeq_status s) {
+    switch (s) {
+    case OEQ_OK: return "OEQ_OK";
+    case OEQ_ERR_INVALID_ARG: return "OEQ_ERR_INVALID_ARG";
+    case OEQ_ERR_UNSUPPORTED: return "OEQ_ERR_UNSUPPORTED";
+    case OEQ_ERR_WORKSPACE: return "OEQ_ERR_WORKSPACE";
+    case OEQ_ERR_HIP: return "OEQ_ERR_HIP";
+    case OEQ_ERR_JIT: return "OEQ_ERR_JIT";
+    }
+    return "unknown oeq_status";
+}
+
+const char *oeq_last_error(void) { return g_last_error.c_str(); }
+
+oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan) {
+    if (!plan) return fail(OEQ_ERR_INVALID_ARG, "plan output pointer is NULL");
+    *plan = nullptr;
+    oeq_plan *p = new oeq_plan();
+    std::string why;
+    oeq_status st = oeq::plan_build(desc, p, &why);
+    if (st == OEQ_OK) {
+        p->source = oeq::emit_source(*p);
+        st = oeq::jit_compile(*p, &why);
+    }
+    if (st != OEQ_OK) {
+        delete p;
+        return fail(st, why);
+    }
+    *plan = p;
+    return OEQ_OK;
+}
+
+void oeq_plan_destroy(oeq_plan *plan) {
+    if (!plan) return;
+    for (auto &kv : plan->modules)
+        if (kv.second.module) {
+            int cur = 0;
+            if (hipGetDevice(&cur) == hipSuccess && hipSetDevice(kv.first) == hipSuccess) {
+                (void)hipModuleUnload(kv.second.module);
+                (void)hipSetDevice(cur);
+            }
+        }
+    delete plan;
+}
+
+oeq_status oeq_plan_dims(const oeq_plan *p, int64_t *x_dim, int64_t *y_dim, int64_t *out_dim, int64_t *n_paths,
+                         int64_t *w_per_edge) {
+    if (!p) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (x_dim) *x_dim = p->XD;
+    if (y_dim) *y_dim = p->YD;
+    if (out_dim) *out_dim = p->OD;
+    if (n_paths) *n_paths = static_cast<int64_t>(p->paths.size());
+    if (w_per_edge) *w_per_edge = static_cast<int64_t>(p->paths.size()) * p->U;
+    return OEQ_OK;
+}
+
+oeq_status oeq_plan_paths(const oeq_plan *p, int32_t *out6, int32_t capacity) {
+    if (!p || !out6) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
+    if (capacity < static_cast<int32_t>(p->paths.size())) return fail(OEQ_ERR_INVALID_ARG, "capacity too small");
+    for (size_t k = 0; k < p->paths.size(); ++k) {
+        const auto &pa = p->paths[k];
+        int32_t *o = out6 + 6 * k;
+        o[0] = pa.i1;
+        o[1] = pa.l1;
+        o[2] = pa.l2;
+        o[3] = pa.l3;
+        o[4] = pa.ob;
+        o[5] = pa.parity3;
+    }
+    return OEQ_OK;
+}
+
+oeq_status oeq_cg_table(int32_t l1, int32_t l2, int32_t l3, double *out) {
+    if (!out) return fail(OEQ_ERR_INVALID_ARG, "output is NULL");
+    std::vector<double> t;
+    if (!oeq::cg_real_table(l1, l2, l3, t)) return fail(OEQ_ERR_INVALID_ARG, "no table for these degrees");
+    std::memcpy(out, t.data(), sizeof(double) * t.size());
+    return OEQ_OK;
+}
+
+oeq_status oeq_workspace_size(const oeq_plan *p, int64_t n_nodes, int64_t n_edges, oeq_bwd_mode mode,
+                              size_t *bytes) {
+    if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
+    if (n_nodes < 0 || n_edges < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
+    if (mode == OEQ_BWD_ATOMIC) {
+        *bytes = 0;
+        return OEQ_OK;
+    }
+    if (mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    DetWorkspace w;
+    oeq_status st = det_layout(p, n_nodes, n_edges, nullptr, &w);
+    if (st != OEQ_OK) return st;
+    *bytes = w.bytes;
+    return OEQ_OK;
+}
+
+oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,
+                           const void *x, const void *Y, const void *W, void *out, void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
+    if (E > 0 && (!x || !Y || !W)) return fail(OEQ_ERR_INVALID_ARG, "x, Y or W is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *args[] = {&rowptr, &src, &x, &Y, &W, &out};
+    return launch(p, "oeq_fwd", static_cast<unsigned>(N), static_cast<unsigned>(p->uch * 64), s, args);
+}
+
+oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,
+                           const void *x, const void *Y, const void *W, const void *g, void *gx, void *gY, void *gW,
+                           oeq_bwd_mode mode, void *workspace, size_t workspace_bytes, void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    if (E > 0 && (!x || !Y || !W || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, Y, W or grad_out is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (E == 0) return gx ? fill_zero(p, gx, N * p->XD, s) : OEQ_OK;
+    if (!gx && !gY && !gW) return OEQ_OK;
+    int flags = (gW ? 1 : 0) | (gY ? 2 : 0);
+    const unsigned grid = static_cast<unsigned>(N), block = static_cast<unsigned>(p->uch * 64);
+    if (!gx) {
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gY, &gW, &flags};
+        return launch(p, "oeq_bwd_nogx", grid, block, s, args);
+    }
+    if (mode == OEQ_BWD_ATOMIC) {
+        st = fill_zero(p, gx, N * p->XD, s);
+        if (st != OEQ_OK) return st;
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gY, &gW, &flags};
+        return launch(p, "oeq_bwd_atomic", grid, block, s, args);
+    }
+    DetWorkspace w;
+    st = det_prepare(p, N, E, src, workspace, workspace_bytes, s, &w);
+    if (st != OEQ_OK) return st;
+    void *h = w.h;
+    void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &h, &gY, &gW, &flags};
+    st = launch(p, "oeq_bwd_rows", grid, block, s, args);
+    if (st != OEQ_OK) return st;
+    return det_finish(p, N, w, gx, s);
+}
+
+oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,
+                            const void *x, const void *Y, const void *W, const void *g, const void *ggx,
+                            const void *ggY, const void *ggW, void *dx, void *dY, void *dW, void *dg,
+                            oeq_bwd_mode mode, void *workspace, size_t workspace_bytes, void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    if (E > 0 && (!x || !Y || !W || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, Y, W or grad_out is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int tm = (ggx ? 1 : 0) | (ggY ? 2 : 0) | (ggW ? 4 : 0);
+    const int64_t PU = static_cast<int64_t>(p->paths.size()) * p->U;
+    if (E == 0 || tm == 0) {
+        if (dx && (st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+        if (dY && (st = fill_zero(p, dY, E * p->YD, s)) != OEQ_OK) return st;
+        if (dW && (st = fill_zero(p, dW, E * PU, s)) != OEQ_OK) return st;
+        if (dg && (st = fill_zero(p, dg, N * p->OD, s)) != OEQ_OK) return st;
+        return OEQ_OK;
+    }
+    int dxmode = 0;
+    DetWorkspace w;
+    void *dx_target = nullptr;
+    if (dx) {
+        if (!(tm & 6)) {
+            // d_x = Bx(ggY,W,g) + Bx(Y,ggW,g) vanishes without a Y or W tangent
+            if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+        } else if (mode == OEQ_BWD_ATOMIC) {
+            if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+            dxmode = 1;
+            dx_target = dx;
+        } else {
+            if ((st = det_prepare(p, N, E, src, workspace, workspace_bytes, s, &w)) != OEQ_OK) return st;
+            dxmode = 2;
+            dx_target = w.h;
+        }
+    }
+    if (!dxmode && !dY && !dW && !dg) return OEQ_OK;
+    int flags = (dW ? 1 : 0) | (dY ? 2 : 0) | (dg ? 4 : 0) | (dxmode << 3);
+    const std::string name = "oeq_dbwd_" + std::to_string(tm);
+    void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dY, &dW, &dg, &flags};
+    st = launch(p, name.c_str(), static_cast<unsigned>(N), static_cast<unsigned>(p->uch * 64), s, args);
+    if (st != OEQ_OK) return st;
+    if (dxmode == 2) return det_finish(p, N, w, dx, s);
+    return OEQ_OK;
+}
+
+oeq_status oeq_csr_workspace_size(int64_t n_nodes, int64_t n_edges, size_t *bytes) {
+    if (!bytes || n_nodes < 0 || n_edges < 0) return fail(OEQ_ERR_INVALID_ARG, "bad arguments");
+    const hipError_t e = oeq::sender_csr_workspace(n_nodes, n_edges, bytes);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, hipGetErrorString(e));
+    return OEQ_OK;
+}
+
+oeq_status oeq_sender_csr(int64_t n_nodes, int64_t n_edges, const int32_t *src, int32_t *srowptr, int32_t *sperm,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_nodes < 0 || n_edges < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
+    if (n_nodes >= std::numeric_limits<int32_t>::max() || n_edges >= std::numeric_limits<int32_t>::max())
+        return fail(OEQ_ERR_UNSUPPORTED, "sizes must fit int32");
+    if (!srowptr || (n_edges > 0 && (!src || !sperm))) return fail(OEQ_ERR_INVALID_ARG, "NULL array");
+    size_t need = 0;
+    oeq_status st = oeq_csr_workspace_size(n_nodes, n_edges, &need);
+    if (st != OEQ_OK) return st;
+    if (!workspace || workspace_bytes < need) return fail(OEQ_ERR_WORKSPACE, "workspace too small");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+        return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    const hipError_t e = oeq::sender_csr(n_nodes, n_edges, src, srowptr, sperm, workspace,
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, hipGetErrorString(e));
+    return OEQ_OK;
+}
+
+oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr, const int32_t *src, void *stream) {
+    if (n_nodes < 0 || n_edges < 0 || !rowptr || (n_edges > 0 && !src))
+        return fail(OEQ_ERR_INVALID_ARG, "bad arguments");
+    int bad = 0;
+    const hipError_t e = oeq::csr_check(n_nodes, n_edges, rowptr, src, static_cast<hipStream_t>(stream), &bad);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, hipGetErrorString(e));
+    if (bad) return fail(OEQ_ERR_INVALID_ARG, "invalid CSR (mask " + std::to_string(bad) + ")");
+    return OEQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,323 @@
+// Kernel templates of the fused UVU CG tensor-product convolution (gfx950).
+//
+// This text is compiled at plan time with hipRTC, after a prelude emitted by
+// the planner that defines, for one descriptor and dtype:
+//   real_t; U, UCH (64-channel chunks), NXC / NOC (values per channel of an x
+//   row / output row), P (paths), YD ((L+1)^2), PY (YD rounded up to a power of
+//   two), LGPY (log2 PY), GY_TILE, XD, OD;
+//   g_load_x / g_load_g / g_store_out / g_store_x / g_atomic_x: per-lane
+//   moves between a node row and registers (lane u holds channel u);
+//   g_fwd_edge: out += f(x, Y, W) for one edge, the unrolled sparse CG stream;
+//   g_bwd_edge<GW, GY, GX>: the three VJP components of one edge (accumulating).
+//
+// Ownership follows "Receiver-streaming convolutions for channel-wise UVU tensor
+// products" (opening post): a workgroup owns one receiver, its UCH waves split the
+// channels (lane = channel), and the waves stream that receiver's edges in CSR
+// order.  The forward keeps the output row in registers and stores it once (no
+// atomics).  The backward passes treat one edge at a time per wave: W-gradients
+// are stored directly, Y-gradients are reduced across the 64 lanes and then
+// across the waves through LDS, x-gradients go to the senders either by
+// hardware atomics or as per-edge rows summed later per sender.
+
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int N>
+__device__ __forceinline__ void zero(real_t (&a)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) a[i] = real_t(0);
+}
+
+// Y row of edge e (wave-uniform: scalar loads).
+__device__ __forceinline__ void load_y(const real_t *__restrict__ Y, int e, real_t (&yv)[YD]) {
+    const real_t *yr = Y + (i64)e * YD;
+#pragma unroll
+    for (int k = 0; k < YD; ++k) yv[k] = yr[k];
+}
+
+// W[e, :, u] (one value per path; consecutive lanes read consecutive channels).
+__device__ __forceinline__ void load_w(const real_t *__restrict__ W, int e, int u, real_t (&wv)[P]) {
+    const real_t *wr = W + (i64)e * (P * U) + u;
+#pragma unroll
+    for (int p = 0; p < P; ++p) wv[p] = wr[p * U];
+}
+
+__device__ __forceinline__ void store_w(real_t *__restrict__ G, int e, int u, const real_t (&wv)[P]) {
+    real_t *wr = G + (i64)e * (P * U) + u;
+#pragma unroll
+    for (int p = 0; p < P; ++p) wr[p * U] = wv[p];
+}
+
+// Sum of PY values over the 64 lanes of a wave, in a fixed order.  On return,
+// lane l holds in v[0] the total of value (l >> (6 - LGPY)); the lanes whose low
+// (6 - LGPY) bits are zero are the ones to write it.  Each halving step keeps
+// half of the values and adds the partner lane's copy of them (reduce-scatter),
+// the remaining steps are a plain butterfly.
+__device__ __forceinline__ void wave_reduce_scatter(real_t (&v)[PY], int lane) {
+#pragma unroll
+    for (int st = 0; st < LGPY; ++st) {
+        const int d = 32 >> st;
+        const int h = PY >> (st + 1);
+        const bool hi = (lane & d) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const real_t keep = hi ? v[i + h] : v[i];
+            const real_t send = hi ? v[i] : v[i + h];
+            v[i] = keep + __shfl_xor(send, d, 64);
+        }
+    }
+#pragma unroll
+    for (int d = (32 >> LGPY); d >= 1; d >>= 1) v[0] += __shfl_xor(v[0], d, 64);
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_fill_zero(real_t *__restrict__ p, i64 n) {
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x)
+        p[i] = real_t(0);
+}
+
+// ---------------------------------------------------------------------------
+// Forward: out[r] = sum over the receiver's edges of the per-edge messages.
+// ---------------------------------------------------------------------------
+extern "C" __global__ void __launch_bounds__(UCH * 64)
+oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src,
+        const real_t *__restrict__ x, const real_t *__restrict__ Y,
+        const real_t *__restrict__ W, real_t *__restrict__ out) {
+    const int r = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int u = uni(threadIdx.x >> 6) * 64 + lane;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;  // inactive lanes read channel 0 and store nothing
+    real_t acc[NOC];
+    zero(acc);
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    if (e0 < e1) {
+        // software pipeline: the next edge's loads are in flight while this one computes
+        int s = uni(src[e0]);
+        real_t yv[YD], xv[NXC], wv[P];
+        load_y(Y, e0, yv);
+        g_load_x(x + (i64)s * XD, uu, xv);
+        load_w(W, e0, uu, wv);
+        for (int e = e0; e < e1; ++e) {
+            real_t yn[YD], xn[NXC], wn[P];
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            load_y(Y, en, yn);
+            g_load_x(x + (i64)sn * XD, uu, xn);
+            load_w(W, en, uu, wn);
+            g_fwd_edge(xv, yv, wv, acc);
+#pragma unroll
+            for (int k = 0; k < YD; ++k) yv[k] = yn[k];
+#pragma unroll
+            for (int k = 0; k < NXC; ++k) xv[k] = xn[k];
+#pragma unroll
+            for (int k = 0; k < P; ++k) wv[k] = wn[k];
+        }
+    }
+    if (act) g_store_out(out + (i64)r * OD, u, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Y-gradient staging: per-wave lane-reduced rows in LDS, summed over the waves
+// of the workgroup (fixed order) every GY_TILE edges.
+// ---------------------------------------------------------------------------
+struct GyStage {
+    real_t red[UCH][GY_TILE][PY];
+};
+
+__device__ __forceinline__ void gy_push(GyStage &st, real_t *__restrict__ gY, int e, int j,
+                                        real_t (&gy)[YD], int lane, int wv) {
+    real_t v[PY];
+#pragma unroll
+    for (int k = 0; k < PY; ++k) v[k] = (k < YD) ? gy[k] : real_t(0);
+    wave_reduce_scatter(v, lane);
+    const int idx = lane >> (6 - LGPY);
+    const bool writer = (lane & ((1 << (6 - LGPY)) - 1)) == 0;
+    if (UCH == 1) {
+        if (writer && idx < YD) gY[(i64)e * YD + idx] = v[0];
+    } else {
+        if (writer) st.red[wv][j][idx] = v[0];
+    }
+}
+
+__device__ __forceinline__ void gy_flush(GyStage &st, real_t *__restrict__ gY, int base, int n) {
+    if (UCH == 1) return;
+    __syncthreads();
+    for (int k = threadIdx.x; k < n * YD; k += UCH * 64) {
+        const int j = k / YD, m = k - j * YD;
+        real_t s = st.red[0][j][m];
+#pragma unroll
+        for (int w = 1; w < UCH; ++w) s += st.red[w][j][m];
+        gY[(i64)(base + j) * YD + m] = s;
+    }
+    __syncthreads();
+}
+
+// flags: bit0 store grad_W, bit1 store grad_Y
+// GXMODE: 0 no x gradient, 1 atomic add into gx[src[e]], 2 store row h[e] (summed per sender later)
+template <int GXMODE>
+__device__ __forceinline__ void bwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
+                                         const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                         const real_t *__restrict__ W, const real_t *__restrict__ g,
+                                         real_t *__restrict__ gx, real_t *__restrict__ gY,
+                                         real_t *__restrict__ gW, int flags) {
+    __shared__ GyStage st;
+    const int r = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv = uni(threadIdx.x >> 6);
+    const int u = wv * 64 + lane;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;
+    const bool want_gw = (flags & 1) != 0, want_gy = (flags & 2) != 0;
+    real_t gv[NOC];
+    g_load_g(g + (i64)r * OD, uu, gv);
+    if (!act) zero(gv);  // inactive lanes contribute nothing to the lane sums
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    for (int base = e0; base < e1; base += GY_TILE) {
+        const int n = (e1 - base < GY_TILE) ? e1 - base : GY_TILE;
+        for (int j = 0; j < n; ++j) {
+            const int e = base + j;
+            const int s = uni(src[e]);
+            real_t yv[YD], xv[NXC], wv_[P];
+            load_y(Y, e, yv);
+            g_load_x(x + (i64)s * XD, uu, xv);
+            load_w(W, e, uu, wv_);
+            real_t gw[P], gy[YD], gxp[NXC];
+            zero(gw);
+            zero(gy);
+            zero(gxp);
+            g_bwd_edge<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
+            if (want_gw && act) store_w(gW, e, u, gw);
+            if (want_gy) gy_push(st, gY, e, j, gy, lane, wv);
+            if (GXMODE == 1 && act) g_atomic_x(gx + (i64)s * XD, u, gxp);
+            if (GXMODE == 2 && act) g_store_x(gx + (i64)e * XD, u, gxp);
+        }
+        if (want_gy) gy_flush(st, gY, base, n);
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64)
+oeq_bwd_nogx(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+             const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
+             real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
+    bwd_body<0>(rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64)
+oeq_bwd_atomic(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+               const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
+               real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
+    bwd_body<1>(rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64)
+oeq_bwd_rows(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+             const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
+             real_t *__restrict__ h, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
+    bwd_body<2>(rowptr, src, x, Y, W, g, h, gY, gW, flags);
+}
+
+// ---------------------------------------------------------------------------
+// Deterministic x gradient: gx[s] = sum of h[e] over the sender's edges, in the
+// sender CSR's (increasing edge id) order.
+// ---------------------------------------------------------------------------
+extern "C" __global__ void __launch_bounds__(256)
+oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
+               const real_t *__restrict__ h, real_t *__restrict__ gx, int n_nodes) {
+    const int s = blockIdx.x;
+    if (s >= n_nodes) return;
+    const int k0 = uni(srowptr[s]), k1 = uni(srowptr[s + 1]);
+    for (i64 c = threadIdx.x; c < XD; c += 256) {
+        real_t acc = real_t(0);
+        for (int k = k0; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * XD + c];
+        gx[(i64)s * XD + c] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Double backward.  TM: which tangents are present (1 gg_x, 2 gg_Y, 4 gg_W).
+//   d_grad_out = f(ggx,Y,W) + f(x,ggY,W) + f(x,Y,ggW)      (receiver-local)
+//   d_W = BW(ggx,Y,g) + BW(x,ggY,g),  d_Y = BY(ggx,W,g) + BY(x,ggW,g)
+//   d_x = Bx(ggY,W,g) + Bx(Y,ggW,g)                         (to senders)
+// flags: bit0 d_W, bit1 d_Y, bit2 d_grad_out, bits 3-4 d_x mode (0 none, 1 atomic, 2 rows)
+// ---------------------------------------------------------------------------
+template <int TM>
+__device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
+                                          const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                          const real_t *__restrict__ W, const real_t *__restrict__ g,
+                                          const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,
+                                          const real_t *__restrict__ ggW, real_t *__restrict__ dx,
+                                          real_t *__restrict__ dY, real_t *__restrict__ dW,
+                                          real_t *__restrict__ dg, int flags) {
+    __shared__ GyStage st;
+    const int r = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wv = uni(threadIdx.x >> 6);
+    const int u = wv * 64 + lane;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;
+    const bool want_dw = (flags & 1) != 0, want_dy = (flags & 2) != 0, want_dg = (flags & 4) != 0;
+    const int dxmode = (flags >> 3) & 3;
+    constexpr bool HAS_DX = (TM & 6) != 0;
+    real_t gv[NOC];
+    g_load_g(g + (i64)r * OD, uu, gv);
+    if (!act) zero(gv);
+    real_t dgacc[NOC];
+    zero(dgacc);
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    for (int base = e0; base < e1; base += GY_TILE) {
+        const int n = (e1 - base < GY_TILE) ? e1 - base : GY_TILE;
+        for (int j = 0; j < n; ++j) {
+            const int e = base + j;
+            const int s = uni(src[e]);
+            real_t yv[YD], xv[NXC], wv_[P];
+            load_y(Y, e, yv);
+            g_load_x(x + (i64)s * XD, uu, xv);
+            load_w(W, e, uu, wv_);
+            real_t dw[P], dy[YD], dxp[NXC];
+            zero(dw);
+            zero(dy);
+            zero(dxp);
+            if (TM & 1) {
+                real_t tx[NXC];
+                g_load_x(ggx + (i64)s * XD, uu, tx);
+                if (want_dg) g_fwd_edge(tx, yv, wv_, dgacc);
+                g_bwd_edge<true, true, false>(tx, yv, wv_, gv, dw, dy, dxp);
+            }
+            if (TM & 2) {
+                real_t ty[YD];
+                load_y(ggY, e, ty);
+                if (want_dg) g_fwd_edge(xv, ty, wv_, dgacc);
+                g_bwd_edge<true, false, true>(xv, ty, wv_, gv, dw, dy, dxp);
+            }
+            if (TM & 4) {
+                real_t tw[P];
+                load_w(ggW, e, uu, tw);
+                if (want_dg) g_fwd_edge(xv, yv, tw, dgacc);
+                g_bwd_edge<false, true, true>(xv, yv, tw, gv, dw, dy, dxp);
+            }
+            if (want_dw && act) store_w(dW, e, u, dw);
+            if (want_dy) gy_push(st, dY, e, j, dy, lane, wv);
+            if (HAS_DX && dxmode == 1 && act) g_atomic_x(dx + (i64)s * XD, u, dxp);
+            if (HAS_DX && dxmode == 2 && act) g_store_x(dx + (i64)e * XD, u, dxp);
+        }
+        if (want_dy) gy_flush(st, dY, base, n);
+    }
+    if (want_dg && act) g_store_out(dg + (i64)r * OD, u, dgacc);
+}
+
+#define OEQ_DBWD_KERNEL(TM)                                                                       \
+    extern "C" __global__ void __launch_bounds__(UCH * 64) oeq_dbwd_##TM(                          \
+        const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x, \
+        const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,  \
+        const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,                            \
+        const real_t *__restrict__ ggW, real_t *__restrict__ dx, real_t *__restrict__ dY,          \
+        real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {                             \
+        dbwd_body<TM>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);              \
+    }
+OEQ_DBWD_KERNEL(1)
+OEQ_DBWD_KERNEL(2)
+OEQ_DBWD_KERNEL(3)
+OEQ_DBWD_KERNEL(4)
+OEQ_DBWD_KERNEL(5)
+OEQ_DBWD_KERNEL(6)
+OEQ_DBWD_KERNEL(7)

@@ -1,0 +1,160 @@
+// Path planning: descriptor validation, path enumeration, sparse CG tables and
+// row layouts.
+//
+// A path couples x block i1 (degree l1, parity p1) with the Y harmonics of
+// degree l2 into an output of degree l3; with no explicit list, every l3 allowed
+// by the triangle rule |l1-l2| <= l3 <= l1+l2 (and l3 <= lmax_out) is used, with
+// output parity p1 (-1)^l2, x blocks in descriptor order, then l2 ascending, then
+// l3 ascending.  Each path keeps only the non-zero entries of its real-basis CG
+// table (compact storage of the structurally non-zero part, as the UMA kernel
+// work compacts its rotation blocks in "Optimize UMA SO2 and Wigner inference
+// kernels").
+#include <cstdlib>
+#include <sstream>
+
+#include "planner.hpp"
+
+namespace oeq {
+
+namespace {
+
+oeq_status fail(std::string *why, oeq_status st, const std::string &msg) {
+    if (why) *why = msg;
+    return st;
+}
+
+}  // namespace
+
+oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
+    if (!d) return fail(why, OEQ_ERR_INVALID_ARG, "descriptor is NULL");
+    if (d->dtype != OEQ_F32 && d->dtype != OEQ_F64)
+        return fail(why, OEQ_ERR_UNSUPPORTED, "dtype must be OEQ_F32 or OEQ_F64");
+    if (!d->x_irreps || d->n_x <= 0 || d->n_x > 16)
+        return fail(why, OEQ_ERR_INVALID_ARG, "x_irreps must hold 1..16 blocks");
+    if (d->y_lmax < 0 || d->y_lmax > kLMax)
+        return fail(why, OEQ_ERR_UNSUPPORTED, "y_lmax must be in 0..3");
+    p->dtype = d->dtype;
+    p->L = d->y_lmax;
+    p->YD = (d->y_lmax + 1) * (d->y_lmax + 1);
+    p->U = d->x_irreps[0].mul;
+    if (p->U <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "multiplicity must be >= 1");
+    if (p->U > 4096) return fail(why, OEQ_ERR_UNSUPPORTED, "multiplicity above 4096");
+    int lane = 0;
+    for (int i = 0; i < d->n_x; ++i) {
+        const oeq_irrep &ir = d->x_irreps[i];
+        if (ir.mul != p->U)
+            return fail(why, OEQ_ERR_UNSUPPORTED, "channel-wise product needs one multiplicity for all x blocks");
+        if (ir.l < 0 || ir.l > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "x degree must be in 0..3");
+        if (ir.parity != 1 && ir.parity != -1) return fail(why, OEQ_ERR_INVALID_ARG, "parity must be +1 or -1");
+        p->xb.push_back({ir.l, ir.parity, lane, static_cast<int64_t>(p->U) * lane});
+        lane += 2 * ir.l + 1;
+    }
+    p->NXC = lane;
+    p->XD = static_cast<int64_t>(p->U) * lane;
+
+    // Output blocks and the path list.
+    struct Raw { int i1, l2, ob; };
+    std::vector<Raw> raw;
+    std::vector<std::pair<int, int>> out_lp;  // (l, parity) of each output block
+    if (d->paths == nullptr) {
+        if (d->lmax_out < 0 || d->lmax_out > kLMax)
+            return fail(why, OEQ_ERR_UNSUPPORTED, "lmax_out must be in 0..3");
+        if (d->out_irreps) {
+            if (d->n_out <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "n_out must be positive");
+            for (int o = 0; o < d->n_out; ++o) {
+                const oeq_irrep &ir = d->out_irreps[o];
+                if (ir.mul != p->U) return fail(why, OEQ_ERR_UNSUPPORTED, "output multiplicity must equal U");
+                if (ir.l < 0 || ir.l > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "output degree must be in 0..3");
+                if (ir.parity != 1 && ir.parity != -1)
+                    return fail(why, OEQ_ERR_INVALID_ARG, "parity must be +1 or -1");
+                out_lp.push_back({ir.l, ir.parity});
+            }
+        }
+        for (int i = 0; i < d->n_x; ++i) {
+            const int l1 = d->x_irreps[i].l, p1 = d->x_irreps[i].parity;
+            for (int l2 = 0; l2 <= d->y_lmax; ++l2) {
+                const int p3 = p1 * ((l2 % 2) ? -1 : 1);
+                const int hi = std::min(l1 + l2, static_cast<int>(d->lmax_out));
+                for (int l3 = std::abs(l1 - l2); l3 <= hi; ++l3) {
+                    if (d->out_irreps) {
+                        // paths into a given output irrep are summed into its block
+                        int ob = -1;
+                        for (size_t o = 0; o < out_lp.size(); ++o)
+                            if (out_lp[o].first == l3 && out_lp[o].second == p3) {
+                                ob = static_cast<int>(o);
+                                break;
+                            }
+                        if (ob >= 0) raw.push_back({i, l2, ob});
+                    } else {
+                        raw.push_back({i, l2, static_cast<int>(out_lp.size())});
+                        out_lp.push_back({l3, p3});
+                    }
+                }
+            }
+        }
+    } else {
+        if (!d->out_irreps || d->n_out <= 0)
+            return fail(why, OEQ_ERR_INVALID_ARG, "an explicit path list needs out_irreps");
+        if (d->n_paths <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "n_paths must be positive");
+        for (int o = 0; o < d->n_out; ++o) {
+            const oeq_irrep &ir = d->out_irreps[o];
+            if (ir.mul != p->U) return fail(why, OEQ_ERR_UNSUPPORTED, "output multiplicity must equal U");
+            if (ir.l < 0 || ir.l > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "output degree must be in 0..3");
+            if (ir.parity != 1 && ir.parity != -1) return fail(why, OEQ_ERR_INVALID_ARG, "parity must be +1 or -1");
+            out_lp.push_back({ir.l, ir.parity});
+        }
+        for (int k = 0; k < d->n_paths; ++k) {
+            const oeq_path &pa = d->paths[k];
+            if (pa.in1 < 0 || pa.in1 >= d->n_x) return fail(why, OEQ_ERR_INVALID_ARG, "path in1 out of range");
+            if (pa.in2 < 0 || pa.in2 > d->y_lmax) return fail(why, OEQ_ERR_INVALID_ARG, "path l2 out of range");
+            if (pa.out < 0 || pa.out >= d->n_out) return fail(why, OEQ_ERR_INVALID_ARG, "path out out of range");
+            const int l1 = d->x_irreps[pa.in1].l, l3 = out_lp[pa.out].first;
+            if (l3 < std::abs(l1 - pa.in2) || l3 > l1 + pa.in2)
+                return fail(why, OEQ_ERR_INVALID_ARG, "path violates the triangle rule");
+            const int p3 = d->x_irreps[pa.in1].parity * ((pa.in2 % 2) ? -1 : 1);
+            if (p3 != out_lp[pa.out].second) return fail(why, OEQ_ERR_INVALID_ARG, "path violates parity");
+            raw.push_back({pa.in1, pa.in2, pa.out});
+        }
+    }
+    if (raw.empty()) return fail(why, OEQ_ERR_INVALID_ARG, "the descriptor has no paths");
+    if (raw.size() > 128) return fail(why, OEQ_ERR_UNSUPPORTED, "more than 128 paths");
+
+    lane = 0;
+    for (const auto &lp : out_lp) {
+        p->ob.push_back({lp.first, lp.second, lane, static_cast<int64_t>(p->U) * lane});
+        lane += 2 * lp.first + 1;
+    }
+    p->NOC = lane;
+    p->OD = static_cast<int64_t>(p->U) * lane;
+
+    p->total_nnz = 0;
+    for (const Raw &r : raw) {
+        Path pa;
+        pa.i1 = r.i1;
+        pa.l1 = p->xb[r.i1].l;
+        pa.l2 = r.l2;
+        pa.l3 = p->ob[r.ob].l;
+        pa.ob = r.ob;
+        pa.parity3 = p->ob[r.ob].parity;
+        std::vector<double> t;
+        if (!cg_real_table(pa.l1, pa.l2, pa.l3, t)) return fail(why, OEQ_ERR_INVALID_ARG, "invalid path");
+        const int n2 = 2 * pa.l2 + 1, n3 = 2 * pa.l3 + 1;
+        for (int a = 0; a < 2 * pa.l1 + 1; ++a)
+            for (int b = 0; b < n2; ++b)
+                for (int c = 0; c < n3; ++c) {
+                    const double v = t[(static_cast<size_t>(a) * n2 + b) * n3 + c];
+                    if (v != 0.0) pa.nz.push_back({a, b, c, v});
+                }
+        p->total_nnz += static_cast<int>(pa.nz.size());
+        p->paths.push_back(std::move(pa));
+    }
+
+    p->uch = (p->U + 63) / 64;
+    if (const char *s = std::getenv("OEQ_GY_TILE")) {
+        const int v = std::atoi(s);
+        if (v >= 1 && v <= 256) p->gy_tile = v;
+    }
+    return OEQ_OK;
+}
+
+}  // namespace oeq

@@ -1,0 +1,91 @@
+// Host-side plan of a channel-wise (UVU) CG tensor-product convolution: the
+// validated irreps, the path list with its sparse real-basis CG tables, the row
+// layouts, the emitted HIP source and the runtime-compiled code object.
+#pragma once
+
+#include <cstdint>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "oeq.h"
+
+namespace oeq {
+
+constexpr int kLMax = 3;
+
+// Dense real-basis CG table for (l1, l2, l3) (see cg_tables.cpp); false outside
+// the triangle rule or l > 3.
+bool cg_real_table(int l1, int l2, int l3, std::vector<double> &out);
+
+struct NonZero {
+    int m1, m2, m3;  // 0-based: m + l
+    double c;
+};
+
+struct Path {
+    int i1;          // x block
+    int l1, l2, l3;
+    int ob;          // output block
+    int parity3;
+    std::vector<NonZero> nz;
+};
+
+struct Block {
+    int l, parity;
+    int lane_off;    // offset of this block among one channel's values (sum of 2l+1 before it)
+    int64_t row_off; // offset of this block in a node row (U * lane_off)
+};
+
+// Kernels of one compiled module, on one device.
+struct DeviceModule {
+    hipModule_t module = nullptr;
+    std::map<std::string, hipFunction_t> fn;
+};
+
+struct oeq_plan_impl;
+
+}  // namespace oeq
+
+struct oeq_plan {
+    oeq_dtype dtype;
+    int U = 0;
+    int L = 0;                  // Y degrees 0..L
+    int YD = 0;                 // (L+1)^2
+    int NXC = 0, NOC = 0;       // per-channel x and output widths
+    int64_t XD = 0, OD = 0;     // node row widths
+    std::vector<oeq::Block> xb, ob;
+    std::vector<oeq::Path> paths;
+    int total_nnz = 0;
+
+    // Launch shape.
+    int uch = 1;                // 64-channel chunks (waves per receiver)
+    int gy_tile = 32;           // edges per LDS gY flush in the backward kernels
+
+    std::string source;         // emitted HIP source
+    std::vector<char> code;     // gfx950 code object
+    std::string code_key;       // cache key (hash of source + options)
+
+    std::mutex mu;
+    std::map<int, oeq::DeviceModule> modules;  // per device id
+};
+
+namespace oeq {
+
+// Validates the descriptor and fills the structural part of the plan (paths,
+// tables, layouts).  Returns OEQ_OK or an error with a message in *why.
+oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why);
+
+// Emits the HIP source of every kernel of the plan.
+std::string emit_source(const oeq_plan &p);
+
+// Compiles p.source with hipRTC (or loads it from the on-disk cache).
+oeq_status jit_compile(oeq_plan &p, std::string *why);
+
+// Loads the module on the current device (once) and returns the kernel.
+oeq_status get_kernel(oeq_plan &p, const char *name, hipFunction_t *fn, std::string *why);
+
+}  // namespace oeq

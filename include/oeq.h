@@ -1,0 +1,192 @@
+/*
+ * oeq.h - C ABI of the fused channel-wise (UVU) Clebsch-Gordan tensor-product
+ * graph convolution for AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Receiver-streaming convolutions for channel-wise UVU tensor
+ * products", opening post; the CG tensor product and its fusion with graph
+ * convolution as in the abstract of "An Efficient Sparse Kernel Generator for
+ * O(3)-Equivariant Deep Networks"):
+ *
+ *   for every edge e = (s -> r) of a receiver-sorted graph, every path
+ *   p = (x block i1 of degree l1, Y degree l2 -> output degree l3) and every
+ *   channel u < U:
+ *     out[r, blk(p), u, m3] += sum_{m1,m2} C_{l1 l2 l3}[m1,m2,m3]
+ *                              * x[s, i1, u, m1] * Y[e, l2, m2] * W[e, p, u]
+ *
+ * C is the real-basis Clebsch-Gordan table (orthonormal, real spherical-harmonic
+ * basis with the Condon-Shortley phase, m = -l..l, l=1 ordered (y, z, x), each
+ * table signed so that its first non-zero entry in row-major (m1, m2, m3) order is
+ * positive).  W carries every weight: there is no extra normalisation factor.
+ *
+ * Memory layouts (all row-major, element offsets computed in 64 bits):
+ *   rowptr [N+1] int32   receiver CSR, rowptr[0] = 0, rowptr[N] = E, non-decreasing
+ *   src    [E]   int32   sender of edge e; edge e belongs to receiver r when
+ *                        rowptr[r] <= e < rowptr[r+1]
+ *   x      [N, XD]       x block i at xoff_i, element u*(2 l_i + 1) + (m + l_i)
+ *   Y      [E, (L+1)^2]  element l2*l2 + (m2 + l2)
+ *   W      [E, P, U]
+ *   out    [N, OD]       output block o at ooff_o, element u*(2 l_o + 1) + (m + l_o)
+ * Gradients use the layout of the tensor they belong to.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor is caller-allocated device memory, element type = the plan's
+ *     dtype (float or double), naturally aligned.  The library never allocates
+ *     device memory inside a compute call; scratch memory is the caller's
+ *     workspace (see oeq_workspace_size).
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  Outputs are overwritten, never accumulated into.
+ *   - Arguments are checked on the host only (no device reads, no
+ *     synchronisation).  Graph preconditions (CSR shape above, 0 <= src[e] < N)
+ *     are the caller's responsibility and are not checked; violating them is
+ *     undefined behaviour.  oeq_csr_check validates them synchronously.
+ *   - Errors are reported as oeq_status codes, never by aborting;
+ *     oeq_last_error() gives a per-thread message for the last failure.  Faults
+ *     during kernel execution surface at the caller's next synchronisation.
+ *   - A plan is immutable after creation and may be used from several threads
+ *     and streams at once.
+ *   - Supported: degrees l <= 3 for x, Y and outputs; every x block with the
+ *     same multiplicity U >= 1; dtype float32 or float64.
+ */
+#ifndef OEQ_H
+#define OEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    OEQ_OK = 0,
+    OEQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum        */
+    OEQ_ERR_UNSUPPORTED = 2, /* l > 3, mixed multiplicities, unknown dtype   */
+    OEQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
+    OEQ_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed   */
+    OEQ_ERR_JIT = 5          /* runtime compilation of the kernels failed    */
+} oeq_status;
+
+typedef enum { OEQ_F32 = 0, OEQ_F64 = 1 } oeq_dtype;
+
+/* How the x gradient is scattered to senders in the backward passes.
+ * ATOMIC: hardware floating-point atomics (summation order varies run to run).
+ * DETERMINISTIC: per-edge contributions are written to the workspace and
+ * summed per sender in increasing edge id (bitwise repeatable). */
+typedef enum { OEQ_BWD_ATOMIC = 0, OEQ_BWD_DETERMINISTIC = 1 } oeq_bwd_mode;
+
+typedef struct {
+    int32_t mul;    /* multiplicity (channels)                */
+    int32_t l;      /* degree 0..3                            */
+    int32_t parity; /* +1 even, -1 odd                        */
+} oeq_irrep;
+
+typedef struct {
+    int32_t in1; /* index into the x irreps                              */
+    int32_t in2; /* Y degree l2 (Y holds every degree 0..L)              */
+    int32_t out; /* index into the output irreps                         */
+} oeq_path;
+
+typedef struct {
+    const oeq_irrep *x_irreps; /* host memory                                   */
+    int32_t n_x;
+    int32_t y_lmax;            /* L: Y carries degrees 0..L, multiplicity 1 each */
+    const oeq_irrep *out_irreps; /* NULL: one output block per path, in path order */
+    int32_t n_out;
+    const oeq_path *paths;     /* NULL: enumerate every triangle-allowed path:   */
+    int32_t n_paths;           /*   x blocks in order, l2 = 0..L,                */
+                               /*   l3 = |l1-l2|..min(l1+l2, lmax_out),          */
+                               /*   output parity p1 * (-1)^l2                   */
+    int32_t lmax_out;          /* used when paths == NULL                        */
+    oeq_dtype dtype;
+} oeq_tp_desc;
+
+typedef struct oeq_plan oeq_plan; /* opaque, host-owned */
+
+/* Builds the path list and the real-basis CG tables, emits the specialised HIP
+ * kernels and compiles them for gfx950 (runtime compilation, cached on disk by a
+ * hash of the generated source in $OEQ_CACHE_DIR, default: a "jitcache" folder
+ * beside the library).  Host-only; the code object is loaded on a device at the
+ * first compute call there.  *plan is set to NULL on failure. */
+oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan);
+void oeq_plan_destroy(oeq_plan *plan);
+
+/* Row widths: x_dim = XD, y_dim = (L+1)^2, out_dim = OD, w_per_edge = P*U. */
+oeq_status oeq_plan_dims(const oeq_plan *plan, int64_t *x_dim, int64_t *y_dim,
+                         int64_t *out_dim, int64_t *n_paths, int64_t *w_per_edge);
+
+/* Path k of the plan as (x block, l1, l2, l3, output block, output parity),
+ * written to out6[6*k .. 6*k+5] for k < n_paths (host memory). */
+oeq_status oeq_plan_paths(const oeq_plan *plan, int32_t *out6, int32_t capacity);
+
+/* The plan's real-basis CG table for (l1, l2, l3) as a dense fp64 array
+ * [(2l1+1)(2l2+1)(2l3+1)] in host memory (the values the kernels use, before
+ * rounding to the plan dtype).  Returns OEQ_ERR_INVALID_ARG outside the
+ * triangle rule or l > 3. */
+oeq_status oeq_cg_table(int32_t l1, int32_t l2, int32_t l3, double *out);
+
+/* Workspace bytes a backward or double-backward call needs (0 for ATOMIC). */
+oeq_status oeq_workspace_size(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                              oeq_bwd_mode mode, size_t *bytes);
+
+/* Forward: out = f(x, Y, W).  Receiver-stationary: one lane owns one
+ * (receiver, channel), streams the receiver's edges and writes its output row
+ * once, without atomics ("Receiver-streaming convolutions ...", opening post,
+ * forward ownership).  Bitwise repeatable. */
+oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                           const int32_t *rowptr, const int32_t *src, const void *x,
+                           const void *Y, const void *W, void *out, void *stream);
+
+/* Vector-Jacobian product of <grad_out, f(x, Y, W)>:
+ *   grad_W[e,p,u] = sum C x[s,u,m1] Y[e,m2] grad_out[r,u,m3]
+ *   grad_Y[e,m2]  = sum_u sum_p sum C x[s,u,m1] W[e,p,u] grad_out[r,u,m3]
+ *   grad_x[s,u,m1]= sum_{e: src[e]=s} sum_p sum C Y[e,m2] W[e,p,u] grad_out[r,u,m3]
+ * Edge-stationary ("Receiver-streaming convolutions ...", opening post, backward
+ * ownership): a wave owns an edge at a time, lanes span channels, grad_W is
+ * written directly, grad_Y is reduced across lanes, grad_x is scattered per
+ * `mode`.  Any of grad_x, grad_Y, grad_W may be NULL (not computed).
+ * DETERMINISTIC needs `workspace` of oeq_workspace_size bytes (256-byte aligned). */
+oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                           const int32_t *rowptr, const int32_t *src, const void *x,
+                           const void *Y, const void *W, const void *grad_out,
+                           void *grad_x, void *grad_Y, void *grad_W, oeq_bwd_mode mode,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Double backward: gradients of
+ *   S = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_W, grad_W>
+ * (grad_* the VJP above) with respect to x, Y, W and grad_out.  Since f is
+ * linear in each of x, Y, W separately,
+ *   d_grad_out = f(gg_x,Y,W) + f(x,gg_Y,W) + f(x,Y,gg_W)
+ *   d_x = Bx(gg_Y,W,g) + Bx(Y,gg_W,g),   d_Y = BY(gg_x,W,g) + BY(x,gg_W,g),
+ *   d_W = BW(gg_x,Y,g) + BW(x,gg_Y,g)
+ * with Bx, BY, BW the three VJP components (the abstract of "An Efficient Sparse
+ * Kernel Generator ..." names an identity for these higher derivatives without
+ * printing it; this is the one used here).  A NULL tangent is zero; a NULL
+ * output is not computed. */
+oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                            const int32_t *rowptr, const int32_t *src, const void *x,
+                            const void *Y, const void *W, const void *grad_out,
+                            const void *gg_x, const void *gg_Y, const void *gg_W,
+                            void *d_x, void *d_Y, void *d_W, void *d_grad_out,
+                            oeq_bwd_mode mode, void *workspace, size_t workspace_bytes,
+                            void *stream);
+
+/* Sender CSR of a receiver CSR (stable counting sort by sender): srowptr[N+1],
+ * sperm[E] = edge ids grouped by sender, increasing within a sender.  Device
+ * arrays; uses `workspace` of oeq_csr_workspace_size bytes; asynchronous. */
+oeq_status oeq_csr_workspace_size(int64_t n_nodes, int64_t n_edges, size_t *bytes);
+oeq_status oeq_sender_csr(int64_t n_nodes, int64_t n_edges, const int32_t *src,
+                          int32_t *srowptr, int32_t *sperm, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Synchronously validates a receiver CSR on the device (rowptr monotone,
+ * rowptr[0] = 0, rowptr[N] = E, 0 <= src < N).  Test helper: synchronises. */
+oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr,
+                         const int32_t *src, void *stream);
+
+const char *oeq_status_string(oeq_status status);
+const char *oeq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OEQ_H */

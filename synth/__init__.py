@@ -174,6 +174,27 @@ def normal(rng: np.random.Generator, shape, dtype, scale: float = 1.0,
     return out.reshape(shape)
 
 
+# ---------------------------------------------------------------------------
+# Sub-graphs (selecting edges; used to evaluate sampled rows)
+# ---------------------------------------------------------------------------
+
+
+def subgraph(rowptr: np.ndarray, src: np.ndarray, edges: np.ndarray):
+    """Receiver CSR over the same N nodes that keeps only the listed edges
+    (sorted ascending, so receivers stay non-decreasing).  Returns
+    (rowptr_sub, src_sub, edges)."""
+    edges = np.asarray(sorted(set(int(e) for e in edges)), dtype=np.int64)
+    N = len(rowptr) - 1
+    recv = np.searchsorted(rowptr, edges, side="right") - 1
+    counts = np.bincount(recv, minlength=N)
+    rp = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return rp, src[edges].astype(np.int32), edges
+
+
+def edges_of_rows(rowptr: np.ndarray, rows) -> np.ndarray:
+    return np.concatenate([np.arange(rowptr[r], rowptr[r + 1]) for r in rows] + [np.zeros(0, np.int64)])
+
+
 def _children(seed: int):
     return [np.random.Generator(np.random.PCG64(c))
             for c in np.random.SeedSequence(seed).spawn(_NCHILD)]

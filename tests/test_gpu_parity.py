@@ -1,0 +1,278 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Small and medium problems are compared element by element on every output;
+the full 5,000-node / 280,000-edge workloads run in the same launch shape the
+benchmark times and are compared on sampled rows (receivers for the forward,
+edges for the W and Y gradients, senders for the x gradient), which the oracle
+evaluates on the sub-graph of exactly those edges.  Bound: relative L2 per
+output tensor <= 1e-5 (fp32) or 1e-12 (fp64); integer outputs bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import RTOL, edges_of_rows, inputs, oracle_desc, plan_for, rel_l2, sample, subgraph, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+oeq = pytest.importorskip("cg_tensor_product_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+W_ = synth.WORKLOADS
+# Reduced versions of the named workloads (full comparison): several receivers'
+# worth of edge tiles with a ragged tail (degree 56 = 32 + 24).
+REDUCED = {
+    "tiny_fp64": W_["tiny_fp64"],
+    "mace_medium_fp32": W_["mace_medium_fp32"].scaled(n_nodes=240),
+    "mace_medium_fp64": W_["mace_medium_fp64"].scaled(n_nodes=240),
+    "mace_large_fp32": W_["mace_large_fp32"].scaled(n_nodes=160),
+    "wide_proxy_fp32": W_["wide_proxy_fp32"].scaled(n_nodes=96),
+}
+_rng = np.random.default_rng(77)
+_deg = _rng.integers(0, 121, size=150)
+_deg[[0, 7, 149]] = 0
+EDGE_CASES = {
+    # U = 96: a full 64-lane wave plus a half-empty one; degrees 0..120 with empty rows
+    "ragged_u96_f32": synth.Workload("ragged_u96_f32", 150, 0, synth._irr("96x0e+96x1o+96x2e"), 3, 3,
+                                     "f32", "unit", 31, degrees=tuple(int(v) for v in _deg)),
+    # one channel, an l=3 x block, fp64
+    "u1_l3_f64": synth.Workload("u1_l3_f64", 40, 9, synth._irr("1x3o+1x1e"), 3, 3, "f64", "unit", 32),
+    # U = 8 with Y degrees 0..1 only (padded lane reduction) and outputs up to l=2
+    "u8_l1_f32": synth.Workload("u8_l1_f32", 50, 12, synth._irr("8x0e+8x1o+8x2e"), 1, 2, "f32", "unit", 33),
+}
+SMALL = {**REDUCED, **EDGE_CASES}
+
+
+def _dev_inputs(inp, dt):
+    d = {}
+    for k in ("rowptr", "src"):
+        d[k] = to_dev(inp[k])
+    for k in ("x", "Y", "W", "g", "v"):
+        if k in inp:
+            d[k] = to_dev(inp[k])
+    return d
+
+
+def _case(name):
+    wl = SMALL[name]
+    d, inp = inputs(wl, want=("x", "Y", "W", "g", "v"))
+    return wl, d, inp, _dev_inputs(inp, wl.dtype), plan_for(wl)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fwd_parity(name):
+    wl, d, inp, g, plan = _case(name)
+    print(f"[fwd] {name} N={wl.n_nodes} E={inp['E']}", flush=True)
+    out = oeq.oeq_tp_conv_fwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"])
+    torch.cuda.synchronize()
+    ref = oracle.fwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"])
+    assert rel_l2(out.cpu().numpy(), ref) <= RTOL[wl.dtype]
+    deg = np.diff(inp["rowptr"])
+    assert not out.cpu().numpy()[deg == 0].any()          # receivers without edges
+
+
+@pytest.mark.parametrize("mode", ["atomic", "deterministic"])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_bwd_parity(name, mode):
+    wl, d, inp, g, plan = _case(name)
+    print(f"[bwd] {name} {mode} N={wl.n_nodes} E={inp['E']}", flush=True)
+    gx, gY, gW = oeq.oeq_tp_conv_bwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], mode=mode)
+    torch.cuda.synchronize()
+    rx, rY, rW = oracle.bwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"])
+    tol = RTOL[wl.dtype]
+    assert rel_l2(gx.cpu().numpy(), rx) <= tol
+    assert rel_l2(gY.cpu().numpy(), rY) <= tol
+    assert rel_l2(gW.cpu().numpy(), rW) <= tol
+
+
+@pytest.mark.parametrize("name", ["mace_medium_fp32", "u8_l1_f32"])
+def test_bwd_partial_outputs(name):
+    """Requesting a subset of the gradients gives the same values for it."""
+    wl, d, inp, g, plan = _case(name)
+    full = oeq.oeq_tp_conv_bwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"])
+    for need in (("Y",), ("W",), ("x",), ("Y", "W")):
+        part = oeq.oeq_tp_conv_bwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], need=need)
+        for k, a, b in zip(("x", "Y", "W"), full, part):
+            if k in need:
+                assert rel_l2(b.cpu().numpy(), a.cpu().numpy()) <= RTOL[wl.dtype]
+            else:
+                assert b is None
+
+
+@pytest.mark.parametrize("mode", ["atomic", "deterministic"])
+@pytest.mark.parametrize("name", ["mace_large_fp32", "wide_proxy_fp32", "ragged_u96_f32", "tiny_fp64"])
+def test_hvp_parity(name, mode):
+    """Double backward with a tangent on x only (the HVP of the workloads)."""
+    wl, d, inp, g, plan = _case(name)
+    print(f"[hvp] {name} {mode}", flush=True)
+    res = oeq.oeq_tp_conv_dbwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], gg_x=g["v"],
+                               mode=mode)
+    torch.cuda.synchronize()
+    ref = oracle.dbwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"], ggx=inp["v"])
+    tol = RTOL[wl.dtype]
+    assert not res["x"].any().item()                       # exactly zero without Y or W tangents
+    assert rel_l2(res["Y"].cpu().numpy(), ref["dY"]) <= tol
+    assert rel_l2(res["W"].cpu().numpy(), ref["dW"]) <= tol
+    assert rel_l2(res["grad_out"].cpu().numpy(), ref["dg"]) <= tol
+
+
+@pytest.mark.parametrize("mode", ["atomic", "deterministic"])
+@pytest.mark.parametrize("mask", [1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("name", ["u8_l1_f32", "u1_l3_f64", "ragged_u96_f32"])
+def test_dbwd_all_tangents(name, mask, mode):
+    wl, d, inp, g, plan = _case(name)
+    tx = synth.extra_normal(wl, inp["x"].shape, 0)
+    tY = synth.extra_normal(wl, inp["Y"].shape, 1)
+    tW = synth.extra_normal(wl, inp["W"].shape, 2)
+    gx_ = to_dev(tx) if mask & 1 else None
+    gY_ = to_dev(tY) if mask & 2 else None
+    gW_ = to_dev(tW) if mask & 4 else None
+    res = oeq.oeq_tp_conv_dbwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], gg_x=gx_,
+                               gg_Y=gY_, gg_W=gW_, mode=mode)
+    torch.cuda.synchronize()
+    ref = oracle.dbwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"],
+                      ggx=tx if mask & 1 else None, ggY=tY if mask & 2 else None, ggW=tW if mask & 4 else None)
+    tol = RTOL[wl.dtype]
+    for k, rk in (("x", "dx"), ("Y", "dY"), ("W", "dW"), ("grad_out", "dg")):
+        got = res[k].cpu().numpy()
+        if not np.any(ref[rk]):
+            assert not got.any(), k
+        else:
+            assert rel_l2(got, ref[rk]) <= tol, k
+
+
+def test_empty_graph_and_no_nodes():
+    wl = W_["mace_medium_fp32"].scaled(n_nodes=20, degree=0)
+    d, inp = inputs(wl)
+    g = _dev_inputs(inp, wl.dtype)
+    plan = plan_for(wl)
+    assert inp["E"] == 0
+    out = oeq.oeq_tp_conv_fwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"])
+    gx, gY, gW = oeq.oeq_tp_conv_bwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"])
+    res = oeq.oeq_tp_conv_dbwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], gg_x=g["x"],
+                               mode="deterministic")
+    torch.cuda.synchronize()
+    assert out.shape == (20, plan.out_dim) and not out.any().item()
+    assert not gx.any().item() and gY.shape == (0, 16) and gW.shape == (0, plan.n_paths, plan.U)
+    assert not res["x"].any().item() and not res["grad_out"].any().item()
+    z = torch.zeros(1, dtype=torch.int32, device="cuda")
+    e = torch.zeros(0, dtype=torch.int32, device="cuda")
+    x0 = torch.zeros(0, plan.x_dim, device="cuda")
+    y0 = torch.zeros(0, 16, device="cuda")
+    w0 = torch.zeros(0, plan.n_paths, plan.U, device="cuda")
+    assert oeq.oeq_tp_conv_fwd(plan, z, e, x0, y0, w0).shape == (0, plan.out_dim)
+
+
+def test_sender_csr_bit_exact():
+    wl = SMALL["ragged_u96_f32"]
+    _, inp = inputs(wl, want=())
+    srp, spm = oeq.oeq_sender_csr(to_dev(inp["src"]), wl.n_nodes)
+    r_srp, r_spm = oracle.sender_csr(wl.n_nodes, inp["src"])
+    assert np.array_equal(srp.cpu().numpy(), r_srp)
+    assert np.array_equal(spm.cpu().numpy(), r_spm)
+    big = W_["mace_medium_fp32"]
+    _, inp = inputs(big, want=())
+    srp, spm = oeq.oeq_sender_csr(to_dev(inp["src"]), big.n_nodes)
+    r_srp, r_spm = oracle.sender_csr(big.n_nodes, inp["src"])
+    assert np.array_equal(srp.cpu().numpy(), r_srp) and np.array_equal(spm.cpu().numpy(), r_spm)
+
+
+def test_csr_check():
+    wl = SMALL["ragged_u96_f32"]
+    _, inp = inputs(wl, want=())
+    rp, src = to_dev(inp["rowptr"]), to_dev(inp["src"])
+    oeq.oeq_csr_check(rp, src)
+    bad = src.clone()
+    bad[3] = wl.n_nodes
+    with pytest.raises(oeq.OeqError):
+        oeq.oeq_csr_check(rp, bad)
+
+
+@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "ragged_u96_f32"])
+def test_bitwise_repeatable(name):
+    """The forward and the deterministic backward are bitwise repeatable; the
+    atomic backward agrees with them within the tolerance."""
+    wl, d, inp, g, plan = _case(name)
+    a = [oeq.oeq_tp_conv_fwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"]) for _ in range(3)]
+    b = [oeq.oeq_tp_conv_bwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], mode="deterministic")
+         for _ in range(3)]
+    c = oeq.oeq_tp_conv_bwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], mode="atomic")
+    torch.cuda.synchronize()
+    assert all(torch.equal(a[0], t) for t in a[1:])
+    for k in range(3):
+        assert all(torch.equal(b[0][k], t[k]) for t in b[1:])
+    assert torch.equal(b[0][1], c[1]) and torch.equal(b[0][2], c[2])   # gY, gW do not depend on the mode
+    assert rel_l2(c[0].cpu().numpy(), b[0][0].cpu().numpy()) <= RTOL[wl.dtype]
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, sampled comparison, benchmark launch shape
+# ---------------------------------------------------------------------------
+
+def _sampled_fwd_ref(d, inp, rows):
+    rp, sr, _ = subgraph(inp["rowptr"], inp["src"], edges_of_rows(inp["rowptr"], rows))
+    e = edges_of_rows(inp["rowptr"], rows)
+    return oracle.fwd(d, rp, sr, inp["x"], inp["Y"][e], inp["W"][e], rows=rows)
+
+
+def _sampled_edges_ref(d, inp, edges, x):
+    rp, sr, e = subgraph(inp["rowptr"], inp["src"], edges)
+    return oracle.bwd_edges(d, rp, sr, x, inp["Y"][e], inp["W"][e], inp["g"])
+
+
+def _sampled_gx_ref(d, inp, senders, Y, W):
+    e = np.nonzero(np.isin(inp["src"], senders))[0]
+    rp, sr, e = subgraph(inp["rowptr"], inp["src"], e)
+    return oracle.bwd_gx(d, rp, sr, Y[e], W[e], inp["g"], senders=senders)
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32", "wide_proxy_fp32"])
+def test_full_size_sampled(name):
+    wl = W_[name]
+    want = ("x", "Y", "W", "g", "v") if "hvp" in wl.ops else ("x", "Y", "W", "g")
+    d, inp = inputs(wl, want=want)
+    print(f"[full] {name} N={wl.n_nodes} E={inp['E']} inputs ready", flush=True)
+    g = _dev_inputs(inp, wl.dtype)
+    plan = plan_for(wl)
+    tol = RTOL[wl.dtype]
+    rows = sample(wl.n_nodes, 40, 1)
+    edges = sample(inp["E"], 200, 2)
+    senders = sample(wl.n_nodes, 24, 3)
+    rows_t, edges_t, send_t = (torch.from_numpy(a).cuda() for a in (rows, edges, senders))
+
+    out = oeq.oeq_tp_conv_fwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"])
+    got = out[rows_t].cpu().numpy()
+    del out
+    assert rel_l2(got, _sampled_fwd_ref(d, inp, rows)) <= tol
+    print(f"[full] {name} fwd ok", flush=True)
+
+    rW, rY = _sampled_edges_ref(d, inp, edges, inp["x"])
+    rx = _sampled_gx_ref(d, inp, senders, inp["Y"], inp["W"])
+    for mode in ("atomic", "deterministic"):
+        gx, gY, gW = oeq.oeq_tp_conv_bwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], mode=mode)
+        assert rel_l2(gx[send_t].cpu().numpy(), rx) <= tol
+        assert rel_l2(gY[edges_t].cpu().numpy(), rY) <= tol
+        assert rel_l2(gW[edges_t].cpu().numpy(), rW) <= tol
+        del gx, gY, gW
+        print(f"[full] {name} bwd {mode} ok", flush=True)
+
+    if "hvp" in wl.ops:
+        res = oeq.oeq_tp_conv_dbwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], gg_x=g["v"],
+                                   want=("Y", "W", "grad_out"))
+        dW, dY = _sampled_edges_ref(d, inp, edges, inp["v"])
+        dg = _sampled_fwd_ref(d, dict(inp, x=inp["v"]), rows)
+        assert rel_l2(res["Y"][edges_t].cpu().numpy(), dY) <= tol
+        assert rel_l2(res["W"][edges_t].cpu().numpy(), dW) <= tol
+        assert rel_l2(res["grad_out"][rows_t].cpu().numpy(), dg) <= tol
+        print(f"[full] {name} hvp ok", flush=True)
+    torch.cuda.synchronize()

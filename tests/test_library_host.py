@@ -1,0 +1,157 @@
+"""Host-side checks of the C-ABI library (no GPU needed).
+
+The library loads, exports every symbol its header declares, builds the same
+path lists and CG tables as the oracle (the two are written independently), and
+rejects bad arguments with status codes before touching a device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import oracle_desc
+
+oeq = pytest.importorskip("cg_tensor_product_amd")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+TRIPLES = [(l1, l2, l3) for l1 in range(4) for l2 in range(4) for l3 in range(4)
+           if abs(l1 - l2) <= l3 <= l1 + l2]
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "oeq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(oeq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = oeq.lib()
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(oeq.EXPORTED)
+
+
+def test_status_strings():
+    lib = oeq.lib()
+    for code, name in oeq.STATUS.items():
+        assert lib.oeq_status_string(code).decode() == name
+
+
+@pytest.mark.parametrize("l1,l2,l3", TRIPLES)
+def test_planner_tables_equal_oracle(l1, l2, l3):
+    got = oeq.oeq_cg_table(l1, l2, l3)
+    ref = oracle.cg_real(l1, l2, l3)
+    assert np.array_equal(got != 0, ref != 0)          # same sparsity, bit for bit
+    assert np.abs(got - ref).max() <= 1e-15
+
+
+def test_cg_table_rejects_bad_degrees():
+    with pytest.raises(oeq.OeqError) as e:
+        oeq.oeq_cg_table(1, 1, 3)
+    assert e.value.status == 1
+    with pytest.raises(oeq.OeqError):
+        oeq.oeq_cg_table(4, 0, 4)
+
+
+@pytest.mark.parametrize("name", list(synth.WORKLOADS))
+def test_plan_paths_and_dims_equal_oracle(name):
+    wl = synth.WORKLOADS[name]
+    d = oracle_desc(wl)
+    p = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    en = oracle.enumerate_paths(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    got = p.paths()
+    assert [(i1, l2, l3, p3) for (i1, _, l2, l3, _, p3) in got] == en
+    assert [ob for (*_, ob, _) in got] == list(range(len(en)))
+    assert (p.x_dim, p.y_dim, p.out_dim, p.n_paths, p.w_per_edge) == (
+        d.x_dim, d.y_dim, d.out_dim, d.P, d.P * d.U)
+
+
+def test_plan_with_output_irreps_sums_paths():
+    # 1o x (0e + 2e) -> 1o: two paths into one output block
+    p = oeq.Plan("4x1o", 2, 1, "f32", out_irreps="4x1o")
+    assert p.n_paths == 2 and p.out_dim == 12
+    assert [t[4] for t in p.paths()] == [0, 0]
+    q = oeq.Plan("4x1o", 2, 1, "f32", paths=[(0, 0, 0), (0, 2, 0)], out_irreps="4x1o")
+    assert q.paths() == p.paths()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x_irreps="8x0e+4x1o", y_lmax=2), 2),          # mixed multiplicities
+    (dict(x_irreps="8x4e", y_lmax=2), 2),               # degree above 3
+    (dict(x_irreps="8x0e", y_lmax=4), 2),               # Y degree above 3
+    (dict(x_irreps="8x1o", y_lmax=1, dtype="f16"), 2),  # unsupported dtype
+    (dict(x_irreps=(), y_lmax=1), 1),                    # no x blocks
+    (dict(x_irreps="8x1o", y_lmax=1, paths=[(0, 1, 0)], out_irreps="8x1o"), 1),  # parity violated
+    (dict(x_irreps="8x1o", y_lmax=1, paths=[(0, 1, 0)], out_irreps="8x3o"), 1),  # triangle violated
+    (dict(x_irreps="8x1o", y_lmax=1, paths=[(0, 0, 0)]), 1),                     # paths without outputs
+    (dict(x_irreps="8x0e", y_lmax=2, lmax_out=1, out_irreps="8x3e"), 1),        # no path survives
+])
+def test_plan_create_errors(kw, status):
+    with pytest.raises(oeq.OeqError) as e:
+        oeq.Plan(**kw)
+    assert e.value.status == status
+
+
+def _raw_call(plan, N, E, rowptr=16, src=16, x=16, mode=0, ws=None, wsb=0, gx=16):
+    lib = oeq.lib()
+    P = ctypes.c_void_p
+    return lib.oeq_tp_conv_bwd(plan, N, E, P(rowptr) if rowptr else None, P(src) if src else None,
+                               P(x) if x else None, P(16), P(16), P(16), P(gx) if gx else None, P(16), P(16),
+                               mode, P(ws) if ws else None, wsb, None)
+
+
+def test_compute_argument_errors_before_any_device_work():
+    p = oeq.Plan("8x0e+8x1o", 2, 1, "f64")
+    lib = oeq.lib()
+    P = ctypes.c_void_p
+    assert lib.oeq_tp_conv_fwd(None, 4, 4, P(16), P(16), P(16), P(16), P(16), P(16), None) == 1
+    assert lib.oeq_tp_conv_fwd(p.handle, -1, 4, P(16), P(16), P(16), P(16), P(16), P(16), None) == 1
+    assert lib.oeq_tp_conv_fwd(p.handle, 0, 4, P(16), P(16), P(16), P(16), P(16), P(16), None) == 1
+    assert lib.oeq_tp_conv_fwd(p.handle, 4, 4, None, P(16), P(16), P(16), P(16), P(16), None) == 1
+    assert lib.oeq_tp_conv_fwd(p.handle, 4, 4, P(16), P(16), None, P(16), P(16), P(16), None) == 1
+    assert lib.oeq_tp_conv_fwd(p.handle, 4, 4, P(16), P(16), P(16), P(16), P(16), None, None) == 1
+    assert lib.oeq_tp_conv_fwd(p.handle, 2**31, 4, P(16), P(16), P(16), P(16), P(16), P(16), None) == 2
+    # N = 0 with no edges is a valid empty call
+    assert lib.oeq_tp_conv_fwd(p.handle, 0, 0, P(16), None, None, None, None, None, None) == 0
+    assert _raw_call(p.handle, 4, 4, mode=7) == 1
+    assert _raw_call(p.handle, 4, 4, x=None) == 1
+    assert _raw_call(p.handle, 4, 4, src=None) == 1
+    assert _raw_call(p.handle, 4, 4, mode=1, ws=None) == 3          # deterministic needs a workspace
+    assert _raw_call(p.handle, 4, 4, mode=1, ws=4096 + 8, wsb=1 << 20) == 3   # misaligned
+    assert "aligned" in lib.oeq_last_error().decode()
+    # nothing requested: returns without work
+    lib2 = lib.oeq_tp_conv_bwd(p.handle, 4, 4, P(16), P(16), P(16), P(16), P(16), P(16), None, None, None,
+                               0, None, 0, None)
+    assert lib2 == 0
+
+
+def test_workspace_size_atomic_is_zero():
+    p = oeq.Plan("8x0e+8x1o", 2, 1, "f64")
+    assert oeq.oeq_workspace_size(p, 64, 1024, "atomic") == 0
+    b = ctypes.c_size_t()
+    assert oeq.lib().oeq_workspace_size(p.handle, 64, 1024, 9, ctypes.byref(b)) == 1
+    assert oeq.lib().oeq_workspace_size(None, 64, 1024, 0, ctypes.byref(b)) == 1
+
+
+def test_generated_source_has_no_packed_fp32_and_caches(tmp_path, monkeypatch):
+    """The emitted kernels compile for gfx950 on the host (runtime compiler, no
+    device), and the code object lands in the cache directory."""
+    import subprocess
+    import sys
+    env = dict(os.environ, OEQ_CACHE_DIR=str(tmp_path))
+    code = ("import sys; sys.path.insert(0, %r); import cg_tensor_product_amd as m; "
+            "m.Plan('16x0e+16x1o', 1, 1, 'f32')" % ROOT)
+    subprocess.run([sys.executable, "-c", code], check=True, env=env)
+    objs = list(tmp_path.glob("*.hsaco"))
+    assert len(objs) == 1
+    dis = subprocess.run(["/opt/rocm/llvm/bin/llvm-objdump", "-d", str(objs[0])],
+                         capture_output=True, text=True)
+    if dis.returncode == 0:
+        assert "v_pk_fma_f32" not in dis.stdout and "v_pk_mul_f32" not in dis.stdout
+        assert "oeq_fwd" in dis.stdout and "oeq_bwd_atomic" in dis.stdout
