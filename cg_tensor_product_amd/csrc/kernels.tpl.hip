@@ -47,26 +47,111 @@ __device__ __forceinline__ void store_w(real_t *__restrict__ G, int e, int u, co
     for (int p = 0; p < P; ++p) wr[p * U] = wv[p];
 }
 
+// Cross-lane moves on 32-bit words; a double moves as two words.
+//   swap32(a, b): a <- [a lanes 0-31 | b lanes 0-31], b <- [a lanes 32-63 | b lanes 32-63]
+//   swap16(a, b): per 32-lane half, a <- [a row 0 | b row 0], b <- [a row 1 | b row 1]
+//   (v_permlane32_swap / v_permlane16_swap; rows are 16 lanes)
+//   ror8: rotate by 8 inside each 16-lane row (the partner lane^8), DPP row_ror:8
+//   xor4: the value of lane^4 (ds_swizzle, bit mode, xor mask 4)
+//   qxor2 / qxor1: the value of lane^2 / lane^1 (DPP quad_perm)
+__device__ __forceinline__ unsigned lo32(double v) { return (unsigned)(__double_as_longlong(v) & 0xffffffffull); }
+__device__ __forceinline__ unsigned hi32(double v) { return (unsigned)(__double_as_longlong(v) >> 32); }
+__device__ __forceinline__ double mk64(unsigned lo, unsigned hi) {
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ void swap32(float &a, float &b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(double &a, double &b) {
+    auto l = __builtin_amdgcn_permlane32_swap(lo32(a), lo32(b), false, false);
+    auto h = __builtin_amdgcn_permlane32_swap(hi32(a), hi32(b), false, false);
+    a = mk64(l[0], h[0]);
+    b = mk64(l[1], h[1]);
+}
+__device__ __forceinline__ void swap16(float &a, float &b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap16(double &a, double &b) {
+    auto l = __builtin_amdgcn_permlane16_swap(lo32(a), lo32(b), false, false);
+    auto h = __builtin_amdgcn_permlane16_swap(hi32(a), hi32(b), false, false);
+    a = mk64(l[0], h[0]);
+    b = mk64(l[1], h[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+    return mk64((unsigned)__builtin_amdgcn_update_dpp(0, (int)lo32(v), CTRL, 0xF, 0xF, false),
+                (unsigned)__builtin_amdgcn_update_dpp(0, (int)hi32(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor4(float v) { return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x101F)); }
+__device__ __forceinline__ double xor4(double v) {
+    return mk64((unsigned)__builtin_amdgcn_ds_swizzle((int)lo32(v), 0x101F),
+                (unsigned)__builtin_amdgcn_ds_swizzle((int)hi32(v), 0x101F));
+}
+constexpr int kRor8 = 0x128, kQxor2 = 0x4E, kQxor1 = 0xB1;
+
 // Sum of PY values over the 64 lanes of a wave, in a fixed order.  On return,
-// lane l holds in v[0] the total of value (l >> (6 - LGPY)); the lanes whose low
-// (6 - LGPY) bits are zero are the ones to write it.  Each halving step keeps
-// half of the values and adds the partner lane's copy of them (reduce-scatter),
-// the remaining steps are a plain butterfly.
+// lane l holds in v[0] the total of value (l >> (6 - LGPY)); every lane whose
+// low (6 - LGPY) bits are zero may write it.  The first LGPY steps halve the
+// values held per lane (at lane distances 32, 16, 8, 4: each lane keeps the half
+// its distance bit selects and adds its partner's copy of that half); the other
+// steps are plain butterflies over the remaining distances.
 __device__ __forceinline__ void wave_reduce_scatter(real_t (&v)[PY], int lane) {
-#pragma unroll
-    for (int st = 0; st < LGPY; ++st) {
-        const int d = 32 >> st;
-        const int h = PY >> (st + 1);
-        const bool hi = (lane & d) != 0;
+    if constexpr (LGPY >= 1) {
+        constexpr int h = PY / 2;
 #pragma unroll
         for (int i = 0; i < h; ++i) {
-            const real_t keep = hi ? v[i + h] : v[i];
-            const real_t send = hi ? v[i] : v[i + h];
-            v[i] = keep + __shfl_xor(send, d, 64);
+            real_t a = v[i], b = v[i + h];
+            swap32(a, b);
+            v[i] = a + b;
         }
+    } else {
+        real_t a = v[0], b = v[0];
+        swap32(a, b);
+        v[0] = a + b;
     }
+    if constexpr (LGPY >= 2) {
+        constexpr int h = PY / 4;
 #pragma unroll
-    for (int d = (32 >> LGPY); d >= 1; d >>= 1) v[0] += __shfl_xor(v[0], d, 64);
+        for (int i = 0; i < h; ++i) {
+            real_t a = v[i], b = v[i + h];
+            swap16(a, b);
+            v[i] = a + b;
+        }
+    } else {
+        real_t a = v[0], b = v[0];
+        swap16(a, b);
+        v[0] = a + b;
+    }
+    if constexpr (LGPY >= 3) {
+        constexpr int h = PY / 8;
+        const bool up = (lane & 8) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const real_t s0 = v[i] + dpp<kRor8>(v[i]);
+            const real_t s1 = v[i + h] + dpp<kRor8>(v[i + h]);
+            v[i] = up ? s1 : s0;
+        }
+    } else {
+        v[0] = v[0] + dpp<kRor8>(v[0]);
+    }
+    if constexpr (LGPY >= 4) {
+        const bool up = (lane & 4) != 0;
+        const real_t s0 = v[0] + xor4(v[0]);
+        const real_t s1 = v[1] + xor4(v[1]);
+        v[0] = up ? s1 : s0;
+    } else {
+        v[0] = v[0] + xor4(v[0]);
+    }
+    v[0] = v[0] + dpp<kQxor2>(v[0]);
+    v[0] = v[0] + dpp<kQxor1>(v[0]);
 }
 
 extern "C" __global__ void __launch_bounds__(256)
