@@ -51,6 +51,13 @@ oeq_status fill_zero(oeq_plan *p, void *ptr, int64_t n, hipStream_t stream) {
     return launch(p, "oeq_fill_zero", static_cast<unsigned>(blocks), 256, stream, args);
 }
 
+// Reorders atomically accumulated x-gradient rows from m-major to u-major blocks.
+oeq_status untranspose(oeq_plan *p, int64_t N, void *gx, hipStream_t stream) {
+    if (!p->xt) return OEQ_OK;
+    void *args[] = {&gx};
+    return launch(p, "oeq_x_untranspose", static_cast<unsigned>(N), 256, stream, args);
+}
+
 struct DetWorkspace {
     void *h = nullptr;
     int32_t *srowptr = nullptr, *sperm = nullptr;
@@ -230,7 +237,9 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
         st = fill_zero(p, gx, N * p->XD, s);
         if (st != OEQ_OK) return st;
         void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gY, &gW, &flags};
-        return launch(p, "oeq_bwd_atomic", grid, block, s, args);
+        st = launch(p, "oeq_bwd_atomic", grid, block, s, args);
+        if (st != OEQ_OK) return st;
+        return untranspose(p, N, gx, s);
     }
     DetWorkspace w;
     st = det_prepare(p, N, E, src, workspace, workspace_bytes, s, &w);
@@ -285,6 +294,7 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
     st = launch(p, name.c_str(), static_cast<unsigned>(N), static_cast<unsigned>(p->uch * 64), s, args);
     if (st != OEQ_OK) return st;
     if (dxmode == 2) return det_finish(p, N, w, dx, s);
+    if (dxmode == 1) return untranspose(p, N, dx, s);
     return OEQ_OK;
 }
 

@@ -66,12 +66,30 @@ void emit_moves(std::ostringstream &o, const oeq_plan &p) {
         o << " }\n";
     }
     o << "}\n";
+    // x-gradient scatter: with XT the block is addressed m-major (element m*U + u),
+    // so consecutive lanes hit consecutive addresses; oeq_x_untranspose restores
+    // the u-major layout afterwards.
     o << "__device__ __forceinline__ void g_atomic_x(real_t *__restrict__ xr, int u, const real_t (&v)[NXC]) {\n";
     for (const auto &b : p.xb) {
         const int n = 2 * b.l + 1;
-        o << "  { real_t *q = xr + " << b.row_off << "LL + (i64)u * " << n << ";";
-        for (int m = 0; m < n; ++m) o << " atomicAdd(q + " << m << ", v[" << b.lane_off + m << "]);";
+        if (p.xt) {
+            o << "  { real_t *q = xr + " << b.row_off << "LL + u;";
+            for (int m = 0; m < n; ++m)
+                o << " atomicAdd(q + " << static_cast<int64_t>(m) * p.U << ", v[" << b.lane_off + m << "]);";
+        } else {
+            o << "  { real_t *q = xr + " << b.row_off << "LL + (i64)u * " << n << ";";
+            for (int m = 0; m < n; ++m) o << " atomicAdd(q + " << m << ", v[" << b.lane_off + m << "]);";
+        }
         o << " }\n";
+    }
+    o << "}\n";
+    // m-major -> u-major inside one node row held in LDS
+    o << "__device__ __forceinline__ void g_untranspose_row(const real_t *__restrict__ t, real_t *__restrict__ row) {\n";
+    for (const auto &b : p.xb) {
+        const int n = 2 * b.l + 1;
+        o << "  for (int i = threadIdx.x; i < " << static_cast<int64_t>(n) * p.U << "; i += blockDim.x) { const int u = i / "
+          << n << ", m = i - u * " << n << "; row[" << b.row_off << "LL + i] = t[" << b.row_off << "LL + m * " << p.U
+          << " + u]; }\n";
     }
     o << "}\n";
     // output row <-> registers
@@ -235,6 +253,7 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr int GY_TILE = " << p.gy_tile << ";\n";
     o << "constexpr i64 XD = " << p.XD << "LL;\n";
     o << "constexpr i64 OD = " << p.OD << "LL;\n";
+    o << "constexpr bool XT = " << (p.xt ? "true" : "false") << ";\n";
     emit_moves(o, p);
     emit_fwd_edge(o, p);
     emit_bwd_edge(o, p);

@@ -201,6 +201,19 @@ oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src,
     if (act) g_store_out(out + (i64)r * OD, u, acc);
 }
 
+// The atomic x-gradient is accumulated m-major inside each x block (so the
+// lanes of one atomic instruction address consecutive words); this restores the
+// u-major row layout in place, one node row per workgroup.
+extern "C" __global__ void __launch_bounds__(256)
+oeq_x_untranspose(real_t *__restrict__ gx) {
+    __shared__ real_t t[XT ? XD : 1];
+    real_t *row = gx + (i64)blockIdx.x * XD;
+    if (!XT) return;
+    for (int i = threadIdx.x; i < XD; i += 256) t[i] = row[i];
+    __syncthreads();
+    g_untranspose_row(t, row);
+}
+
 // ---------------------------------------------------------------------------
 // Y-gradient staging: per-wave lane-reduced rows in LDS, summed over the waves
 // of the workgroup (fixed order) every GY_TILE edges.
@@ -257,26 +270,40 @@ __device__ __forceinline__ void bwd_body(const int *__restrict__ rowptr, const i
     g_load_g(g + (i64)r * OD, uu, gv);
     if (!act) zero(gv);  // inactive lanes contribute nothing to the lane sums
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
-    for (int base = e0; base < e1; base += GY_TILE) {
-        const int n = (e1 - base < GY_TILE) ? e1 - base : GY_TILE;
-        for (int j = 0; j < n; ++j) {
-            const int e = base + j;
-            const int s = uni(src[e]);
-            real_t yv[YD], xv[NXC], wv_[P];
-            load_y(Y, e, yv);
-            g_load_x(x + (i64)s * XD, uu, xv);
-            load_w(W, e, uu, wv_);
-            real_t gw[P], gy[YD], gxp[NXC];
-            zero(gw);
-            zero(gy);
-            zero(gxp);
-            g_bwd_edge<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
-            if (want_gw && act) store_w(gW, e, u, gw);
-            if (want_gy) gy_push(st, gY, e, j, gy, lane, wv);
-            if (GXMODE == 1 && act) g_atomic_x(gx + (i64)s * XD, u, gxp);
-            if (GXMODE == 2 && act) g_store_x(gx + (i64)e * XD, u, gxp);
+    if (e0 >= e1) return;
+    // software pipeline: the next edge's loads are in flight while this one computes
+    int s = uni(src[e0]);
+    real_t yv[YD], xv[NXC], wv_[P];
+    load_y(Y, e0, yv);
+    g_load_x(x + (i64)s * XD, uu, xv);
+    load_w(W, e0, uu, wv_);
+    for (int e = e0; e < e1; ++e) {
+        const int en = (e + 1 < e1) ? e + 1 : e;
+        const int sn = uni(src[en]);
+        real_t yn[YD], xn[NXC], wn[P];
+        load_y(Y, en, yn);
+        g_load_x(x + (i64)sn * XD, uu, xn);
+        load_w(W, en, uu, wn);
+        const int j = uni((e - e0) % GY_TILE);
+        real_t gw[P], gy[YD], gxp[NXC];
+        zero(gw);
+        zero(gy);
+        zero(gxp);
+        g_bwd_edge<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
+        if (want_gw && act) store_w(gW, e, u, gw);
+        if (want_gy) {
+            gy_push(st, gY, e, j, gy, lane, wv);
+            if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, gY, e - j, j + 1);
         }
-        if (want_gy) gy_flush(st, gY, base, n);
+        if (GXMODE == 1 && act) g_atomic_x(gx + (i64)s * XD, u, gxp);
+        if (GXMODE == 2 && act) g_store_x(gx + (i64)e * XD, u, gxp);
+        s = sn;
+#pragma unroll
+        for (int k = 0; k < YD; ++k) yv[k] = yn[k];
+#pragma unroll
+        for (int k = 0; k < NXC; ++k) xv[k] = xn[k];
+#pragma unroll
+        for (int k = 0; k < P; ++k) wv_[k] = wn[k];
     }
 }
 
@@ -349,43 +376,54 @@ __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const 
     real_t dgacc[NOC];
     zero(dgacc);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
-    for (int base = e0; base < e1; base += GY_TILE) {
-        const int n = (e1 - base < GY_TILE) ? e1 - base : GY_TILE;
-        for (int j = 0; j < n; ++j) {
-            const int e = base + j;
-            const int s = uni(src[e]);
-            real_t yv[YD], xv[NXC], wv_[P];
-            load_y(Y, e, yv);
-            g_load_x(x + (i64)s * XD, uu, xv);
-            load_w(W, e, uu, wv_);
+    // per-edge operands (unused ones are dropped by the compiler for a given TM)
+    struct Ops {
+        real_t y[YD], x[NXC], w[P], tx[NXC], ty[YD], tw[P];
+    };
+    auto load = [&](int e, int s, Ops &o) {
+        load_y(Y, e, o.y);
+        g_load_x(x + (i64)s * XD, uu, o.x);
+        load_w(W, e, uu, o.w);
+        if (TM & 1) g_load_x(ggx + (i64)s * XD, uu, o.tx);
+        if (TM & 2) load_y(ggY, e, o.ty);
+        if (TM & 4) load_w(ggW, e, uu, o.tw);
+    };
+    if (e0 < e1) {
+        int s = uni(src[e0]);
+        Ops cur;
+        load(e0, s, cur);
+        for (int e = e0; e < e1; ++e) {
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            Ops nxt;
+            load(en, sn, nxt);
+            const int j = uni((e - e0) % GY_TILE);
             real_t dw[P], dy[YD], dxp[NXC];
             zero(dw);
             zero(dy);
             zero(dxp);
             if (TM & 1) {
-                real_t tx[NXC];
-                g_load_x(ggx + (i64)s * XD, uu, tx);
-                if (want_dg) g_fwd_edge(tx, yv, wv_, dgacc);
-                g_bwd_edge<true, true, false>(tx, yv, wv_, gv, dw, dy, dxp);
+                if (want_dg) g_fwd_edge(cur.tx, cur.y, cur.w, dgacc);
+                g_bwd_edge<true, true, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
             }
             if (TM & 2) {
-                real_t ty[YD];
-                load_y(ggY, e, ty);
-                if (want_dg) g_fwd_edge(xv, ty, wv_, dgacc);
-                g_bwd_edge<true, false, true>(xv, ty, wv_, gv, dw, dy, dxp);
+                if (want_dg) g_fwd_edge(cur.x, cur.ty, cur.w, dgacc);
+                g_bwd_edge<true, false, true>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
             }
             if (TM & 4) {
-                real_t tw[P];
-                load_w(ggW, e, uu, tw);
-                if (want_dg) g_fwd_edge(xv, yv, tw, dgacc);
-                g_bwd_edge<false, true, true>(xv, yv, tw, gv, dw, dy, dxp);
+                if (want_dg) g_fwd_edge(cur.x, cur.y, cur.tw, dgacc);
+                g_bwd_edge<false, true, true>(cur.x, cur.y, cur.tw, gv, dw, dy, dxp);
             }
             if (want_dw && act) store_w(dW, e, u, dw);
-            if (want_dy) gy_push(st, dY, e, j, dy, lane, wv);
+            if (want_dy) {
+                gy_push(st, dY, e, j, dy, lane, wv);
+                if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, dY, e - j, j + 1);
+            }
             if (HAS_DX && dxmode == 1 && act) g_atomic_x(dx + (i64)s * XD, u, dxp);
             if (HAS_DX && dxmode == 2 && act) g_store_x(dx + (i64)e * XD, u, dxp);
+            s = sn;
+            cur = nxt;
         }
-        if (want_dy) gy_flush(st, dY, base, n);
     }
     if (want_dg && act) g_store_out(dg + (i64)r * OD, u, dgacc);
 }

@@ -150,6 +150,8 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     }
 
     p->uch = (p->U + 63) / 64;
+    // m-major atomics need one node row in LDS for the final reorder
+    p->xt = p->XD * (p->dtype == OEQ_F64 ? 8 : 4) <= 65536 && std::getenv("OEQ_NO_XT") == nullptr;
     if (const char *s = std::getenv("OEQ_GY_TILE")) {
         const int v = std::atoi(s);
         if (v >= 1 && v <= 256) p->gy_tile = v;

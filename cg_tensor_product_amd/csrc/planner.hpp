@@ -64,6 +64,7 @@ struct oeq_plan {
     // Launch shape.
     int uch = 1;                // 64-channel chunks (waves per receiver)
     int gy_tile = 32;           // edges per LDS gY flush in the backward kernels
+    bool xt = false;            // x-gradient atomics use an m-major row (needs the row in LDS)
 
     std::string source;         // emitted HIP source
     std::vector<char> code;     // gfx950 code object
