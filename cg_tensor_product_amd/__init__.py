@@ -28,7 +28,8 @@ _MODES = {"atomic": OEQ_BWD_ATOMIC, "deterministic": OEQ_BWD_DETERMINISTIC}
 STATUS = {0: "OEQ_OK", 1: "OEQ_ERR_INVALID_ARG", 2: "OEQ_ERR_UNSUPPORTED", 3: "OEQ_ERR_WORKSPACE",
           4: "OEQ_ERR_HIP", 5: "OEQ_ERR_JIT"}
 
-EXPORTED = ["oeq_plan_create", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_paths", "oeq_cg_table",
+EXPORTED = ["oeq_plan_create", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_paths", "oeq_plan_code_key",
+            "oeq_cg_table",
             "oeq_workspace_size", "oeq_tp_conv_fwd", "oeq_tp_conv_bwd", "oeq_tp_conv_dbwd",
             "oeq_csr_workspace_size", "oeq_sender_csr", "oeq_csr_check", "oeq_status_string",
             "oeq_last_error"]
@@ -77,6 +78,8 @@ def lib():
     L.oeq_plan_dims.restype = st
     L.oeq_plan_paths.argtypes = [P, P, I32]
     L.oeq_plan_paths.restype = st
+    L.oeq_plan_code_key.argtypes = [P, ctypes.c_char_p, SZ]
+    L.oeq_plan_code_key.restype = st
     L.oeq_cg_table.argtypes = [I32, I32, I32, P]
     L.oeq_cg_table.restype = st
     L.oeq_workspace_size.argtypes = [P, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
@@ -164,6 +167,13 @@ class Plan:
         buf = np.zeros(6 * self.n_paths, dtype=np.int32)
         _check(lib().oeq_plan_paths(self._h, buf.ctypes.data, self.n_paths))
         return [tuple(int(v) for v in buf[6 * k:6 * k + 6]) for k in range(self.n_paths)]
+
+    @property
+    def code_key(self) -> str:
+        """Hash identifying the compiled kernels of this plan."""
+        buf = ctypes.create_string_buffer(64)
+        _check(lib().oeq_plan_code_key(self._h, buf, 64))
+        return buf.value.decode()
 
     def torch_dtype(self):
         import torch

@@ -180,6 +180,13 @@ oeq_status oeq_plan_paths(const oeq_plan *p, int32_t *out6, int32_t capacity) {
     return OEQ_OK;
 }
 
+oeq_status oeq_plan_code_key(const oeq_plan *p, char *buf, size_t len) {
+    if (!p || !buf) return fail(OEQ_ERR_INVALID_ARG, "plan or buffer is NULL");
+    if (len < p->code_key.size() + 1) return fail(OEQ_ERR_INVALID_ARG, "buffer too small");
+    std::memcpy(buf, p->code_key.c_str(), p->code_key.size() + 1);
+    return OEQ_OK;
+}
+
 oeq_status oeq_cg_table(int32_t l1, int32_t l2, int32_t l3, double *out) {
     if (!out) return fail(OEQ_ERR_INVALID_ARG, "output is NULL");
     std::vector<double> t;

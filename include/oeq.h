@@ -118,6 +118,11 @@ oeq_status oeq_plan_dims(const oeq_plan *plan, int64_t *x_dim, int64_t *y_dim,
  * written to out6[6*k .. 6*k+5] for k < n_paths (host memory). */
 oeq_status oeq_plan_paths(const oeq_plan *plan, int32_t *out6, int32_t capacity);
 
+/* Identifier of the plan's compiled code object (hex hash of the generated
+ * source and compile options), NUL-terminated into buf (host memory, at least
+ * 17 bytes).  Lets measurements tie counter data to the exact kernels. */
+oeq_status oeq_plan_code_key(const oeq_plan *plan, char *buf, size_t len);
+
 /* The plan's real-basis CG table for (l1, l2, l3) as a dense fp64 array
  * [(2l1+1)(2l2+1)(2l3+1)] in host memory (the values the kernels use, before
  * rounding to the plan dtype).  Returns OEQ_ERR_INVALID_ARG outside the
