@@ -284,8 +284,7 @@ def oeq_tp_conv_bwd(plan: Plan, rowptr, src, x, Y, W, grad_out, mode: str = "ato
     if out is None:
         out = tuple(_empty(s, dt, dev) if k in need else None for k, s in zip(("x", "Y", "W"), shapes))
     gx, gY, gW = (_want(t, s, dt, n) for t, s, n in zip(out, shapes, ("grad_x", "grad_Y", "grad_W")))
-    ws, nbytes = (workspace, workspace.numel()) if workspace is not None else (
-        _workspace(plan, N, E, mode, dev) if gx is not None else (None, 0))
+    ws, nbytes = (workspace, workspace.numel()) if workspace is not None else _workspace(plan, N, E, mode, dev)
     _check(lib().oeq_tp_conv_bwd(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W),
                                  _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gW), _MODES[mode], _ptr(ws), nbytes,
                                  _stream()))
@@ -311,8 +310,7 @@ def oeq_tp_conv_dbwd(plan: Plan, rowptr, src, x, Y, W, grad_out, gg_x=None, gg_Y
         "W": _empty((E, plan.n_paths, plan.U), dt, dev) if "W" in want else None,
         "grad_out": _empty((N, plan.out_dim), dt, dev) if "grad_out" in want else None,
     }
-    ws, nbytes = (workspace, workspace.numel()) if workspace is not None else (
-        _workspace(plan, N, E, mode, dev) if d["x"] is not None else (None, 0))
+    ws, nbytes = (workspace, workspace.numel()) if workspace is not None else _workspace(plan, N, E, mode, dev)
     _check(lib().oeq_tp_conv_dbwd(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W),
                                   _ptr(grad_out), _ptr(gg_x), _ptr(gg_Y), _ptr(gg_W), _ptr(d["x"]), _ptr(d["Y"]),
                                   _ptr(d["W"]), _ptr(d["grad_out"]), _MODES[mode], _ptr(ws), nbytes, _stream()))

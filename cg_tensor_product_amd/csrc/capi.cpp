@@ -1,5 +1,6 @@
 // C ABI entry points: argument checks (host only, no device reads, no
 // synchronisation), workspace carving and stream-ordered kernel launches.
+#include <algorithm>
 #include <cstring>
 #include <limits>
 #include <string>
@@ -20,13 +21,19 @@ constexpr size_t kAlign = 256;
 size_t up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 size_t esize(const oeq_plan *p) { return p->dtype == OEQ_F64 ? 8 : 4; }
 
+// Threads per workgroup: one wave per (64-channel chunk, path group).
+unsigned fwd_block(const oeq_plan *p) { return static_cast<unsigned>(p->uch * p->fwd_groups.size() * 64); }
+unsigned bwd_block(const oeq_plan *p) { return static_cast<unsigned>(p->uch * 64); }
+
 oeq_status check_graph(const oeq_plan *p, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src) {
     if (!p) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
     if (N < 0 || E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative node or edge count");
     if (N >= std::numeric_limits<int32_t>::max() || E >= std::numeric_limits<int32_t>::max())
         return fail(OEQ_ERR_UNSUPPORTED, "node and edge counts must fit the int32 CSR");
     if (N == 0 && E != 0) return fail(OEQ_ERR_INVALID_ARG, "edges without nodes");
-    if (N * p->uch * 64 >= (int64_t(1) << 32)) return fail(OEQ_ERR_UNSUPPORTED, "too many nodes for one launch");
+    if (N * std::max<int64_t>(fwd_block(p), static_cast<int64_t>(bwd_block(p)) * p->bwd_groups.size()) >=
+        (int64_t(1) << 32))
+        return fail(OEQ_ERR_UNSUPPORTED, "too many nodes for one launch");
     if (N > 0 && !rowptr) return fail(OEQ_ERR_INVALID_ARG, "rowptr is NULL");
     if (E > 0 && !src) return fail(OEQ_ERR_INVALID_ARG, "src is NULL");
     return OEQ_OK;
@@ -58,50 +65,77 @@ oeq_status untranspose(oeq_plan *p, int64_t N, void *gx, hipStream_t stream) {
     return launch(p, "oeq_x_untranspose", static_cast<unsigned>(N), 256, stream, args);
 }
 
-struct DetWorkspace {
+// Caller-provided scratch, carved in 256-byte aligned pieces:
+//   gy_part  partial Y-gradient rows of each backward path group (several groups only)
+//   h, srowptr, sperm, csr_scratch   deterministic x-gradient (per-edge rows, sender CSR)
+struct Workspace {
+    void *gy_part = nullptr;
     void *h = nullptr;
     int32_t *srowptr = nullptr, *sperm = nullptr;
     void *csr_scratch = nullptr;
     size_t bytes = 0;
 };
 
-oeq_status det_layout(const oeq_plan *p, int64_t N, int64_t E, char *base, DetWorkspace *w) {
-    size_t csr_bytes = 0;
-    const hipError_t e = oeq::sender_csr_workspace(N, E, &csr_bytes);
-    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR workspace: ") + hipGetErrorString(e));
+oeq_status ws_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, bool gy_part, char *base, Workspace *w) {
     size_t off = 0;
-    w->h = base + off;
-    off += up(static_cast<size_t>(E) * static_cast<size_t>(p->XD) * esize(p));
-    w->srowptr = reinterpret_cast<int32_t *>(base + off);
-    off += up(sizeof(int32_t) * static_cast<size_t>(N + 1));
-    w->sperm = reinterpret_cast<int32_t *>(base + off);
-    off += up(sizeof(int32_t) * static_cast<size_t>(E > 0 ? E : 1));
-    w->csr_scratch = base + off;
-    off += up(csr_bytes);
+    if (gy_part) {
+        w->gy_part = base + off;
+        off += up(p->bwd_groups.size() * static_cast<size_t>(E) * p->YD * esize(p));
+    }
+    if (det) {
+        size_t csr_bytes = 0;
+        const hipError_t e = oeq::sender_csr_workspace(N, E, &csr_bytes);
+        if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR workspace: ") + hipGetErrorString(e));
+        w->h = base + off;
+        off += up(static_cast<size_t>(E) * static_cast<size_t>(p->XD) * esize(p));
+        w->srowptr = reinterpret_cast<int32_t *>(base + off);
+        off += up(sizeof(int32_t) * static_cast<size_t>(N + 1));
+        w->sperm = reinterpret_cast<int32_t *>(base + off);
+        off += up(sizeof(int32_t) * static_cast<size_t>(E > 0 ? E : 1));
+        w->csr_scratch = base + off;
+        off += up(csr_bytes);
+    }
     w->bytes = off;
     return OEQ_OK;
 }
 
-// x-gradient by per-edge rows (already written to w.h) summed per sender.
-oeq_status det_prepare(oeq_plan *p, int64_t N, int64_t E, const int32_t *src, void *workspace, size_t ws_bytes,
-                       hipStream_t stream, DetWorkspace *w) {
-    if (!workspace) return fail(OEQ_ERR_WORKSPACE, "deterministic mode needs a workspace");
+// Carves the workspace a call needs; fails before any device work if it is
+// missing, misaligned or too small.
+oeq_status ws_bind(const oeq_plan *p, int64_t N, int64_t E, bool det, bool gy_part, void *workspace,
+                   size_t ws_bytes, Workspace *w) {
+    if (!det && !gy_part) return OEQ_OK;
+    if (!workspace) return fail(OEQ_ERR_WORKSPACE, "this call needs a workspace (see oeq_workspace_size)");
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
         return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    oeq_status st = det_layout(p, N, E, static_cast<char *>(workspace), w);
+    oeq_status st = ws_layout(p, N, E, det, gy_part, static_cast<char *>(workspace), w);
     if (st != OEQ_OK) return st;
     if (ws_bytes < w->bytes) return fail(OEQ_ERR_WORKSPACE, "workspace smaller than oeq_workspace_size");
-    const hipError_t e = oeq::sender_csr(N, E, src, w->srowptr, w->sperm, w->csr_scratch, stream);
+    return OEQ_OK;
+}
+
+oeq_status sender_csr_into(int64_t N, int64_t E, const int32_t *src, const Workspace &w, hipStream_t stream) {
+    const hipError_t e = oeq::sender_csr(N, E, src, w.srowptr, w.sperm, w.csr_scratch, stream);
     if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR: ") + hipGetErrorString(e));
     return OEQ_OK;
 }
 
-oeq_status det_finish(oeq_plan *p, int64_t N, const DetWorkspace &w, void *gx, hipStream_t stream) {
+// x-gradient by per-edge rows (already written to w.h) summed per sender.
+oeq_status det_finish(oeq_plan *p, int64_t N, const Workspace &w, void *gx, hipStream_t stream) {
     void *h = w.h;
     int32_t *srp = w.srowptr, *spm = w.sperm;
     int n = static_cast<int>(N);
     void *args[] = {&srp, &spm, &h, &gx, &n};
     return launch(p, "oeq_sender_sum", static_cast<unsigned>(N), 256, stream, args);
+}
+
+oeq_status gy_combine(oeq_plan *p, const Workspace &w, void *gY, int64_t E, hipStream_t stream) {
+    int64_t n = E * p->YD;
+    if (n <= 0) return OEQ_OK;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    void *part = w.gy_part;
+    void *args[] = {&part, &gY, &n};
+    return launch(p, "oeq_gy_combine", static_cast<unsigned>(blocks), 256, stream, args);
 }
 
 }  // namespace
@@ -199,13 +233,10 @@ oeq_status oeq_workspace_size(const oeq_plan *p, int64_t n_nodes, int64_t n_edge
                               size_t *bytes) {
     if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
     if (n_nodes < 0 || n_edges < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
-    if (mode == OEQ_BWD_ATOMIC) {
-        *bytes = 0;
-        return OEQ_OK;
-    }
-    if (mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
-    DetWorkspace w;
-    oeq_status st = det_layout(p, n_nodes, n_edges, nullptr, &w);
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    Workspace w;
+    oeq_status st = ws_layout(p, n_nodes, n_edges, mode == OEQ_BWD_DETERMINISTIC, p->bwd_groups.size() > 1,
+                              nullptr, &w);
     if (st != OEQ_OK) return st;
     *bytes = w.bytes;
     return OEQ_OK;
@@ -220,7 +251,7 @@ oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     oeq_plan *p = const_cast<oeq_plan *>(plan);
     hipStream_t s = static_cast<hipStream_t>(stream);
     void *args[] = {&rowptr, &src, &x, &Y, &W, &out};
-    return launch(p, "oeq_fwd", static_cast<unsigned>(N), static_cast<unsigned>(p->uch * 64), s, args);
+    return launch(p, "oeq_fwd", static_cast<unsigned>(N), fwd_block(p), s, args);
 }
 
 oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,
@@ -234,28 +265,32 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (E == 0) return gx ? fill_zero(p, gx, N * p->XD, s) : OEQ_OK;
     if (!gx && !gY && !gW) return OEQ_OK;
+    const bool det = gx && mode == OEQ_BWD_DETERMINISTIC;
+    const bool gyp = gY && p->bwd_groups.size() > 1;
+    Workspace w;
+    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w)) != OEQ_OK) return st;
     int flags = (gW ? 1 : 0) | (gY ? 2 : 0);
-    const unsigned grid = static_cast<unsigned>(N), block = static_cast<unsigned>(p->uch * 64);
+    void *gy_target = gyp ? w.gy_part : gY;
+    int64_t gy_stride = gyp ? E * p->YD : 0;
+    const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(p->bwd_groups.size()));
+    const unsigned block = bwd_block(p);
     if (!gx) {
-        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gY, &gW, &flags};
-        return launch(p, "oeq_bwd_nogx", grid, block, s, args);
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride};
+        st = launch(p, "oeq_bwd_nogx", grid, block, s, args);
+    } else if (mode == OEQ_BWD_ATOMIC) {
+        if ((st = fill_zero(p, gx, N * p->XD, s)) != OEQ_OK) return st;
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride};
+        if ((st = launch(p, "oeq_bwd_atomic", grid, block, s, args)) != OEQ_OK) return st;
+        st = untranspose(p, N, gx, s);
+    } else {
+        if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
+        void *h = w.h;
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &h, &gy_target, &gW, &flags, &gy_stride};
+        if ((st = launch(p, "oeq_bwd_rows", grid, block, s, args)) != OEQ_OK) return st;
+        st = det_finish(p, N, w, gx, s);
     }
-    if (mode == OEQ_BWD_ATOMIC) {
-        st = fill_zero(p, gx, N * p->XD, s);
-        if (st != OEQ_OK) return st;
-        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gY, &gW, &flags};
-        st = launch(p, "oeq_bwd_atomic", grid, block, s, args);
-        if (st != OEQ_OK) return st;
-        return untranspose(p, N, gx, s);
-    }
-    DetWorkspace w;
-    st = det_prepare(p, N, E, src, workspace, workspace_bytes, s, &w);
     if (st != OEQ_OK) return st;
-    void *h = w.h;
-    void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &h, &gY, &gW, &flags};
-    st = launch(p, "oeq_bwd_rows", grid, block, s, args);
-    if (st != OEQ_OK) return st;
-    return det_finish(p, N, w, gx, s);
+    return gyp ? gy_combine(p, w, gY, E, s) : OEQ_OK;
 }
 
 oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,
@@ -277,32 +312,37 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
         if (dg && (st = fill_zero(p, dg, N * p->OD, s)) != OEQ_OK) return st;
         return OEQ_OK;
     }
+    // d_x = Bx(ggY,W,g) + Bx(Y,ggW,g) vanishes without a Y or W tangent
+    const bool dx_live = dx && (tm & 6);
+    const bool det = dx_live && mode == OEQ_BWD_DETERMINISTIC;
+    const bool gyp = dY && p->bwd_groups.size() > 1;
+    Workspace w;
+    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w)) != OEQ_OK) return st;
+    if (dx && !dx_live && (st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
     int dxmode = 0;
-    DetWorkspace w;
     void *dx_target = nullptr;
-    if (dx) {
-        if (!(tm & 6)) {
-            // d_x = Bx(ggY,W,g) + Bx(Y,ggW,g) vanishes without a Y or W tangent
-            if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
-        } else if (mode == OEQ_BWD_ATOMIC) {
-            if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
-            dxmode = 1;
-            dx_target = dx;
-        } else {
-            if ((st = det_prepare(p, N, E, src, workspace, workspace_bytes, s, &w)) != OEQ_OK) return st;
-            dxmode = 2;
-            dx_target = w.h;
-        }
+    if (dx_live && !det) {
+        if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+        dxmode = 1;
+        dx_target = dx;
+    } else if (det) {
+        if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
+        dxmode = 2;
+        dx_target = w.h;
     }
     if (!dxmode && !dY && !dW && !dg) return OEQ_OK;
     int flags = (dW ? 1 : 0) | (dY ? 2 : 0) | (dg ? 4 : 0) | (dxmode << 3);
+    void *dy_target = gyp ? w.gy_part : dY;
+    int64_t gy_stride = gyp ? E * p->YD : 0;
     const std::string name = "oeq_dbwd_" + std::to_string(tm);
-    void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dY, &dW, &dg, &flags};
-    st = launch(p, name.c_str(), static_cast<unsigned>(N), static_cast<unsigned>(p->uch * 64), s, args);
+    void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dy_target, &dW, &dg, &flags,
+                    &gy_stride};
+    st = launch(p, name.c_str(), static_cast<unsigned>(N * static_cast<int64_t>(p->bwd_groups.size())), bwd_block(p),
+                s, args);
     if (st != OEQ_OK) return st;
-    if (dxmode == 2) return det_finish(p, N, w, dx, s);
-    if (dxmode == 1) return untranspose(p, N, dx, s);
-    return OEQ_OK;
+    if (dxmode == 2 && (st = det_finish(p, N, w, dx, s)) != OEQ_OK) return st;
+    if (dxmode == 1 && (st = untranspose(p, N, dx, s)) != OEQ_OK) return st;
+    return gyp ? gy_combine(p, w, dY, E, s) : OEQ_OK;
 }
 
 oeq_status oeq_csr_workspace_size(int64_t n_nodes, int64_t n_edges, size_t *bytes) {

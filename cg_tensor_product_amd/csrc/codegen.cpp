@@ -7,15 +7,26 @@
 // O(3)-Equivariant Deep Networks", abstract).  Nothing is gathered from a table
 // at run time.
 //
+// The paths are split into groups; one wave computes one group for 64 channels
+// of one receiver, so a wave holds only its group's accumulators, weights and
+// gradients (fewer registers, more waves in flight).  Each group becomes a
+// struct FG<k> (forward) or BG<k> (backward passes) with static member functions
+// working on compact per-group register arrays:
+//   NX / NW / NO      x values, paths (weights) and output values per lane
+//   load_x, load_w, load_g, store_w, store_out, store_x, atomic_x
+//   edge              forward of one edge into the accumulators
+//   vjp<GW, GY, GX>   the three VJP components of one edge (accumulating)
+//
 // Forward, per edge and lane (channel u), for every (x block i1, Y degree l2):
 //   z[m1][m2] = x[m1] * Y[l2, m2]                    (shared by the paths of the pair)
 //   t[m3]     = sum_{(m1,m2,m3) in nz(p)} c * z[m1][m2]
 //   acc_p[m3] += W[p] * t[m3]
-// Backward, per path p, with g the lane's output-gradient block of p:
+// VJP, per path p, with g the lane's output-gradient block of p:
 //   T[m1][m2] = sum_{m3} c * g[m3]
 //   q[m1]     = sum_{m2} Y[m2] T[m1][m2]   ->  gW[p] += sum_{m1} x[m1] q[m1]
 //                                              gx[m1] += W[p] q[m1]
 //   s[m2]     = sum_{m1} x[m1] T[m1][m2]   ->  gY[m2] += W[p] s[m2]
+#include <algorithm>
 #include <cstdio>
 #include <map>
 #include <set>
@@ -48,144 +59,160 @@ std::string fma_term(const std::string &acc, double c, const std::string &v, boo
     return acc + " = fmar(" + lit(c) + ", " + v + ", " + acc + ");";
 }
 
-void emit_moves(std::ostringstream &o, const oeq_plan &p) {
-    // x row <-> registers
-    o << "__device__ __forceinline__ void g_load_x(const real_t *__restrict__ xr, int u, real_t (&v)[NXC]) {\n";
-    for (const auto &b : p.xb) {
-        const int n = 2 * b.l + 1;
-        o << "  { const real_t *q = xr + " << b.row_off << "LL + (i64)u * " << n << ";";
-        for (int m = 0; m < n; ++m) o << " v[" << b.lane_off + m << "] = q[" << m << "];";
-        o << " }\n";
+std::string S(long long v) { return std::to_string(v); }
+
+// Local register layout of one group.
+struct Local {
+    std::vector<int> paths;                 // global path ids, ascending
+    std::map<int, int> xoff;                // x block -> local lane offset
+    std::map<int, int> ooff;                // output block -> local lane offset
+    std::map<int, int> widx;                // global path -> local weight index
+    int nx = 0, nw = 0, no = 0;
+};
+
+Local make_local(const oeq_plan &p, const std::vector<int> &paths) {
+    Local L;
+    L.paths = paths;
+    std::sort(L.paths.begin(), L.paths.end());
+    std::set<int> xs, os;
+    for (int k : L.paths) {
+        xs.insert(p.paths[k].i1);
+        os.insert(p.paths[k].ob);
     }
-    o << "}\n";
-    o << "__device__ __forceinline__ void g_store_x(real_t *__restrict__ xr, int u, const real_t (&v)[NXC]) {\n";
-    for (const auto &b : p.xb) {
-        const int n = 2 * b.l + 1;
-        o << "  { real_t *q = xr + " << b.row_off << "LL + (i64)u * " << n << ";";
-        for (int m = 0; m < n; ++m) o << " q[" << m << "] = v[" << b.lane_off + m << "];";
-        o << " }\n";
+    for (int i : xs) {
+        L.xoff[i] = L.nx;
+        L.nx += 2 * p.xb[i].l + 1;
     }
-    o << "}\n";
-    // x-gradient scatter: with XT the block is addressed m-major (element m*U + u),
-    // so consecutive lanes hit consecutive addresses; oeq_x_untranspose restores
-    // the u-major layout afterwards.
-    o << "__device__ __forceinline__ void g_atomic_x(real_t *__restrict__ xr, int u, const real_t (&v)[NXC]) {\n";
-    for (const auto &b : p.xb) {
+    for (int o : os) {
+        L.ooff[o] = L.no;
+        L.no += 2 * p.ob[o].l + 1;
+    }
+    for (int k : L.paths) L.widx[k] = L.nw++;
+    return L;
+}
+
+// Moves between a node row (u-major blocks) and a lane's compact registers.
+void emit_row_move(std::ostringstream &o, const char *sig, const std::map<int, int> &blocks,
+                   const std::vector<Block> &bl, bool load, const char *ptr) {
+    o << "  static __device__ __forceinline__ void " << sig << " {\n";
+    for (const auto &kv : blocks) {
+        const Block &b = bl[kv.first];
         const int n = 2 * b.l + 1;
-        if (p.xt) {
-            o << "  { real_t *q = xr + " << b.row_off << "LL + u;";
-            for (int m = 0; m < n; ++m)
-                o << " atomicAdd(q + " << static_cast<int64_t>(m) * p.U << ", v[" << b.lane_off + m << "]);";
-        } else {
-            o << "  { real_t *q = xr + " << b.row_off << "LL + (i64)u * " << n << ";";
-            for (int m = 0; m < n; ++m) o << " atomicAdd(q + " << m << ", v[" << b.lane_off + m << "]);";
+        o << "    { " << (load ? "const " : "") << "real_t *q = " << ptr << " + " << b.row_off << "LL + (i64)u * " << n
+          << ";";
+        for (int m = 0; m < n; ++m) {
+            if (load)
+                o << " v[" << kv.second + m << "] = q[" << m << "];";
+            else
+                o << " q[" << m << "] = v[" << kv.second + m << "];";
         }
         o << " }\n";
     }
-    o << "}\n";
-    // m-major -> u-major inside one node row held in LDS
-    o << "__device__ __forceinline__ void g_untranspose_row(const real_t *__restrict__ t, real_t *__restrict__ row) {\n";
-    for (const auto &b : p.xb) {
-        const int n = 2 * b.l + 1;
-        o << "  for (int i = threadIdx.x; i < " << static_cast<int64_t>(n) * p.U << "; i += blockDim.x) { const int u = i / "
-          << n << ", m = i - u * " << n << "; row[" << b.row_off << "LL + i] = t[" << b.row_off << "LL + m * " << p.U
-          << " + u]; }\n";
-    }
-    o << "}\n";
-    // output row <-> registers
-    o << "__device__ __forceinline__ void g_load_g(const real_t *__restrict__ gr, int u, real_t (&v)[NOC]) {\n";
-    for (const auto &b : p.ob) {
-        const int n = 2 * b.l + 1;
-        o << "  { const real_t *q = gr + " << b.row_off << "LL + (i64)u * " << n << ";";
-        for (int m = 0; m < n; ++m) o << " v[" << b.lane_off + m << "] = q[" << m << "];";
-        o << " }\n";
-    }
-    o << "}\n";
-    o << "__device__ __forceinline__ void g_store_out(real_t *__restrict__ orow, int u, const real_t (&v)[NOC]) {\n";
-    for (const auto &b : p.ob) {
-        const int n = 2 * b.l + 1;
-        o << "  { real_t *q = orow + " << b.row_off << "LL + (i64)u * " << n << ";";
-        for (int m = 0; m < n; ++m) o << " q[" << m << "] = v[" << b.lane_off + m << "];";
-        o << " }\n";
-    }
-    o << "}\n";
+    o << "  }\n";
 }
 
-void emit_fwd_edge(std::ostringstream &o, const oeq_plan &p) {
-    o << "__device__ __forceinline__ void g_fwd_edge(const real_t (&x)[NXC], const real_t (&y)[YD], "
-         "const real_t (&w)[P], real_t (&acc)[NOC]) {\n";
-    // group the paths by (x block, l2): the products x*Y are shared inside a group
-    std::map<std::pair<int, int>, std::vector<int>> groups;
-    for (size_t k = 0; k < p.paths.size(); ++k)
-        groups[{p.paths[k].i1, p.paths[k].l2}].push_back(static_cast<int>(k));
-    for (const auto &gkv : groups) {
+void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int g, const std::vector<int> &paths) {
+    const Local L = make_local(p, paths);
+    o << "template <> struct " << name << "<" << g << "> {\n";
+    o << "  static constexpr int NX = " << L.nx << ", NW = " << L.nw << ", NO = " << L.no << ";\n";
+    emit_row_move(o, "load_x(const real_t *__restrict__ xr, int u, real_t (&v)[NX])", L.xoff, p.xb, true, "xr");
+    emit_row_move(o, "store_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX])", L.xoff, p.xb, false, "xr");
+    emit_row_move(o, "load_g(const real_t *__restrict__ gr, int u, real_t (&v)[NO])", L.ooff, p.ob, true, "gr");
+    emit_row_move(o, "store_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO])", L.ooff, p.ob, false, "orow");
+    // x-gradient scatter: with XT the block is addressed m-major (element m*U + u),
+    // so consecutive lanes hit consecutive words; oeq_x_untranspose restores the
+    // u-major layout afterwards.
+    o << "  static __device__ __forceinline__ void atomic_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX]) {\n";
+    for (const auto &kv : L.xoff) {
+        const Block &b = p.xb[kv.first];
+        const int n = 2 * b.l + 1;
+        if (p.xt) {
+            o << "    { real_t *q = xr + " << b.row_off << "LL + u;";
+            for (int m = 0; m < n; ++m)
+                o << " atomicAdd(q + " << S(static_cast<long long>(m) * p.U) << ", v[" << kv.second + m << "]);";
+        } else {
+            o << "    { real_t *q = xr + " << b.row_off << "LL + (i64)u * " << n << ";";
+            for (int m = 0; m < n; ++m) o << " atomicAdd(q + " << m << ", v[" << kv.second + m << "]);";
+        }
+        o << " }\n";
+    }
+    o << "  }\n";
+    // weights: we = W + e*P*U
+    o << "  static __device__ __forceinline__ void load_w(const real_t *__restrict__ we, int u, real_t (&v)[NW]) {";
+    for (int k : L.paths) o << " v[" << L.widx.at(k) << "] = LDW(we + " << S(static_cast<long long>(k) * p.U) << " + u);";
+    o << " }\n";
+    o << "  static __device__ __forceinline__ void store_w(real_t *__restrict__ ge, int u, const real_t (&v)[NW]) {";
+    for (int k : L.paths) o << " STW(ge + " << S(static_cast<long long>(k) * p.U) << " + u, v[" << L.widx.at(k) << "]);";
+    o << " }\n";
+
+    // forward of one edge
+    o << "  static __device__ __forceinline__ void edge(const real_t (&x)[NX], const real_t (&y)[YD], "
+         "const real_t (&w)[NW], real_t (&acc)[NO]) {\n";
+    std::map<std::pair<int, int>, std::vector<int>> pairs;  // (x block, l2) -> paths
+    for (int k : L.paths) pairs[{p.paths[k].i1, p.paths[k].l2}].push_back(k);
+    for (const auto &gkv : pairs) {
         const int i1 = gkv.first.first, l2 = gkv.first.second;
-        const auto &xb = p.xb[i1];
+        const int xo = L.xoff.at(i1);
         std::set<std::pair<int, int>> used;
         for (int k : gkv.second)
             for (const auto &nz : p.paths[k].nz) used.insert({nz.m1, nz.m2});
-        o << "  { // x block " << i1 << " (l=" << xb.l << ") x Y l=" << l2 << "\n";
+        o << "    { // x block " << i1 << " (l=" << p.xb[i1].l << ") x Y l=" << l2 << "\n";
         for (const auto &ab : used)
-            o << "    const real_t z" << ab.first << "_" << ab.second << " = x[" << xb.lane_off + ab.first
-              << "] * y[" << l2 * l2 + ab.second << "];\n";
+            o << "      const real_t z" << ab.first << "_" << ab.second << " = x[" << xo + ab.first << "] * y["
+              << l2 * l2 + ab.second << "];\n";
         for (int k : gkv.second) {
             const Path &pa = p.paths[k];
-            const auto &obk = p.ob[pa.ob];
-            o << "    { // path " << k << ": " << pa.l1 << " x " << pa.l2 << " -> " << pa.l3 << "\n";
+            const int oo = L.ooff.at(pa.ob);
+            o << "      { // path " << k << ": " << pa.l1 << " x " << pa.l2 << " -> " << pa.l3 << "\n";
             for (int m3 = 0; m3 < 2 * pa.l3 + 1; ++m3) {
                 bool first = true;
                 std::ostringstream line;
                 for (const auto &nz : pa.nz) {
                     if (nz.m3 != m3) continue;
-                    line << " " << fma_term("t", nz.c,
-                                            "z" + std::to_string(nz.m1) + "_" + std::to_string(nz.m2), first);
+                    line << " " << fma_term("t", nz.c, "z" + S(nz.m1) + "_" + S(nz.m2), first);
                     first = false;
                 }
                 if (first) continue;  // no coefficient reaches this m3
-                const std::string a = "acc[" + std::to_string(obk.lane_off + m3) + "]";
-                o << "      { real_t t;" << line.str() << " " << a << " = fmar(w[" << k << "], t, " << a
+                const std::string a = "acc[" + S(oo + m3) + "]";
+                o << "        { real_t t;" << line.str() << " " << a << " = fmar(w[" << L.widx.at(k) << "], t, " << a
                   << "); }\n";
             }
-            o << "    }\n";
+            o << "      }\n";
         }
-        o << "  }\n";
+        o << "    }\n";
     }
-    o << "}\n";
-}
+    o << "  }\n";
 
-void emit_bwd_edge(std::ostringstream &o, const oeq_plan &p) {
-    o << "template <bool GW, bool GY, bool GX>\n"
-         "__device__ __forceinline__ void g_bwd_edge(const real_t (&x)[NXC], const real_t (&y)[YD], "
-         "const real_t (&w)[P], const real_t (&g)[NOC], real_t (&gw)[P], real_t (&gy)[YD], real_t (&gx)[NXC]) {\n";
-    for (size_t k = 0; k < p.paths.size(); ++k) {
+    // VJP of one edge
+    o << "  template <bool GW, bool GY, bool GX>\n"
+         "  static __device__ __forceinline__ void vjp(const real_t (&x)[NX], const real_t (&y)[YD], "
+         "const real_t (&w)[NW], const real_t (&g)[NO], real_t (&gw)[NW], real_t (&gy)[YD], real_t (&gx)[NX]) {\n";
+    for (int k : L.paths) {
         const Path &pa = p.paths[k];
-        const auto &xb = p.xb[pa.i1];
-        const auto &obk = p.ob[pa.ob];
+        const int xo = L.xoff.at(pa.i1), oo = L.ooff.at(pa.ob), wk = L.widx.at(k);
         const int n1 = 2 * pa.l1 + 1, n2 = 2 * pa.l2 + 1;
         const int yo = pa.l2 * pa.l2;
-        o << "  { // path " << k << ": " << pa.l1 << " x " << pa.l2 << " -> " << pa.l3 << "\n";
-        // T[a][b] = sum_m3 c g[m3]
+        o << "    { // path " << k << ": " << pa.l1 << " x " << pa.l2 << " -> " << pa.l3 << "\n";
         std::map<std::pair<int, int>, std::vector<const NonZero *>> T;
         for (const auto &nz : pa.nz) T[{nz.m1, nz.m2}].push_back(&nz);
         for (const auto &tkv : T) {
-            const std::string nm = "T" + std::to_string(tkv.first.first) + "_" + std::to_string(tkv.first.second);
-            o << "    real_t " << nm << ";";
+            const std::string nm = "T" + S(tkv.first.first) + "_" + S(tkv.first.second);
+            o << "      real_t " << nm << ";";
             bool first = true;
             for (const NonZero *nz : tkv.second) {
-                o << " " << fma_term(nm, nz->c, "g[" + std::to_string(obk.lane_off + nz->m3) + "]", first);
+                o << " " << fma_term(nm, nz->c, "g[" + S(oo + nz->m3) + "]", first);
                 first = false;
             }
             o << "\n";
         }
-        // q[a] = sum_b y[b] T[a][b]
-        o << "    if constexpr (GW || GX) {\n";
+        o << "      if constexpr (GW || GX) {\n";
         for (int a = 0; a < n1; ++a) {
             bool first = true;
             std::ostringstream line;
             for (const auto &tkv : T) {
                 if (tkv.first.first != a) continue;
-                const std::string tn = "T" + std::to_string(a) + "_" + std::to_string(tkv.first.second);
-                const std::string yv = "y[" + std::to_string(yo + tkv.first.second) + "]";
+                const std::string tn = "T" + S(a) + "_" + S(tkv.first.second);
+                const std::string yv = "y[" + S(yo + tkv.first.second) + "]";
                 if (first)
                     line << " q = " << yv << " * " << tn << ";";
                 else
@@ -193,22 +220,19 @@ void emit_bwd_edge(std::ostringstream &o, const oeq_plan &p) {
                 first = false;
             }
             if (first) continue;
-            o << "      { real_t q;" << line.str();
-            o << " if constexpr (GW) gw[" << k << "] = fmar(x[" << xb.lane_off + a << "], q, gw[" << k
-              << "]);";
-            o << " if constexpr (GX) gx[" << xb.lane_off + a << "] = fmar(w[" << k << "], q, gx["
-              << xb.lane_off + a << "]); }\n";
+            o << "        { real_t q;" << line.str();
+            o << " if constexpr (GW) gw[" << wk << "] = fmar(x[" << xo + a << "], q, gw[" << wk << "]);";
+            o << " if constexpr (GX) gx[" << xo + a << "] = fmar(w[" << wk << "], q, gx[" << xo + a << "]); }\n";
         }
-        o << "    }\n";
-        // s[b] = sum_a x[a] T[a][b]
-        o << "    if constexpr (GY) {\n";
+        o << "      }\n";
+        o << "      if constexpr (GY) {\n";
         for (int b = 0; b < n2; ++b) {
             bool first = true;
             std::ostringstream line;
             for (const auto &tkv : T) {
                 if (tkv.first.second != b) continue;
-                const std::string tn = "T" + std::to_string(tkv.first.first) + "_" + std::to_string(b);
-                const std::string xv = "x[" + std::to_string(xb.lane_off + tkv.first.first) + "]";
+                const std::string tn = "T" + S(tkv.first.first) + "_" + S(b);
+                const std::string xv = "x[" + S(xo + tkv.first.first) + "]";
                 if (first)
                     line << " s = " << xv << " * " << tn << ";";
                 else
@@ -216,11 +240,24 @@ void emit_bwd_edge(std::ostringstream &o, const oeq_plan &p) {
                 first = false;
             }
             if (first) continue;
-            o << "      { real_t s;" << line.str() << " gy[" << yo + b << "] = fmar(w[" << k
-              << "], s, gy[" << yo + b << "]); }\n";
+            o << "        { real_t s;" << line.str() << " gy[" << yo + b << "] = fmar(w[" << wk << "], s, gy[" << yo + b
+              << "]); }\n";
         }
+        o << "      }\n";
         o << "    }\n";
-        o << "  }\n";
+    }
+    o << "  }\n";
+    o << "};\n";
+}
+
+void emit_untranspose(std::ostringstream &o, const oeq_plan &p) {
+    // m-major -> u-major inside one node row held in LDS
+    o << "__device__ __forceinline__ void g_untranspose_row(const real_t *__restrict__ t, real_t *__restrict__ row) {\n";
+    for (const auto &b : p.xb) {
+        const int n = 2 * b.l + 1;
+        o << "  for (int i = threadIdx.x; i < " << S(static_cast<long long>(n) * p.U)
+          << "; i += blockDim.x) { const int u = i / " << n << ", m = i - u * " << n << "; row[" << b.row_off
+          << "LL + i] = t[" << b.row_off << "LL + m * " << p.U << " + u]; }\n";
     }
     o << "}\n";
 }
@@ -237,15 +274,38 @@ std::string emit_source(const oeq_plan &p) {
     o << "// Generated for: U=" << p.U << ", x blocks";
     for (const auto &b : p.xb) o << " " << b.l << (b.parity > 0 ? "e" : "o");
     o << ", Y degrees 0.." << p.L << ", " << p.paths.size() << " paths, " << p.total_nnz
-      << " CG non-zeros, dtype " << (p.dtype == OEQ_F64 ? "f64" : "f32") << "\n";
+      << " CG non-zeros, dtype " << (p.dtype == OEQ_F64 ? "f64" : "f32") << "; forward groups of";
+    for (const auto &g : p.fwd_groups) o << " " << g.size();
+    o << " paths, backward groups of";
+    for (const auto &g : p.bwd_groups) o << " " << g.size();
+    o << " paths\n";
     o << "typedef " << (p.dtype == OEQ_F64 ? "double" : "float") << " real_t;\n";
     o << "typedef long long i64;\n";
     o << "__device__ __forceinline__ float fmar(float a, float b, float c) { return __builtin_fmaf(a, b, c); }\n";
     o << "__device__ __forceinline__ double fmar(double a, double b, double c) { return __builtin_fma(a, b, c); }\n";
+    if (p.nt_w) {
+        // W and its gradients are streamed once: non-temporal accesses keep them out of the way of x and g
+        o << "#define LDW(ptr) __builtin_nontemporal_load(ptr)\n";
+        o << "#define STW(ptr, v) __builtin_nontemporal_store((v), (ptr))\n";
+    } else {
+        o << "#define LDW(ptr) (*(ptr))\n";
+        o << "#define STW(ptr, v) (*(ptr) = (v))\n";
+    }
+    // a scheduling barrier after the next edge's loads keeps them from being sunk
+    // toward their uses, which would expose the full memory latency every edge
+    o << (p.pin_fwd ? "#define PIN_FWD() __builtin_amdgcn_sched_barrier(0)\n" : "#define PIN_FWD() ((void)0)\n");
+    o << (p.pin_bwd ? "#define PIN_BWD() __builtin_amdgcn_sched_barrier(0)\n" : "#define PIN_BWD() ((void)0)\n");
+    // occupancy window handed to the compiler's scheduler (waves per SIMD)
+    auto occ = [](const std::pair<int, int> &w) {
+        return w.first > 0 ? "__attribute__((amdgpu_waves_per_eu(" + S(w.first) + ", " + S(w.second) + ")))"
+                           : std::string();
+    };
+    o << "#define FWD_OCCUPANCY " << occ(p.fwd_waves) << "\n";
+    o << "#define BWD_OCCUPANCY " << occ(p.bwd_waves) << "\n";
     o << "constexpr int U = " << p.U << ";\n";
     o << "constexpr int UCH = " << p.uch << ";\n";
-    o << "constexpr int NXC = " << p.NXC << ";\n";
-    o << "constexpr int NOC = " << p.NOC << ";\n";
+    o << "constexpr int NGF = " << p.fwd_groups.size() << ";\n";
+    o << "constexpr int NGB = " << p.bwd_groups.size() << ";\n";
     o << "constexpr int P = " << p.paths.size() << ";\n";
     o << "constexpr int YD = " << p.YD << ";\n";
     o << "constexpr int PY = " << py << ";\n";
@@ -254,9 +314,11 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr i64 XD = " << p.XD << "LL;\n";
     o << "constexpr i64 OD = " << p.OD << "LL;\n";
     o << "constexpr bool XT = " << (p.xt ? "true" : "false") << ";\n";
-    emit_moves(o, p);
-    emit_fwd_edge(o, p);
-    emit_bwd_edge(o, p);
+    o << "template <int G> struct FG;\n";
+    o << "template <int G> struct BG;\n";
+    for (size_t g = 0; g < p.fwd_groups.size(); ++g) emit_group(o, p, "FG", static_cast<int>(g), p.fwd_groups[g]);
+    for (size_t g = 0; g < p.bwd_groups.size(); ++g) emit_group(o, p, "BG", static_cast<int>(g), p.bwd_groups[g]);
+    emit_untranspose(o, p);
     o << kKernelTemplate;
     return o.str();
 }

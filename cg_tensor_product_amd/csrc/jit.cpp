@@ -94,6 +94,10 @@ oeq_status jit_compile(oeq_plan &p, std::string *why) {
     const std::string dir = cache_dir();
     const bool use_cache = !dir.empty() && std::getenv("OEQ_NO_CACHE") == nullptr;
     const std::string path = dir + "/" + p.code_key + ".hsaco";
+    if (std::getenv("OEQ_DUMP_SOURCE") && !dir.empty()) {
+        mkdir(dir.c_str(), 0775);
+        std::ofstream(dir + "/" + p.code_key + ".hip") << p.source;
+    }
     if (use_cache && read_file(path, p.code)) return OEQ_OK;
 
     hiprtcProgram prog;

@@ -1,23 +1,22 @@
 // Kernel templates of the fused UVU CG tensor-product convolution (gfx950).
 //
 // This text is compiled at plan time with hipRTC, after a prelude emitted by
-// the planner that defines, for one descriptor and dtype:
-//   real_t; U, UCH (64-channel chunks), NXC / NOC (values per channel of an x
-//   row / output row), P (paths), YD ((L+1)^2), PY (YD rounded up to a power of
-//   two), LGPY (log2 PY), GY_TILE, XD, OD;
-//   g_load_x / g_load_g / g_store_out / g_store_x / g_atomic_x: per-lane
-//   moves between a node row and registers (lane u holds channel u);
-//   g_fwd_edge: out += f(x, Y, W) for one edge, the unrolled sparse CG stream;
-//   g_bwd_edge<GW, GY, GX>: the three VJP components of one edge (accumulating).
+// the planner that defines, for one descriptor and dtype: real_t; U, UCH
+// (64-channel chunks), NGF / NGB (forward / backward path groups), P (paths), YD
+// ((L+1)^2), PY (YD rounded up to a power of two), LGPY (log2 PY), GY_TILE, XD,
+// OD, XT; LDW / STW (loads and stores of W and its gradients); and the group
+// structs FG<g> / BG<g> (see the planner's code generator) holding the unrolled
+// sparse CG streams of one group of paths.
 //
 // Ownership follows "Receiver-streaming convolutions for channel-wise UVU tensor
-// products" (opening post): a workgroup owns one receiver, its UCH waves split the
-// channels (lane = channel), and the waves stream that receiver's edges in CSR
-// order.  The forward keeps the output row in registers and stores it once (no
-// atomics).  The backward passes treat one edge at a time per wave: W-gradients
-// are stored directly, Y-gradients are reduced across the 64 lanes and then
-// across the waves through LDS, x-gradients go to the senders either by
-// hardware atomics or as per-edge rows summed later per sender.
+// products" (opening post): a workgroup owns one receiver; each of its waves owns
+// one 64-channel chunk (lane = channel) of one path group and streams the
+// receiver's edges in CSR order.  The forward keeps its output values in
+// registers and stores them once (no atomics).  The backward passes treat one
+// edge at a time per wave: W-gradients are stored directly, Y-gradients are
+// reduced across the 64 lanes and then across the waves through LDS, and
+// x-gradients go to the senders either by hardware atomics or as per-edge rows
+// summed later per sender.
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -32,19 +31,6 @@ __device__ __forceinline__ void load_y(const real_t *__restrict__ Y, int e, real
     const real_t *yr = Y + (i64)e * YD;
 #pragma unroll
     for (int k = 0; k < YD; ++k) yv[k] = yr[k];
-}
-
-// W[e, :, u] (one value per path; consecutive lanes read consecutive channels).
-__device__ __forceinline__ void load_w(const real_t *__restrict__ W, int e, int u, real_t (&wv)[P]) {
-    const real_t *wr = W + (i64)e * (P * U) + u;
-#pragma unroll
-    for (int p = 0; p < P; ++p) wv[p] = wr[p * U];
-}
-
-__device__ __forceinline__ void store_w(real_t *__restrict__ G, int e, int u, const real_t (&wv)[P]) {
-    real_t *wr = G + (i64)e * (P * U) + u;
-#pragma unroll
-    for (int p = 0; p < P; ++p) wr[p * U] = wv[p];
 }
 
 // Cross-lane moves on 32-bit words; a double moves as two words.
@@ -163,42 +149,63 @@ oeq_fill_zero(real_t *__restrict__ p, i64 n) {
 // ---------------------------------------------------------------------------
 // Forward: out[r] = sum over the receiver's edges of the per-edge messages.
 // ---------------------------------------------------------------------------
-extern "C" __global__ void __launch_bounds__(UCH * 64)
-oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src,
-        const real_t *__restrict__ x, const real_t *__restrict__ Y,
-        const real_t *__restrict__ W, real_t *__restrict__ out) {
-    const int r = blockIdx.x;
-    const int lane = threadIdx.x & 63;
-    const int u = uni(threadIdx.x >> 6) * 64 + lane;
+template <int G>
+__device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ rowptr,
+                                          const int *__restrict__ src, const real_t *__restrict__ x,
+                                          const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                          real_t *__restrict__ out) {
+    using Gr = FG<G>;
     const bool act = (U % 64 == 0) || (u < U);
     const int uu = act ? u : 0;  // inactive lanes read channel 0 and store nothing
-    real_t acc[NOC];
+    real_t acc[Gr::NO];
     zero(acc);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     if (e0 < e1) {
         // software pipeline: the next edge's loads are in flight while this one computes
         int s = uni(src[e0]);
-        real_t yv[YD], xv[NXC], wv[P];
+        real_t yv[YD], xv[Gr::NX], wv[Gr::NW];
         load_y(Y, e0, yv);
-        g_load_x(x + (i64)s * XD, uu, xv);
-        load_w(W, e0, uu, wv);
+        Gr::load_x(x + (i64)s * XD, uu, xv);
+        Gr::load_w(W + (i64)e0 * (P * U), uu, wv);
         for (int e = e0; e < e1; ++e) {
-            real_t yn[YD], xn[NXC], wn[P];
+            real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
             const int en = (e + 1 < e1) ? e + 1 : e;
             const int sn = uni(src[en]);
             load_y(Y, en, yn);
-            g_load_x(x + (i64)sn * XD, uu, xn);
-            load_w(W, en, uu, wn);
-            g_fwd_edge(xv, yv, wv, acc);
+            Gr::load_x(x + (i64)sn * XD, uu, xn);
+            Gr::load_w(W + (i64)en * (P * U), uu, wn);
+            // keep the next edge's loads ahead of this edge's arithmetic
+            PIN_FWD();
+            Gr::edge(xv, yv, wv, acc);
 #pragma unroll
             for (int k = 0; k < YD; ++k) yv[k] = yn[k];
 #pragma unroll
-            for (int k = 0; k < NXC; ++k) xv[k] = xn[k];
+            for (int k = 0; k < Gr::NX; ++k) xv[k] = xn[k];
 #pragma unroll
-            for (int k = 0; k < P; ++k) wv[k] = wn[k];
+            for (int k = 0; k < Gr::NW; ++k) wv[k] = wn[k];
         }
     }
-    if (act) g_store_out(out + (i64)r * OD, u, acc);
+    if (act) Gr::store_out(out + (i64)r * OD, u, acc);
+}
+
+template <int G>
+__device__ __forceinline__ void fwd_dispatch(int grp, int r, int u, const int *__restrict__ rowptr,
+                                             const int *__restrict__ src, const real_t *__restrict__ x,
+                                             const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                             real_t *__restrict__ out) {
+    if (grp == G) {
+        fwd_group<G>(r, u, rowptr, src, x, Y, W, out);
+        return;
+    }
+    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1>(grp, r, u, rowptr, src, x, Y, W, out);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
+oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+        const real_t *__restrict__ Y, const real_t *__restrict__ W, real_t *__restrict__ out) {
+    const int w = uni(threadIdx.x >> 6);
+    const int grp = w / UCH, uc = w - grp * UCH;
+    fwd_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out);
 }
 
 // The atomic x-gradient is accumulated m-major inside each x block (so the
@@ -216,7 +223,10 @@ oeq_x_untranspose(real_t *__restrict__ gx) {
 
 // ---------------------------------------------------------------------------
 // Y-gradient staging: per-wave lane-reduced rows in LDS, summed over the waves
-// of the workgroup (fixed order) every GY_TILE edges.
+// of the workgroup (fixed order) every GY_TILE edges.  In the backward passes a
+// workgroup is one (receiver, path group); with several groups each writes its
+// partial Y-gradient rows to its own slice of the workspace and oeq_gy_combine
+// adds the slices in group order.
 // ---------------------------------------------------------------------------
 struct GyStage {
     real_t red[UCH][GY_TILE][PY];
@@ -252,80 +262,118 @@ __device__ __forceinline__ void gy_flush(GyStage &st, real_t *__restrict__ gY, i
 
 // flags: bit0 store grad_W, bit1 store grad_Y
 // GXMODE: 0 no x gradient, 1 atomic add into gx[src[e]], 2 store row h[e] (summed per sender later)
-template <int GXMODE>
-__device__ __forceinline__ void bwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
-                                         const real_t *__restrict__ x, const real_t *__restrict__ Y,
-                                         const real_t *__restrict__ W, const real_t *__restrict__ g,
-                                         real_t *__restrict__ gx, real_t *__restrict__ gY,
-                                         real_t *__restrict__ gW, int flags) {
-    __shared__ GyStage st;
-    const int r = blockIdx.x;
+template <int GXMODE, int G>
+__device__ __forceinline__ void bwd_group(GyStage &st, int r, int wv, int u, const int *__restrict__ rowptr,
+                                          const int *__restrict__ src, const real_t *__restrict__ x,
+                                          const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                          const real_t *__restrict__ g, real_t *__restrict__ gx,
+                                          real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
+    using Gr = BG<G>;
     const int lane = threadIdx.x & 63;
-    const int wv = uni(threadIdx.x >> 6);
-    const int u = wv * 64 + lane;
     const bool act = (U % 64 == 0) || (u < U);
     const int uu = act ? u : 0;
     const bool want_gw = (flags & 1) != 0, want_gy = (flags & 2) != 0;
-    real_t gv[NOC];
-    g_load_g(g + (i64)r * OD, uu, gv);
+    real_t gv[Gr::NO];
+    Gr::load_g(g + (i64)r * OD, uu, gv);
     if (!act) zero(gv);  // inactive lanes contribute nothing to the lane sums
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     if (e0 >= e1) return;
     // software pipeline: the next edge's loads are in flight while this one computes
     int s = uni(src[e0]);
-    real_t yv[YD], xv[NXC], wv_[P];
+    real_t yv[YD], xv[Gr::NX], wv_[Gr::NW];
     load_y(Y, e0, yv);
-    g_load_x(x + (i64)s * XD, uu, xv);
-    load_w(W, e0, uu, wv_);
+    Gr::load_x(x + (i64)s * XD, uu, xv);
+    Gr::load_w(W + (i64)e0 * (P * U), uu, wv_);
     for (int e = e0; e < e1; ++e) {
         const int en = (e + 1 < e1) ? e + 1 : e;
         const int sn = uni(src[en]);
-        real_t yn[YD], xn[NXC], wn[P];
+        real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
         load_y(Y, en, yn);
-        g_load_x(x + (i64)sn * XD, uu, xn);
-        load_w(W, en, uu, wn);
+        Gr::load_x(x + (i64)sn * XD, uu, xn);
+        Gr::load_w(W + (i64)en * (P * U), uu, wn);
+        // keep the next edge's loads ahead of this edge's arithmetic
+        PIN_BWD();
         const int j = uni((e - e0) % GY_TILE);
-        real_t gw[P], gy[YD], gxp[NXC];
+        real_t gw[Gr::NW], gy[YD], gxp[Gr::NX];
         zero(gw);
         zero(gy);
         zero(gxp);
-        g_bwd_edge<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
-        if (want_gw && act) store_w(gW, e, u, gw);
+        Gr::template vjp<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
+        if (want_gw && act) Gr::store_w(gW + (i64)e * (P * U), u, gw);
         if (want_gy) {
             gy_push(st, gY, e, j, gy, lane, wv);
             if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, gY, e - j, j + 1);
         }
-        if (GXMODE == 1 && act) g_atomic_x(gx + (i64)s * XD, u, gxp);
-        if (GXMODE == 2 && act) g_store_x(gx + (i64)e * XD, u, gxp);
+        if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * XD, u, gxp);
+        if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * XD, u, gxp);
         s = sn;
 #pragma unroll
         for (int k = 0; k < YD; ++k) yv[k] = yn[k];
 #pragma unroll
-        for (int k = 0; k < NXC; ++k) xv[k] = xn[k];
+        for (int k = 0; k < Gr::NX; ++k) xv[k] = xn[k];
 #pragma unroll
-        for (int k = 0; k < P; ++k) wv_[k] = wn[k];
+        for (int k = 0; k < Gr::NW; ++k) wv_[k] = wn[k];
     }
 }
 
-extern "C" __global__ void __launch_bounds__(UCH * 64)
+template <int GXMODE, int G>
+__device__ __forceinline__ void bwd_dispatch(GyStage &st, int r, int grp, int wv, int u, const int *__restrict__ rowptr,
+                                             const int *__restrict__ src, const real_t *__restrict__ x,
+                                             const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                             const real_t *__restrict__ g, real_t *__restrict__ gx,
+                                             real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
+    if (grp == G) {
+        bwd_group<GXMODE, G>(st, r, wv, u, rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+        return;
+    }
+    if constexpr (G + 1 < NGB)
+        bwd_dispatch<GXMODE, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+}
+
+template <int GXMODE>
+__device__ __forceinline__ void bwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
+                                         const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                         const real_t *__restrict__ W, const real_t *__restrict__ g,
+                                         real_t *__restrict__ gx, real_t *__restrict__ gY,
+                                         real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    __shared__ GyStage st;
+    const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
+    const int wv = uni(threadIdx.x >> 6);
+    bwd_dispatch<GXMODE, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, gx,
+                            gY + grp * gy_stride, gW, flags);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
 oeq_bwd_nogx(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
              const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
-             real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
-    bwd_body<0>(rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+             real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    bwd_body<0>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride);
 }
 
-extern "C" __global__ void __launch_bounds__(UCH * 64)
+extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
 oeq_bwd_atomic(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
                const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
-               real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
-    bwd_body<1>(rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+               real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    bwd_body<1>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride);
 }
 
-extern "C" __global__ void __launch_bounds__(UCH * 64)
+extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
 oeq_bwd_rows(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
              const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
-             real_t *__restrict__ h, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
-    bwd_body<2>(rowptr, src, x, Y, W, g, h, gY, gW, flags);
+             real_t *__restrict__ h, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    bwd_body<2>(rowptr, src, x, Y, W, g, h, gY, gW, flags, gy_stride);
+}
+
+// Y-gradient of several path groups: gY = sum over groups of the partial rows,
+// in group order.
+extern "C" __global__ void __launch_bounds__(256)
+oeq_gy_combine(const real_t *__restrict__ part, real_t *__restrict__ gY, i64 n) {
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x) {
+        real_t s = part[i];
+#pragma unroll
+        for (int gidx = 1; gidx < NGB; ++gidx) s += part[gidx * n + i];
+        gY[i] = s;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -340,7 +388,16 @@ oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
     const int k0 = uni(srowptr[s]), k1 = uni(srowptr[s + 1]);
     for (i64 c = threadIdx.x; c < XD; c += 256) {
         real_t acc = real_t(0);
-        for (int k = k0; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * XD + c];
+        int k = k0;
+        // eight rows in flight, added in edge order
+        for (; k + 8 <= k1; k += 8) {
+            real_t t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[j] = h[(i64)uni(sperm[k + j]) * XD + c];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += t[j];
+        }
+        for (; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * XD + c];
         gx[(i64)s * XD + c] = acc;
     }
 }
@@ -352,41 +409,38 @@ oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
 //   d_x = Bx(ggY,W,g) + Bx(Y,ggW,g)                         (to senders)
 // flags: bit0 d_W, bit1 d_Y, bit2 d_grad_out, bits 3-4 d_x mode (0 none, 1 atomic, 2 rows)
 // ---------------------------------------------------------------------------
-template <int TM>
-__device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
-                                          const real_t *__restrict__ x, const real_t *__restrict__ Y,
-                                          const real_t *__restrict__ W, const real_t *__restrict__ g,
-                                          const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,
-                                          const real_t *__restrict__ ggW, real_t *__restrict__ dx,
-                                          real_t *__restrict__ dY, real_t *__restrict__ dW,
-                                          real_t *__restrict__ dg, int flags) {
-    __shared__ GyStage st;
-    const int r = blockIdx.x;
+template <int TM, int G>
+__device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, const int *__restrict__ rowptr,
+                                           const int *__restrict__ src, const real_t *__restrict__ x,
+                                           const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                           const real_t *__restrict__ g, const real_t *__restrict__ ggx,
+                                           const real_t *__restrict__ ggY, const real_t *__restrict__ ggW,
+                                           real_t *__restrict__ dx, real_t *__restrict__ dY,
+                                           real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {
+    using Gr = BG<G>;
     const int lane = threadIdx.x & 63;
-    const int wv = uni(threadIdx.x >> 6);
-    const int u = wv * 64 + lane;
     const bool act = (U % 64 == 0) || (u < U);
     const int uu = act ? u : 0;
     const bool want_dw = (flags & 1) != 0, want_dy = (flags & 2) != 0, want_dg = (flags & 4) != 0;
     const int dxmode = (flags >> 3) & 3;
     constexpr bool HAS_DX = (TM & 6) != 0;
-    real_t gv[NOC];
-    g_load_g(g + (i64)r * OD, uu, gv);
+    real_t gv[Gr::NO];
+    Gr::load_g(g + (i64)r * OD, uu, gv);
     if (!act) zero(gv);
-    real_t dgacc[NOC];
+    real_t dgacc[Gr::NO];
     zero(dgacc);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     // per-edge operands (unused ones are dropped by the compiler for a given TM)
     struct Ops {
-        real_t y[YD], x[NXC], w[P], tx[NXC], ty[YD], tw[P];
+        real_t y[YD], x[Gr::NX], w[Gr::NW], tx[Gr::NX], ty[YD], tw[Gr::NW];
     };
     auto load = [&](int e, int s, Ops &o) {
         load_y(Y, e, o.y);
-        g_load_x(x + (i64)s * XD, uu, o.x);
-        load_w(W, e, uu, o.w);
-        if (TM & 1) g_load_x(ggx + (i64)s * XD, uu, o.tx);
+        Gr::load_x(x + (i64)s * XD, uu, o.x);
+        Gr::load_w(W + (i64)e * (P * U), uu, o.w);
+        if (TM & 1) Gr::load_x(ggx + (i64)s * XD, uu, o.tx);
         if (TM & 2) load_y(ggY, e, o.ty);
-        if (TM & 4) load_w(ggW, e, uu, o.tw);
+        if (TM & 4) Gr::load_w(ggW + (i64)e * (P * U), uu, o.tw);
     };
     if (e0 < e1) {
         int s = uni(src[e0]);
@@ -397,45 +451,78 @@ __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const 
             const int sn = uni(src[en]);
             Ops nxt;
             load(en, sn, nxt);
+            // keep the next edge's loads ahead of this edge's arithmetic
+            PIN_BWD();
             const int j = uni((e - e0) % GY_TILE);
-            real_t dw[P], dy[YD], dxp[NXC];
+            real_t dw[Gr::NW], dy[YD], dxp[Gr::NX];
             zero(dw);
             zero(dy);
             zero(dxp);
             if (TM & 1) {
-                if (want_dg) g_fwd_edge(cur.tx, cur.y, cur.w, dgacc);
-                g_bwd_edge<true, true, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
+                if (want_dg) Gr::edge(cur.tx, cur.y, cur.w, dgacc);
+                Gr::template vjp<true, true, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
             }
             if (TM & 2) {
-                if (want_dg) g_fwd_edge(cur.x, cur.ty, cur.w, dgacc);
-                g_bwd_edge<true, false, true>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
+                if (want_dg) Gr::edge(cur.x, cur.ty, cur.w, dgacc);
+                Gr::template vjp<true, false, true>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
             }
             if (TM & 4) {
-                if (want_dg) g_fwd_edge(cur.x, cur.y, cur.tw, dgacc);
-                g_bwd_edge<false, true, true>(cur.x, cur.y, cur.tw, gv, dw, dy, dxp);
+                if (want_dg) Gr::edge(cur.x, cur.y, cur.tw, dgacc);
+                Gr::template vjp<false, true, true>(cur.x, cur.y, cur.tw, gv, dw, dy, dxp);
             }
-            if (want_dw && act) store_w(dW, e, u, dw);
+            if (want_dw && act) Gr::store_w(dW + (i64)e * (P * U), u, dw);
             if (want_dy) {
                 gy_push(st, dY, e, j, dy, lane, wv);
                 if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, dY, e - j, j + 1);
             }
-            if (HAS_DX && dxmode == 1 && act) g_atomic_x(dx + (i64)s * XD, u, dxp);
-            if (HAS_DX && dxmode == 2 && act) g_store_x(dx + (i64)e * XD, u, dxp);
+            if (HAS_DX && dxmode == 1 && act) Gr::atomic_x(dx + (i64)s * XD, u, dxp);
+            if (HAS_DX && dxmode == 2 && act) Gr::store_x(dx + (i64)e * XD, u, dxp);
             s = sn;
             cur = nxt;
         }
     }
-    if (want_dg && act) g_store_out(dg + (i64)r * OD, u, dgacc);
+    if (want_dg && act) Gr::store_out(dg + (i64)r * OD, u, dgacc);
+}
+
+template <int TM, int G>
+__device__ __forceinline__ void dbwd_dispatch(GyStage &st, int r, int grp, int wv, int u, const int *__restrict__ rowptr,
+                                              const int *__restrict__ src, const real_t *__restrict__ x,
+                                              const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                              const real_t *__restrict__ g, const real_t *__restrict__ ggx,
+                                              const real_t *__restrict__ ggY, const real_t *__restrict__ ggW,
+                                              real_t *__restrict__ dx, real_t *__restrict__ dY,
+                                              real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {
+    if (grp == G) {
+        dbwd_group<TM, G>(st, r, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
+        return;
+    }
+    if constexpr (G + 1 < NGB)
+        dbwd_dispatch<TM, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
+}
+
+template <int TM>
+__device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
+                                          const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                          const real_t *__restrict__ W, const real_t *__restrict__ g,
+                                          const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,
+                                          const real_t *__restrict__ ggW, real_t *__restrict__ dx,
+                                          real_t *__restrict__ dY, real_t *__restrict__ dW,
+                                          real_t *__restrict__ dg, int flags, i64 gy_stride) {
+    __shared__ GyStage st;
+    const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
+    const int wv = uni(threadIdx.x >> 6);
+    dbwd_dispatch<TM, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx,
+                         dY + grp * gy_stride, dW, dg, flags);
 }
 
 #define OEQ_DBWD_KERNEL(TM)                                                                       \
-    extern "C" __global__ void __launch_bounds__(UCH * 64) oeq_dbwd_##TM(                          \
+    extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY oeq_dbwd_##TM(                  \
         const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x, \
         const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,  \
         const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,                            \
         const real_t *__restrict__ ggW, real_t *__restrict__ dx, real_t *__restrict__ dY,          \
-        real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {                             \
-        dbwd_body<TM>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);              \
+        real_t *__restrict__ dW, real_t *__restrict__ dg, int flags, i64 gy_stride) {              \
+        dbwd_body<TM>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags, gy_stride);   \
     }
 OEQ_DBWD_KERNEL(1)
 OEQ_DBWD_KERNEL(2)

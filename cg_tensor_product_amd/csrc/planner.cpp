@@ -9,7 +9,12 @@
 // table (compact storage of the structurally non-zero part, as the UMA kernel
 // work compacts its rotation blocks in "Optimize UMA SO2 and Wigner inference
 // kernels").
+#include <algorithm>
+#include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <map>
+#include <set>
 #include <sstream>
 
 #include "planner.hpp"
@@ -25,6 +30,93 @@ oeq_status fail(std::string *why, oeq_status st, const std::string &msg) {
 
 }  // namespace
 
+// Splits the paths into at most `want` groups by longest-processing-time
+// assignment of indivisible units.  Paths that share an output block always
+// stay together (a block is written by one wave); so do paths that share the
+// (x block, l2) pair in the forward (they share products x*Y), and paths that
+// share an x block in the backward passes (that block's gradient is then owned
+// by one wave, so per-edge x-gradient rows never overlap).
+std::vector<std::vector<int>> partition_paths(const oeq_plan &p, bool fwd, int want) {
+    const int n = static_cast<int>(p.paths.size());
+    std::vector<int> parent(n);
+    for (int i = 0; i < n; ++i) parent[i] = i;
+    auto find = [&](int a) {
+        while (parent[a] != a) a = parent[a] = parent[parent[a]];
+        return a;
+    };
+    auto unite = [&](int a, int b) { parent[find(a)] = find(b); };
+    for (int a = 0; a < n; ++a)
+        for (int b = a + 1; b < n; ++b) {
+            const Path &pa = p.paths[a], &pb = p.paths[b];
+            const bool same = fwd ? (pa.i1 == pb.i1 && pa.l2 == pb.l2) : (pa.i1 == pb.i1);
+            if (same || pa.ob == pb.ob) unite(a, b);
+        }
+    std::map<int, std::vector<int>> units;
+    for (int k = 0; k < n; ++k) units[find(k)].push_back(k);
+    std::vector<std::pair<double, std::vector<int>>> uc;
+    for (auto &kv : units) {
+        double c = 0.0;
+        for (int k : kv.second) {
+            const Path &pa = p.paths[k];
+            const double nnz = static_cast<double>(pa.nz.size());
+            c += fwd ? nnz + (2 * pa.l3 + 1) + (2 * pa.l1 + 1)
+                     : nnz + 2.0 * (2 * pa.l1 + 1) * (2 * pa.l2 + 1) + 2 * (2 * pa.l1 + 1) + (2 * pa.l2 + 1);
+        }
+        uc.push_back({c, kv.second});
+    }
+    std::stable_sort(uc.begin(), uc.end(), [](const auto &a, const auto &b) { return a.first > b.first; });
+    const int g = std::max(1, std::min(want, static_cast<int>(uc.size())));
+    std::vector<std::vector<int>> groups(g);
+    std::vector<double> load(g, 0.0);
+    for (auto &u : uc) {
+        const int t = static_cast<int>(std::min_element(load.begin(), load.end()) - load.begin());
+        load[t] += u.first;
+        groups[t].insert(groups[t].end(), u.second.begin(), u.second.end());
+    }
+    for (auto &gr : groups) std::sort(gr.begin(), gr.end());
+    std::sort(groups.begin(), groups.end());
+    return groups;
+}
+
+// Rough per-lane register demand of a group (values held across the edge loop
+// plus the largest transient product set), used to choose the group count.
+int group_registers(const oeq_plan &p, const std::vector<int> &paths, bool fwd) {
+    std::set<int> xs, os;
+    int transient = 0;
+    for (int k : paths) {
+        const Path &pa = p.paths[k];
+        xs.insert(pa.i1);
+        os.insert(pa.ob);
+        transient = std::max(transient, (2 * pa.l1 + 1) * (2 * pa.l2 + 1));
+    }
+    int nx = 0, no = 0;
+    for (int i : xs) nx += 2 * p.xb[i].l + 1;
+    for (int o : os) no += 2 * p.ob[o].l + 1;
+    const int nw = static_cast<int>(paths.size());
+    const int vals = fwd ? no + 2 * (nx + nw) + transient : no + 2 * (nx + nw) + p.YD + nx + transient;
+    return vals * (p.dtype == OEQ_F64 ? 2 : 1) + 20;
+}
+
+std::vector<std::vector<int>> choose_groups(const oeq_plan &p, bool fwd) {
+    const char *env = std::getenv(fwd ? "OEQ_FWD_GROUPS" : "OEQ_BWD_GROUPS");
+    const int max_g = std::max(1, 16 / p.uch);  // at most 16 waves per workgroup
+    if (env) return partition_paths(p, fwd, std::max(1, std::min(std::atoi(env), max_g)));
+    // Measured on MI355X: splitting the backward passes costs more (a lane
+    // reduction of the Y-gradient per group and per edge) than the occupancy it
+    // buys; the forward gains once one group would need more than ~160 registers.
+    if (!fwd) return partition_paths(p, fwd, 1);
+    const int budget = 160;
+    std::vector<std::vector<int>> best = partition_paths(p, fwd, 1);
+    for (int g = 1; g <= max_g; ++g) {
+        auto cand = partition_paths(p, fwd, g);
+        best = cand;
+        int worst = 0;
+        for (const auto &gr : cand) worst = std::max(worst, group_registers(p, gr, fwd));
+        if (worst <= budget || static_cast<int>(cand.size()) < g) break;
+    }
+    return best;
+}
+
 oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     if (!d) return fail(why, OEQ_ERR_INVALID_ARG, "descriptor is NULL");
     if (d->dtype != OEQ_F32 && d->dtype != OEQ_F64)
@@ -38,7 +130,7 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     p->YD = (d->y_lmax + 1) * (d->y_lmax + 1);
     p->U = d->x_irreps[0].mul;
     if (p->U <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "multiplicity must be >= 1");
-    if (p->U > 4096) return fail(why, OEQ_ERR_UNSUPPORTED, "multiplicity above 4096");
+    if (p->U > 1024) return fail(why, OEQ_ERR_UNSUPPORTED, "multiplicity above 1024");
     int lane = 0;
     for (int i = 0; i < d->n_x; ++i) {
         const oeq_irrep &ir = d->x_irreps[i];
@@ -152,6 +244,24 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     p->uch = (p->U + 63) / 64;
     // m-major atomics need one node row in LDS for the final reorder
     p->xt = p->XD * (p->dtype == OEQ_F64 ? 8 : 4) <= 65536 && std::getenv("OEQ_NO_XT") == nullptr;
+    p->nt_w = std::getenv("OEQ_NO_NT") == nullptr;
+    // measured on MI355X: pinning pays for the fp64 forward, not for fp32 or the backward passes
+    p->pin_fwd = p->dtype == OEQ_F64;
+    p->pin_bwd = false;
+    if (const char *e = std::getenv("OEQ_PIN")) {
+        p->pin_fwd = std::strchr(e, 'f') != nullptr;
+        p->pin_bwd = std::strchr(e, 'b') != nullptr;
+    }
+    auto waves = [](const char *name, std::pair<int, int> &w) {
+        if (const char *e = std::getenv(name)) {
+            int a = 0, b = 0;
+            if (std::sscanf(e, "%d,%d", &a, &b) == 2 && a >= 1 && b >= a && b <= 8) w = {a, b};
+        }
+    };
+    waves("OEQ_FWD_WAVES", p->fwd_waves);
+    waves("OEQ_BWD_WAVES", p->bwd_waves);
+    p->fwd_groups = choose_groups(*p, true);
+    p->bwd_groups = choose_groups(*p, false);
     if (const char *s = std::getenv("OEQ_GY_TILE")) {
         const int v = std::atoi(s);
         if (v >= 1 && v <= 256) p->gy_tile = v;

@@ -65,6 +65,12 @@ struct oeq_plan {
     int uch = 1;                // 64-channel chunks (waves per receiver)
     int gy_tile = 32;           // edges per LDS gY flush in the backward kernels
     bool xt = false;            // x-gradient atomics use an m-major row (needs the row in LDS)
+    bool nt_w = true;           // non-temporal loads/stores for W and its gradients
+    // keep the software-pipelined loads ahead of the arithmetic (forward, backward passes)
+    bool pin_fwd = false, pin_bwd = false;
+    std::pair<int, int> fwd_waves{0, 0}, bwd_waves{0, 0};  // (min, max) waves per SIMD; 0 = compiler default
+    // Path groups: one wave computes one group for 64 channels of a receiver.
+    std::vector<std::vector<int>> fwd_groups, bwd_groups;
 
     std::string source;         // emitted HIP source
     std::vector<char> code;     // gfx950 code object

@@ -129,7 +129,10 @@ oeq_status oeq_plan_code_key(const oeq_plan *plan, char *buf, size_t len);
  * triangle rule or l > 3. */
 oeq_status oeq_cg_table(int32_t l1, int32_t l2, int32_t l3, double *out);
 
-/* Workspace bytes a backward or double-backward call needs (0 for ATOMIC). */
+/* Workspace bytes a backward or double-backward call may need for `mode`
+ * (per-group partial Y-gradients when the plan splits its paths over several
+ * backward groups; per-edge x-gradient rows and the sender CSR for
+ * DETERMINISTIC).  0 means no workspace is needed. */
 oeq_status oeq_workspace_size(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                               oeq_bwd_mode mode, size_t *bytes);
 
@@ -149,7 +152,8 @@ oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edge
  * ownership): a wave owns an edge at a time, lanes span channels, grad_W is
  * written directly, grad_Y is reduced across lanes, grad_x is scattered per
  * `mode`.  Any of grad_x, grad_Y, grad_W may be NULL (not computed).
- * DETERMINISTIC needs `workspace` of oeq_workspace_size bytes (256-byte aligned). */
+ * `workspace` (256-byte aligned) must hold oeq_workspace_size(mode) bytes when
+ * that size is not 0; a missing or small workspace gives OEQ_ERR_WORKSPACE. */
 oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                            const int32_t *rowptr, const int32_t *src, const void *x,
                            const void *Y, const void *W, const void *grad_out,

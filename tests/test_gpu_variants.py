@@ -1,0 +1,77 @@
+"""GPU parity of the kernel variants the planner can choose: path-group counts
+for the forward and backward passes, the x-gradient atomic layout and plain
+(temporal) weight accesses.  Each variant is a separate plan (the choice is made
+when the plan is compiled) and is compared with the oracle like the defaults."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import RTOL, inputs, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+oeq = pytest.importorskip("cg_tensor_product_amd")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _plan(wl, env):
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        return oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+CASES = [
+    ("mace_large_fp32", {"OEQ_FWD_GROUPS": "1", "OEQ_BWD_GROUPS": "1"}),
+    ("mace_large_fp32", {"OEQ_FWD_GROUPS": "4", "OEQ_BWD_GROUPS": "2"}),
+    ("mace_large_fp32", {"OEQ_NO_XT": "1", "OEQ_NO_NT": "1"}),
+    ("mace_large_fp32", {"OEQ_FWD_GROUPS": "3", "OEQ_PIN": "fb", "OEQ_FWD_WAVES": "1,2"}),
+    ("mace_medium_fp64", {"OEQ_FWD_GROUPS": "3", "OEQ_BWD_GROUPS": "1", "OEQ_GY_TILE": "7"}),
+    ("tiny_fp64", {"OEQ_FWD_GROUPS": "6", "OEQ_BWD_GROUPS": "2"}),
+]
+
+
+@pytest.mark.parametrize("name,env", CASES, ids=[f"{n}-{'-'.join(f'{k[4:]}{v}' for k, v in e.items())}"
+                                                 for n, e in CASES])
+def test_variant_parity(name, env):
+    wl = synth.WORKLOADS[name]
+    if wl.n_nodes > 200:
+        wl = wl.scaled(n_nodes=120)
+    d, inp = inputs(wl, want=("x", "Y", "W", "g", "v"))
+    dev = {k: to_dev(inp[k]) for k in ("rowptr", "src", "x", "Y", "W", "g", "v")}
+    plan = _plan(wl, env)
+    print(f"[variant] {name} {env}", flush=True)
+    tol = RTOL[wl.dtype]
+    out = oeq.oeq_tp_conv_fwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"])
+    ref = oracle.fwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"])
+    assert rel_l2(out.cpu().numpy(), ref) <= tol
+    rx, rY, rW = oracle.bwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"])
+    for mode in ("atomic", "deterministic"):
+        gx, gY, gW = oeq.oeq_tp_conv_bwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                                         mode=mode)
+        assert rel_l2(gx.cpu().numpy(), rx) <= tol
+        assert rel_l2(gY.cpu().numpy(), rY) <= tol
+        assert rel_l2(gW.cpu().numpy(), rW) <= tol
+    res = oeq.oeq_tp_conv_dbwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                               gg_x=dev["v"], gg_W=dev["W"])
+    refd = oracle.dbwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"], ggx=inp["v"],
+                       ggW=inp["W"])
+    for k, rk in (("x", "dx"), ("Y", "dY"), ("W", "dW"), ("grad_out", "dg")):
+        assert rel_l2(res[k].cpu().numpy(), refd[rk]) <= tol, k
+    torch.cuda.synchronize()

@@ -131,9 +131,15 @@ def test_compute_argument_errors_before_any_device_work():
     assert lib2 == 0
 
 
-def test_workspace_size_atomic_is_zero():
+def test_workspace_size_atomic(monkeypatch):
+    # one backward path group -> no scratch in atomic mode
+    assert oeq.oeq_workspace_size(oeq.Plan("8x0e+8x1o", 2, 1, "f64"), 64, 1024, "atomic") == 0
+    # two groups -> per-group partial Y-gradient rows
+    monkeypatch.setenv("OEQ_BWD_GROUPS", "2")
     p = oeq.Plan("8x0e+8x1o", 2, 1, "f64")
-    assert oeq.oeq_workspace_size(p, 64, 1024, "atomic") == 0
+    monkeypatch.delenv("OEQ_BWD_GROUPS")
+    assert oeq.oeq_workspace_size(p, 64, 1024, "atomic") == 2 * 1024 * 9 * 8
+    assert oeq.oeq_workspace_size(p, 64, 1024, "deterministic") > 1024 * 32 * 8
     b = ctypes.c_size_t()
     assert oeq.lib().oeq_workspace_size(p.handle, 64, 1024, 9, ctypes.byref(b)) == 1
     assert oeq.lib().oeq_workspace_size(None, 64, 1024, 0, ctypes.byref(b)) == 1
