@@ -41,11 +41,14 @@ _lib = None
 
 
 def lib():
+    """The oracle library.  ORACLE_SO names another build of oracle.c (the
+    mutation tests load deliberately broken copies this way)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_SO):
+        path = os.environ.get("ORACLE_SO", _SO)
+        if path == _SO and not os.path.exists(_SO):
             build()
-        L = ctypes.CDLL(_SO)
+        L = ctypes.CDLL(path)
         d, i, i64, p = ctypes.c_double, ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
         L.oracle_cg_complex.restype = d
         L.oracle_cg_complex.argtypes = [i] * 6
