@@ -60,6 +60,24 @@ def measured_traffic(workload, kernel, code_key):
     return None
 
 
+def stream_reference(torch, nbytes=2 << 30):
+    """Same-box context for the HBM figures: a plain device-to-device copy of
+    2 GiB (bytes read + written per second), best of 5."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    best = float("inf")
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * nbytes / (best * 1e-3) / 1e9, "bytes": 2 * nbytes}
+
+
 def cpu_baseline(wl, d, inp, target_s=10.0):
     """The oracle (fp64 loops, OpenMP over independent rows) on the same
     workload: forward of every receiver and the full VJP (W and Y gradients of
@@ -194,6 +212,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": None,
     }
+    res["stream_reference"] = stream_reference(torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, d, inp)
     print(json.dumps(res), flush=True)

@@ -91,6 +91,7 @@ def test_plan_with_output_irreps_sums_paths():
     (dict(x_irreps="8x1o", y_lmax=1, paths=[(0, 1, 0)], out_irreps="8x3o"), 1),  # triangle violated
     (dict(x_irreps="8x1o", y_lmax=1, paths=[(0, 0, 0)]), 1),                     # paths without outputs
     (dict(x_irreps="8x0e", y_lmax=2, lmax_out=1, out_irreps="8x3e"), 1),        # no path survives
+    (dict(x_irreps="2048x0e", y_lmax=1), 2),                                     # more than 1024 channels
 ])
 def test_plan_create_errors(kw, status):
     with pytest.raises(oeq.OeqError) as e:
