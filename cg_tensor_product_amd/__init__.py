@@ -292,8 +292,10 @@ def oeq_tp_conv_bwd(plan: Plan, rowptr, src, x, Y, W, grad_out, mode: str = "ato
 
 
 def oeq_tp_conv_dbwd(plan: Plan, rowptr, src, x, Y, W, grad_out, gg_x=None, gg_Y=None, gg_W=None,
-                     mode: str = "atomic", want=("x", "Y", "W", "grad_out"), workspace=None):
-    """Double backward: dict with d_x, d_Y, d_W, d_grad_out (None if not in want)."""
+                     mode: str = "atomic", want=("x", "Y", "W", "grad_out"), workspace=None, out=None):
+    """Double backward: dict with d_x, d_Y, d_W, d_grad_out (None if not in want).
+    out: optional dict of preallocated outputs with the same keys (a missing or None
+    entry is not requested); it overrides want."""
     N, E = _graph(rowptr, src)
     dt = plan.torch_dtype()
     _want(x, (N, plan.x_dim), dt, "x")
@@ -304,12 +306,14 @@ def oeq_tp_conv_dbwd(plan: Plan, rowptr, src, x, Y, W, grad_out, gg_x=None, gg_Y
     _want(gg_Y, (E, plan.y_dim), dt, "gg_Y")
     _want(gg_W, (E, plan.n_paths, plan.U), dt, "gg_W")
     dev = rowptr.device
-    d = {
-        "x": _empty((N, plan.x_dim), dt, dev) if "x" in want else None,
-        "Y": _empty((E, plan.y_dim), dt, dev) if "Y" in want else None,
-        "W": _empty((E, plan.n_paths, plan.U), dt, dev) if "W" in want else None,
-        "grad_out": _empty((N, plan.out_dim), dt, dev) if "grad_out" in want else None,
-    }
+    shapes = {"x": (N, plan.x_dim), "Y": (E, plan.y_dim), "W": (E, plan.n_paths, plan.U),
+              "grad_out": (N, plan.out_dim)}
+    if out is not None:
+        d = {k: out.get(k) for k in shapes}
+        for k, t in d.items():
+            _want(t, shapes[k], dt, "d_" + k)
+    else:
+        d = {k: _empty(shp, dt, dev) if k in want else None for k, shp in shapes.items()}
     ws, nbytes = (workspace, workspace.numel()) if workspace is not None else _workspace(plan, N, E, mode, dev)
     _check(lib().oeq_tp_conv_dbwd(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W),
                                   _ptr(grad_out), _ptr(gg_x), _ptr(gg_Y), _ptr(gg_W), _ptr(d["x"]), _ptr(d["Y"]),

@@ -1,6 +1,7 @@
 // C ABI entry points: argument checks (host only, no device reads, no
 // synchronisation), workspace carving and stream-ordered kernel launches.
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <limits>
 #include <string>
@@ -138,6 +139,13 @@ oeq_status gy_combine(oeq_plan *p, const Workspace &w, void *gY, int64_t E, hipS
     return launch(p, "oeq_gy_combine", static_cast<unsigned>(blocks), 256, stream, args);
 }
 
+// flags bit0: add into out instead of overwriting it
+oeq_status fwd_launch(oeq_plan *p, int64_t N, const int32_t *rowptr, const int32_t *src, const void *x, const void *Y,
+                      const void *W, void *out, int flags, hipStream_t s) {
+    void *args[] = {&rowptr, &src, &x, &Y, &W, &out, &flags};
+    return launch(p, "oeq_fwd", static_cast<unsigned>(N), fwd_block(p), s, args);
+}
+
 }  // namespace
 
 extern "C" {
@@ -248,10 +256,7 @@ oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     if (st != OEQ_OK) return st;
     if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
     if (E > 0 && (!x || !Y || !W)) return fail(OEQ_ERR_INVALID_ARG, "x, Y or W is NULL");
-    oeq_plan *p = const_cast<oeq_plan *>(plan);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    void *args[] = {&rowptr, &src, &x, &Y, &W, &out};
-    return launch(p, "oeq_fwd", static_cast<unsigned>(N), fwd_block(p), s, args);
+    return fwd_launch(const_cast<oeq_plan *>(plan), N, rowptr, src, x, Y, W, out, 0, static_cast<hipStream_t>(stream));
 }
 
 oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,
@@ -331,15 +336,89 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
         dx_target = w.h;
     }
     if (!dxmode && !dY && !dW && !dg) return OEQ_OK;
-    int flags = (dW ? 1 : 0) | (dY ? 2 : 0) | (dg ? 4 : 0) | (dxmode << 3);
     void *dy_target = gyp ? w.gy_part : dY;
     int64_t gy_stride = gyp ? E * p->YD : 0;
-    const std::string name = "oeq_dbwd_" + std::to_string(tm);
-    void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dy_target, &dW, &dg, &flags,
-                    &gy_stride};
-    st = launch(p, name.c_str(), static_cast<unsigned>(N * static_cast<int64_t>(p->bwd_groups.size())), bwd_block(p),
-                s, args);
-    if (st != OEQ_OK) return st;
+    const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(p->bwd_groups.size()));
+    auto pass = [&](const std::string &name, int flags) {
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dy_target, &dW, &dg, &flags,
+                        &gy_stride};
+        return launch(p, name.c_str(), grid, bwd_block(p), s, args);
+    };
+    auto spills = [&](const std::string &name, bool *yes) {
+        hipFunction_t fn = nullptr;
+        std::string why;
+        const oeq_status r = oeq::get_kernel(*p, name.c_str(), &fn, &why);
+        if (r != OEQ_OK) return fail(r, why);
+        int scratch = 0;
+        *yes = hipFuncGetAttribute(&scratch, HIP_FUNC_ATTRIBUTE_LOCAL_SIZE_BYTES, fn) == hipSuccess && scratch > 0;
+        return OEQ_OK;
+    };
+    const std::string T = std::to_string(tm);
+    // Passes of the split double backward (kernel name, which tangent bits it covers).
+    //   d_W  = BW(gg_x,Y,g) + BW(x,gg_Y,g)                 oeq_dbwd_<tm&3>_1 (reads no weights)
+    //   d_Y  = BY(gg_x,W,g) + BY(x,gg_W,g), d_x = Bx(gg_Y,W,g) + Bx(Y,gg_W,g)
+    //        level 1: oeq_dbwd_<tm>_10 in one pass; level 2: one pass per tangent
+    //   d_grad_out = f(gg_x,Y,W) + f(x,gg_Y,W) + f(x,Y,gg_W)  forward kernel, accumulating
+    const bool single = tm == 1 || tm == 2 || tm == 4;
+    const bool want_w = dW && (tm & 3), want_yx = (dY && (tm & 5)) || dxmode;
+    std::vector<std::string> yx1;  // level-1 d_Y / d_x pass
+    if (want_yx) yx1.push_back(single ? (tm == 1 ? "oeq_dbwd_1_2" : tm == 2 ? "oeq_dbwd_2_8" : "oeq_dbwd_4_10")
+                                      : "oeq_dbwd_" + T + "_10");
+    int level = p->dbwd_split;  // 0 one fused pass, 1 or 2 split
+    if (level < 0) {
+        bool sp = false;
+        if ((st = spills("oeq_dbwd_" + T, &sp)) != OEQ_OK) return st;
+        level = 0;
+        if (sp) {
+            level = 1;
+            std::vector<std::string> k1 = yx1;
+            if (want_w) k1.push_back("oeq_dbwd_" + std::to_string(tm & 3) + "_1");
+            for (const auto &k : k1) {
+                if ((st = spills(k, &sp)) != OEQ_OK) return st;
+                if (sp) level = 2;
+            }
+        }
+    }
+    if (level == 0) {
+        const int flags = (dW ? 1 : 0) | (dY ? 2 : 0) | (dg ? 4 : 0) | (dxmode << 3);
+        if ((st = pass("oeq_dbwd_" + T, flags)) != OEQ_OK) return st;
+    } else {
+        if (want_w && (st = pass("oeq_dbwd_" + std::to_string(tm & 3) + "_1", 1)) != OEQ_OK) return st;
+        if (dW && !want_w && (st = fill_zero(p, dW, E * PU, s)) != OEQ_OK) return st;
+        if (want_yx && (level == 1 || single)) {
+            if ((st = pass(yx1[0], (dY && (tm & 5) ? 2 : 0) | (dxmode << 3))) != OEQ_OK) return st;
+        } else if (want_yx) {
+            bool wrote_dy = false, wrote_h = false;
+            const struct {
+                int bit;
+                const char *name;
+                bool y, x;
+            } parts[] = {{1, "oeq_dbwd_1_2", true, false}, {2, "oeq_dbwd_2_8", false, true},
+                         {4, "oeq_dbwd_4_10", true, true}};
+            for (const auto &q : parts) {
+                if (!(tm & q.bit)) continue;
+                const bool py = dY && q.y;
+                const int dm = q.x ? dxmode : 0;
+                if (!py && !dm) continue;
+                const int flags = (py ? 2 : 0) | (dm << 3) | (py && wrote_dy ? 64 : 0) | (dm == 2 && wrote_h ? 256 : 0);
+                if ((st = pass(q.name, flags)) != OEQ_OK) return st;
+                wrote_dy |= py;
+                wrote_h |= dm == 2;
+            }
+        }
+        if (dY && !(tm & 5) &&
+            (st = fill_zero(p, dy_target, E * p->YD * (gyp ? static_cast<int64_t>(p->bwd_groups.size()) : 1), s)) !=
+                OEQ_OK)
+            return st;
+        if (dg) {
+            int f = 0;
+            if ((tm & 1) && (st = fwd_launch(p, N, rowptr, src, ggx, Y, W, dg, f, s)) != OEQ_OK) return st;
+            f = tm & 1;
+            if ((tm & 2) && (st = fwd_launch(p, N, rowptr, src, x, ggY, W, dg, f, s)) != OEQ_OK) return st;
+            f = tm & 3 ? 1 : 0;
+            if ((tm & 4) && (st = fwd_launch(p, N, rowptr, src, x, Y, ggW, dg, f, s)) != OEQ_OK) return st;
+        }
+    }
     if (dxmode == 2 && (st = det_finish(p, N, w, dx, s)) != OEQ_OK) return st;
     if (dxmode == 1 && (st = untranspose(p, N, dx, s)) != OEQ_OK) return st;
     return gyp ? gy_combine(p, w, dY, E, s) : OEQ_OK;

@@ -93,7 +93,7 @@ Local make_local(const oeq_plan &p, const std::vector<int> &paths) {
 
 // Moves between a node row (u-major blocks) and a lane's compact registers.
 void emit_row_move(std::ostringstream &o, const char *sig, const std::map<int, int> &blocks,
-                   const std::vector<Block> &bl, bool load, const char *ptr) {
+                   const std::vector<Block> &bl, bool load, const char *ptr, bool add = false) {
     o << "  static __device__ __forceinline__ void " << sig << " {\n";
     for (const auto &kv : blocks) {
         const Block &b = bl[kv.first];
@@ -104,7 +104,7 @@ void emit_row_move(std::ostringstream &o, const char *sig, const std::map<int, i
             if (load)
                 o << " v[" << kv.second + m << "] = q[" << m << "];";
             else
-                o << " q[" << m << "] = v[" << kv.second + m << "];";
+                o << " q[" << m << "] " << (add ? "+=" : "=") << " v[" << kv.second + m << "];";
         }
         o << " }\n";
     }
@@ -119,6 +119,10 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
     emit_row_move(o, "store_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX])", L.xoff, p.xb, false, "xr");
     emit_row_move(o, "load_g(const real_t *__restrict__ gr, int u, real_t (&v)[NO])", L.ooff, p.ob, true, "gr");
     emit_row_move(o, "store_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO])", L.ooff, p.ob, false, "orow");
+    // accumulating variants (double backward split into one pass per tangent)
+    emit_row_move(o, "add_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX])", L.xoff, p.xb, false, "xr", true);
+    emit_row_move(o, "add_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO])", L.ooff, p.ob, false, "orow",
+                  true);
     // x-gradient scatter: with XT the block is addressed m-major (element m*U + u),
     // so consecutive lanes hit consecutive words; oeq_x_untranspose restores the
     // u-major layout afterwards.
@@ -143,6 +147,12 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
     o << " }\n";
     o << "  static __device__ __forceinline__ void store_w(real_t *__restrict__ ge, int u, const real_t (&v)[NW]) {";
     for (int k : L.paths) o << " STW(ge + " << S(static_cast<long long>(k) * p.U) << " + u, v[" << L.widx.at(k) << "]);";
+    o << " }\n";
+    o << "  static __device__ __forceinline__ void add_w(real_t *__restrict__ ge, int u, const real_t (&v)[NW]) {";
+    for (int k : L.paths) {
+        const std::string a = "ge + " + S(static_cast<long long>(k) * p.U) + " + u";
+        o << " STW(" << a << ", LDW(" << a << ") + v[" << L.widx.at(k) << "]);";
+    }
     o << " }\n";
 
     // forward of one edge

@@ -153,12 +153,12 @@ template <int G>
 __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ rowptr,
                                           const int *__restrict__ src, const real_t *__restrict__ x,
                                           const real_t *__restrict__ Y, const real_t *__restrict__ W,
-                                          real_t *__restrict__ out) {
+                                          real_t *__restrict__ out, bool acc) {
     using Gr = FG<G>;
     const bool act = (U % 64 == 0) || (u < U);
     const int uu = act ? u : 0;  // inactive lanes read channel 0 and store nothing
-    real_t acc[Gr::NO];
-    zero(acc);
+    real_t sum[Gr::NO];
+    zero(sum);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     if (e0 < e1) {
         // software pipeline: the next edge's loads are in flight while this one computes
@@ -176,7 +176,7 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
             Gr::load_w(W + (i64)en * (P * U), uu, wn);
             // keep the next edge's loads ahead of this edge's arithmetic
             PIN_FWD();
-            Gr::edge(xv, yv, wv, acc);
+            Gr::edge(xv, yv, wv, sum);
 #pragma unroll
             for (int k = 0; k < YD; ++k) yv[k] = yn[k];
 #pragma unroll
@@ -185,27 +185,33 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
             for (int k = 0; k < Gr::NW; ++k) wv[k] = wn[k];
         }
     }
-    if (act) Gr::store_out(out + (i64)r * OD, u, acc);
+    if (act) {
+        if (acc)
+            Gr::add_out(out + (i64)r * OD, u, sum);
+        else
+            Gr::store_out(out + (i64)r * OD, u, sum);
+    }
 }
 
 template <int G>
 __device__ __forceinline__ void fwd_dispatch(int grp, int r, int u, const int *__restrict__ rowptr,
                                              const int *__restrict__ src, const real_t *__restrict__ x,
                                              const real_t *__restrict__ Y, const real_t *__restrict__ W,
-                                             real_t *__restrict__ out) {
+                                             real_t *__restrict__ out, bool acc) {
     if (grp == G) {
-        fwd_group<G>(r, u, rowptr, src, x, Y, W, out);
+        fwd_group<G>(r, u, rowptr, src, x, Y, W, out, acc);
         return;
     }
-    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1>(grp, r, u, rowptr, src, x, Y, W, out);
+    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1>(grp, r, u, rowptr, src, x, Y, W, out, acc);
 }
 
 extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
 oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
-        const real_t *__restrict__ Y, const real_t *__restrict__ W, real_t *__restrict__ out) {
+        const real_t *__restrict__ Y, const real_t *__restrict__ W, real_t *__restrict__ out, int flags) {
+    // flags: bit0 add into out instead of overwriting it
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
-    fwd_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out);
+    fwd_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out, (flags & 1) != 0);
 }
 
 // The atomic x-gradient is accumulated m-major inside each x block (so the
@@ -233,7 +239,7 @@ struct GyStage {
 };
 
 __device__ __forceinline__ void gy_push(GyStage &st, real_t *__restrict__ gY, int e, int j,
-                                        real_t (&gy)[YD], int lane, int wv) {
+                                        real_t (&gy)[YD], int lane, int wv, bool acc = false) {
     real_t v[PY];
 #pragma unroll
     for (int k = 0; k < PY; ++k) v[k] = (k < YD) ? gy[k] : real_t(0);
@@ -241,13 +247,13 @@ __device__ __forceinline__ void gy_push(GyStage &st, real_t *__restrict__ gY, in
     const int idx = lane >> (6 - LGPY);
     const bool writer = (lane & ((1 << (6 - LGPY)) - 1)) == 0;
     if (UCH == 1) {
-        if (writer && idx < YD) gY[(i64)e * YD + idx] = v[0];
+        if (writer && idx < YD) gY[(i64)e * YD + idx] = acc ? gY[(i64)e * YD + idx] + v[0] : v[0];
     } else {
         if (writer) st.red[wv][j][idx] = v[0];
     }
 }
 
-__device__ __forceinline__ void gy_flush(GyStage &st, real_t *__restrict__ gY, int base, int n) {
+__device__ __forceinline__ void gy_flush(GyStage &st, real_t *__restrict__ gY, int base, int n, bool acc = false) {
     if (UCH == 1) return;
     __syncthreads();
     for (int k = threadIdx.x; k < n * YD; k += UCH * 64) {
@@ -255,7 +261,8 @@ __device__ __forceinline__ void gy_flush(GyStage &st, real_t *__restrict__ gY, i
         real_t s = st.red[0][j][m];
 #pragma unroll
         for (int w = 1; w < UCH; ++w) s += st.red[w][j][m];
-        gY[(i64)(base + j) * YD + m] = s;
+        real_t *dst = gY + (i64)(base + j) * YD + m;
+        *dst = acc ? *dst + s : s;
     }
     __syncthreads();
 }
@@ -407,9 +414,14 @@ oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
 //   d_grad_out = f(ggx,Y,W) + f(x,ggY,W) + f(x,Y,ggW)      (receiver-local)
 //   d_W = BW(ggx,Y,g) + BW(x,ggY,g),  d_Y = BY(ggx,W,g) + BY(x,ggW,g)
 //   d_x = Bx(ggY,W,g) + Bx(Y,ggW,g)                         (to senders)
-// flags: bit0 d_W, bit1 d_Y, bit2 d_grad_out, bits 3-4 d_x mode (0 none, 1 atomic, 2 rows)
+// OUT: the outputs the kernel is built for (1 d_W, 2 d_Y, 4 d_grad_out, 8 d_x); a
+// kernel for a subset holds fewer live registers.
+// flags: bit0 d_W, bit1 d_Y, bit2 d_grad_out, bits 3-4 d_x mode (0 none, 1 atomic, 2 rows),
+//        bits 5-8 add into d_W / d_Y / d_grad_out / the d_x rows instead of overwriting
 // ---------------------------------------------------------------------------
-template <int TM, int G>
+constexpr int DW = 1, DY = 2, DG = 4, DX = 8;
+
+template <int TM, int OUT, int G>
 __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, const int *__restrict__ rowptr,
                                            const int *__restrict__ src, const real_t *__restrict__ x,
                                            const real_t *__restrict__ Y, const real_t *__restrict__ W,
@@ -421,13 +433,18 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
     const int lane = threadIdx.x & 63;
     const bool act = (U % 64 == 0) || (u < U);
     const int uu = act ? u : 0;
-    const bool want_dw = (flags & 1) != 0, want_dy = (flags & 2) != 0, want_dg = (flags & 4) != 0;
-    const int dxmode = (flags >> 3) & 3;
-    constexpr bool HAS_DX = (TM & 6) != 0;
+    const bool want_dw = (OUT & DW) && (flags & 1) != 0, want_dy = (OUT & DY) && (flags & 2) != 0,
+               want_dg = (OUT & DG) && (flags & 4) != 0;
+    const int dxmode = (OUT & DX) ? (flags >> 3) & 3 : 0;
+    // add into the outputs instead of overwriting (one pass per tangent)
+    const bool acc_dw = (flags & 32) != 0, acc_dy = (flags & 64) != 0, acc_dg = (flags & 128) != 0,
+               acc_h = (flags & 256) != 0;
+    constexpr bool HAS_DX = (TM & 6) != 0 && (OUT & DX) != 0;
+    constexpr bool GW_ = (OUT & DW) != 0, GY_ = (OUT & DY) != 0, GX_ = (OUT & DX) != 0;
     real_t gv[Gr::NO];
     Gr::load_g(g + (i64)r * OD, uu, gv);
     if (!act) zero(gv);
-    real_t dgacc[Gr::NO];
+    real_t dgacc[(OUT & DG) ? Gr::NO : 1];
     zero(dgacc);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     // per-edge operands (unused ones are dropped by the compiler for a given TM)
@@ -458,33 +475,52 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
             zero(dw);
             zero(dy);
             zero(dxp);
-            if (TM & 1) {
-                if (want_dg) Gr::edge(cur.tx, cur.y, cur.w, dgacc);
-                Gr::template vjp<true, true, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
+            if constexpr ((TM & 1) != 0) {
+                if constexpr ((OUT & DG) != 0)
+                    if (want_dg) Gr::edge(cur.tx, cur.y, cur.w, dgacc);
+                if constexpr (GW_ || GY_) Gr::template vjp<GW_, GY_, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
             }
-            if (TM & 2) {
-                if (want_dg) Gr::edge(cur.x, cur.ty, cur.w, dgacc);
-                Gr::template vjp<true, false, true>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
+            if constexpr ((TM & 2) != 0) {
+                if constexpr ((OUT & DG) != 0)
+                    if (want_dg) Gr::edge(cur.x, cur.ty, cur.w, dgacc);
+                if constexpr (GW_ || GX_) Gr::template vjp<GW_, false, GX_>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
             }
-            if (TM & 4) {
-                if (want_dg) Gr::edge(cur.x, cur.y, cur.tw, dgacc);
-                Gr::template vjp<false, true, true>(cur.x, cur.y, cur.tw, gv, dw, dy, dxp);
+            if constexpr ((TM & 4) != 0) {
+                if constexpr ((OUT & DG) != 0)
+                    if (want_dg) Gr::edge(cur.x, cur.y, cur.tw, dgacc);
+                if constexpr (GY_ || GX_) Gr::template vjp<false, GY_, GX_>(cur.x, cur.y, cur.tw, gv, dw, dy, dxp);
             }
-            if (want_dw && act) Gr::store_w(dW + (i64)e * (P * U), u, dw);
+            if (want_dw && act) {
+                if (acc_dw)
+                    Gr::add_w(dW + (i64)e * (P * U), u, dw);
+                else
+                    Gr::store_w(dW + (i64)e * (P * U), u, dw);
+            }
             if (want_dy) {
-                gy_push(st, dY, e, j, dy, lane, wv);
-                if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, dY, e - j, j + 1);
+                gy_push(st, dY, e, j, dy, lane, wv, acc_dy);
+                if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, dY, e - j, j + 1, acc_dy);
             }
             if (HAS_DX && dxmode == 1 && act) Gr::atomic_x(dx + (i64)s * XD, u, dxp);
-            if (HAS_DX && dxmode == 2 && act) Gr::store_x(dx + (i64)e * XD, u, dxp);
+            if (HAS_DX && dxmode == 2 && act) {
+                if (acc_h)
+                    Gr::add_x(dx + (i64)e * XD, u, dxp);
+                else
+                    Gr::store_x(dx + (i64)e * XD, u, dxp);
+            }
             s = sn;
             cur = nxt;
         }
     }
-    if (want_dg && act) Gr::store_out(dg + (i64)r * OD, u, dgacc);
+    if constexpr ((OUT & DG) != 0)
+    if (want_dg && act) {
+        if (acc_dg)
+            Gr::add_out(dg + (i64)r * OD, u, dgacc);
+        else
+            Gr::store_out(dg + (i64)r * OD, u, dgacc);
+    }
 }
 
-template <int TM, int G>
+template <int TM, int OUT, int G>
 __device__ __forceinline__ void dbwd_dispatch(GyStage &st, int r, int grp, int wv, int u, const int *__restrict__ rowptr,
                                               const int *__restrict__ src, const real_t *__restrict__ x,
                                               const real_t *__restrict__ Y, const real_t *__restrict__ W,
@@ -493,14 +529,15 @@ __device__ __forceinline__ void dbwd_dispatch(GyStage &st, int r, int grp, int w
                                               real_t *__restrict__ dx, real_t *__restrict__ dY,
                                               real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {
     if (grp == G) {
-        dbwd_group<TM, G>(st, r, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
+        dbwd_group<TM, OUT, G>(st, r, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
         return;
     }
     if constexpr (G + 1 < NGB)
-        dbwd_dispatch<TM, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
+        dbwd_dispatch<TM, OUT, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg,
+                                      flags);
 }
 
-template <int TM>
+template <int TM, int OUT>
 __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
                                           const real_t *__restrict__ x, const real_t *__restrict__ Y,
                                           const real_t *__restrict__ W, const real_t *__restrict__ g,
@@ -511,23 +548,39 @@ __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const 
     __shared__ GyStage st;
     const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
     const int wv = uni(threadIdx.x >> 6);
-    dbwd_dispatch<TM, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx,
+    dbwd_dispatch<TM, OUT, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx,
                          dY + grp * gy_stride, dW, dg, flags);
 }
 
-#define OEQ_DBWD_KERNEL(TM)                                                                       \
-    extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY oeq_dbwd_##TM(                  \
+// oeq_dbwd_<TM>: every output in one pass.  oeq_dbwd_<TM>_<OUT>: the passes of
+// the split double backward (d_W; d_Y and d_x; d_grad_out is left to the
+// forward kernel, one accumulating launch per tangent).
+#define OEQ_DBWD_KERNEL(NAME, TM, OUT)                                                              \
+    extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY NAME(                      \
         const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x, \
         const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,  \
         const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,                            \
         const real_t *__restrict__ ggW, real_t *__restrict__ dx, real_t *__restrict__ dY,          \
         real_t *__restrict__ dW, real_t *__restrict__ dg, int flags, i64 gy_stride) {              \
-        dbwd_body<TM>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags, gy_stride);   \
+        dbwd_body<TM, OUT>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags, gy_stride); \
     }
-OEQ_DBWD_KERNEL(1)
-OEQ_DBWD_KERNEL(2)
-OEQ_DBWD_KERNEL(3)
-OEQ_DBWD_KERNEL(4)
-OEQ_DBWD_KERNEL(5)
-OEQ_DBWD_KERNEL(6)
-OEQ_DBWD_KERNEL(7)
+OEQ_DBWD_KERNEL(oeq_dbwd_1, 1, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_2, 2, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_3, 3, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_4, 4, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_5, 5, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_6, 6, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_7, 7, 15)
+// d_W = BW(gg_x,Y,g) + BW(x,gg_Y,g): reads no weights
+OEQ_DBWD_KERNEL(oeq_dbwd_1_1, 1, 1)
+OEQ_DBWD_KERNEL(oeq_dbwd_2_1, 2, 1)
+OEQ_DBWD_KERNEL(oeq_dbwd_3_1, 3, 1)
+// d_Y and d_x of several tangents in one pass over W and gg_W
+OEQ_DBWD_KERNEL(oeq_dbwd_3_10, 3, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_5_10, 5, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_6_10, 6, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_7_10, 7, 10)
+// one tangent: d_Y = BY(gg_x,W,g); d_x = Bx(gg_Y,W,g); d_Y, d_x = BY(x,gg_W,g), Bx(Y,gg_W,g)
+OEQ_DBWD_KERNEL(oeq_dbwd_1_2, 1, 2)
+OEQ_DBWD_KERNEL(oeq_dbwd_2_8, 2, 8)
+OEQ_DBWD_KERNEL(oeq_dbwd_4_10, 4, 10)

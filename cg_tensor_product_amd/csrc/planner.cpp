@@ -266,6 +266,10 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         const int v = std::atoi(s);
         if (v >= 1 && v <= 256) p->gy_tile = v;
     }
+    if (const char *s = std::getenv("OEQ_DBWD_SPLIT")) {
+        const int v = std::atoi(s);
+        p->dbwd_split = v < 0 ? 0 : v > 2 ? 2 : v;
+    }
     return OEQ_OK;
 }
 

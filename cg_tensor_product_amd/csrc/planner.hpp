@@ -64,6 +64,7 @@ struct oeq_plan {
     // Launch shape.
     int uch = 1;                // 64-channel chunks (waves per receiver)
     int gy_tile = 32;           // edges per LDS gY flush in the backward kernels
+    int dbwd_split = -1;        // double backward: 0 one fused pass; 1 split by output; 2 also one d_Y/d_x pass per tangent; -1 the first that does not spill
     bool xt = false;            // x-gradient atomics use an m-major row (needs the row in LDS)
     bool nt_w = true;           // non-temporal loads/stores for W and its gradients
     // keep the software-pipelined loads ahead of the arithmetic (forward, backward passes)

@@ -276,3 +276,46 @@ def test_full_size_sampled(name):
         assert rel_l2(res["grad_out"][rows_t].cpu().numpy(), dg) <= tol
         print(f"[full] {name} hvp ok", flush=True)
     torch.cuda.synchronize()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("mode", ["atomic", "deterministic"])
+def test_full_size_double_backward_all_tangents(mode):
+    """Double backward with tangents on x, Y and W at full size (the force-training
+    path), compared on sampled rows with the oracle's double backward evaluated on
+    the sub-graph of exactly the edges each sampled output depends on."""
+    wl = W_["mace_large_fp32"]
+    d, inp = inputs(wl, want=("x", "Y", "W", "g", "v"))
+    tY = synth.extra_normal(wl, inp["Y"].shape, 1)
+    tW = synth.extra_normal(wl, inp["W"].shape, 2)
+    print(f"[full-dbwd] {mode} inputs ready", flush=True)
+    g = _dev_inputs(inp, wl.dtype)
+    gY_, gW_ = to_dev(tY), to_dev(tW)
+    plan = plan_for(wl)
+    res = oeq.oeq_tp_conv_dbwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"], g["g"], gg_x=g["v"],
+                               gg_Y=gY_, gg_W=gW_, mode=mode)
+    torch.cuda.synchronize()
+    tol = RTOL[wl.dtype]
+    rows = sample(wl.n_nodes, 24, 11)
+    edges = sample(inp["E"], 160, 12)
+    senders = sample(wl.n_nodes, 16, 13)
+
+    def sub(edge_ids):
+        rp, sr, e = subgraph(inp["rowptr"], inp["src"], edge_ids)
+        return rp, sr, e
+
+    rp, sr, e = sub(edges_of_rows(inp["rowptr"], rows))
+    ref = oracle.dbwd(d, rp, sr, inp["x"], inp["Y"][e], inp["W"][e], inp["g"], ggx=inp["v"], ggY=tY[e],
+                      ggW=tW[e], rows=rows, want=("dg",))
+    assert rel_l2(res["grad_out"][torch.from_numpy(rows).cuda()].cpu().numpy(), ref["dg"]) <= tol
+    rp, sr, e = sub(edges)
+    ref = oracle.dbwd(d, rp, sr, inp["x"], inp["Y"][e], inp["W"][e], inp["g"], ggx=inp["v"], ggY=tY[e],
+                      ggW=tW[e], want=("dY", "dW"))
+    et = torch.from_numpy(e).cuda()
+    assert rel_l2(res["Y"][et].cpu().numpy(), ref["dY"]) <= tol
+    assert rel_l2(res["W"][et].cpu().numpy(), ref["dW"]) <= tol
+    rp, sr, e = sub(np.nonzero(np.isin(inp["src"], senders))[0])
+    ref = oracle.dbwd(d, rp, sr, inp["x"], inp["Y"][e], inp["W"][e], inp["g"], ggx=inp["v"], ggY=tY[e],
+                      ggW=tW[e], senders=senders, want=("dx",))
+    assert rel_l2(res["x"][torch.from_numpy(senders).cuda()].cpu().numpy(), ref["dx"]) <= tol
+    print(f"[full-dbwd] {mode} ok", flush=True)

@@ -44,6 +44,11 @@ CASES = [
     ("mace_large_fp32", {"OEQ_FWD_GROUPS": "3", "OEQ_PIN": "fb", "OEQ_FWD_WAVES": "1,2"}),
     ("mace_medium_fp64", {"OEQ_FWD_GROUPS": "3", "OEQ_BWD_GROUPS": "1", "OEQ_GY_TILE": "7"}),
     ("tiny_fp64", {"OEQ_FWD_GROUPS": "6", "OEQ_BWD_GROUPS": "2"}),
+    ("tiny_fp64", {"OEQ_DBWD_SPLIT": "1", "OEQ_BWD_GROUPS": "2"}),
+    ("tiny_fp64", {"OEQ_DBWD_SPLIT": "2", "OEQ_BWD_GROUPS": "2"}),
+    ("mace_medium_fp32", {"OEQ_DBWD_SPLIT": "1"}),
+    ("mace_medium_fp32", {"OEQ_DBWD_SPLIT": "2"}),
+    ("mace_medium_fp32", {"OEQ_DBWD_SPLIT": "0"}),
 ]
 
 
@@ -68,10 +73,30 @@ def test_variant_parity(name, env):
         assert rel_l2(gx.cpu().numpy(), rx) <= tol
         assert rel_l2(gY.cpu().numpy(), rY) <= tol
         assert rel_l2(gW.cpu().numpy(), rW) <= tol
-    res = oeq.oeq_tp_conv_dbwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
-                               gg_x=dev["v"], gg_W=dev["W"])
-    refd = oracle.dbwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"], ggx=inp["v"],
-                       ggW=inp["W"])
-    for k, rk in (("x", "dx"), ("Y", "dY"), ("W", "dW"), ("grad_out", "dg")):
-        assert rel_l2(res[k].cpu().numpy(), refd[rk]) <= tol, k
+    tY = synth.extra_normal(wl, inp["Y"].shape, 1)
+    tYd = to_dev(tY)
+    # every tangent set, all outputs and each output alone; outputs start as NaN so
+    # a pass that leaves one unwritten fails
+    shapes = {"x": inp["x"].shape, "Y": inp["Y"].shape, "W": inp["W"].shape, "grad_out": inp["g"].shape}
+    for mask in range(1, 8):
+        refd = oracle.dbwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"],
+                           ggx=inp["v"] if mask & 1 else None, ggY=tY if mask & 2 else None,
+                           ggW=inp["W"] if mask & 4 else None)
+        for mode in ("atomic", "deterministic"):
+            for want in (("x", "Y", "W", "grad_out"), ("x",), ("Y",), ("W",), ("grad_out",)):
+                if len(want) == 1 and mask not in (3, 7):
+                    continue
+                res = {k: torch.full(shapes[k], float("nan"), dtype=plan.torch_dtype(), device="cuda")
+                       for k in want}
+                oeq.oeq_tp_conv_dbwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                                     gg_x=dev["v"] if mask & 1 else None, gg_Y=tYd if mask & 2 else None,
+                                     gg_W=dev["W"] if mask & 4 else None, mode=mode, out=res)
+                for k, rk in (("x", "dx"), ("Y", "dY"), ("W", "dW"), ("grad_out", "dg")):
+                    if k not in want:
+                        continue
+                    got = res[k].cpu().numpy()
+                    if not np.any(refd[rk]):
+                        assert not got.any(), (mask, mode, want, k)
+                    else:
+                        assert rel_l2(got, refd[rk]) <= tol, (mask, mode, want, k)
     torch.cuda.synchronize()
