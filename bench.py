@@ -41,7 +41,9 @@ def algorithmic_bytes(wl, P, out_dim, E):
     fwd = W + Y + x + o + csr
     vjp = (W + Y + x + o + csr) + (W + Y + x)       # read W,Y,x,g,CSR; write gW,gY,gx
     hvp = (W + Y + x + o + csr) + (W + Y + o)       # read W,Y,v,g,CSR; write dW,dY,dg
-    return {"fwd": fwd, "vjp": vjp, "hvp": hvp}
+    # every tangent: read x,Y,W,g and gg_x,gg_Y,gg_W, CSR; write dx,dY,dW,dg
+    dbwd = (2 * (W + Y + x) + o + csr) + (W + Y + x + o)
+    return {"fwd": fwd, "vjp": vjp, "hvp": hvp, "dbwd": dbwd}
 
 
 def measured_traffic(workload, kernel, code_key):
@@ -78,6 +80,57 @@ def stream_reference(torch, nbytes=2 << 30):
     return {"copy_GBps": 2 * nbytes / (best * 1e-3) / 1e9, "bytes": 2 * nbytes}
 
 
+def side_rows(torch, oeq, plan, dev, N, E, ab, reps=10):
+    """Mean duration of the other rows of the hot path on the same inputs (each
+    call bracketed by HIP events on the current stream): the deterministic VJP,
+    the Hessian-vector product (tangent on x only) and the double backward with
+    all three tangents.  Context only: the step is forward + atomic VJP."""
+    dt = plan.torch_dtype()
+    v = torch.randn(N, plan.x_dim, dtype=dt, device="cuda")
+    grads = (torch.empty(N, plan.x_dim, dtype=dt, device="cuda"), torch.empty(E, plan.y_dim, dtype=dt, device="cuda"),
+             torch.empty(E, plan.n_paths, plan.U, dtype=dt, device="cuda"))
+    outs = {"x": grads[0], "Y": grads[1], "W": grads[2],
+            "grad_out": torch.empty(N, plan.out_dim, dtype=dt, device="cuda")}
+    hvp_outs = {k: outs[k] for k in ("Y", "W", "grad_out")}
+
+    def ws(mode):
+        n = oeq.oeq_workspace_size(plan, N, E, mode)
+        if not n:
+            return None
+        raw = torch.empty(n + 256, dtype=torch.uint8, device="cuda")
+        off = (-raw.data_ptr()) % 256
+        return raw[off:off + n]
+
+    wsd, wsa = ws("deterministic"), ws("atomic")
+    calls = {
+        "vjp_deterministic": (ab["vjp"], lambda: oeq.oeq_tp_conv_bwd(
+            plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"], mode="deterministic",
+            out=grads, workspace=wsd)),
+        "hvp": (ab["hvp"], lambda: oeq.oeq_tp_conv_dbwd(
+            plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"], gg_x=v, out=hvp_outs,
+            workspace=wsa)),
+        # the tangents of Y and W reuse Y and W themselves: the cost does not depend on their values
+        "dbwd_all_tangents": (ab["dbwd"], lambda: oeq.oeq_tp_conv_dbwd(
+            plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"], gg_x=v, gg_Y=dev["Y"],
+            gg_W=dev["W"], out=outs, workspace=wsa)),
+    }
+    res = {}
+    for name, (nbytes, fn) in calls.items():
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        res[name] = {"ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes, "edges_per_s": E / (ms * 1e-3)}
+    del v, grads, outs, wsd, wsa
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, d, inp, target_s=10.0):
     """The oracle (fp64 loops, OpenMP over independent rows) on the same
     workload: forward of every receiver and the full VJP (W and Y gradients of
@@ -108,6 +161,8 @@ def main():
     ap.add_argument("--workload", default="mace_medium_fp32")
     ap.add_argument("--mode", default="atomic", choices=["atomic", "deterministic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-rows", action="store_true",
+                    help="skip timing the deterministic VJP, HVP and all-tangent double backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device 3 times (a plain copy kernel of known size, "
                          "to scale HBM byte counters)")
@@ -212,6 +267,8 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic},
         "cpu_baseline": None,
     }
+    if not args.no_side_rows:
+        res["side_rows"] = side_rows(torch, oeq, plan, dev, N, E, ab)
     res["stream_reference"] = stream_reference(torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, d, inp)
