@@ -161,6 +161,8 @@ def main():
     ap.add_argument("--workload", default="mace_medium_fp32")
     ap.add_argument("--mode", default="atomic", choices=["atomic", "deterministic"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "receiver", "sender"],
+                    help="schedule of both passes: the plan's data-movement choice per pass (auto), or forced")
     ap.add_argument("--no-side-rows", action="store_true",
                     help="skip timing the deterministic VJP, HVP and all-tangent double backward")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -197,12 +199,32 @@ def main():
         off = (-raw.data_ptr()) % 256
         ws = raw[off:off + nbytes]
 
+    # the plan's data-movement model picks each pass's schedule; the sender view of the
+    # graph is graph preparation (like the CSR), built before the timed region
+    choice = plan.schedule()
+    sched_f = choice["fwd"] if args.schedule == "auto" else args.schedule
+    sched = choice["bwd"] if args.schedule == "auto" else args.schedule
+    view = oeq.oeq_sender_view(dev["rowptr"], dev["src"]) if "sender" in (sched, sched_f) else None
+    ws_sender = None
+    if sched == "sender":
+        nb = oeq.oeq_workspace_size(plan, N, E, "atomic")
+        if nb:
+            raw_s = torch.empty(nb + 256, dtype=torch.uint8, device="cuda")
+            ws_sender = raw_s[(-raw_s.data_ptr()) % 256:][:nb]
+
     def fwd():
-        oeq.oeq_tp_conv_fwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], out=out)
+        if sched_f == "sender":
+            oeq.oeq_tp_conv_fwd_sender(plan, view, dev["x"], dev["Y"], dev["W"], out=out)
+        else:
+            oeq.oeq_tp_conv_fwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], out=out)
 
     def vjp():
-        oeq.oeq_tp_conv_bwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
-                            mode=args.mode, out=grads, workspace=ws)
+        if sched == "sender":
+            oeq.oeq_tp_conv_bwd_sender(plan, view, dev["x"], dev["Y"], dev["W"], dev["g"], out=grads,
+                                       workspace=ws_sender)
+        else:
+            oeq.oeq_tp_conv_bwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                                mode=args.mode, out=grads, workspace=ws)
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -238,7 +260,9 @@ def main():
     step_bytes = ab["fwd"] + ab["vjp"]
     dom, dom_ms, dom_bytes = ("vjp", vjp_ms, ab["vjp"]) if vjp_ms >= fwd_ms else ("fwd", fwd_ms, ab["fwd"])
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    kname = {"fwd": "oeq_fwd", "vjp": "oeq_bwd_atomic" if args.mode == "atomic" else "oeq_bwd_rows"}[dom]
+    vjp_kernel = "oeq_bwd_sender" if sched == "sender" else (
+        "oeq_bwd_atomic" if args.mode == "atomic" else "oeq_bwd_rows")
+    kname = {"fwd": "oeq_fwd_sender" if sched_f == "sender" else "oeq_fwd", "vjp": vjp_kernel}[dom]
     traffic = measured_traffic(wl.name, kname, plan.code_key)
     res = {
         "metric": "edges/s and achieved HBM GB/s, fused CG-TP conv fwd+VJP, 5k nodes/280k edges",
@@ -255,7 +279,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "nodes": N, "edges": E, "degree": wl.degree,
                    "x_irreps": "+".join(f"{m}x{l}{'e' if p > 0 else 'o'}" for m, l, p in wl.x_irreps),
-                   "y_lmax": wl.y_lmax, "paths": d.P, "step": f"forward + VJP ({args.mode} x-gradient)"},
+                   "y_lmax": wl.y_lmax, "paths": d.P,
+                   "step": f"forward ({sched_f}-stationary) + VJP ("
+                           + ("sender-stationary" if sched == "sender" else f"receiver-stationary, {args.mode} x-gradient")
+                           + ")"},
         "achieved_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
         "kernels": {
             "fwd": {"ms": fwd_ms, "GBps": ab["fwd"] / (fwd_ms * 1e-3) / 1e9, "bytes": ab["fwd"],

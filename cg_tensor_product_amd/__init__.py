@@ -32,7 +32,9 @@ EXPORTED = ["oeq_plan_create", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_pa
             "oeq_cg_table",
             "oeq_workspace_size", "oeq_tp_conv_fwd", "oeq_tp_conv_bwd", "oeq_tp_conv_dbwd",
             "oeq_csr_workspace_size", "oeq_sender_csr", "oeq_csr_check", "oeq_status_string",
-            "oeq_last_error"]
+            "oeq_last_error", "oeq_plan_schedule", "oeq_sender_view", "oeq_tp_conv_fwd_sender",
+            "oeq_tp_conv_bwd_sender"]
+SCHEDULES = {0: "receiver", 1: "sender"}
 
 
 class OeqError(RuntimeError):
@@ -96,6 +98,15 @@ def lib():
     L.oeq_sender_csr.restype = st
     L.oeq_csr_check.argtypes = [I64, I64, P, P, P]
     L.oeq_csr_check.restype = st
+    L.oeq_plan_schedule.argtypes = [P, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                     ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    L.oeq_plan_schedule.restype = st
+    L.oeq_sender_view.argtypes = [I64, I64, P, P, P, P, P, P, SZ, P]
+    L.oeq_sender_view.restype = st
+    L.oeq_tp_conv_fwd_sender.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P]
+    L.oeq_tp_conv_fwd_sender.restype = st
+    L.oeq_tp_conv_bwd_sender.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+    L.oeq_tp_conv_bwd_sender.restype = st
     L.oeq_status_string.argtypes = [ctypes.c_int]
     L.oeq_status_string.restype = ctypes.c_char_p
     L.oeq_last_error.argtypes = []
@@ -174,6 +185,14 @@ class Plan:
         buf = ctypes.create_string_buffer(64)
         _check(lib().oeq_plan_code_key(self._h, buf, 64))
         return buf.value.decode()
+
+    def schedule(self):
+        """oeq_plan_schedule: {"fwd": "receiver"|"sender", "bwd": ..., "move_fwd": [r, s],
+        "move_bwd": [r, s]} (the data-movement model's per-edge, per-channel elements)."""
+        f, b = ctypes.c_int(), ctypes.c_int()
+        mf, mb = (ctypes.c_double * 2)(), (ctypes.c_double * 2)()
+        _check(lib().oeq_plan_schedule(self._h, ctypes.byref(f), ctypes.byref(b), mf, mb))
+        return {"fwd": SCHEDULES[f.value], "bwd": SCHEDULES[b.value], "move_fwd": list(mf), "move_bwd": list(mb)}
 
     def torch_dtype(self):
         import torch
@@ -341,3 +360,59 @@ def oeq_sender_csr(src, n_nodes: int):
 def oeq_csr_check(rowptr, src) -> None:
     N, E = _graph(rowptr, src)
     _check(lib().oeq_csr_check(N, E, _ptr(rowptr), _ptr(src), _stream()))
+
+
+def oeq_sender_view(rowptr, src):
+    """Device sender view (srowptr[N+1], sperm[E], sdst[E]) int32 of a receiver CSR."""
+    import torch
+    N, E = _graph(rowptr, src)
+    dev = src.device
+    srowptr = torch.empty(N + 1, dtype=torch.int32, device=dev)
+    sperm = torch.empty(max(E, 1), dtype=torch.int32, device=dev)[:E]
+    sdst = torch.empty(max(E, 1), dtype=torch.int32, device=dev)[:E]
+    nbytes = ctypes.c_size_t()
+    _check(lib().oeq_csr_workspace_size(N, E, ctypes.byref(nbytes)))
+    raw = torch.empty(nbytes.value + 256, dtype=torch.uint8, device=dev)
+    off = (-raw.data_ptr()) % 256
+    ws = raw[off:off + nbytes.value]
+    _check(lib().oeq_sender_view(N, E, _ptr(rowptr), _ptr(src), _ptr(srowptr), _ptr(sperm), _ptr(sdst), _ptr(ws),
+                                 nbytes.value, _stream()))
+    return srowptr, sperm, sdst
+
+
+def oeq_tp_conv_fwd_sender(plan: Plan, view, x, Y, W, out=None):
+    """Sender-stationary forward; view = oeq_sender_view(rowptr, src)."""
+    srowptr, sperm, sdst = view
+    N, E = srowptr.shape[0] - 1, sperm.shape[0]
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(Y, (E, plan.y_dim), dt, "Y")
+    _want(W, (E, plan.n_paths, plan.U), dt, "W")
+    if out is None:
+        out = _empty((N, plan.out_dim), dt, x.device)
+    _want(out, (N, plan.out_dim), dt, "out")
+    _check(lib().oeq_tp_conv_fwd_sender(plan.handle, N, E, _ptr(srowptr), _ptr(sperm), _ptr(sdst), _ptr(x), _ptr(Y),
+                                        _ptr(W), _ptr(out), _stream()))
+    return out
+
+
+def oeq_tp_conv_bwd_sender(plan: Plan, view, x, Y, W, grad_out, want=("x", "Y", "W"), out=None, workspace=None):
+    """Sender-stationary VJP: (grad_x, grad_Y, grad_W), None where not in want."""
+    srowptr, sperm, sdst = view
+    N, E = srowptr.shape[0] - 1, sperm.shape[0]
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(Y, (E, plan.y_dim), dt, "Y")
+    _want(W, (E, plan.n_paths, plan.U), dt, "W")
+    _want(grad_out, (N, plan.out_dim), dt, "grad_out")
+    shapes = ((N, plan.x_dim), (E, plan.y_dim), (E, plan.n_paths, plan.U))
+    if out is None:
+        out = tuple(_empty(shp, dt, x.device) if k in want else None for k, shp in zip(("x", "Y", "W"), shapes))
+    for t, shp, k in zip(out, shapes, ("grad_x", "grad_Y", "grad_W")):
+        _want(t, shp, dt, k)
+    ws, nbytes = (workspace, workspace.numel()) if workspace is not None else _workspace(plan, N, E, "atomic",
+                                                                                        x.device)
+    _check(lib().oeq_tp_conv_bwd_sender(plan.handle, N, E, _ptr(srowptr), _ptr(sperm), _ptr(sdst), _ptr(x), _ptr(Y),
+                                        _ptr(W), _ptr(grad_out), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(ws),
+                                        nbytes, _stream()))
+    return out

@@ -141,6 +141,18 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
         o << " }\n";
     }
     o << "  }\n";
+    // output scatter of the sender-stationary forward: always m-major inside each
+    // output block (element m*U + u); oeq_out_untranspose restores the row layout
+    o << "  static __device__ __forceinline__ void atomic_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO]) {\n";
+    for (const auto &kv : L.ooff) {
+        const Block &b = p.ob[kv.first];
+        const int n = 2 * b.l + 1;
+        o << "    { real_t *q = orow + " << b.row_off << "LL + u;";
+        for (int m = 0; m < n; ++m)
+            o << " atomicAdd(q + " << S(static_cast<long long>(m) * p.U) << ", v[" << kv.second + m << "]);";
+        o << " }\n";
+    }
+    o << "  }\n";
     // weights: we = W + e*P*U
     o << "  static __device__ __forceinline__ void load_w(const real_t *__restrict__ we, int u, real_t (&v)[NW]) {";
     for (int k : L.paths) o << " v[" << L.widx.at(k) << "] = LDW(we + " << S(static_cast<long long>(k) * p.U) << " + u);";
@@ -268,6 +280,21 @@ void emit_untranspose(std::ostringstream &o, const oeq_plan &p) {
         o << "  for (int i = threadIdx.x; i < " << S(static_cast<long long>(n) * p.U)
           << "; i += blockDim.x) { const int u = i / " << n << ", m = i - u * " << n << "; row[" << b.row_off
           << "LL + i] = t[" << b.row_off << "LL + m * " << p.U << " + u]; }\n";
+    }
+    o << "}\n";
+    // the same for an output row, one block at a time through a buffer of the largest block
+    int64_t big = 1;
+    for (const auto &b : p.ob) big = std::max<int64_t>(big, static_cast<int64_t>(2 * b.l + 1) * p.U);
+    o << "constexpr int OUT_BLOCK_MAX = " << big << ";\n";
+    o << "__device__ __forceinline__ void g_untranspose_out_row(real_t *__restrict__ t, real_t *__restrict__ row) {\n";
+    for (const auto &b : p.ob) {
+        const int n = 2 * b.l + 1;
+        const long long cnt = static_cast<long long>(n) * p.U;
+        o << "  for (int i = threadIdx.x; i < " << cnt << "; i += blockDim.x) t[i] = row[" << b.row_off << "LL + i];\n";
+        o << "  __syncthreads();\n";
+        o << "  for (int i = threadIdx.x; i < " << cnt << "; i += blockDim.x) { const int u = i / " << n
+          << ", m = i - u * " << n << "; row[" << b.row_off << "LL + i] = t[m * " << p.U << " + u]; }\n";
+        o << "  __syncthreads();\n";
     }
     o << "}\n";
 }

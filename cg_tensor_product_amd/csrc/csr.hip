@@ -83,6 +83,24 @@ __global__ void __launch_bounds__(256) k_rank(const int *__restrict__ rowptr, in
     }
 }
 
+// The receiver of each edge in sender order: the receiver-CSR row r holding edge
+// e = sperm[k], i.e. the largest r with rowptr[r] <= e (rows may be empty).
+__global__ void __launch_bounds__(256) k_sdst(const int *__restrict__ rowptr, int n_nodes,
+                                              const int *__restrict__ sperm, int n_edges, int *__restrict__ sdst) {
+    for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < n_edges; k += gridDim.x * blockDim.x) {
+        const int e = sperm[k];
+        int lo = 0, hi = n_nodes;  // rowptr[lo] <= e < rowptr[hi]
+        while (hi - lo > 1) {
+            const int mid = lo + (hi - lo) / 2;
+            if (rowptr[mid] <= e)
+                lo = mid;
+            else
+                hi = mid;
+        }
+        sdst[k] = lo;
+    }
+}
+
 __global__ void __launch_bounds__(256) k_csr_check(const int *__restrict__ rowptr, const int *__restrict__ src,
                                                   int n_nodes, int n_edges, int *__restrict__ bad) {
     const int64_t n = n_nodes > n_edges ? n_nodes : n_edges;
@@ -128,6 +146,15 @@ hipError_t sender_csr(int64_t n_nodes, int64_t n_edges, const int32_t *src, int3
         hipLaunchKernelGGL(k_place, dim3(grid_for(E, 256)), dim3(256), 0, stream, src, E, srowptr, cursor, tmp);
         hipLaunchKernelGGL(k_rank, dim3(grid_for(N, 4)), dim3(256), 0, stream, srowptr, N, tmp, sperm);
     }
+    return hipGetLastError();
+}
+
+hipError_t sender_view(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr, const int32_t *src, int32_t *srowptr,
+                       int32_t *sperm, int32_t *sdst, void *workspace, hipStream_t stream) {
+    hipError_t e = sender_csr(n_nodes, n_edges, src, srowptr, sperm, workspace, stream);
+    if (e != hipSuccess || n_edges == 0) return e;
+    hipLaunchKernelGGL(k_sdst, dim3(grid_for(n_edges, 256)), dim3(256), 0, stream, rowptr,
+                       static_cast<int>(n_nodes), sperm, static_cast<int>(n_edges), sdst);
     return hipGetLastError();
 }
 

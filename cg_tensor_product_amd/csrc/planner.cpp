@@ -270,6 +270,34 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         const int v = std::atoi(s);
         p->dbwd_split = v < 0 ? 0 : v > 2 ? 2 : v;
     }
+    {
+        std::vector<bool> used(p->xb.size(), false);
+        for (const Path &pa : p->paths) used[pa.i1] = true;
+        p->x_unused = std::find(used.begin(), used.end(), false) != used.end();
+    }
+    // Data-movement model ("source stationary" versus "destination stationary", to be
+    // decided from the input and output irreps: [RS] maintainer reply).  Both schedules
+    // stream W and Y once; they differ in the per-edge, per-channel elements gathered
+    // from or scattered to node rows, with an atomic element weighted kAtomic gathered
+    // elements:
+    //   forward   receiver-stationary: gather x[s] (NXC)       sender-stationary: atomic add into out[r] (NOC)
+    //   VJP       receiver-stationary: gather x[s] + atomic gx   sender-stationary: gather g[r] (NOC)
+    // kAtomic is measured on MI355X: 143 M fp32 atomic adds (the sender-stationary
+    // forward of the invariant workload) took 0.48 ms where 573 M gathered elements
+    // (its receiver-stationary forward) took 0.34 ms, about 6 to 1.
+    constexpr double kAtomic = 6.0;
+    p->move_fwd[0] = p->NXC;
+    p->move_fwd[1] = kAtomic * p->NOC;
+    p->move_bwd[0] = (1.0 + kAtomic) * p->NXC;
+    p->move_bwd[1] = p->NOC;
+    p->sched_fwd = p->move_fwd[1] < p->move_fwd[0] ? 1 : 0;
+    p->sched_bwd = p->move_bwd[1] < p->move_bwd[0] ? 1 : 0;
+    if (const char *s = std::getenv("OEQ_SCHEDULE")) {  // two letters, forward then VJP: r or s
+        if (std::strlen(s) == 2) {
+            p->sched_fwd = s[0] == 's';
+            p->sched_bwd = s[1] == 's';
+        }
+    }
     return OEQ_OK;
 }
 

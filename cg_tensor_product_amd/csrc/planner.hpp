@@ -66,6 +66,11 @@ struct oeq_plan {
     int gy_tile = 32;           // edges per LDS gY flush in the backward kernels
     int dbwd_split = -1;        // double backward: 0 one fused pass; 1 split by output; 2 also one d_Y/d_x pass per tangent; -1 the first that does not spill
     bool xt = false;            // x-gradient atomics use an m-major row (needs the row in LDS)
+    bool x_unused = false;      // some x block feeds no path (its gradient is zero)
+    // Schedule the data-movement model prefers for each pass (0 receiver-, 1 sender-stationary)
+    // and the per-edge bytes it compares.
+    int sched_fwd = 0, sched_bwd = 0;
+    double move_fwd[2] = {0, 0}, move_bwd[2] = {0, 0};
     bool nt_w = true;           // non-temporal loads/stores for W and its gradients
     // keep the software-pipelined loads ahead of the arithmetic (forward, backward passes)
     bool pin_fwd = false, pin_bwd = false;

@@ -187,6 +187,59 @@ oeq_status oeq_sender_csr(int64_t n_nodes, int64_t n_edges, const int32_t *src,
                           int32_t *srowptr, int32_t *sperm, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* ---- Sender-stationary schedule ------------------------------------------
+ * The maintainers' reply in "Receiver-streaming convolutions ..." proposes two
+ * implementations of the convolution, "source stationary" and "destination
+ * stationary", with the one that moves less data chosen at initialisation from
+ * the input and output irreps.  The entry points above are destination
+ * (receiver) stationary.  These are the source (sender) stationary pair: a
+ * workgroup owns one sender, keeps its x row in registers and visits the
+ * sender's out-edges through the sender view of the graph.
+ *
+ * oeq_plan_schedule reports the plan's choice and the per-edge, per-channel
+ * costs of its model, in gathered elements (both schedules stream W and Y once;
+ * one atomic add counts as 6 gathered elements, the ratio measured on MI355X):
+ *   forward: receiver-stationary gathers x[s] (move_fwd[0] = x width per channel);
+ *            sender-stationary adds into out[r] atomically (move_fwd[1] = 6 x
+ *            output width per channel);
+ *   VJP:     receiver-stationary gathers x[s] and adds into grad_x[s] atomically
+ *            (move_bwd[0] = 7 x width); sender-stationary gathers grad_out[r]
+ *            (move_bwd[1] = output width).
+ * The smaller count wins (ties: receiver-stationary).  Each pointer may be NULL. */
+typedef enum { OEQ_RECEIVER_STATIONARY = 0, OEQ_SENDER_STATIONARY = 1 } oeq_schedule;
+oeq_status oeq_plan_schedule(const oeq_plan *plan, oeq_schedule *fwd, oeq_schedule *bwd,
+                             double *move_fwd2, double *move_bwd2);
+
+/* Sender view of a receiver CSR: oeq_sender_csr's srowptr[N+1] and sperm[E],
+ * plus sdst[E] = the receiver of edge sperm[k].  Device arrays, built with
+ * kernels only; `workspace` of oeq_csr_workspace_size bytes (256-byte aligned);
+ * asynchronous.  A model whose graph is fixed builds it once. */
+oeq_status oeq_sender_view(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr,
+                           const int32_t *src, int32_t *srowptr, int32_t *sperm,
+                           int32_t *sdst, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/* Forward, sender-stationary: out = f(x, Y, W) as oeq_tp_conv_fwd, with each
+ * edge's message added into out[receiver] by floating-point atomics (so the
+ * summation order varies run to run).  out is zeroed and reordered by the call
+ * (two light kernels around the main one). */
+oeq_status oeq_tp_conv_fwd_sender(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                  const int32_t *srowptr, const int32_t *sperm,
+                                  const int32_t *sdst, const void *x, const void *Y,
+                                  const void *W, void *out, void *stream);
+
+/* VJP, sender-stationary: the gradients of oeq_tp_conv_bwd.  grad_out[r] is
+ * gathered per edge; grad_W and grad_Y are per edge; grad_x of each sender is
+ * accumulated in registers and stored once, without atomics, so every output is
+ * bitwise repeatable.  Any gradient pointer may be NULL.  `workspace` must hold
+ * oeq_workspace_size(plan, N, E, OEQ_BWD_ATOMIC) bytes when that size is not 0. */
+oeq_status oeq_tp_conv_bwd_sender(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                  const int32_t *srowptr, const int32_t *sperm,
+                                  const int32_t *sdst, const void *x, const void *Y,
+                                  const void *W, const void *grad_out, void *grad_x,
+                                  void *grad_Y, void *grad_W, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Synchronously validates a receiver CSR on the device (rowptr monotone,
  * rowptr[0] = 0, rowptr[N] = E, 0 <= src < N).  Test helper: synchronises. */
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr,

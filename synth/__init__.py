@@ -96,6 +96,11 @@ WORKLOADS = {
     # 256x0e+256x1o+256x2e, fp32, W ~ N(0,1) materialised (multi-GB).
     "wide_proxy_fp32": Workload("wide_proxy_fp32", 5000, 56, _irr("256x0e+256x1o+256x2e"), 3, 3,
                                 "f32", "unit", 5005, ("fwd", "bwd", "hvp")),
+    # Invariant (l3 = 0) outputs of degree-0..3 features: 128x0e+128x1o+128x2e+128x3o, 4 paths.
+    # An x row is four times wider than an output row: the shape for which moving
+    # output rows (sender-stationary) is cheaper than moving x rows.
+    "invariant_fp32": Workload("invariant_fp32", 5000, 56, _irr("128x0e+128x1o+128x2e+128x3o"), 3, 0,
+                               "f32", "inv_sqrt_paths", 6006),
 }
 
 

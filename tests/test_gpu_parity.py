@@ -36,6 +36,7 @@ REDUCED = {
     "mace_medium_fp64": W_["mace_medium_fp64"].scaled(n_nodes=240),
     "mace_large_fp32": W_["mace_large_fp32"].scaled(n_nodes=160),
     "wide_proxy_fp32": W_["wide_proxy_fp32"].scaled(n_nodes=96),
+    "invariant_fp32": W_["invariant_fp32"].scaled(n_nodes=200),
 }
 _rng = np.random.default_rng(77)
 _deg = _rng.integers(0, 121, size=150)
@@ -236,7 +237,8 @@ def _sampled_gx_ref(d, inp, senders, Y, W):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32", "wide_proxy_fp32"])
+@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32", "wide_proxy_fp32",
+                                  "invariant_fp32"])
 def test_full_size_sampled(name):
     wl = W_[name]
     want = ("x", "Y", "W", "g", "v") if "hvp" in wl.ops else ("x", "Y", "W", "g")

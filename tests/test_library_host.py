@@ -162,3 +162,49 @@ def test_generated_source_has_no_packed_fp32_and_caches(tmp_path, monkeypatch):
     if dis.returncode == 0:
         assert "v_pk_fma_f32" not in dis.stdout and "v_pk_mul_f32" not in dis.stdout
         assert "oeq_fwd" in dis.stdout and "oeq_bwd_atomic" in dis.stdout
+
+
+def test_schedule_model_prefers_moving_the_narrower_rows(monkeypatch):
+    """The data-movement model of oeq_plan_schedule, in gathered elements per edge
+    and channel, an atomic add counting 6: the receiver-stationary forward gathers
+    an x row (x width), the sender-stationary one adds into an output row (6 x
+    output width); the VJPs move 7 x width (x gather + atomic x gradient) and the
+    output width (g gather)."""
+    med = oeq.Plan("128x0e+128x1o", 3, 3, "f32").schedule()       # x width 4, output width 55
+    assert med == {"fwd": "receiver", "bwd": "receiver", "move_fwd": [4.0, 330.0], "move_bwd": [28.0, 55.0]}
+    wl = synth.WORKLOADS["invariant_fp32"]                          # x width 16, output width 4
+    inv = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype).schedule()
+    assert inv == {"fwd": "receiver", "bwd": "sender", "move_fwd": [16.0, 24.0], "move_bwd": [112.0, 4.0]}
+    # 0e x 0e -> 0e only: x width 1, output width 1
+    one = oeq.Plan("8x0e", 0, 0, "f64").schedule()
+    assert one == {"fwd": "receiver", "bwd": "sender", "move_fwd": [1.0, 6.0], "move_bwd": [7.0, 1.0]}
+    monkeypatch.setenv("OEQ_SCHEDULE", "sr")
+    forced = oeq.Plan("128x0e+128x1o", 3, 3, "f32").schedule()
+    assert forced["fwd"] == "sender" and forced["bwd"] == "receiver"
+
+
+def test_sender_entry_argument_errors_before_any_device_work():
+    p = oeq.Plan("8x0e+8x1o", 2, 1, "f64")
+    lib = oeq.lib()
+    P = ctypes.c_void_p
+    f = lib.oeq_tp_conv_fwd_sender
+    assert f(None, 4, 4, P(16), P(16), P(16), P(16), P(16), P(16), P(16), None) == 1
+    assert f(p.handle, 4, 4, None, P(16), P(16), P(16), P(16), P(16), P(16), None) == 1     # srowptr
+    assert f(p.handle, 4, 4, P(16), None, P(16), P(16), P(16), P(16), P(16), None) == 1     # sperm
+    assert f(p.handle, 4, 4, P(16), P(16), None, P(16), P(16), P(16), P(16), None) == 1     # sdst
+    assert f(p.handle, 4, 4, P(16), P(16), P(16), None, P(16), P(16), P(16), None) == 1     # x
+    assert f(p.handle, 4, 4, P(16), P(16), P(16), P(16), P(16), P(16), None, None) == 1     # out
+    b = lib.oeq_tp_conv_bwd_sender
+    assert b(p.handle, 4, 4, P(16), P(16), None, P(16), P(16), P(16), P(16), P(16), P(16), P(16), None, 0,
+             None) == 1
+    assert b(p.handle, 4, 4, P(16), P(16), P(16), P(16), P(16), P(16), None, P(16), P(16), P(16), None, 0,
+             None) == 1                                                                   # grad_out
+    # nothing requested: returns without work
+    assert b(p.handle, 4, 4, P(16), P(16), P(16), P(16), P(16), P(16), P(16), None, None, None, None, 0,
+             None) == 0
+    v = lib.oeq_sender_view
+    assert v(4, 4, None, P(16), P(16), P(16), P(16), P(256), 1 << 20, None) == 1          # rowptr
+    assert v(4, 4, P(16), P(16), P(16), P(16), None, P(256), 1 << 20, None) == 1          # sdst
+    assert v(4, 4, P(16), P(16), P(16), P(16), P(16), None, 0, None) == 3                  # workspace
+    assert v(4, 4, P(16), P(16), P(16), P(16), P(16), P(256 + 8), 1 << 20, None) == 3     # misaligned
+    assert v(0, 4, P(16), P(16), P(16), P(16), P(16), P(256), 1 << 20, None) == 1         # edges without nodes

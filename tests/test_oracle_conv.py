@@ -66,7 +66,10 @@ def test_path_enumeration_counts_and_order():
     got = {k: oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max).P
            for k, wl in synth.WORKLOADS.items()}
     assert got == {"tiny_fp64": 6, "mace_medium_fp32": 13, "mace_medium_fp64": 13,
-                   "mace_large_fp32": 24, "wide_proxy_fp32": 24}
+                   "mace_large_fp32": 24, "wide_proxy_fp32": 24, "invariant_fp32": 4}
+    # invariant outputs: l3 = 0 needs l2 = l1, and p1 (-1)^l1 is even for 0e, 1o, 2e, 3o
+    assert oracle.enumerate_paths(synth.WORKLOADS["invariant_fp32"].x_irreps, 3, 0) == [
+        (0, 0, 0, 1), (1, 1, 0, 1), (2, 2, 0, 1), (3, 3, 0, 1)]
     en = oracle.enumerate_paths(synth.WORKLOADS["tiny_fp64"].x_irreps, 2, 1)
     # 0e x 0e -> 0e, 0e x 1o -> 1o, 1o x 0e -> 1o, 1o x 1o -> 0e, 1o x 1o -> 1e, 1o x 2e -> 1o
     assert en == [(0, 0, 0, 1), (0, 1, 1, -1), (1, 0, 1, -1), (1, 1, 0, 1), (1, 1, 1, 1),
