@@ -58,6 +58,77 @@ def sh_real(L: int, vec: np.ndarray) -> np.ndarray:
     return np.concatenate(cols, axis=1)
 
 
+def sh_of_vectors(L: int, vec: np.ndarray) -> np.ndarray:
+    """Real component-normalised SH of the directions of vectors of any length,
+    [E, (L+1)^2].  A zero vector has no direction: it gets Y_00 = 1 and zeros."""
+    vec = np.asarray(vec, dtype=np.float64)
+    r = np.linalg.norm(vec, axis=1)
+    live = r > 0
+    n = np.zeros_like(vec)
+    n[live] = vec[live] / r[live, None]
+    n[~live] = (0.0, 0.0, 1.0)
+    Y = sh_real(L, n)
+    Y[~live, 1:] = 0.0
+    return Y
+
+
+def _legendre_parts(l: int, m: int):
+    """q = d^m P_l / dt^m and q' as polynomial coefficient arrays."""
+    c = np.zeros(l + 1)
+    c[l] = 1.0
+    q = _poly.polyder(_leg.leg2poly(c), m) if m > 0 else _leg.leg2poly(c)
+    return q, _poly.polyder(q)
+
+
+def sh_grad_of_vectors(L: int, vec: np.ndarray) -> np.ndarray:
+    """Gradient of sh_of_vectors with respect to the vector, [E, (L+1)^2, 3], by
+    the chain rule through the polar angles:
+        grad Y = (dY/dtheta) e_theta / r + (dY/dphi) e_phi / (r sin theta),
+    dY/dphi = i m Y for the complex harmonics, and for P_l^m(t) = (1-t^2)^(m/2) q(t),
+    t = cos theta: dP/dtheta = -sin(theta)^(m-1) [sin^2(theta) q'(t) - m cos(theta) q(t)]
+    (m = 0: -sin(theta) q'(t)); then carried to the real basis like the values.
+    Undefined on the z axis (sin theta = 0) for m > 0; zero for a zero vector."""
+    vec = np.asarray(vec, dtype=np.float64)
+    E = len(vec)
+    r = np.linalg.norm(vec, axis=1)
+    live = r > 0
+    x, y, z = (vec[:, k] / np.where(live, r, 1.0) for k in range(3))
+    ct = np.clip(z, -1.0, 1.0)
+    theta = np.arccos(ct)
+    st = np.sin(theta)
+    phi = np.arctan2(y, x)
+    e_theta = np.stack([ct * np.cos(phi), ct * np.sin(phi), -st], axis=1)
+    e_phi = np.stack([-np.sin(phi), np.cos(phi), np.zeros(E)], axis=1)
+    rr = np.where(live, r, 1.0)
+    cols = []
+    for l in range(L + 1):
+        gc = np.zeros((E, 2 * l + 1, 3), dtype=complex)
+        for m in range(0, l + 1):
+            nrm = math.sqrt((2 * l + 1) / (4 * math.pi) * math.factorial(l - m) / math.factorial(l + m))
+            q, dq = _legendre_parts(l, m)
+            qv, dqv = _poly.polyval(ct, q), _poly.polyval(ct, dq)
+            if m == 0:
+                dP = -st * dqv
+                P_over_s = np.zeros(E)          # multiplied by m = 0 below
+            else:
+                dP = -st ** (m - 1) * (st * st * dqv - m * ct * qv)
+                P_over_s = st ** (m - 1) * qv   # P_l^m / sin(theta)
+            ph = np.exp(1j * m * phi)
+            dtheta = nrm * (-1) ** m * dP * ph
+            dphi_over_s = nrm * (-1) ** m * P_over_s * ph * (1j * m)
+            g = (dtheta[:, None] * e_theta + dphi_over_s[:, None] * e_phi) / rr[:, None]
+            gc[:, m + l, :] = g
+            if m > 0:
+                gc[:, -m + l, :] = (-1) ** m * np.conj(g)
+        A = real_basis(l)
+        gl = math.sqrt(4 * math.pi) * np.einsum("mk,ekd->emd", A, gc)
+        assert np.abs(gl.imag).max(initial=0.0) < 1e-9
+        cols.append(gl.real)
+    G = np.concatenate(cols, axis=1)
+    G[~live] = 0.0
+    return G
+
+
 def small_d(l: int, mp: int, m: int, beta: float) -> float:
     s = 0.0
     cb, sb = math.cos(beta / 2), math.sin(beta / 2)
