@@ -33,7 +33,8 @@ EXPORTED = ["oeq_plan_create", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_pa
             "oeq_workspace_size", "oeq_tp_conv_fwd", "oeq_tp_conv_bwd", "oeq_tp_conv_dbwd",
             "oeq_csr_workspace_size", "oeq_sender_csr", "oeq_csr_check", "oeq_status_string",
             "oeq_last_error", "oeq_plan_schedule", "oeq_sender_view", "oeq_tp_conv_fwd_sender",
-            "oeq_tp_conv_bwd_sender"]
+            "oeq_tp_conv_bwd_sender", "oeq_sph_harm", "oeq_sph_harm_bwd", "oeq_tp_conv_fwd_vec",
+            "oeq_workspace_size_vec", "oeq_tp_conv_bwd_vec"]
 SCHEDULES = {0: "receiver", 1: "sender"}
 
 
@@ -107,6 +108,16 @@ def lib():
     L.oeq_tp_conv_fwd_sender.restype = st
     L.oeq_tp_conv_bwd_sender.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
     L.oeq_tp_conv_bwd_sender.restype = st
+    L.oeq_sph_harm.argtypes = [P, I64, P, P, P]
+    L.oeq_sph_harm.restype = st
+    L.oeq_sph_harm_bwd.argtypes = [P, I64, P, P, P, P]
+    L.oeq_sph_harm_bwd.restype = st
+    L.oeq_tp_conv_fwd_vec.argtypes = [P, I64, I64, P, P, P, P, P, P, P]
+    L.oeq_tp_conv_fwd_vec.restype = st
+    L.oeq_workspace_size_vec.argtypes = [P, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
+    L.oeq_workspace_size_vec.restype = st
+    L.oeq_tp_conv_bwd_vec.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, SZ, P]
+    L.oeq_tp_conv_bwd_vec.restype = st
     L.oeq_status_string.argtypes = [ctypes.c_int]
     L.oeq_status_string.restype = ctypes.c_char_p
     L.oeq_last_error.argtypes = []
@@ -415,4 +426,75 @@ def oeq_tp_conv_bwd_sender(plan: Plan, view, x, Y, W, grad_out, want=("x", "Y", 
     _check(lib().oeq_tp_conv_bwd_sender(plan.handle, N, E, _ptr(srowptr), _ptr(sperm), _ptr(sdst), _ptr(x), _ptr(Y),
                                         _ptr(W), _ptr(grad_out), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(ws),
                                         nbytes, _stream()))
+    return out
+
+
+def oeq_sph_harm(plan: Plan, vec, out=None):
+    """Y[E, (L+1)^2] of edge vectors vec[E, 3]."""
+    E = vec.shape[0]
+    dt = plan.torch_dtype()
+    _want(vec, (E, 3), dt, "vec")
+    if out is None:
+        out = _empty((E, plan.y_dim), dt, vec.device)
+    _want(out, (E, plan.y_dim), dt, "Y")
+    _check(lib().oeq_sph_harm(plan.handle, E, _ptr(vec), _ptr(out), _stream()))
+    return out
+
+
+def oeq_sph_harm_bwd(plan: Plan, vec, grad_Y, out=None):
+    """grad_vec[E, 3] = sum_m grad_Y[e, m] dY[e, m] / dvec[e]."""
+    E = vec.shape[0]
+    dt = plan.torch_dtype()
+    _want(vec, (E, 3), dt, "vec")
+    _want(grad_Y, (E, plan.y_dim), dt, "grad_Y")
+    if out is None:
+        out = _empty((E, 3), dt, vec.device)
+    _want(out, (E, 3), dt, "grad_vec")
+    _check(lib().oeq_sph_harm_bwd(plan.handle, E, _ptr(vec), _ptr(grad_Y), _ptr(out), _stream()))
+    return out
+
+
+def oeq_tp_conv_fwd_vec(plan: Plan, rowptr, src, x, vec, W, out=None):
+    """Forward with Y evaluated in the kernel from the edge vectors."""
+    N, E = _graph(rowptr, src)
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(vec, (E, 3), dt, "vec")
+    _want(W, (E, plan.n_paths, plan.U), dt, "W")
+    if out is None:
+        out = _empty((N, plan.out_dim), dt, rowptr.device)
+    _want(out, (N, plan.out_dim), dt, "out")
+    _check(lib().oeq_tp_conv_fwd_vec(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(vec), _ptr(W),
+                                     _ptr(out), _stream()))
+    return out
+
+
+def oeq_workspace_size_vec(plan: Plan, n_nodes: int, n_edges: int, mode: str = "atomic") -> int:
+    b = ctypes.c_size_t()
+    _check(lib().oeq_workspace_size_vec(plan.handle, n_nodes, n_edges, _MODES[mode], ctypes.byref(b)))
+    return b.value
+
+
+def oeq_tp_conv_bwd_vec(plan: Plan, rowptr, src, x, vec, W, grad_out, mode: str = "atomic",
+                        want=("x", "vec", "W"), out=None, workspace=None):
+    """VJP to (x, vec, W) of the forward from edge vectors."""
+    import torch
+    N, E = _graph(rowptr, src)
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(vec, (E, 3), dt, "vec")
+    _want(W, (E, plan.n_paths, plan.U), dt, "W")
+    _want(grad_out, (N, plan.out_dim), dt, "grad_out")
+    shapes = ((N, plan.x_dim), (E, 3), (E, plan.n_paths, plan.U))
+    if out is None:
+        out = tuple(_empty(shp, dt, x.device) if k in want else None for k, shp in zip(("x", "vec", "W"), shapes))
+    for t, shp, k in zip(out, shapes, ("grad_x", "grad_vec", "grad_W")):
+        _want(t, shp, dt, k)
+    if workspace is None:
+        nbytes = oeq_workspace_size_vec(plan, N, E, mode)
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=x.device)
+        workspace = raw[(-raw.data_ptr()) % 256:][:nbytes]
+    _check(lib().oeq_tp_conv_bwd_vec(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(vec), _ptr(W),
+                                     _ptr(grad_out), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _MODES[mode],
+                                     _ptr(workspace), workspace.numel(), _stream()))
     return out

@@ -146,6 +146,13 @@ oeq_status fwd_launch(oeq_plan *p, int64_t N, const int32_t *rowptr, const int32
     return launch(p, "oeq_fwd", static_cast<unsigned>(N), fwd_block(p), s, args);
 }
 
+// Grid-stride launch of a per-edge kernel (vec, a, b, n) over E edges.
+oeq_status edge_launch(oeq_plan *p, const char *name, int64_t E, void **args, hipStream_t stream) {
+    int64_t blocks = (E + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    return launch(p, name, static_cast<unsigned>(blocks), 256, stream, args);
+}
+
 }  // namespace
 
 extern "C" {
@@ -519,6 +526,75 @@ oeq_status oeq_tp_conv_bwd_sender(const oeq_plan *plan, int64_t N, int64_t E, co
     void *args[] = {&srowptr, &sperm, &sdst, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride};
     if ((st = launch(p, "oeq_bwd_sender", grid, bwd_block(p), s, args)) != OEQ_OK) return st;
     return gyp ? gy_combine(p, w, gY, E, s) : OEQ_OK;
+}
+
+oeq_status oeq_sph_harm(const oeq_plan *plan, int64_t E, const void *vec, void *Y, void *stream) {
+    if (!plan) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative edge count");
+    if (E == 0) return OEQ_OK;
+    if (!vec || !Y) return fail(OEQ_ERR_INVALID_ARG, "vec or Y is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    void *args[] = {&vec, &Y, &E};
+    return edge_launch(p, "oeq_sph_harm", E, args, static_cast<hipStream_t>(stream));
+}
+
+oeq_status oeq_sph_harm_bwd(const oeq_plan *plan, int64_t E, const void *vec, const void *gY, void *gvec,
+                            void *stream) {
+    if (!plan) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative edge count");
+    if (E == 0) return OEQ_OK;
+    if (!vec || !gY || !gvec) return fail(OEQ_ERR_INVALID_ARG, "vec, grad_Y or grad_vec is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    void *args[] = {&vec, &gY, &gvec, &E};
+    return edge_launch(p, "oeq_sph_harm_bwd", E, args, static_cast<hipStream_t>(stream));
+}
+
+oeq_status oeq_tp_conv_fwd_vec(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr,
+                               const int32_t *src, const void *x, const void *vec, const void *W, void *out,
+                               void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
+    if (E > 0 && (!x || !vec || !W)) return fail(OEQ_ERR_INVALID_ARG, "x, vec or W is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    void *args[] = {&rowptr, &src, &x, &vec, &W, &out};
+    return launch(p, "oeq_fwd_vec", static_cast<unsigned>(N), fwd_block(p), static_cast<hipStream_t>(stream), args);
+}
+
+oeq_status oeq_workspace_size_vec(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, size_t *bytes) {
+    size_t base = 0;
+    oeq_status st = oeq_workspace_size(p, N, E, mode, &base);
+    if (st != OEQ_OK) return st;
+    const size_t rows = up(static_cast<size_t>(E) * p->YD * esize(p));
+    *bytes = 2 * rows + base;  // Y rows, Y-gradient rows, then the VJP's own workspace
+    return OEQ_OK;
+}
+
+oeq_status oeq_tp_conv_bwd_vec(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr,
+                               const int32_t *src, const void *x, const void *vec, const void *W, const void *g,
+                               void *gx, void *gvec, void *gW, oeq_bwd_mode mode, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    if (E > 0 && (!x || !vec || !W || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, vec, W or grad_out is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (E == 0) return gx ? fill_zero(p, gx, N * p->XD, s) : OEQ_OK;
+    if (!gx && !gvec && !gW) return OEQ_OK;
+    size_t need = 0;
+    if ((st = oeq_workspace_size_vec(p, N, E, mode, &need)) != OEQ_OK) return st;
+    if (!workspace || workspace_bytes < need) return fail(OEQ_ERR_WORKSPACE, "workspace too small");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+        return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+    const size_t rows = up(static_cast<size_t>(E) * p->YD * esize(p));
+    void *Yw = ws, *gYw = gvec ? ws + rows : nullptr;
+    if ((st = oeq_sph_harm(p, E, vec, Yw, stream)) != OEQ_OK) return st;
+    if ((st = oeq_tp_conv_bwd(p, N, E, rowptr, src, x, Yw, W, g, gx, gYw, gW, mode, ws + 2 * rows,
+                              workspace_bytes - 2 * rows, stream)) != OEQ_OK)
+        return st;
+    return gvec ? oeq_sph_harm_bwd(p, E, vec, gYw, gvec, stream) : OEQ_OK;
 }
 
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr, const int32_t *src, void *stream) {

@@ -344,6 +344,7 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr int NGF = " << p.fwd_groups.size() << ";\n";
     o << "constexpr int NGB = " << p.bwd_groups.size() << ";\n";
     o << "constexpr int P = " << p.paths.size() << ";\n";
+    o << "constexpr int LY = " << p.L << ";\n";
     o << "constexpr int YD = " << p.YD << ";\n";
     o << "constexpr int PY = " << py << ";\n";
     o << "constexpr int LGPY = " << lgpy << ";\n";

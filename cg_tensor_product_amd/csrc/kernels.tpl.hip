@@ -33,6 +33,133 @@ __device__ __forceinline__ void load_y(const real_t *__restrict__ Y, int e, real
     for (int k = 0; k < YD; ++k) yv[k] = yr[k];
 }
 
+// ---------------------------------------------------------------------------
+// Real spherical harmonics of an edge vector v (degrees 0..LY, m = -l..l, l = 1
+// ordered (y, z, x), component normalisation: the squares of degree l sum to
+// 2l+1), evaluated on the direction n = v/|v| from the Cartesian polynomial forms
+// of the Condon-Shortley real harmonics.  A zero vector has no direction: it
+// gives Y_00 = 1 and zeros, and a zero gradient.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float sqrt_r(float v) { return __builtin_sqrtf(v); }
+__device__ __forceinline__ double sqrt_r(double v) { return __builtin_sqrt(v); }
+__device__ __forceinline__ real_t rsqrt_or_zero(real_t r2) {
+    return r2 > real_t(0) ? real_t(1) / sqrt_r(r2) : real_t(0);
+}
+
+__device__ __forceinline__ void sh_eval(real_t vx, real_t vy, real_t vz, real_t (&Yv)[YD]) {
+    const real_t inv = rsqrt_or_zero(vx * vx + vy * vy + vz * vz);
+    const real_t x = vx * inv, y = vy * inv, z = vz * inv;
+    const bool live = inv > real_t(0);
+    Yv[0] = real_t(1);
+    if constexpr (LY >= 1) {
+        const real_t s3 = real_t(1.7320508075688772);  // sqrt(3)
+        Yv[1] = s3 * y;
+        Yv[2] = s3 * z;
+        Yv[3] = s3 * x;
+    }
+    if constexpr (LY >= 2) {
+        const real_t s15 = real_t(3.872983346207417), s5 = real_t(2.23606797749979);
+        Yv[4] = s15 * x * y;
+        Yv[5] = s15 * y * z;
+        Yv[6] = live ? real_t(0.5) * s5 * (real_t(3) * z * z - real_t(1)) : real_t(0);
+        Yv[7] = s15 * x * z;
+        Yv[8] = real_t(0.5) * s15 * (x * x - y * y);
+    }
+    if constexpr (LY >= 3) {
+        const real_t a = real_t(2.091650066335189);   // sqrt(35/8)
+        const real_t b = real_t(10.246950765959598);  // sqrt(105)
+        const real_t c = real_t(1.6201851746019651);  // sqrt(21/8)
+        const real_t h7 = real_t(1.3228756555322954); // sqrt(7)/2
+        const real_t zz5 = real_t(5) * z * z - real_t(1);
+        Yv[9] = a * y * (real_t(3) * x * x - y * y);
+        Yv[10] = b * x * y * z;
+        Yv[11] = c * y * zz5;
+        Yv[12] = h7 * z * (real_t(5) * z * z - real_t(3));
+        Yv[13] = c * x * zz5;
+        Yv[14] = real_t(0.5) * b * z * (x * x - y * y);
+        Yv[15] = a * x * (x * x - real_t(3) * y * y);
+    }
+}
+
+// Vector gradient of sum_m gy[m] Y_m(v): with P_m the Cartesian polynomials above
+// (any smooth extension off the sphere), grad = (I - n n^T) (sum_m gy[m] grad P_m(n)) / |v|.
+__device__ __forceinline__ void sh_grad(real_t vx, real_t vy, real_t vz, const real_t (&gy)[YD], real_t &gvx,
+                                        real_t &gvy, real_t &gvz) {
+    const real_t inv = rsqrt_or_zero(vx * vx + vy * vy + vz * vz);
+    const real_t x = vx * inv, y = vy * inv, z = vz * inv;
+    real_t ax = real_t(0), ay = real_t(0), az = real_t(0);
+    if constexpr (LY >= 1) {
+        const real_t s3 = real_t(1.7320508075688772);
+        ax += s3 * gy[3];
+        ay += s3 * gy[1];
+        az += s3 * gy[2];
+    }
+    if constexpr (LY >= 2) {
+        const real_t s15 = real_t(3.872983346207417), s5 = real_t(2.23606797749979);
+        // d/d(x,y,z) of s15 xy, s15 yz, s5/2 (3z^2-1), s15 xz, s15/2 (x^2-y^2)
+        ax += s15 * (gy[4] * y + gy[7] * z + gy[8] * x);
+        ay += s15 * (gy[4] * x + gy[5] * z - gy[8] * y);
+        az += s15 * (gy[5] * y + gy[7] * x) + real_t(3) * s5 * gy[6] * z;
+    }
+    if constexpr (LY >= 3) {
+        const real_t a = real_t(2.091650066335189), b = real_t(10.246950765959598);
+        const real_t c = real_t(1.6201851746019651), h7 = real_t(1.3228756555322954);
+        const real_t zz5 = real_t(5) * z * z - real_t(1);
+        // a y(3x^2-y^2): (6a xy, 3a(x^2-y^2), 0)      b xyz: (b yz, b xz, b xy)
+        // c y(5z^2-1): (0, c(5z^2-1), 10c yz)         sqrt(7)/2 (5z^3-3z): (0, 0, sqrt(7)/2 (15z^2-3))
+        // c x(5z^2-1): (c(5z^2-1), 0, 10c xz)         b/2 z(x^2-y^2): (b xz, -b yz, b/2 (x^2-y^2))
+        // a x(x^2-3y^2): (3a(x^2-y^2), -6a xy, 0)
+        const real_t d2 = x * x - y * y;
+        ax += real_t(6) * a * x * y * gy[9] + b * y * z * gy[10] + c * zz5 * gy[13] + b * x * z * gy[14] +
+              real_t(3) * a * d2 * gy[15];
+        ay += real_t(3) * a * d2 * gy[9] + b * x * z * gy[10] + c * zz5 * gy[11] - b * y * z * gy[14] -
+              real_t(6) * a * x * y * gy[15];
+        az += b * x * y * gy[10] + real_t(10) * c * y * z * gy[11] +
+              h7 * (real_t(15) * z * z - real_t(3)) * gy[12] + real_t(10) * c * x * z * gy[13] +
+              real_t(0.5) * b * d2 * gy[14];
+    }
+    const real_t dot = ax * x + ay * y + az * z;
+    gvx = (ax - dot * x) * inv;
+    gvy = (ay - dot * y) * inv;
+    gvz = (az - dot * z) * inv;
+}
+
+// Y row of edge e from its vector (YV) or from memory
+template <bool YV>
+__device__ __forceinline__ void edge_y(const real_t *__restrict__ Ysrc, int e, real_t (&yv)[YD]) {
+    if constexpr (YV) {
+        const real_t *v = Ysrc + (i64)e * 3;
+        sh_eval(v[0], v[1], v[2], yv);
+    } else {
+        load_y(Ysrc, e, yv);
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_sph_harm(const real_t *__restrict__ vec, real_t *__restrict__ Y, i64 n_edges) {
+    for (i64 e = (i64)blockIdx.x * blockDim.x + threadIdx.x; e < n_edges; e += (i64)gridDim.x * blockDim.x) {
+        real_t yv[YD];
+        sh_eval(vec[e * 3], vec[e * 3 + 1], vec[e * 3 + 2], yv);
+#pragma unroll
+        for (int k = 0; k < YD; ++k) Y[e * YD + k] = yv[k];
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_sph_harm_bwd(const real_t *__restrict__ vec, const real_t *__restrict__ gY, real_t *__restrict__ gvec,
+                 i64 n_edges) {
+    for (i64 e = (i64)blockIdx.x * blockDim.x + threadIdx.x; e < n_edges; e += (i64)gridDim.x * blockDim.x) {
+        real_t g[YD];
+#pragma unroll
+        for (int k = 0; k < YD; ++k) g[k] = gY[e * YD + k];
+        real_t a, b, c;
+        sh_grad(vec[e * 3], vec[e * 3 + 1], vec[e * 3 + 2], g, a, b, c);
+        gvec[e * 3] = a;
+        gvec[e * 3 + 1] = b;
+        gvec[e * 3 + 2] = c;
+    }
+}
+
 // Cross-lane moves on 32-bit words; a double moves as two words.
 //   swap32(a, b): a <- [a lanes 0-31 | b lanes 0-31], b <- [a lanes 32-63 | b lanes 32-63]
 //   swap16(a, b): per 32-lane half, a <- [a row 0 | b row 0], b <- [a row 1 | b row 1]
@@ -149,7 +276,7 @@ oeq_fill_zero(real_t *__restrict__ p, i64 n) {
 // ---------------------------------------------------------------------------
 // Forward: out[r] = sum over the receiver's edges of the per-edge messages.
 // ---------------------------------------------------------------------------
-template <int G>
+template <int G, bool YV>
 __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ rowptr,
                                           const int *__restrict__ src, const real_t *__restrict__ x,
                                           const real_t *__restrict__ Y, const real_t *__restrict__ W,
@@ -164,14 +291,14 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
         // software pipeline: the next edge's loads are in flight while this one computes
         int s = uni(src[e0]);
         real_t yv[YD], xv[Gr::NX], wv[Gr::NW];
-        load_y(Y, e0, yv);
+        edge_y<YV>(Y, e0, yv);
         Gr::load_x(x + (i64)s * XD, uu, xv);
         Gr::load_w(W + (i64)e0 * (P * U), uu, wv);
         for (int e = e0; e < e1; ++e) {
             real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
             const int en = (e + 1 < e1) ? e + 1 : e;
             const int sn = uni(src[en]);
-            load_y(Y, en, yn);
+            edge_y<YV>(Y, en, yn);
             Gr::load_x(x + (i64)sn * XD, uu, xn);
             Gr::load_w(W + (i64)en * (P * U), uu, wn);
             // keep the next edge's loads ahead of this edge's arithmetic
@@ -193,16 +320,16 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
     }
 }
 
-template <int G>
+template <int G, bool YV>
 __device__ __forceinline__ void fwd_dispatch(int grp, int r, int u, const int *__restrict__ rowptr,
                                              const int *__restrict__ src, const real_t *__restrict__ x,
                                              const real_t *__restrict__ Y, const real_t *__restrict__ W,
                                              real_t *__restrict__ out, bool acc) {
     if (grp == G) {
-        fwd_group<G>(r, u, rowptr, src, x, Y, W, out, acc);
+        fwd_group<G, YV>(r, u, rowptr, src, x, Y, W, out, acc);
         return;
     }
-    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1>(grp, r, u, rowptr, src, x, Y, W, out, acc);
+    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1, YV>(grp, r, u, rowptr, src, x, Y, W, out, acc);
 }
 
 extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
@@ -211,7 +338,18 @@ oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_
     // flags: bit0 add into out instead of overwriting it
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
-    fwd_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out, (flags & 1) != 0);
+    fwd_dispatch<0, false>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out,
+                           (flags & 1) != 0);
+}
+
+// The forward with Y evaluated in the kernel from the edge vectors vec[E, 3]
+// (no Y tensor): each wave computes the harmonics of the edge it streams.
+extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
+oeq_fwd_vec(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+            const real_t *__restrict__ vec, const real_t *__restrict__ W, real_t *__restrict__ out) {
+    const int w = uni(threadIdx.x >> 6);
+    const int grp = w / UCH, uc = w - grp * UCH;
+    fwd_dispatch<0, true>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, vec, W, out, false);
 }
 
 // The atomic x-gradient is accumulated m-major inside each x block (so the

@@ -240,6 +240,42 @@ oeq_status oeq_tp_conv_bwd_sender(const oeq_plan *plan, int64_t n_nodes, int64_t
                                   void *grad_Y, void *grad_W, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* ---- Y from edge vectors ---------------------------------------------------
+ * The step before the tensor product: Y[e] = the real spherical harmonics of the
+ * direction of the edge vector vec[e] = (x, y, z) (the pages' receiver-major edges
+ * are built from atom positions; "Receiver-streaming convolutions ...", opening
+ * post), and the gradient carried back from Y to the vectors.  Convention as for
+ * Y everywhere in this library: degrees 0..L of the plan, m = -l..l, degree 1
+ * ordered (y, z, x), Condon-Shortley phase, component normalisation (the squares
+ * of degree l sum to 2l+1).  The vector need not be unit length; a zero vector
+ * gives Y_00 = 1, all other degrees 0, and a zero gradient.  vec is [E, 3] in the
+ * plan's dtype. */
+oeq_status oeq_sph_harm(const oeq_plan *plan, int64_t n_edges, const void *vec, void *Y,
+                        void *stream);
+
+/* grad_vec[e] = sum_m grad_Y[e, m] dY[e, m] / dvec[e]  ([E, 3]). */
+oeq_status oeq_sph_harm_bwd(const oeq_plan *plan, int64_t n_edges, const void *vec,
+                            const void *grad_Y, void *grad_vec, void *stream);
+
+/* Forward from edge vectors: out = f(x, Y(vec), W), with the harmonics evaluated
+ * inside the forward kernel (no Y tensor is read or written).  Otherwise as
+ * oeq_tp_conv_fwd. */
+oeq_status oeq_tp_conv_fwd_vec(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                               const int32_t *rowptr, const int32_t *src, const void *x,
+                               const void *vec, const void *W, void *out, void *stream);
+
+/* VJP from edge vectors: grad_x, grad_W as oeq_tp_conv_bwd, and
+ * grad_vec[e] = sum_m grad_Y[e,m] dY[e,m]/dvec[e] in place of grad_Y.  Runs
+ * oeq_sph_harm into the workspace, the VJP, then oeq_sph_harm_bwd.  `workspace`
+ * (256-byte aligned) must hold oeq_workspace_size_vec(mode) bytes. */
+oeq_status oeq_workspace_size_vec(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                  oeq_bwd_mode mode, size_t *bytes);
+oeq_status oeq_tp_conv_bwd_vec(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                               const int32_t *rowptr, const int32_t *src, const void *x,
+                               const void *vec, const void *W, const void *grad_out,
+                               void *grad_x, void *grad_vec, void *grad_W, oeq_bwd_mode mode,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* Synchronously validates a receiver CSR on the device (rowptr monotone,
  * rowptr[0] = 0, rowptr[N] = E, 0 <= src < N).  Test helper: synchronises. */
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr,

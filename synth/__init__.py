@@ -219,6 +219,12 @@ def generate(wl: Workload, n_paths: int, out_dim: int, want=("x", "Y", "W", "g")
         vec = unit_vectors(E, rngs[_VEC])
         out["vec"] = vec
         out["Y"] = real_sh_cartesian(wl.y_lmax, vec).astype(dt)
+    if "evec" in want:
+        # edge vectors with lengths: the unit vectors above times lengths uniform in [0.5, 5)
+        unit = out["vec"] if "vec" in out else unit_vectors(E, _children(wl.seed)[_VEC])
+        lrng = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence(wl.seed).spawn(_NCHILD)[_EXTRA].spawn(100)[99]))
+        out["evec"] = (unit * (0.5 + 4.5 * lrng.random((E, 1)))).astype(dt)
     if "x" in want:
         out["x"] = normal(rngs[_X], (wl.n_nodes, wl.x_dim), dt)
     if "W" in want:
