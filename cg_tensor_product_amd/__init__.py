@@ -34,7 +34,8 @@ EXPORTED = ["oeq_plan_create", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_pa
             "oeq_csr_workspace_size", "oeq_sender_csr", "oeq_csr_check", "oeq_status_string",
             "oeq_last_error", "oeq_plan_schedule", "oeq_sender_view", "oeq_tp_conv_fwd_sender",
             "oeq_tp_conv_bwd_sender", "oeq_sph_harm", "oeq_sph_harm_bwd", "oeq_tp_conv_fwd_vec",
-            "oeq_workspace_size_vec", "oeq_tp_conv_bwd_vec"]
+            "oeq_workspace_size_vec", "oeq_tp_conv_bwd_vec", "oeq_radial_workspace_size", "oeq_radial_fwd",
+            "oeq_radial_bwd"]
 SCHEDULES = {0: "receiver", 1: "sender"}
 
 
@@ -118,6 +119,13 @@ def lib():
     L.oeq_workspace_size_vec.restype = st
     L.oeq_tp_conv_bwd_vec.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, SZ, P]
     L.oeq_tp_conv_bwd_vec.restype = st
+    D = ctypes.c_double
+    L.oeq_radial_workspace_size.argtypes = [P, I64, I32, ctypes.POINTER(SZ)]
+    L.oeq_radial_workspace_size.restype = st
+    L.oeq_radial_fwd.argtypes = [P, I64, P, D, I32, P, P, P, P, SZ, P]
+    L.oeq_radial_fwd.restype = st
+    L.oeq_radial_bwd.argtypes = [P, I64, P, D, I32, P, P, P, P, P, P, P, SZ, P]
+    L.oeq_radial_bwd.restype = st
     L.oeq_status_string.argtypes = [ctypes.c_int]
     L.oeq_status_string.restype = ctypes.c_char_p
     L.oeq_last_error.argtypes = []
@@ -498,3 +506,46 @@ def oeq_tp_conv_bwd_vec(plan: Plan, rowptr, src, x, vec, W, grad_out, mode: str 
                                      _ptr(grad_out), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _MODES[mode],
                                      _ptr(workspace), workspace.numel(), _stream()))
     return out
+
+
+def _radial_ws(plan, E, hidden, device):
+    import torch
+    b = ctypes.c_size_t()
+    _check(lib().oeq_radial_workspace_size(plan.handle, E, hidden, ctypes.byref(b)))
+    raw = torch.empty(b.value + 256, dtype=torch.uint8, device=device)
+    return raw[(-raw.data_ptr()) % 256:][:b.value]
+
+
+def oeq_radial_fwd(plan: Plan, vec, r_cut: float, W1, W2, out=None, workspace=None):
+    """Radial weights W [E, P, U] from edge vectors (see oeq.h for the form)."""
+    E = vec.shape[0]
+    dt = plan.torch_dtype()
+    H = W1.shape[1]
+    _want(vec, (E, 3), dt, "vec")
+    _want(W1, (8, H), dt, "W1")
+    _want(W2, (H, plan.n_paths * plan.U), dt, "W2")
+    if out is None:
+        out = _empty((E, plan.n_paths, plan.U), dt, vec.device)
+    _want(out, (E, plan.n_paths, plan.U), dt, "W")
+    ws = workspace if workspace is not None else _radial_ws(plan, E, H, vec.device)
+    _check(lib().oeq_radial_fwd(plan.handle, E, _ptr(vec), float(r_cut), H, _ptr(W1), _ptr(W2), _ptr(out), _ptr(ws),
+                                ws.numel(), _stream()))
+    return out
+
+
+def oeq_radial_bwd(plan: Plan, vec, r_cut: float, W1, W2, grad_W, want=("vec", "W1", "W2"), workspace=None):
+    """(grad_vec, grad_W1, grad_W2) of <grad_W, W(vec, W1, W2)>; None where not in want."""
+    E = vec.shape[0]
+    dt = plan.torch_dtype()
+    H = W1.shape[1]
+    _want(vec, (E, 3), dt, "vec")
+    _want(W1, (8, H), dt, "W1")
+    _want(W2, (H, plan.n_paths * plan.U), dt, "W2")
+    _want(grad_W, (E, plan.n_paths, plan.U), dt, "grad_W")
+    gv = _empty((E, 3), dt, vec.device) if "vec" in want else None
+    g1 = _empty((8, H), dt, vec.device) if "W1" in want else None
+    g2 = _empty((H, plan.n_paths * plan.U), dt, vec.device) if "W2" in want else None
+    ws = workspace if workspace is not None else _radial_ws(plan, E, H, vec.device)
+    _check(lib().oeq_radial_bwd(plan.handle, E, _ptr(vec), float(r_cut), H, _ptr(W1), _ptr(W2), _ptr(grad_W),
+                                _ptr(gv), _ptr(g1), _ptr(g2), _ptr(ws), ws.numel(), _stream()))
+    return gv, g1, g2

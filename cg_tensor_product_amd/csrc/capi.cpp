@@ -1,6 +1,7 @@
 // C ABI entry points: argument checks (host only, no device reads, no
 // synchronisation), workspace carving and stream-ordered kernel launches.
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <cstring>
 #include <limits>
@@ -151,6 +152,95 @@ oeq_status edge_launch(oeq_plan *p, const char *name, int64_t E, void **args, hi
     int64_t blocks = (E + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     return launch(p, name, static_cast<unsigned>(blocks), 256, stream, args);
+}
+
+// C[M,N] = alpha op(A)[M,K] op(B)[K,N] on the matrix cores (oeq_gemm).  With
+// splits > 1 the K range is cut into that many pieces whose tiles go to `part`
+// ([splits, M, N]) and are then added in order into C.
+oeq_status gemm(oeq_plan *p, int M, int N, int K, const void *A, int64_t lda, bool ta, const void *B, int64_t ldb,
+                bool tb, void *C, int64_t ldc, double alpha, int splits, void *part, hipStream_t s) {
+    if (M <= 0 || N <= 0) return OEQ_OK;
+    int kchunk = std::max(K, 1);
+    if (splits > 1) {
+        kchunk = ((K + splits - 1) / splits + 15) / 16 * 16;
+        splits = (K + kchunk - 1) / kchunk;
+    }
+    if (splits < 1) splits = 1;
+    int ta_i = ta ? 1 : 0, tb_i = tb ? 1 : 0;
+    void *dst = splits > 1 ? part : C;
+    int64_t ldd = splits > 1 ? N : ldc;
+    int64_t stride = static_cast<int64_t>(M) * N;
+    float af = static_cast<float>(alpha);
+    void *ap = p->dtype == OEQ_F64 ? static_cast<void *>(&alpha) : static_cast<void *>(&af);
+    void *args[] = {&M, &N, &K, &A, &lda, &ta_i, &B, &ldb, &tb_i, &dst, &ldd, &stride, &kchunk, ap};
+    hipFunction_t fn = nullptr;
+    std::string why;
+    oeq_status st = oeq::get_kernel(*p, "oeq_gemm", &fn, &why);
+    if (st != OEQ_OK) return fail(st, why);
+    const hipError_t e = hipModuleLaunchKernel(fn, static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((M + 63) / 64),
+                                               static_cast<unsigned>(splits), 256, 1, 1, 0, s, args, nullptr);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("launch oeq_gemm: ") + hipGetErrorString(e));
+    if (splits == 1) return OEQ_OK;
+    int64_t blocks = std::min<int64_t>((stride + 255) / 256, 65536);
+    void *rargs[] = {&part, &splits, &stride, &M, &N, &C, &ldc};
+    return launch(p, "oeq_gemm_reduce", static_cast<unsigned>(blocks), 256, s, rargs);
+}
+
+// Workspace of the radial-weight passes: B [E,8], h [E,H], dh [E,H], dB [E,8], then the
+// split-K partials of the two products summed over edges.
+struct RadialWs {
+    size_t B = 0, h = 0, dh = 0, dB = 0, pW2 = 0, pW1 = 0, bytes = 0;
+    int splits = 1;
+};
+constexpr int kRadialNB = 8;
+
+RadialWs radial_layout(const oeq_plan *p, int64_t E, int H) {
+    RadialWs w;
+    const size_t es = esize(p), PU = p->paths.size() * static_cast<size_t>(p->U);
+    w.splits = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (E + 4095) / 4096)));
+    size_t off = 0;
+    w.B = off;
+    off += up(static_cast<size_t>(E) * kRadialNB * es);
+    w.h = off;
+    off += up(static_cast<size_t>(E) * H * es);
+    w.dh = off;
+    off += up(static_cast<size_t>(E) * H * es);
+    w.dB = off;
+    off += up(static_cast<size_t>(E) * kRadialNB * es);
+    w.pW2 = off;
+    off += up(static_cast<size_t>(w.splits) * H * PU * es);
+    w.pW1 = off;
+    off += up(static_cast<size_t>(w.splits) * kRadialNB * H * es);
+    w.bytes = off;
+    return w;
+}
+
+oeq_status radial_check(const oeq_plan *p, int64_t E, double r_cut, int H, const void *vec, const void *W1,
+                        const void *W2, void *workspace, size_t bytes, RadialWs *w) {
+    if (!p) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative edge count");
+    if (E >= std::numeric_limits<int32_t>::max()) return fail(OEQ_ERR_UNSUPPORTED, "edge count must fit int32");
+    if (H < 1 || H > 1024) return fail(OEQ_ERR_UNSUPPORTED, "hidden width must be 1..1024");
+    if (!(r_cut > 0.0)) return fail(OEQ_ERR_INVALID_ARG, "r_cut must be positive");
+    if (E > 0 && (!vec || !W1 || !W2)) return fail(OEQ_ERR_INVALID_ARG, "vec, W1 or W2 is NULL");
+    *w = radial_layout(p, E, H);
+    if (E > 0 && (!workspace || bytes < w->bytes)) return fail(OEQ_ERR_WORKSPACE, "workspace too small");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+        return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    return OEQ_OK;
+}
+
+// B and h of every edge into the workspace
+oeq_status radial_hidden(oeq_plan *p, int64_t E, const void *vec, double r_cut, int H, const void *W1, char *ws,
+                         const RadialWs &w, hipStream_t s) {
+    void *Bp = ws + w.B, *hp = ws + w.h;
+    float rcf = static_cast<float>(r_cut);
+    void *rc = p->dtype == OEQ_F64 ? static_cast<void *>(&r_cut) : static_cast<void *>(&rcf);
+    void *bargs[] = {&vec, rc, &Bp, &E};
+    oeq_status st = edge_launch(p, "oeq_radial_basis", E, bargs, s);
+    if (st != OEQ_OK) return st;
+    void *hargs[] = {&Bp, &W1, &H, &hp, &E};
+    return edge_launch(p, "oeq_radial_hidden", E * H, hargs, s);
 }
 
 }  // namespace
@@ -595,6 +685,74 @@ oeq_status oeq_tp_conv_bwd_vec(const oeq_plan *plan, int64_t N, int64_t E, const
                               workspace_bytes - 2 * rows, stream)) != OEQ_OK)
         return st;
     return gvec ? oeq_sph_harm_bwd(p, E, vec, gYw, gvec, stream) : OEQ_OK;
+}
+
+oeq_status oeq_radial_workspace_size(const oeq_plan *p, int64_t E, int32_t hidden, size_t *bytes) {
+    if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
+    if (E < 0 || hidden < 1 || hidden > 1024) return fail(OEQ_ERR_INVALID_ARG, "bad size");
+    *bytes = radial_layout(p, E, hidden).bytes;
+    return OEQ_OK;
+}
+
+oeq_status oeq_radial_fwd(const oeq_plan *plan, int64_t E, const void *vec, double r_cut, int32_t hidden,
+                          const void *W1, const void *W2, void *W, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    RadialWs w;
+    oeq_status st = radial_check(plan, E, r_cut, hidden, vec, W1, W2, workspace, workspace_bytes, &w);
+    if (st != OEQ_OK) return st;
+    if (E == 0) return OEQ_OK;
+    if (!W) return fail(OEQ_ERR_INVALID_ARG, "W is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    if ((st = radial_hidden(p, E, vec, r_cut, hidden, W1, ws, w, s)) != OEQ_OK) return st;
+    const int PU = static_cast<int>(p->paths.size()) * p->U;
+    return gemm(p, static_cast<int>(E), PU, hidden, ws + w.h, hidden, false, W2, PU, false, W, PU,
+                1.0 / std::sqrt(static_cast<double>(hidden)), 1, nullptr, s);
+}
+
+oeq_status oeq_radial_bwd(const oeq_plan *plan, int64_t E, const void *vec, double r_cut, int32_t hidden,
+                          const void *W1, const void *W2, const void *gW, void *gvec, void *gW1, void *gW2,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    RadialWs w;
+    oeq_status st = radial_check(plan, E, r_cut, hidden, vec, W1, W2, workspace, workspace_bytes, &w);
+    if (st != OEQ_OK) return st;
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int H = hidden, PU = static_cast<int>(p->paths.size()) * p->U;
+    if (E == 0) {  // sums over no edges
+        if (gW1 && (st = fill_zero(p, gW1, int64_t(kRadialNB) * H, s)) != OEQ_OK) return st;
+        return gW2 ? fill_zero(p, gW2, int64_t(H) * PU, s) : OEQ_OK;
+    }
+    if (!gW) return fail(OEQ_ERR_INVALID_ARG, "grad_W is NULL");
+    if (!gvec && !gW1 && !gW2) return OEQ_OK;
+    char *ws = static_cast<char *>(workspace);
+    const int Ei = static_cast<int>(E);
+    const double sh = 1.0 / std::sqrt(static_cast<double>(H)), s8 = 1.0 / std::sqrt(double(kRadialNB));
+    if ((st = radial_hidden(p, E, vec, r_cut, H, W1, ws, w, s)) != OEQ_OK) return st;
+    // gW2 = h^T gW / sqrt(H): a sum over edges
+    if (gW2 && (st = gemm(p, H, PU, Ei, ws + w.h, H, true, gW, PU, false, gW2, PU, sh, w.splits, ws + w.pW2, s)) !=
+                   OEQ_OK)
+        return st;
+    if (!gvec && !gW1) return OEQ_OK;
+    // dh = gW W2^T / sqrt(H), then dpre = dh silu'(pre) in place
+    void *dh = ws + w.dh, *Bp = ws + w.B;
+    if ((st = gemm(p, Ei, H, PU, gW, PU, false, W2, PU, true, dh, H, sh, 1, nullptr, s)) != OEQ_OK) return st;
+    void *dargs[] = {&Bp, &W1, const_cast<int *>(&H), &dh, &E};
+    if ((st = edge_launch(p, "oeq_radial_dpre", E * H, dargs, s)) != OEQ_OK) return st;
+    // gW1 = B^T dpre / sqrt(8): a sum over edges
+    if (gW1 && (st = gemm(p, kRadialNB, H, Ei, Bp, kRadialNB, true, dh, H, false, gW1, H, s8, w.splits,
+                          ws + w.pW1, s)) != OEQ_OK)
+        return st;
+    if (!gvec) return OEQ_OK;
+    // dB = dpre W1^T / sqrt(8), then the chain through r = |vec|
+    void *dB = ws + w.dB;
+    if ((st = gemm(p, Ei, kRadialNB, H, dh, H, false, W1, H, true, dB, kRadialNB, s8, 1, nullptr, s)) != OEQ_OK)
+        return st;
+    float rcf = static_cast<float>(r_cut);
+    void *rc = p->dtype == OEQ_F64 ? static_cast<void *>(&r_cut) : static_cast<void *>(&rcf);
+    void *gargs[] = {&vec, rc, &dB, &gvec, &E};
+    return edge_launch(p, "oeq_radial_gvec", E, gargs, s);
 }
 
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr, const int32_t *src, void *stream) {

@@ -726,6 +726,226 @@ oeq_bwd_sender(const int *__restrict__ srowptr, const int *__restrict__ sperm, c
 }
 
 // ---------------------------------------------------------------------------
+// Dense matrix products on the matrix cores (the radial-weight MLP).
+//   C[M,N] = alpha op(A)[M,K] op(B)[K,N]   (row-major; op = identity or transpose)
+// A workgroup of 4 waves owns a 64x64 tile of C; each wave a 32x32 quarter as
+// 2x2 blocks of the 16x16x4 MFMA (v_mfma_f32_16x16x4f32 / v_mfma_f64_16x16x4f64).
+// K advances 16 at a time through LDS.  blockIdx.z splits K: split s covers
+// [s*kchunk, (s+1)*kchunk) and writes its tile to C + s*split_stride; with more
+// than one split, oeq_gemm_reduce adds the partial tiles in split order.
+// Operand lanes: A[l%16][l/16], B[l/16][l%16]; result value v of lane l is row
+// 4(l/16)+v (fp32) or l/16+4v (fp64), column l%16.
+// ---------------------------------------------------------------------------
+typedef float mfma_f4 __attribute__((ext_vector_type(4)));
+typedef double mfma_d4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ mfma_f4 mfma16(float a, float b, mfma_f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ mfma_d4 mfma16(double a, double b, mfma_d4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+typedef real_t mfma_acc __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ int mfma_row(int l, int v) {
+    return sizeof(real_t) == 4 ? 4 * (l >> 4) + v : (l >> 4) + 4 * v;
+}
+
+constexpr int GT = 64, GK = 32;
+constexpr int GLOADS = GT * GK / 256;  // elements of each operand tile per thread
+
+// element q of this thread's share of the A (or B) tile of the K chunk at k0, zero outside
+__device__ __forceinline__ void gemm_tile_coords(int idx, bool t_major, int &rc, int &k) {
+    // consecutive threads walk the contiguous dimension of the stored operand
+    if (t_major) { k = idx / GT; rc = idx % GT; } else { rc = idx / GK; k = idx % GK; }
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_gemm(int M, int N, int K, const real_t *__restrict__ A, i64 lda, int ta, const real_t *__restrict__ B, i64 ldb,
+         int tb, real_t *__restrict__ C, i64 ldc, i64 split_stride, int kchunk, real_t alpha) {
+    __shared__ real_t As[GT][GK + 1];
+    __shared__ real_t Bs[GK][GT + 1];
+    const int t = threadIdx.x, l = t & 63, w = t >> 6;
+    const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+    const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
+    C += (i64)blockIdx.z * split_stride;
+    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
+    mfma_acc acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_acc{0, 0, 0, 0};
+    // register stage: the next chunk's loads are in flight while this chunk computes
+    real_t ra[GLOADS], rb[GLOADS];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int q = 0; q < GLOADS; ++q) {
+            int m, k, n, kk;
+            gemm_tile_coords(t + q * 256, ta != 0, m, k);
+            gemm_tile_coords(t + q * 256, tb == 0, n, kk);
+            const int gm = m0 + m, gk = k0 + k, gn = n0 + n, gk2 = k0 + kk;
+            ra[q] = (gm < M && gk < ke) ? (ta ? A[(i64)gk * lda + gm] : A[(i64)gm * lda + gk]) : real_t(0);
+            rb[q] = (gn < N && gk2 < ke) ? (tb ? B[(i64)gn * ldb + gk2] : B[(i64)gk2 * ldb + gn]) : real_t(0);
+        }
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int q = 0; q < GLOADS; ++q) {
+            int m, k, n, kk;
+            gemm_tile_coords(t + q * 256, ta != 0, m, k);
+            gemm_tile_coords(t + q * 256, tb == 0, n, kk);
+            As[m][k] = ra[q];
+            Bs[kk][n] = rb[q];
+        }
+    };
+    if (kb < ke) fetch(kb);
+    for (int k0 = kb; k0 < ke; k0 += GK) {
+        stash();
+        __syncthreads();
+        if (k0 + GK < ke) fetch(k0 + GK);
+#pragma unroll
+        for (int kk = 0; kk < GK; kk += 4) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const real_t a = As[wr + 16 * i + (l & 15)][kk + (l >> 4)];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const real_t b = Bs[kk + (l >> 4)][wc + 16 * j + (l & 15)];
+                    acc[i][j] = mfma16(a, b, acc[i][j]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int gm = m0 + wr + 16 * i + mfma_row(l, v), gn = n0 + wc + 16 * j + (l & 15);
+                if (gm < M && gn < N) C[(i64)gm * ldc + gn] = alpha * acc[i][j][v];
+            }
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_gemm_reduce(const real_t *__restrict__ part, int splits, i64 split_stride, int M, int N,
+                real_t *__restrict__ C, i64 ldc) {
+    const i64 n = (i64)M * N;
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x) {
+        const i64 m = i / N, c = i - m * N;
+        real_t s = part[m * N + c];
+        for (int q = 1; q < splits; ++q) s += part[(i64)q * split_stride + m * N + c];
+        C[m * ldc + c] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Radial weights from edge lengths (a stated reading; the pages realise them
+// outside the kernels): r = |vec|, d = r / r_cut,
+//   u(d) = 1 - 28 d^6 + 48 d^7 - 21 d^8 (d < 1, else 0)    polynomial cutoff, p = 6
+//   B_n(r) = sqrt(2 / r_cut) sin(n pi r / r_cut) / r u(d),  n = 1..8
+//   h = silu(B W1 / sqrt(8)),  W = h W2 / sqrt(H)   (the two products on the matrix cores)
+// ---------------------------------------------------------------------------
+constexpr int RNB = 8;
+__device__ __forceinline__ float sin_r(float v) { return sinf(v); }
+__device__ __forceinline__ double sin_r(double v) { return sin(v); }
+__device__ __forceinline__ float cos_r(float v) { return cosf(v); }
+__device__ __forceinline__ double cos_r(double v) { return cos(v); }
+__device__ __forceinline__ float exp_r(float v) { return expf(v); }
+__device__ __forceinline__ double exp_r(double v) { return exp(v); }
+
+// B_n(r) and, when D, dB_n/dr
+template <bool D>
+__device__ __forceinline__ void radial_basis(real_t r, real_t rc, real_t (&Bv)[RNB], real_t (&dBv)[RNB]) {
+    const real_t pi = real_t(3.141592653589793);
+    const real_t c = sqrt_r(real_t(2) / rc);
+    const real_t d = r / rc;
+    real_t u = real_t(0), du = real_t(0);
+    if (d < real_t(1)) {
+        const real_t d2 = d * d, d3 = d2 * d, d6 = d3 * d3;
+        u = real_t(1) - real_t(28) * d6 + real_t(48) * d6 * d - real_t(21) * d6 * d2;
+        const real_t om = real_t(1) - d;
+        du = real_t(-168) * d2 * d3 * om * om;  // -p(p+1)(p+2)/2 d^(p-1) (1-d)^2
+    }
+#pragma unroll
+    for (int n = 0; n < RNB; ++n) {
+        const real_t k = real_t(n + 1) * pi / rc;
+        if (r > real_t(0)) {
+            const real_t sn = sin_r(k * r), inv = real_t(1) / r;
+            Bv[n] = c * sn * inv * u;
+            if constexpr (D) {
+                const real_t ds = (k * cos_r(k * r) - sn * inv) * inv;
+                dBv[n] = c * (ds * u + sn * inv * du / rc);
+            }
+        } else {
+            Bv[n] = c * k * u;  // the limit sin(kr)/r -> k
+            if constexpr (D) dBv[n] = real_t(0);
+        }
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_radial_basis(const real_t *__restrict__ vec, real_t rc, real_t *__restrict__ Bout, i64 n_edges) {
+    for (i64 e = (i64)blockIdx.x * blockDim.x + threadIdx.x; e < n_edges; e += (i64)gridDim.x * blockDim.x) {
+        const real_t x = vec[e * 3], y = vec[e * 3 + 1], z = vec[e * 3 + 2];
+        real_t Bv[RNB], unused[RNB];
+        radial_basis<false>(sqrt_r(x * x + y * y + z * z), rc, Bv, unused);
+#pragma unroll
+        for (int n = 0; n < RNB; ++n) Bout[e * RNB + n] = Bv[n];
+    }
+}
+
+// pre = B W1 / sqrt(8) for element (e, j); DPRE: dh[e,j] *= silu'(pre), else h[e,j] = silu(pre)
+template <bool DPRE>
+__device__ __forceinline__ void radial_hidden_body(const real_t *__restrict__ Bm, const real_t *__restrict__ W1,
+                                                   int H, real_t *__restrict__ io, i64 n_edges) {
+    const i64 n = n_edges * H;
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x) {
+        const i64 e = i / H;
+        const int j = (int)(i - e * H);
+        real_t pre = real_t(0);
+#pragma unroll
+        for (int q = 0; q < RNB; ++q) pre = fmar(Bm[e * RNB + q], W1[q * H + j], pre);
+        pre *= real_t(0.35355339059327373);  // 1/sqrt(8)
+        const real_t sg = real_t(1) / (real_t(1) + exp_r(-pre));
+        if constexpr (DPRE)
+            io[i] *= sg * (real_t(1) + pre * (real_t(1) - sg));
+        else
+            io[i] = pre * sg;
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_radial_hidden(const real_t *__restrict__ Bm, const real_t *__restrict__ W1, int H, real_t *__restrict__ h,
+                  i64 n_edges) {
+    radial_hidden_body<false>(Bm, W1, H, h, n_edges);
+}
+
+extern "C" __global__ void __launch_bounds__(256)
+oeq_radial_dpre(const real_t *__restrict__ Bm, const real_t *__restrict__ W1, int H, real_t *__restrict__ dh,
+                i64 n_edges) {
+    radial_hidden_body<true>(Bm, W1, H, dh, n_edges);
+}
+
+// grad_vec[e] = (sum_n dB[e,n] dB_n/dr) vec / r
+extern "C" __global__ void __launch_bounds__(256)
+oeq_radial_gvec(const real_t *__restrict__ vec, real_t rc, const real_t *__restrict__ dB, real_t *__restrict__ gvec,
+                i64 n_edges) {
+    for (i64 e = (i64)blockIdx.x * blockDim.x + threadIdx.x; e < n_edges; e += (i64)gridDim.x * blockDim.x) {
+        const real_t x = vec[e * 3], y = vec[e * 3 + 1], z = vec[e * 3 + 2];
+        const real_t r = sqrt_r(x * x + y * y + z * z);
+        real_t Bv[RNB], dBv[RNB];
+        radial_basis<true>(r, rc, Bv, dBv);
+        real_t dr = real_t(0);
+#pragma unroll
+        for (int n = 0; n < RNB; ++n) dr = fmar(dB[e * RNB + n], dBv[n], dr);
+        const real_t s = r > real_t(0) ? dr / r : real_t(0);
+        gvec[e * 3] = s * x;
+        gvec[e * 3 + 1] = s * y;
+        gvec[e * 3 + 2] = s * z;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Double backward.  TM: which tangents are present (1 gg_x, 2 gg_Y, 4 gg_W).
 //   d_grad_out = f(ggx,Y,W) + f(x,ggY,W) + f(x,Y,ggW)      (receiver-local)
 //   d_W = BW(ggx,Y,g) + BW(x,ggY,g),  d_Y = BY(ggx,W,g) + BY(x,ggW,g)

@@ -276,6 +276,33 @@ oeq_status oeq_tp_conv_bwd_vec(const oeq_plan *plan, int64_t n_nodes, int64_t n_
                                void *grad_x, void *grad_vec, void *grad_W, oeq_bwd_mode mode,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- Radial weights from edge lengths ---------------------------------------
+ * The pages realise W outside the convolution, and fusing its realisation would be
+ * a new operation ("Receiver-streaming convolutions ...", maintainer replies).  They
+ * give no specification; these entry points compute this stated one (the shape
+ * used by MACE-style potentials):
+ *   r = |vec[e]|, d = r / r_cut
+ *   u(d)   = 1 - 28 d^6 + 48 d^7 - 21 d^8 for d < 1, else 0       (polynomial cutoff, p = 6)
+ *   B_n(r) = sqrt(2 / r_cut) sin(n pi r / r_cut) / r * u(d), n = 1..8  (limit n pi / r_cut at r = 0)
+ *   h      = silu(B W1 / sqrt(8))                                 W1 [8, hidden]
+ *   W[e]   = h W2 / sqrt(hidden), viewed as [P, U]                W2 [hidden, P*U]
+ * The two dense products (and the three of the backward) run on the matrix
+ * cores.  vec [E, 3], W1, W2 and W in the plan's dtype; hidden in 1..1024.
+ * `workspace` (256-byte aligned) of oeq_radial_workspace_size bytes. */
+oeq_status oeq_radial_workspace_size(const oeq_plan *plan, int64_t n_edges, int32_t hidden,
+                                     size_t *bytes);
+oeq_status oeq_radial_fwd(const oeq_plan *plan, int64_t n_edges, const void *vec, double r_cut,
+                          int32_t hidden, const void *W1, const void *W2, void *W,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/* Gradients of <grad_W, W(vec, W1, W2)> with respect to vec ([E, 3]), W1 and W2
+ * (sums over the edges, added in a fixed order: bitwise repeatable).  Any of
+ * grad_vec, grad_W1, grad_W2 may be NULL. */
+oeq_status oeq_radial_bwd(const oeq_plan *plan, int64_t n_edges, const void *vec, double r_cut,
+                          int32_t hidden, const void *W1, const void *W2, const void *grad_W,
+                          void *grad_vec, void *grad_W1, void *grad_W2, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
 /* Synchronously validates a receiver CSR on the device (rowptr monotone,
  * rowptr[0] = 0, rowptr[N] = E, 0 <= src < N).  Test helper: synchronises. */
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr,

@@ -208,3 +208,24 @@ def test_sender_entry_argument_errors_before_any_device_work():
     assert v(4, 4, P(16), P(16), P(16), P(16), P(16), None, 0, None) == 3                  # workspace
     assert v(4, 4, P(16), P(16), P(16), P(16), P(16), P(256 + 8), 1 << 20, None) == 3     # misaligned
     assert v(0, 4, P(16), P(16), P(16), P(16), P(16), P(256), 1 << 20, None) == 1         # edges without nodes
+
+
+def test_radial_argument_errors_before_any_device_work():
+    p = oeq.Plan("8x0e+8x1o", 2, 1, "f64")
+    lib = oeq.lib()
+    P = ctypes.c_void_p
+    b = ctypes.c_size_t()
+    assert lib.oeq_radial_workspace_size(p.handle, 100, 16, ctypes.byref(b)) == 0 and b.value > 0
+    assert lib.oeq_radial_workspace_size(p.handle, 100, 0, ctypes.byref(b)) == 1
+    f = lib.oeq_radial_fwd
+    ws, nb = P(4096 * 256), b.value
+    assert f(None, 100, P(16), 6.0, 16, P(16), P(16), P(16), ws, nb, None) == 1
+    assert f(p.handle, 100, P(16), 0.0, 16, P(16), P(16), P(16), ws, nb, None) == 1        # r_cut
+    assert f(p.handle, 100, P(16), 6.0, 2000, P(16), P(16), P(16), ws, nb, None) == 2      # hidden width
+    assert f(p.handle, 100, None, 6.0, 16, P(16), P(16), P(16), ws, nb, None) == 1         # vec
+    assert f(p.handle, 100, P(16), 6.0, 16, P(16), P(16), P(16), None, 0, None) == 3       # workspace
+    assert f(p.handle, 100, P(16), 6.0, 16, P(16), P(16), P(16), P(4096 * 256 + 8), nb, None) == 3
+    g = lib.oeq_radial_bwd
+    assert g(p.handle, 100, P(16), 6.0, 16, P(16), P(16), None, P(16), None, None, ws, nb, None) == 1  # grad_W
+    # nothing requested: returns without work
+    assert g(p.handle, 100, P(16), 6.0, 16, P(16), P(16), P(16), None, None, None, ws, nb, None) == 0
