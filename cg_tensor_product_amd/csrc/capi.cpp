@@ -173,13 +173,20 @@ oeq_status gemm(oeq_plan *p, int M, int N, int K, const void *A, int64_t lda, bo
     float af = static_cast<float>(alpha);
     void *ap = p->dtype == OEQ_F64 ? static_cast<void *>(&alpha) : static_cast<void *>(&af);
     void *args[] = {&M, &N, &K, &A, &lda, &ta_i, &B, &ldb, &tb_i, &dst, &ldd, &stride, &kchunk, ap};
+    // 128-wide tile sides where the matrix fills them; fp64 keeps 64 x 64 (its 128-wide tiles
+    // hold one wave per SIMD and ran slower, as did 128 rows over a 64-row matrix)
+    const bool wide = p->dtype == OEQ_F32;
+    const int bm = wide && M >= 128 ? 128 : 64, bn = wide && N >= 128 ? 128 : 64;
+    const std::string kname = "oeq_gemm_" + std::to_string(bm) + "x" + std::to_string(bn);
+    const char *name = kname.c_str();
     hipFunction_t fn = nullptr;
     std::string why;
-    oeq_status st = oeq::get_kernel(*p, "oeq_gemm", &fn, &why);
+    oeq_status st = oeq::get_kernel(*p, name, &fn, &why);
     if (st != OEQ_OK) return fail(st, why);
-    const hipError_t e = hipModuleLaunchKernel(fn, static_cast<unsigned>((N + 63) / 64), static_cast<unsigned>((M + 63) / 64),
-                                               static_cast<unsigned>(splits), 256, 1, 1, 0, s, args, nullptr);
-    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("launch oeq_gemm: ") + hipGetErrorString(e));
+    const hipError_t e = hipModuleLaunchKernel(fn, static_cast<unsigned>((N + bn - 1) / bn),
+                                               static_cast<unsigned>((M + bm - 1) / bm), static_cast<unsigned>(splits),
+                                               256, 1, 1, 0, s, args, nullptr);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("launch ") + name + ": " + hipGetErrorString(e));
     if (splits == 1) return OEQ_OK;
     int64_t blocks = std::min<int64_t>((stride + 255) / 256, 65536);
     void *rargs[] = {&part, &splits, &stride, &M, &N, &C, &ldc};

@@ -728,9 +728,9 @@ oeq_bwd_sender(const int *__restrict__ srowptr, const int *__restrict__ sperm, c
 // ---------------------------------------------------------------------------
 // Dense matrix products on the matrix cores (the radial-weight MLP).
 //   C[M,N] = alpha op(A)[M,K] op(B)[K,N]   (row-major; op = identity or transpose)
-// A workgroup of 4 waves owns a 64x64 tile of C; each wave a 32x32 quarter as
-// 2x2 blocks of the 16x16x4 MFMA (v_mfma_f32_16x16x4f32 / v_mfma_f64_16x16x4f64).
-// K advances 16 at a time through LDS.  blockIdx.z splits K: split s covers
+// A workgroup of 4 waves owns a BM x BN tile of C (oeq_gemm_<BM>x<BN>, 64 or 128 each);
+// each wave a quarter, as blocks of the 16x16x4 MFMA (v_mfma_f32_16x16x4f32 /
+// v_mfma_f64_16x16x4f64).  K advances 32 at a time through LDS.  blockIdx.z splits K: split s covers
 // [s*kchunk, (s+1)*kchunk) and writes its tile to C + s*split_stride; with more
 // than one split, oeq_gemm_reduce adds the partial tiles in split order.
 // Operand lanes: A[l%16][l/16], B[l/16][l%16]; result value v of lane l is row
@@ -749,51 +749,66 @@ __device__ __forceinline__ int mfma_row(int l, int v) {
     return sizeof(real_t) == 4 ? 4 * (l >> 4) + v : (l >> 4) + 4 * v;
 }
 
-constexpr int GT = 64, GK = 32;
-constexpr int GLOADS = GT * GK / 256;  // elements of each operand tile per thread
+constexpr int GK = 32;
 
-// element q of this thread's share of the A (or B) tile of the K chunk at k0, zero outside
-__device__ __forceinline__ void gemm_tile_coords(int idx, bool t_major, int &rc, int &k) {
-    // consecutive threads walk the contiguous dimension of the stored operand
-    if (t_major) { k = idx / GT; rc = idx % GT; } else { rc = idx / GK; k = idx % GK; }
-}
-
-extern "C" __global__ void __launch_bounds__(256)
-oeq_gemm(int M, int N, int K, const real_t *__restrict__ A, i64 lda, int ta, const real_t *__restrict__ B, i64 ldb,
-         int tb, real_t *__restrict__ C, i64 ldc, i64 split_stride, int kchunk, real_t alpha) {
-    __shared__ real_t As[GT][GK + 1];
-    __shared__ real_t Bs[GK][GT + 1];
+// Workgroup tile GBM x BN (64 or 128 each): 4 waves as 2 x 2, each (GBM/2) x (BN/2) in
+// 16x16 blocks, K staged GK at a time through LDS with the next chunk's loads in registers.
+template <int GBM, int BN>
+__device__ __forceinline__ void gemm_body(int M, int N, int K, const real_t *__restrict__ A, i64 lda, int ta,
+                                          const real_t *__restrict__ B, i64 ldb, int tb, real_t *__restrict__ C,
+                                          i64 ldc, i64 split_stride, int kchunk, real_t alpha) {
+    constexpr int BI = GBM / 32, BJ = BN / 32;           // 16x16 blocks per wave
+    constexpr int LA = GBM * GK / 256, LB = BN * GK / 256;  // elements per thread per chunk
+    __shared__ real_t As[GBM][GK + 1];
+    __shared__ real_t Bs[GK][BN + 1];
     const int t = threadIdx.x, l = t & 63, w = t >> 6;
-    const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+    const int m0 = blockIdx.y * GBM, n0 = blockIdx.x * BN;
     const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
     C += (i64)blockIdx.z * split_stride;
-    const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-    mfma_acc acc[2][2];
+    const int wr = (w >> 1) * (GBM / 2), wc = (w & 1) * (BN / 2);
+    mfma_acc acc[BI][BJ];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma_acc{0, 0, 0, 0};
-    // register stage: the next chunk's loads are in flight while this chunk computes
-    real_t ra[GLOADS], rb[GLOADS];
+        for (int j = 0; j < BJ; ++j) acc[i][j] = mfma_acc{0, 0, 0, 0};
+    real_t ra[LA], rb[LB];
+    // consecutive threads walk the contiguous dimension of each stored operand
+    auto a_at = [&](int q, int &m, int &k) {
+        const int idx = t + q * 256;
+        if (ta) { k = idx / GBM; m = idx % GBM; } else { m = idx / GK; k = idx % GK; }
+    };
+    auto b_at = [&](int q, int &n, int &k) {
+        const int idx = t + q * 256;
+        if (tb) { n = idx / GK; k = idx % GK; } else { k = idx / BN; n = idx % BN; }
+    };
     auto fetch = [&](int k0) {
 #pragma unroll
-        for (int q = 0; q < GLOADS; ++q) {
-            int m, k, n, kk;
-            gemm_tile_coords(t + q * 256, ta != 0, m, k);
-            gemm_tile_coords(t + q * 256, tb == 0, n, kk);
-            const int gm = m0 + m, gk = k0 + k, gn = n0 + n, gk2 = k0 + kk;
+        for (int q = 0; q < LA; ++q) {
+            int m, k;
+            a_at(q, m, k);
+            const int gm = m0 + m, gk = k0 + k;
             ra[q] = (gm < M && gk < ke) ? (ta ? A[(i64)gk * lda + gm] : A[(i64)gm * lda + gk]) : real_t(0);
-            rb[q] = (gn < N && gk2 < ke) ? (tb ? B[(i64)gn * ldb + gk2] : B[(i64)gk2 * ldb + gn]) : real_t(0);
+        }
+#pragma unroll
+        for (int q = 0; q < LB; ++q) {
+            int n, k;
+            b_at(q, n, k);
+            const int gn = n0 + n, gk = k0 + k;
+            rb[q] = (gn < N && gk < ke) ? (tb ? B[(i64)gn * ldb + gk] : B[(i64)gk * ldb + gn]) : real_t(0);
         }
     };
     auto stash = [&]() {
 #pragma unroll
-        for (int q = 0; q < GLOADS; ++q) {
-            int m, k, n, kk;
-            gemm_tile_coords(t + q * 256, ta != 0, m, k);
-            gemm_tile_coords(t + q * 256, tb == 0, n, kk);
+        for (int q = 0; q < LA; ++q) {
+            int m, k;
+            a_at(q, m, k);
             As[m][k] = ra[q];
-            Bs[kk][n] = rb[q];
+        }
+#pragma unroll
+        for (int q = 0; q < LB; ++q) {
+            int n, k;
+            b_at(q, n, k);
+            Bs[k][n] = rb[q];
         }
     };
     if (kb < ke) fetch(kb);
@@ -803,28 +818,39 @@ oeq_gemm(int M, int N, int K, const real_t *__restrict__ A, i64 lda, int ta, con
         if (k0 + GK < ke) fetch(k0 + GK);
 #pragma unroll
         for (int kk = 0; kk < GK; kk += 4) {
+            real_t a[BI], b[BJ];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const real_t a = As[wr + 16 * i + (l & 15)][kk + (l >> 4)];
+            for (int i = 0; i < BI; ++i) a[i] = As[wr + 16 * i + (l & 15)][kk + (l >> 4)];
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const real_t b = Bs[kk + (l >> 4)][wc + 16 * j + (l & 15)];
-                    acc[i][j] = mfma16(a, b, acc[i][j]);
-                }
-            }
+            for (int j = 0; j < BJ; ++j) b[j] = Bs[kk + (l >> 4)][wc + 16 * j + (l & 15)];
+#pragma unroll
+            for (int i = 0; i < BI; ++i)
+#pragma unroll
+                for (int j = 0; j < BJ; ++j) acc[i][j] = mfma16(a[i], b[j], acc[i][j]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < BI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < BJ; ++j)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int gm = m0 + wr + 16 * i + mfma_row(l, v), gn = n0 + wc + 16 * j + (l & 15);
                 if (gm < M && gn < N) C[(i64)gm * ldc + gn] = alpha * acc[i][j][v];
             }
 }
+
+#define OEQ_GEMM_KERNEL(BM, BN)                                                                            \
+    extern "C" __global__ void __launch_bounds__(256) oeq_gemm_##BM##x##BN(                                \
+        int M, int N, int K, const real_t *__restrict__ A, i64 lda, int ta, const real_t *__restrict__ B,  \
+        i64 ldb, int tb, real_t *__restrict__ C, i64 ldc, i64 split_stride, int kchunk, real_t alpha) {    \
+        gemm_body<BM, BN>(M, N, K, A, lda, ta, B, ldb, tb, C, ldc, split_stride, kchunk, alpha);           \
+    }
+OEQ_GEMM_KERNEL(64, 64)
+OEQ_GEMM_KERNEL(64, 128)
+OEQ_GEMM_KERNEL(128, 64)
+OEQ_GEMM_KERNEL(128, 128)
 
 extern "C" __global__ void __launch_bounds__(256)
 oeq_gemm_reduce(const real_t *__restrict__ part, int splits, i64 split_stride, int M, int N,
