@@ -35,7 +35,7 @@ EXPORTED = ["oeq_plan_create", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_pa
             "oeq_last_error", "oeq_plan_schedule", "oeq_sender_view", "oeq_tp_conv_fwd_sender",
             "oeq_tp_conv_bwd_sender", "oeq_sph_harm", "oeq_sph_harm_bwd", "oeq_tp_conv_fwd_vec",
             "oeq_workspace_size_vec", "oeq_tp_conv_bwd_vec", "oeq_radial_workspace_size", "oeq_radial_fwd",
-            "oeq_radial_bwd"]
+            "oeq_radial_bwd", "oeq_tp_conv_fwd_radial"]
 SCHEDULES = {0: "receiver", 1: "sender"}
 
 
@@ -126,6 +126,8 @@ def lib():
     L.oeq_radial_fwd.restype = st
     L.oeq_radial_bwd.argtypes = [P, I64, P, D, I32, P, P, P, P, P, P, P, SZ, P]
     L.oeq_radial_bwd.restype = st
+    L.oeq_tp_conv_fwd_radial.argtypes = [P, I64, I64, P, P, P, P, P, D, P, P, P, P, SZ, P]
+    L.oeq_tp_conv_fwd_radial.restype = st
     L.oeq_status_string.argtypes = [ctypes.c_int]
     L.oeq_status_string.restype = ctypes.c_char_p
     L.oeq_last_error.argtypes = []
@@ -549,3 +551,22 @@ def oeq_radial_bwd(plan: Plan, vec, r_cut: float, W1, W2, grad_W, want=("vec", "
     _check(lib().oeq_radial_bwd(plan.handle, E, _ptr(vec), float(r_cut), H, _ptr(W1), _ptr(W2), _ptr(grad_W),
                                 _ptr(gv), _ptr(g1), _ptr(g2), _ptr(ws), ws.numel(), _stream()))
     return gv, g1, g2
+
+
+def oeq_tp_conv_fwd_radial(plan: Plan, rowptr, src, x, Y, vec, r_cut: float, W1, W2, out=None, workspace=None):
+    """Forward with W formed in the kernel from a hidden width of 8 (W1 [8, 8], W2 [8, P*U])."""
+    N, E = _graph(rowptr, src)
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(Y, (E, plan.y_dim), dt, "Y")
+    _want(vec, (E, 3), dt, "vec")
+    _want(W1, (8, 8), dt, "W1")
+    _want(W2, (8, plan.n_paths * plan.U), dt, "W2")
+    if out is None:
+        out = _empty((N, plan.out_dim), dt, x.device)
+    _want(out, (N, plan.out_dim), dt, "out")
+    ws = workspace if workspace is not None else _radial_ws(plan, E, 8, x.device)
+    _check(lib().oeq_tp_conv_fwd_radial(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(vec),
+                                        float(r_cut), _ptr(W1), _ptr(W2), _ptr(out), _ptr(ws), ws.numel(),
+                                        _stream()))
+    return out

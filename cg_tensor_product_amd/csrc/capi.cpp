@@ -200,6 +200,7 @@ struct RadialWs {
     int splits = 1;
 };
 constexpr int kRadialNB = 8;
+constexpr int kFusedHidden = 8;  // hidden width of the forward that forms W in the kernel
 
 RadialWs radial_layout(const oeq_plan *p, int64_t E, int H) {
     RadialWs w;
@@ -760,6 +761,26 @@ oeq_status oeq_radial_bwd(const oeq_plan *plan, int64_t E, const void *vec, doub
     void *rc = p->dtype == OEQ_F64 ? static_cast<void *>(&r_cut) : static_cast<void *>(&rcf);
     void *gargs[] = {&vec, rc, &dB, &gvec, &E};
     return edge_launch(p, "oeq_radial_gvec", E, gargs, s);
+}
+
+oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr,
+                                  const int32_t *src, const void *x, const void *Y, const void *vec, double r_cut,
+                                  const void *W1, const void *W2, void *out, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
+    if (E > 0 && (!x || !Y)) return fail(OEQ_ERR_INVALID_ARG, "x or Y is NULL");
+    RadialWs w;
+    if ((st = radial_check(plan, E, r_cut, kFusedHidden, vec, W1, W2, workspace, workspace_bytes, &w)) != OEQ_OK)
+        return st;
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    if (E > 0 && (st = radial_hidden(p, E, vec, r_cut, kFusedHidden, W1, ws, w, s)) != OEQ_OK) return st;
+    void *hid = ws + w.h;
+    void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &out};
+    return launch(p, "oeq_fwd_radial", static_cast<unsigned>(N), fwd_block(p), s, args);
 }
 
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr, const int32_t *src, void *stream) {

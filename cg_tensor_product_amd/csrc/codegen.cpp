@@ -157,6 +157,10 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
     o << "  static __device__ __forceinline__ void load_w(const real_t *__restrict__ we, int u, real_t (&v)[NW]) {";
     for (int k : L.paths) o << " v[" << L.widx.at(k) << "] = LDW(we + " << S(static_cast<long long>(k) * p.U) << " + u);";
     o << " }\n";
+    // a row [P, U] that every workgroup reads (the radial network's output matrix): cached loads
+    o << "  static __device__ __forceinline__ void load_wrow(const real_t *__restrict__ row, int u, real_t (&v)[NW]) {";
+    for (int k : L.paths) o << " v[" << L.widx.at(k) << "] = row[" << S(static_cast<long long>(k) * p.U) << " + u];";
+    o << " }\n";
     o << "  static __device__ __forceinline__ void store_w(real_t *__restrict__ ge, int u, const real_t (&v)[NW]) {";
     for (int k : L.paths) o << " STW(ge + " << S(static_cast<long long>(k) * p.U) << " + u, v[" << L.widx.at(k) << "]);";
     o << " }\n";

@@ -615,6 +615,90 @@ oeq_fwd_sender(const int *__restrict__ srowptr, const int *__restrict__ sperm, c
     fwd_sender_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), srowptr, sperm, sdst, x, Y, W, out);
 }
 
+// ---------------------------------------------------------------------------
+// Forward with the radial weights computed in the kernel (no W tensor): with a
+// hidden layer of RH = 8 units, W[e, p, u] = sum_j h[e, j] W2[j, p, u] / sqrt(8).
+// Each lane keeps its 8 x NW slice of W2 in registers (loaded once); per edge
+// it reads the 8 hidden values (wave-uniform) and forms its W values, in place
+// of streaming them.  h [E, 8] comes from oeq_radial_basis + oeq_radial_hidden.
+// ---------------------------------------------------------------------------
+constexpr int RH = 8;
+
+template <int G>
+__device__ __forceinline__ void fwd_radial_group(int r, int u, const int *__restrict__ rowptr,
+                                                 const int *__restrict__ src, const real_t *__restrict__ x,
+                                                 const real_t *__restrict__ Y, const real_t *__restrict__ hid,
+                                                 const real_t *__restrict__ W2, real_t *__restrict__ out) {
+    using Gr = FG<G>;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;
+    real_t w2[RH][Gr::NW];
+#pragma unroll
+    for (int j = 0; j < RH; ++j) {
+        Gr::load_wrow(W2 + (i64)j * (P * U), uu, w2[j]);
+#pragma unroll
+        for (int k = 0; k < Gr::NW; ++k) w2[j][k] *= real_t(0.35355339059327373);  // 1/sqrt(8)
+    }
+    real_t sum[Gr::NO];
+    zero(sum);
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    if (e0 < e1) {
+        int s = uni(src[e0]);
+        real_t yv[YD], xv[Gr::NX], hv[RH];
+        load_y(Y, e0, yv);
+        Gr::load_x(x + (i64)s * XD, uu, xv);
+#pragma unroll
+        for (int j = 0; j < RH; ++j) hv[j] = hid[(i64)e0 * RH + j];
+        for (int e = e0; e < e1; ++e) {
+            real_t yn[YD], xn[Gr::NX], hn[RH];
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            load_y(Y, en, yn);
+            Gr::load_x(x + (i64)sn * XD, uu, xn);
+#pragma unroll
+            for (int j = 0; j < RH; ++j) hn[j] = hid[(i64)en * RH + j];
+            PIN_FWD();
+            real_t wv[Gr::NW];
+#pragma unroll
+            for (int k = 0; k < Gr::NW; ++k) {
+                real_t t = hv[0] * w2[0][k];
+#pragma unroll
+                for (int j = 1; j < RH; ++j) t = fmar(hv[j], w2[j][k], t);
+                wv[k] = t;
+            }
+            Gr::edge(xv, yv, wv, sum);
+#pragma unroll
+            for (int q = 0; q < YD; ++q) yv[q] = yn[q];
+#pragma unroll
+            for (int q = 0; q < Gr::NX; ++q) xv[q] = xn[q];
+#pragma unroll
+            for (int q = 0; q < RH; ++q) hv[q] = hn[q];
+        }
+    }
+    if (act) Gr::store_out(out + (i64)r * OD, u, sum);
+}
+
+template <int G>
+__device__ __forceinline__ void fwd_radial_dispatch(int grp, int r, int u, const int *__restrict__ rowptr,
+                                                    const int *__restrict__ src, const real_t *__restrict__ x,
+                                                    const real_t *__restrict__ Y, const real_t *__restrict__ hid,
+                                                    const real_t *__restrict__ W2, real_t *__restrict__ out) {
+    if (grp == G) {
+        fwd_radial_group<G>(r, u, rowptr, src, x, Y, hid, W2, out);
+        return;
+    }
+    if constexpr (G + 1 < NGF) fwd_radial_dispatch<G + 1>(grp, r, u, rowptr, src, x, Y, hid, W2, out);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
+oeq_fwd_radial(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+               const real_t *__restrict__ Y, const real_t *__restrict__ hid, const real_t *__restrict__ W2,
+               real_t *__restrict__ out) {
+    const int w = uni(threadIdx.x >> 6);
+    const int grp = w / UCH, uc = w - grp * UCH;
+    fwd_radial_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, hid, W2, out);
+}
+
 // m-major -> u-major inside each output block of one node row
 extern "C" __global__ void __launch_bounds__(256)
 oeq_out_untranspose(real_t *__restrict__ out) {

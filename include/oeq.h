@@ -303,6 +303,18 @@ oeq_status oeq_radial_bwd(const oeq_plan *plan, int64_t n_edges, const void *vec
                           void *grad_vec, void *grad_W1, void *grad_W2, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* Forward with the radial weights formed inside the convolution kernel (no W
+ * tensor is written or read): out = f(x, Y, W) with W = oeq_radial_fwd(vec, r_cut,
+ * 8, W1, W2), for a hidden width of exactly 8 (W1 [8, 8], W2 [8, P*U]).  Each lane
+ * keeps its slice of W2 in registers and forms W[e] from the edge's 8 hidden
+ * values.  `workspace` of oeq_radial_workspace_size(plan, E, 8) bytes holds the
+ * basis and the hidden values. */
+oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                  const int32_t *rowptr, const int32_t *src, const void *x,
+                                  const void *Y, const void *vec, double r_cut, const void *W1,
+                                  const void *W2, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* Synchronously validates a receiver CSR on the device (rowptr monotone,
  * rowptr[0] = 0, rowptr[N] = E, 0 <= src < N).  Test helper: synchronises. */
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr,

@@ -105,3 +105,27 @@ def test_radial_full_size_sampled():
     assert rel_l2(W[et].reshape(len(edges), PU).cpu().numpy(), radial.radial_fwd(vec[edges], RC, W1, W2)) <= 1e-5
     rv, _, _ = radial.radial_bwd(vec[edges], RC, W1, W2, gWs)
     assert rel_l2(gv[et].cpu().numpy(), rv) <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["tiny_fp64", "mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32",
+                                  "ragged_u96_f32", "u1_l3_f64", "u8_l1_f32"])
+def test_fwd_radial_fused_parity(name):
+    """The forward that forms W in the kernel (hidden width 8) against the oracle
+    forward on the oracle's radial weights."""
+    import oracle
+    wl = SMALL[name]
+    plan = plan_for(wl)
+    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    inp = synth.generate(wl, d.P, d.out_dim, want=("x", "Y", "evec"))
+    rng = np.random.default_rng(21)
+    dt = wl.np_dtype()
+    W1 = rng.standard_normal((8, 8)).astype(dt)
+    W2 = rng.standard_normal((8, plan.n_paths * plan.U)).astype(dt)
+    dev = {k: to_dev(inp[k]) for k in ("rowptr", "src", "x", "Y", "evec")}
+    out = torch.full((wl.n_nodes, plan.out_dim), float("nan"), dtype=plan.torch_dtype(), device="cuda")
+    oeq.oeq_tp_conv_fwd_radial(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["evec"], RC, to_dev(W1),
+                               to_dev(W2), out=out)
+    torch.cuda.synchronize()
+    Wref = radial.radial_fwd(inp["evec"], RC, W1, W2).reshape(inp["E"], plan.n_paths, plan.U)
+    ref = oracle.fwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], Wref)
+    assert rel_l2(out.cpu().numpy(), ref) <= RTOL[wl.dtype]
