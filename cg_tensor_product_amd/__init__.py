@@ -35,7 +35,7 @@ EXPORTED = ["oeq_plan_create", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_pa
             "oeq_last_error", "oeq_plan_schedule", "oeq_sender_view", "oeq_tp_conv_fwd_sender",
             "oeq_tp_conv_bwd_sender", "oeq_sph_harm", "oeq_sph_harm_bwd", "oeq_tp_conv_fwd_vec",
             "oeq_workspace_size_vec", "oeq_tp_conv_bwd_vec", "oeq_radial_workspace_size", "oeq_radial_fwd",
-            "oeq_radial_bwd", "oeq_tp_conv_fwd_radial"]
+            "oeq_radial_bwd", "oeq_tp_conv_fwd_radial", "oeq_workspace_size_radial", "oeq_tp_conv_bwd_radial"]
 SCHEDULES = {0: "receiver", 1: "sender"}
 
 
@@ -128,6 +128,11 @@ def lib():
     L.oeq_radial_bwd.restype = st
     L.oeq_tp_conv_fwd_radial.argtypes = [P, I64, I64, P, P, P, P, P, D, P, P, P, P, SZ, P]
     L.oeq_tp_conv_fwd_radial.restype = st
+    L.oeq_workspace_size_radial.argtypes = [P, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
+    L.oeq_workspace_size_radial.restype = st
+    L.oeq_tp_conv_bwd_radial.argtypes = [P, I64, I64, P, P, P, P, P, D, P, P, P, P, P, P, P, P, ctypes.c_int, P, SZ,
+                                         P]
+    L.oeq_tp_conv_bwd_radial.restype = st
     L.oeq_status_string.argtypes = [ctypes.c_int]
     L.oeq_status_string.restype = ctypes.c_char_p
     L.oeq_last_error.argtypes = []
@@ -569,4 +574,32 @@ def oeq_tp_conv_fwd_radial(plan: Plan, rowptr, src, x, Y, vec, r_cut: float, W1,
     _check(lib().oeq_tp_conv_fwd_radial(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(vec),
                                         float(r_cut), _ptr(W1), _ptr(W2), _ptr(out), _ptr(ws), ws.numel(),
                                         _stream()))
+    return out
+
+
+def oeq_tp_conv_bwd_radial(plan: Plan, rowptr, src, x, Y, vec, r_cut: float, W1, W2, grad_out, mode: str = "atomic",
+                           want=("x", "Y", "vec", "W1", "W2"), workspace=None):
+    """VJP of oeq_tp_conv_fwd_radial: dict with grad_x, grad_Y, grad_vec, grad_W1, grad_W2
+    (None where not in want)."""
+    import torch
+    N, E = _graph(rowptr, src)
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(Y, (E, plan.y_dim), dt, "Y")
+    _want(vec, (E, 3), dt, "vec")
+    _want(W1, (8, 8), dt, "W1")
+    _want(W2, (8, plan.n_paths * plan.U), dt, "W2")
+    _want(grad_out, (N, plan.out_dim), dt, "grad_out")
+    shapes = {"x": (N, plan.x_dim), "Y": (E, plan.y_dim), "vec": (E, 3), "W1": (8, 8),
+              "W2": (8, plan.n_paths * plan.U)}
+    out = {k: _empty(shp, dt, x.device) if k in want else None for k, shp in shapes.items()}
+    if workspace is None:
+        b = ctypes.c_size_t()
+        _check(lib().oeq_workspace_size_radial(plan.handle, N, E, _MODES[mode], ctypes.byref(b)))
+        raw = torch.empty(b.value + 256, dtype=torch.uint8, device=x.device)
+        workspace = raw[(-raw.data_ptr()) % 256:][:b.value]
+    _check(lib().oeq_tp_conv_bwd_radial(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(vec),
+                                        float(r_cut), _ptr(W1), _ptr(W2), _ptr(grad_out), _ptr(out["x"]),
+                                        _ptr(out["Y"]), _ptr(out["vec"]), _ptr(out["W1"]), _ptr(out["W2"]),
+                                        _MODES[mode], _ptr(workspace), workspace.numel(), _stream()))
     return out

@@ -154,6 +154,38 @@ oeq_status edge_launch(oeq_plan *p, const char *name, int64_t E, void **args, hi
     return launch(p, name, static_cast<unsigned>(blocks), 256, stream, args);
 }
 
+// C[M,N] (ldc) = the sum of `rows` partial [M, N] matrices stored densely in `part`, added in
+// row order: in two stages when there are many (chunks of 32 rows in parallel into `scratch`,
+// ceil(rows/32) x M x N elements, then the chunk sums).
+oeq_status ordered_sum(oeq_plan *p, void *part, int rows, int M, int N, void *C, int64_t ldc, void *scratch,
+                       hipStream_t s) {
+    int64_t n = static_cast<int64_t>(M) * N;
+    if (n <= 0 || rows <= 0) return OEQ_OK;
+    oeq_status st;
+    if (rows > 32 && scratch) {
+        const int chunks = (rows + 31) / 32;
+        void *args[] = {&part, &rows, &n, &scratch};
+        hipFunction_t fn = nullptr;
+        std::string why;
+        if ((st = oeq::get_kernel(*p, "oeq_sum_row_chunks", &fn, &why)) != OEQ_OK) return fail(st, why);
+        const hipError_t e = hipModuleLaunchKernel(fn, static_cast<unsigned>((n + 255) / 256),
+                                                   static_cast<unsigned>(chunks), 1, 256, 1, 1, 0, s, args, nullptr);
+        if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("launch oeq_sum_row_chunks: ") + hipGetErrorString(e));
+        part = scratch;
+        rows = chunks;
+    }
+    int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    void *rargs[] = {&part, &rows, &n, &M, &N, &C, &ldc};
+    return launch(p, "oeq_gemm_reduce", static_cast<unsigned>(blocks), 256, s, rargs);
+}
+
+// Splits of K for a product whose output has `tiles` workgroup tiles: enough workgroups
+// to fill the chip, at least 256 K values each.
+int choose_splits(int64_t K, int64_t tiles) {
+    const int64_t want = (2048 + tiles - 1) / std::max<int64_t>(tiles, 1);
+    return static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(want, K / 256)));
+}
+
 // C[M,N] = alpha op(A)[M,K] op(B)[K,N] on the matrix cores (oeq_gemm).  With
 // splits > 1 the K range is cut into that many pieces whose tiles go to `part`
 // ([splits, M, N]) and are then added in order into C.
@@ -188,24 +220,38 @@ oeq_status gemm(oeq_plan *p, int M, int N, int K, const void *A, int64_t lda, bo
                                                256, 1, 1, 0, s, args, nullptr);
     if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("launch ") + name + ": " + hipGetErrorString(e));
     if (splits == 1) return OEQ_OK;
-    int64_t blocks = std::min<int64_t>((stride + 255) / 256, 65536);
-    void *rargs[] = {&part, &splits, &stride, &M, &N, &C, &ldc};
-    return launch(p, "oeq_gemm_reduce", static_cast<unsigned>(blocks), 256, s, rargs);
+    // the chunk sums go after the partial tiles (the caller sizes `part` with gemm_part_elems)
+    void *scratch = static_cast<char *>(part) + static_cast<size_t>(splits) * stride * esize(p);
+    return ordered_sum(p, part, splits, M, N, C, ldc, scratch, s);
+}
+
+// Elements of `part` a gemm() call with this many splits needs.
+size_t gemm_part_elems(int M, int N, int splits) {
+    const size_t n = static_cast<size_t>(M) * N;
+    return splits > 1 ? n * (splits + (splits + 31) / 32) : 0;
 }
 
 // Workspace of the radial-weight passes: B [E,8], h [E,H], dh [E,H], dB [E,8], then the
 // split-K partials of the two products summed over edges.
 struct RadialWs {
     size_t B = 0, h = 0, dh = 0, dB = 0, pW2 = 0, pW1 = 0, bytes = 0;
-    int splits = 1;
+    int splitsW2 = 1, splitsW1 = 1;
 };
 constexpr int kRadialNB = 8;
+
+// workgroup tiles of gemm() for an M x N output (its tile choice)
+int64_t gemm_tiles(const oeq_plan *p, int M, int N) {
+    const bool wide = p->dtype == OEQ_F32;
+    const int bm = wide && M >= 128 ? 128 : 64, bn = wide && N >= 128 ? 128 : 64;
+    return static_cast<int64_t>((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
 constexpr int kFusedHidden = 8;  // hidden width of the forward that forms W in the kernel
 
 RadialWs radial_layout(const oeq_plan *p, int64_t E, int H) {
     RadialWs w;
     const size_t es = esize(p), PU = p->paths.size() * static_cast<size_t>(p->U);
-    w.splits = static_cast<int>(std::min<int64_t>(64, std::max<int64_t>(1, (E + 4095) / 4096)));
+    w.splitsW2 = choose_splits(E, gemm_tiles(p, H, static_cast<int>(PU)));
+    w.splitsW1 = choose_splits(E, gemm_tiles(p, kRadialNB, H));
     size_t off = 0;
     w.B = off;
     off += up(static_cast<size_t>(E) * kRadialNB * es);
@@ -216,9 +262,9 @@ RadialWs radial_layout(const oeq_plan *p, int64_t E, int H) {
     w.dB = off;
     off += up(static_cast<size_t>(E) * kRadialNB * es);
     w.pW2 = off;
-    off += up(static_cast<size_t>(w.splits) * H * PU * es);
+    off += up(gemm_part_elems(H, static_cast<int>(PU), w.splitsW2) * es);
     w.pW1 = off;
-    off += up(static_cast<size_t>(w.splits) * kRadialNB * H * es);
+    off += up(gemm_part_elems(kRadialNB, H, w.splitsW1) * es);
     w.bytes = off;
     return w;
 }
@@ -405,6 +451,8 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     } else {
         if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
         void *h = w.h;
+        // an x block that feeds no path is never written into the per-edge rows
+        if (p->x_unused && (st = fill_zero(p, h, E * p->XD, s)) != OEQ_OK) return st;
         void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &h, &gy_target, &gW, &flags, &gy_stride};
         if ((st = launch(p, "oeq_bwd_rows", grid, block, s, args)) != OEQ_OK) return st;
         st = det_finish(p, N, w, gx, s);
@@ -449,6 +497,7 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
         if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
         dxmode = 2;
         dx_target = w.h;
+        if (p->x_unused && (st = fill_zero(p, w.h, E * p->XD, s)) != OEQ_OK) return st;
     }
     if (!dxmode && !dY && !dW && !dg) return OEQ_OK;
     void *dy_target = gyp ? w.gy_part : dY;
@@ -739,7 +788,7 @@ oeq_status oeq_radial_bwd(const oeq_plan *plan, int64_t E, const void *vec, doub
     const double sh = 1.0 / std::sqrt(static_cast<double>(H)), s8 = 1.0 / std::sqrt(double(kRadialNB));
     if ((st = radial_hidden(p, E, vec, r_cut, H, W1, ws, w, s)) != OEQ_OK) return st;
     // gW2 = h^T gW / sqrt(H): a sum over edges
-    if (gW2 && (st = gemm(p, H, PU, Ei, ws + w.h, H, true, gW, PU, false, gW2, PU, sh, w.splits, ws + w.pW2, s)) !=
+    if (gW2 && (st = gemm(p, H, PU, Ei, ws + w.h, H, true, gW, PU, false, gW2, PU, sh, w.splitsW2, ws + w.pW2, s)) !=
                    OEQ_OK)
         return st;
     if (!gvec && !gW1) return OEQ_OK;
@@ -749,7 +798,7 @@ oeq_status oeq_radial_bwd(const oeq_plan *plan, int64_t E, const void *vec, doub
     void *dargs[] = {&Bp, &W1, const_cast<int *>(&H), &dh, &E};
     if ((st = edge_launch(p, "oeq_radial_dpre", E * H, dargs, s)) != OEQ_OK) return st;
     // gW1 = B^T dpre / sqrt(8): a sum over edges
-    if (gW1 && (st = gemm(p, kRadialNB, H, Ei, Bp, kRadialNB, true, dh, H, false, gW1, H, s8, w.splits,
+    if (gW1 && (st = gemm(p, kRadialNB, H, Ei, Bp, kRadialNB, true, dh, H, false, gW1, H, s8, w.splitsW1,
                           ws + w.pW1, s)) != OEQ_OK)
         return st;
     if (!gvec) return OEQ_OK;
@@ -781,6 +830,147 @@ oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
     void *hid = ws + w.h;
     void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &out};
     return launch(p, "oeq_fwd_radial", static_cast<unsigned>(N), fwd_block(p), s, args);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of the radial VJP: the radial pieces (width 8), the VJP's sender CSR and
+// per-edge x-gradient rows (deterministic mode), the per-group partial gY and dh rows
+// (several radial groups) and the per-receiver dW2 partials [N, 8, P*U].
+struct RadVjpWs {
+    RadialWs rad;
+    Workspace conv;
+    size_t conv_off = 0, gyp = 0, dhp = 0, w2p = 0, w2s = 0, bytes = 0;
+};
+
+oeq_status radvjp_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, char *base, RadVjpWs *w) {
+    const size_t es = esize(p), PU = p->paths.size() * static_cast<size_t>(p->U), G = p->rad_groups.size();
+    w->rad = radial_layout(p, E, kFusedHidden);
+    size_t off = w->rad.bytes;
+    w->conv_off = off;
+    oeq_status st = ws_layout(p, N, E, det, false, base ? base + off : nullptr, &w->conv);
+    if (st != OEQ_OK) return st;
+    off += up(w->conv.bytes);
+    w->gyp = off;
+    if (G > 1) off += up(G * static_cast<size_t>(E) * p->YD * es);
+    w->dhp = off;
+    if (G > 1) off += up(G * static_cast<size_t>(E) * kFusedHidden * es);
+    w->w2p = off;
+    off += up(static_cast<size_t>(N) * kFusedHidden * PU * es);
+    w->w2s = off;  // chunk sums of those rows
+    off += up(static_cast<size_t>((N + 31) / 32) * kFusedHidden * PU * es);
+    w->bytes = off;
+    return OEQ_OK;
+}
+
+oeq_status combine_parts(oeq_plan *p, void *part, int groups, void *out, int64_t n, hipStream_t s) {
+    if (n <= 0) return OEQ_OK;
+    int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    void *args[] = {&part, &groups, &out, &n};
+    return launch(p, "oeq_part_combine", static_cast<unsigned>(blocks), 256, s, args);
+}
+
+}  // namespace
+
+extern "C" {
+
+oeq_status oeq_workspace_size_radial(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, size_t *bytes) {
+    if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
+    if (N < 0 || E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    RadVjpWs w;
+    oeq_status st = radvjp_layout(p, N, E, mode == OEQ_BWD_DETERMINISTIC, nullptr, &w);
+    if (st != OEQ_OK) return st;
+    *bytes = w.bytes;
+    return OEQ_OK;
+}
+
+oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr,
+                                  const int32_t *src, const void *x, const void *Y, const void *vec, double r_cut,
+                                  const void *W1, const void *W2, const void *g, void *gx, void *gY, void *gvec,
+                                  void *gW1, void *gW2, oeq_bwd_mode mode, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    if (E > 0 && (!x || !Y || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, Y or grad_out is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    if (p->YD < kFusedHidden) return fail(OEQ_ERR_UNSUPPORTED, "the radial VJP needs Y degrees up to at least 2");
+    RadialWs rw;
+    if ((st = radial_check(plan, E, r_cut, kFusedHidden, vec, W1, W2, nullptr, 0, &rw)) != OEQ_OK &&
+        st != OEQ_ERR_WORKSPACE)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int H = kFusedHidden, PU = static_cast<int>(p->paths.size()) * p->U;
+    if (E == 0) {
+        if (gx && (st = fill_zero(p, gx, N * p->XD, s)) != OEQ_OK) return st;
+        if (gW1 && (st = fill_zero(p, gW1, int64_t(kRadialNB) * H, s)) != OEQ_OK) return st;
+        return gW2 ? fill_zero(p, gW2, int64_t(H) * PU, s) : OEQ_OK;
+    }
+    if (!gx && !gY && !gvec && !gW1 && !gW2) return OEQ_OK;
+    const bool det = gx && mode == OEQ_BWD_DETERMINISTIC;
+    RadVjpWs w;
+    if ((st = radvjp_layout(p, N, E, det, static_cast<char *>(workspace), &w)) != OEQ_OK) return st;
+    if (!workspace || workspace_bytes < w.bytes) return fail(OEQ_ERR_WORKSPACE, "workspace too small");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+        return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+    if ((st = radial_hidden(p, E, vec, r_cut, H, W1, ws, w.rad, s)) != OEQ_OK) return st;
+    const int G = static_cast<int>(p->rad_groups.size());
+    const bool want_dh = gvec || gW1;
+    int flags = (gW2 ? 1 : 0) | (gY ? 2 : 0) | (want_dh ? 4 : 0);
+    void *hid = ws + w.rad.h, *dh = ws + w.rad.dh, *w2p = ws + w.w2p;
+    void *gy_target = G > 1 ? ws + w.gyp : gY, *dh_target = G > 1 ? ws + w.dhp : dh;
+    int64_t gy_stride = G > 1 ? E * p->YD : 0, dh_stride = G > 1 ? E * H : 0;
+    const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(G));
+    const unsigned block = bwd_block(p);
+    if (!gx) {
+        void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &g, &gx, &gy_target, &dh_target, &w2p, &flags, &gy_stride,
+                        &dh_stride};
+        if ((st = launch(p, "oeq_bwd_radial_nogx", grid, block, s, args)) != OEQ_OK) return st;
+    } else if (!det) {
+        if ((st = fill_zero(p, gx, N * p->XD, s)) != OEQ_OK) return st;
+        void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &g, &gx, &gy_target, &dh_target, &w2p, &flags, &gy_stride,
+                        &dh_stride};
+        if ((st = launch(p, "oeq_bwd_radial_atomic", grid, block, s, args)) != OEQ_OK) return st;
+        if ((st = untranspose(p, N, gx, s)) != OEQ_OK) return st;
+    } else {
+        if ((st = sender_csr_into(N, E, src, w.conv, s)) != OEQ_OK) return st;
+        void *hrows = w.conv.h;
+        // each group writes the x blocks of its own paths; a block no path uses stays zero
+        if (p->x_unused && (st = fill_zero(p, hrows, E * p->XD, s)) != OEQ_OK) return st;
+        void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &g, &hrows, &gy_target, &dh_target, &w2p, &flags,
+                        &gy_stride, &dh_stride};
+        if ((st = launch(p, "oeq_bwd_radial_rows", grid, block, s, args)) != OEQ_OK) return st;
+        if ((st = det_finish(p, N, w.conv, gx, s)) != OEQ_OK) return st;
+    }
+    if (G > 1) {
+        if (gY && (st = combine_parts(p, gy_target, G, gY, E * p->YD, s)) != OEQ_OK) return st;
+        if (want_dh && (st = combine_parts(p, dh_target, G, dh, E * H, s)) != OEQ_OK) return st;
+    }
+    // sum of the receivers' partial rows, in receiver order
+    if (gW2 && (st = ordered_sum(p, w2p, static_cast<int>(N), kFusedHidden, PU, gW2, PU, ws + w.w2s, s)) != OEQ_OK)
+        return st;
+    if (!want_dh) return OEQ_OK;
+    // the rest of the radial backward from dh: dpre, gW1 = B^T dpre / sqrt(8), dB, grad_vec
+    void *Bp = ws + w.rad.B;
+    const int Ei = static_cast<int>(E);
+    const double s8 = 1.0 / std::sqrt(double(kRadialNB));
+    void *dargs[] = {&Bp, &W1, const_cast<int *>(&H), &dh, &E};
+    if ((st = edge_launch(p, "oeq_radial_dpre", E * H, dargs, s)) != OEQ_OK) return st;
+    if (gW1 && (st = gemm(p, kRadialNB, H, Ei, Bp, kRadialNB, true, dh, H, false, gW1, H, s8, w.rad.splitsW1,
+                          ws + w.rad.pW1, s)) != OEQ_OK)
+        return st;
+    if (!gvec) return OEQ_OK;
+    void *dB = ws + w.rad.dB;
+    if ((st = gemm(p, Ei, kRadialNB, H, dh, H, false, W1, H, true, dB, kRadialNB, s8, 1, nullptr, s)) != OEQ_OK)
+        return st;
+    float rcf = static_cast<float>(r_cut);
+    void *rc = p->dtype == OEQ_F64 ? static_cast<void *>(&r_cut) : static_cast<void *>(&rcf);
+    void *gargs[] = {&vec, rc, &dB, &gvec, &E};
+    return edge_launch(p, "oeq_radial_gvec", E, gargs, s);
 }
 
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr, const int32_t *src, void *stream) {

@@ -319,6 +319,8 @@ std::string emit_source(const oeq_plan &p) {
     for (const auto &g : p.fwd_groups) o << " " << g.size();
     o << " paths, backward groups of";
     for (const auto &g : p.bwd_groups) o << " " << g.size();
+    o << ", radial backward groups of";
+    for (const auto &g : p.rad_groups) o << " " << g.size();
     o << " paths\n";
     o << "typedef " << (p.dtype == OEQ_F64 ? "double" : "float") << " real_t;\n";
     o << "typedef long long i64;\n";
@@ -358,8 +360,11 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr bool XT = " << (p.xt ? "true" : "false") << ";\n";
     o << "template <int G> struct FG;\n";
     o << "template <int G> struct BG;\n";
+    o << "template <int G> struct RG;\n";
+    o << "constexpr int NGR = " << p.rad_groups.size() << ";\n";
     for (size_t g = 0; g < p.fwd_groups.size(); ++g) emit_group(o, p, "FG", static_cast<int>(g), p.fwd_groups[g]);
     for (size_t g = 0; g < p.bwd_groups.size(); ++g) emit_group(o, p, "BG", static_cast<int>(g), p.bwd_groups[g]);
+    for (size_t g = 0; g < p.rad_groups.size(); ++g) emit_group(o, p, "RG", static_cast<int>(g), p.rad_groups[g]);
     emit_untranspose(o, p);
     o << kKernelTemplate;
     return o.str();

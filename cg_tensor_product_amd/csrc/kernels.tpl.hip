@@ -376,30 +376,35 @@ struct GyStage {
     real_t red[UCH][GY_TILE][PY];
 };
 
+// Rows of width RW <= PY (default: the Y width); the radial VJP also stages its
+// 8-wide hidden-value gradients this way.
+template <int RW = YD>
 __device__ __forceinline__ void gy_push(GyStage &st, real_t *__restrict__ gY, int e, int j,
-                                        real_t (&gy)[YD], int lane, int wv, bool acc = false) {
+                                        real_t (&gy)[RW], int lane, int wv, bool acc = false) {
+    static_assert(RW <= PY, "row wider than the reduction");
     real_t v[PY];
 #pragma unroll
-    for (int k = 0; k < PY; ++k) v[k] = (k < YD) ? gy[k] : real_t(0);
+    for (int k = 0; k < PY; ++k) v[k] = (k < RW) ? gy[k] : real_t(0);
     wave_reduce_scatter(v, lane);
     const int idx = lane >> (6 - LGPY);
     const bool writer = (lane & ((1 << (6 - LGPY)) - 1)) == 0;
     if (UCH == 1) {
-        if (writer && idx < YD) gY[(i64)e * YD + idx] = acc ? gY[(i64)e * YD + idx] + v[0] : v[0];
+        if (writer && idx < RW) gY[(i64)e * RW + idx] = acc ? gY[(i64)e * RW + idx] + v[0] : v[0];
     } else {
         if (writer) st.red[wv][j][idx] = v[0];
     }
 }
 
+template <int RW = YD>
 __device__ __forceinline__ void gy_flush(GyStage &st, real_t *__restrict__ gY, int base, int n, bool acc = false) {
     if (UCH == 1) return;
     __syncthreads();
-    for (int k = threadIdx.x; k < n * YD; k += UCH * 64) {
-        const int j = k / YD, m = k - j * YD;
+    for (int k = threadIdx.x; k < n * RW; k += UCH * 64) {
+        const int j = k / RW, m = k - j * RW;
         real_t s = st.red[0][j][m];
 #pragma unroll
         for (int w = 1; w < UCH; ++w) s += st.red[w][j][m];
-        real_t *dst = gY + (i64)(base + j) * YD + m;
+        real_t *dst = gY + (i64)(base + j) * RW + m;
         *dst = acc ? *dst + s : s;
     }
     __syncthreads();
@@ -507,6 +512,16 @@ oeq_bwd_rows(const int *__restrict__ rowptr, const int *__restrict__ src, const 
              const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
              real_t *__restrict__ h, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
     bwd_body<2>(rowptr, src, x, Y, W, g, h, gY, gW, flags, gy_stride);
+}
+
+// Partial rows of several groups added in group order: out[i] = sum_g part[g n + i].
+extern "C" __global__ void __launch_bounds__(256)
+oeq_part_combine(const real_t *__restrict__ part, int groups, real_t *__restrict__ out, i64 n) {
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x) {
+        real_t s = part[i];
+        for (int gidx = 1; gidx < groups; ++gidx) s += part[gidx * n + i];
+        out[i] = s;
+    }
 }
 
 // Y-gradient of several path groups: gY = sum over groups of the partial rows,
@@ -698,6 +713,152 @@ oeq_fwd_radial(const int *__restrict__ rowptr, const int *__restrict__ src, cons
     const int grp = w / UCH, uc = w - grp * UCH;
     fwd_radial_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, hid, W2, out);
 }
+
+// VJP with the radial weights formed in the kernel (hidden width RH = 8).  Per
+// edge, as oeq_bwd_* with W[e] = h[e] W2 / sqrt(8) formed from registers, and in
+// place of grad_W:
+//   dh[e, j]  = sum_{p,u} gW[e,p,u] W2[j,p,u] / sqrt(8)   (lanes, then waves, like gY)
+//   dW2 partial of the workgroup: sum over its edges of h[e, j] gW[e,p,u] / sqrt(8),
+//   stored as row r of dw2p[N, RH, P*U] and summed over receivers in order later.
+// A workgroup is one (receiver, radial path group: RG<g>, NGR of them); with several
+// groups the gY and dh rows are per-group partials, added in group order later.
+// flags: bit0 dW2 partials, bit1 grad_Y, bit2 dh.  Needs PY >= RH (Y degrees >= 2).
+template <int GXMODE, int G>
+__device__ __forceinline__ void bwd_radial_group(GyStage &st, GyStage &sth, int r, int wv, int u,
+                                                 const int *__restrict__ rowptr, const int *__restrict__ src,
+                                                 const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                                 const real_t *__restrict__ hid, const real_t *__restrict__ W2,
+                                                 const real_t *__restrict__ g, real_t *__restrict__ gx,
+                                                 real_t *__restrict__ gY, real_t *__restrict__ dh,
+                                                 real_t *__restrict__ dw2p, int flags) {
+    if constexpr (PY >= RH) {
+        using Gr = RG<G>;
+        const int lane = threadIdx.x & 63;
+        const bool act = (U % 64 == 0) || (u < U);
+        const int uu = act ? u : 0;
+        const bool want_w2 = (flags & 1) != 0, want_gy = (flags & 2) != 0, want_dh = (flags & 4) != 0;
+        real_t w2[RH][Gr::NW], dw2[RH][Gr::NW];
+#pragma unroll
+        for (int j = 0; j < RH; ++j) {
+            Gr::load_wrow(W2 + (i64)j * (P * U), uu, w2[j]);
+#pragma unroll
+            for (int k = 0; k < Gr::NW; ++k) {
+                w2[j][k] *= real_t(0.35355339059327373);  // 1/sqrt(8)
+                dw2[j][k] = real_t(0);
+            }
+        }
+        real_t gv[Gr::NO];
+        Gr::load_g(g + (i64)r * OD, uu, gv);
+        if (!act) zero(gv);  // inactive lanes contribute nothing to the lane sums
+        const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+        if (e0 < e1) {
+            int s = uni(src[e0]);
+            real_t yv[YD], xv[Gr::NX], hv[RH];
+            load_y(Y, e0, yv);
+            Gr::load_x(x + (i64)s * XD, uu, xv);
+#pragma unroll
+            for (int j = 0; j < RH; ++j) hv[j] = hid[(i64)e0 * RH + j];
+            for (int e = e0; e < e1; ++e) {
+                const int en = (e + 1 < e1) ? e + 1 : e;
+                const int sn = uni(src[en]);
+                real_t yn[YD], xn[Gr::NX], hn[RH];
+                load_y(Y, en, yn);
+                Gr::load_x(x + (i64)sn * XD, uu, xn);
+#pragma unroll
+                for (int j = 0; j < RH; ++j) hn[j] = hid[(i64)en * RH + j];
+                PIN_BWD();
+                const int jt = uni((e - e0) % GY_TILE);
+                real_t wv_[Gr::NW];
+#pragma unroll
+                for (int k = 0; k < Gr::NW; ++k) {
+                    real_t t = hv[0] * w2[0][k];
+#pragma unroll
+                    for (int j = 1; j < RH; ++j) t = fmar(hv[j], w2[j][k], t);
+                    wv_[k] = t;
+                }
+                real_t gw[Gr::NW], gy[YD], gxp[Gr::NX];
+                zero(gw);
+                zero(gy);
+                zero(gxp);
+                Gr::template vjp<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
+                if (!act) zero(gw);
+                if (want_w2) {
+#pragma unroll
+                    for (int j = 0; j < RH; ++j)
+#pragma unroll
+                        for (int k = 0; k < Gr::NW; ++k) dw2[j][k] = fmar(hv[j], gw[k], dw2[j][k]);
+                }
+                if (want_dh) {
+                    real_t d[RH];
+#pragma unroll
+                    for (int j = 0; j < RH; ++j) {
+                        real_t t = real_t(0);
+#pragma unroll
+                        for (int k = 0; k < Gr::NW; ++k) t = fmar(gw[k], w2[j][k], t);
+                        d[j] = t;
+                    }
+                    gy_push<RH>(sth, dh, e, jt, d, lane, wv);
+                    if (jt == GY_TILE - 1 || e + 1 == e1) gy_flush<RH>(sth, dh, e - jt, jt + 1);
+                }
+                if (want_gy) {
+                    gy_push(st, gY, e, jt, gy, lane, wv);
+                    if (jt == GY_TILE - 1 || e + 1 == e1) gy_flush(st, gY, e - jt, jt + 1);
+                }
+                if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * XD, u, gxp);
+                if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * XD, u, gxp);
+                s = sn;
+#pragma unroll
+                for (int q = 0; q < YD; ++q) yv[q] = yn[q];
+#pragma unroll
+                for (int q = 0; q < Gr::NX; ++q) xv[q] = xn[q];
+#pragma unroll
+                for (int q = 0; q < RH; ++q) hv[q] = hn[q];
+            }
+        }
+        if (want_w2 && act) {
+#pragma unroll
+            for (int j = 0; j < RH; ++j) {
+#pragma unroll
+                for (int k = 0; k < Gr::NW; ++k) dw2[j][k] *= real_t(0.35355339059327373);
+                Gr::store_w(dw2p + ((i64)r * RH + j) * (P * U), u, dw2[j]);
+            }
+        }
+    }
+}
+
+template <int GXMODE, int G>
+__device__ __forceinline__ void bwd_radial_dispatch(GyStage &st, GyStage &sth, int r, int grp, int wv, int u,
+                                                    const int *__restrict__ rowptr, const int *__restrict__ src,
+                                                    const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                                    const real_t *__restrict__ hid, const real_t *__restrict__ W2,
+                                                    const real_t *__restrict__ g, real_t *__restrict__ gx,
+                                                    real_t *__restrict__ gY, real_t *__restrict__ dh,
+                                                    real_t *__restrict__ dw2p, int flags) {
+    if (grp == G) {
+        bwd_radial_group<GXMODE, G>(st, sth, r, wv, u, rowptr, src, x, Y, hid, W2, g, gx, gY, dh, dw2p, flags);
+        return;
+    }
+    if constexpr (G + 1 < NGR)
+        bwd_radial_dispatch<GXMODE, G + 1>(st, sth, r, grp, wv, u, rowptr, src, x, Y, hid, W2, g, gx, gY, dh, dw2p,
+                                           flags);
+}
+
+#define OEQ_BWD_RADIAL_KERNEL(NAME, GXMODE)                                                              \
+    extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY NAME(                            \
+        const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,      \
+        const real_t *__restrict__ Y, const real_t *__restrict__ hid, const real_t *__restrict__ W2,    \
+        const real_t *__restrict__ g, real_t *__restrict__ gx, real_t *__restrict__ gY,                 \
+        real_t *__restrict__ dh, real_t *__restrict__ dw2p, int flags, i64 gy_stride, i64 dh_stride) {  \
+        __shared__ GyStage st, sth;                                                                     \
+        const int r = blockIdx.x / NGR, grp = blockIdx.x - r * NGR;                                     \
+        const int wv = uni(threadIdx.x >> 6);                                                           \
+        bwd_radial_dispatch<GXMODE, 0>(st, sth, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, \
+                                       hid, W2, g, gx, gY + grp * gy_stride, dh + grp * dh_stride, dw2p,  \
+                                       flags);                                                          \
+    }
+OEQ_BWD_RADIAL_KERNEL(oeq_bwd_radial_nogx, 0)
+OEQ_BWD_RADIAL_KERNEL(oeq_bwd_radial_atomic, 1)
+OEQ_BWD_RADIAL_KERNEL(oeq_bwd_radial_rows, 2)
 
 // m-major -> u-major inside each output block of one node row
 extern "C" __global__ void __launch_bounds__(256)
@@ -935,6 +1096,18 @@ OEQ_GEMM_KERNEL(64, 64)
 OEQ_GEMM_KERNEL(64, 128)
 OEQ_GEMM_KERNEL(128, 64)
 OEQ_GEMM_KERNEL(128, 128)
+
+// First stage of an ordered sum of many partial rows: part [rows, n] -> out
+// [ceil(rows / 32), n], chunk c holding rows 32c .. 32c+31 added in order.
+extern "C" __global__ void __launch_bounds__(256)
+oeq_sum_row_chunks(const real_t *__restrict__ part, int rows, i64 n, real_t *__restrict__ out) {
+    const i64 c = (i64)blockIdx.x * blockDim.x + threadIdx.x;
+    if (c >= n) return;
+    const int r0 = blockIdx.y * 32, r1 = min(rows, r0 + 32);
+    real_t s = part[(i64)r0 * n + c];
+    for (int r = r0 + 1; r < r1; ++r) s += part[(i64)r * n + c];
+    out[(i64)blockIdx.y * n + c] = s;
+}
 
 extern "C" __global__ void __launch_bounds__(256)
 oeq_gemm_reduce(const real_t *__restrict__ part, int splits, i64 split_stride, int M, int N,

@@ -262,6 +262,22 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     waves("OEQ_BWD_WAVES", p->bwd_waves);
     p->fwd_groups = choose_groups(*p, true);
     p->bwd_groups = choose_groups(*p, false);
+    {
+        // the radial VJP keeps 2 x 8 x NW more values per lane than the VJP: split until the
+        // estimate is under budget (estimates of 358 / 636 / 696 compiled to 394 registers /
+        // spills / spills for the medium fp32 / large / medium fp64 configurations)
+        const int max_g = std::max(1, 16 / p->uch), f = p->dtype == OEQ_F64 ? 2 : 1;
+        for (int g = 1; g <= max_g; ++g) {
+            auto cand = partition_paths(*p, false, g);
+            p->rad_groups = cand;
+            int worst = 0;
+            for (const auto &gr : cand)
+                worst = std::max(worst, group_registers(*p, gr, false) + 2 * 8 * static_cast<int>(gr.size()) * f);
+            if (worst <= 400 || static_cast<int>(cand.size()) < g) break;
+        }
+        if (const char *e = std::getenv("OEQ_RAD_GROUPS"))
+            p->rad_groups = partition_paths(*p, false, std::max(1, std::min(std::atoi(e), max_g)));
+    }
     if (const char *s = std::getenv("OEQ_GY_TILE")) {
         const int v = std::atoi(s);
         if (v >= 1 && v <= 256) p->gy_tile = v;

@@ -315,6 +315,24 @@ oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t n_nodes, int64_t
                                   const void *W2, void *out, void *workspace,
                                   size_t workspace_bytes, void *stream);
 
+/* VJP of oeq_tp_conv_fwd_radial (hidden width 8, W formed in the kernel): grad_x
+ * and grad_Y as oeq_tp_conv_bwd, and, in place of grad_W, the gradients of the
+ * radial network: grad_vec [E, 3], grad_W1 [8, 8], grad_W2 [8, P*U].  Per edge the
+ * kernel contracts its W gradient with W2 into the 8 hidden-value gradients
+ * (reduced over lanes and waves like grad_Y) and accumulates h (x) gW into a
+ * per-receiver W2-gradient row; the rows are summed over receivers in order, so
+ * grad_W2 and grad_W1 are bitwise repeatable.  Any output may be NULL.  Needs Y
+ * degrees up to at least 2.  `workspace` of oeq_workspace_size_radial bytes. */
+oeq_status oeq_workspace_size_radial(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                     oeq_bwd_mode mode, size_t *bytes);
+oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                  const int32_t *rowptr, const int32_t *src, const void *x,
+                                  const void *Y, const void *vec, double r_cut, const void *W1,
+                                  const void *W2, const void *grad_out, void *grad_x,
+                                  void *grad_Y, void *grad_vec, void *grad_W1, void *grad_W2,
+                                  oeq_bwd_mode mode, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
 /* Synchronously validates a receiver CSR on the device (rowptr monotone,
  * rowptr[0] = 0, rowptr[N] = E, 0 <= src < N).  Test helper: synchronises. */
 oeq_status oeq_csr_check(int64_t n_nodes, int64_t n_edges, const int32_t *rowptr,

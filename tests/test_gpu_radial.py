@@ -129,3 +129,49 @@ def test_fwd_radial_fused_parity(name):
     Wref = radial.radial_fwd(inp["evec"], RC, W1, W2).reshape(inp["E"], plan.n_paths, plan.U)
     ref = oracle.fwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], Wref)
     assert rel_l2(out.cpu().numpy(), ref) <= RTOL[wl.dtype]
+
+
+@pytest.mark.parametrize("mode", ["atomic", "deterministic"])
+@pytest.mark.parametrize("name", ["tiny_fp64", "mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32",
+                                  "ragged_u96_f32", "u1_l3_f64"])
+def test_bwd_radial_fused_parity(name, mode):
+    """The VJP with W formed in the kernel (hidden width 8) against the oracle:
+    grad_x, grad_Y from the oracle VJP on the oracle's radial weights; grad_vec,
+    grad_W1, grad_W2 from the oracle radial backward of the oracle's grad_W."""
+    import oracle
+    wl = SMALL[name]
+    plan = plan_for(wl)
+    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    inp = synth.generate(wl, d.P, d.out_dim, want=("x", "Y", "evec", "g"))
+    rng = np.random.default_rng(22)
+    dt = wl.np_dtype()
+    W1 = rng.standard_normal((8, 8)).astype(dt)
+    W2 = rng.standard_normal((8, plan.n_paths * plan.U)).astype(dt)
+    dev = {k: to_dev(inp[k]) for k in ("rowptr", "src", "x", "Y", "evec", "g")}
+    print(f"[bwd radial] {name} {mode}", flush=True)
+    res = oeq.oeq_tp_conv_bwd_radial(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["evec"], RC,
+                                     to_dev(W1), to_dev(W2), dev["g"], mode=mode)
+    again = oeq.oeq_tp_conv_bwd_radial(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["evec"], RC,
+                                       to_dev(W1), to_dev(W2), dev["g"], mode=mode, want=("vec", "W1", "W2"))
+    torch.cuda.synchronize()
+    E = inp["E"]
+    Wref = radial.radial_fwd(inp["evec"], RC, W1, W2).reshape(E, plan.n_paths, plan.U)
+    rx, rY, rW = oracle.bwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], Wref, inp["g"])
+    rv, r1, r2 = radial.radial_bwd(inp["evec"], RC, W1, W2, rW.reshape(E, -1))
+    tol = RTOL[wl.dtype]
+    for k, ref in (("x", rx), ("Y", rY), ("vec", rv), ("W1", r1), ("W2", r2)):
+        assert rel_l2(res[k].cpu().numpy(), ref) <= tol, k
+    for k in ("vec", "W1", "W2"):
+        assert torch.equal(res[k], again[k]), k     # fixed summation order
+
+
+def test_bwd_radial_rejects_low_Y_degree():
+    wl = SMALL["u8_l1_f32"]
+    plan = plan_for(wl)
+    N, E = 4, 3
+    rowptr = torch.tensor([0, 1, 2, 3, 3], dtype=torch.int32, device="cuda")
+    src = torch.tensor([1, 2, 0], dtype=torch.int32, device="cuda")
+    f = lambda *s: torch.zeros(*s, dtype=torch.float32, device="cuda")
+    with pytest.raises(oeq.OeqError, match="UNSUPPORTED"):
+        oeq.oeq_tp_conv_bwd_radial(plan, rowptr, src, f(N, plan.x_dim), f(E, plan.y_dim), f(E, 3), RC, f(8, 8),
+                                   f(8, plan.n_paths * plan.U), f(N, plan.out_dim))

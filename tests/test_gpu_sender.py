@@ -114,6 +114,18 @@ def test_sender_unused_x_block_and_shared_output_block():
     got = gx.cpu().numpy()
     assert rel_l2(got, rx) <= 1e-12
     assert not got[:, 8:32].any()                   # the 1o block feeds no path
+    # the receiver-stationary VJP and double backward, deterministic mode (per-edge rows)
+    for mode in ("atomic", "deterministic"):
+        gxr, _, _ = oeq.oeq_tp_conv_bwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                                        mode=mode)
+        got = gxr.cpu().numpy()
+        assert rel_l2(got, rx) <= 1e-12 and not got[:, 8:32].any(), mode
+        tY = synth.extra_normal(wl, inp["Y"].shape, 2)
+        res = oeq.oeq_tp_conv_dbwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                                   gg_Y=to_dev(tY), mode=mode, want=("x",))
+        refd = oracle.dbwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"], ggY=tY)
+        got = res["x"].cpu().numpy()
+        assert rel_l2(got, refd["dx"]) <= 1e-12 and not got[:, 8:32].any(), mode
 
 
 def test_sender_empty_graph():
