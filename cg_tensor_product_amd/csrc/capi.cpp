@@ -825,8 +825,9 @@ oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
         return st;
     oeq_plan *p = const_cast<oeq_plan *>(plan);
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (E == 0) return fill_zero(p, out, N * p->OD, s);  // no edges: W2 and the workspace are not read
     char *ws = static_cast<char *>(workspace);
-    if (E > 0 && (st = radial_hidden(p, E, vec, r_cut, kFusedHidden, W1, ws, w, s)) != OEQ_OK) return st;
+    if ((st = radial_hidden(p, E, vec, r_cut, kFusedHidden, W1, ws, w, s)) != OEQ_OK) return st;
     void *hid = ws + w.h;
     void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &out};
     return launch(p, "oeq_fwd_radial", static_cast<unsigned>(N), fwd_block(p), s, args);

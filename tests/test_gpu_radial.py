@@ -83,6 +83,20 @@ def test_radial_empty():
     torch.cuda.synchronize()
     assert W.shape[0] == 0 and gv.shape == (0, 3)
     assert not g1.cpu().numpy().any() and not g2.cpu().numpy().any()
+    # the in-kernel forward and VJP on a graph without edges
+    N = 5
+    rowptr = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    src = torch.zeros(0, dtype=torch.int32, device="cuda")
+    x = torch.randn(N, plan.x_dim, dtype=torch.float64, device="cuda")
+    Y = torch.zeros(0, plan.y_dim, dtype=torch.float64, device="cuda")
+    g = torch.randn(N, plan.out_dim, dtype=torch.float64, device="cuda")
+    W1s, W2s = W1[:, :8].contiguous(), W2[:8].contiguous()
+    out = torch.full((N, plan.out_dim), float("nan"), dtype=torch.float64, device="cuda")
+    oeq.oeq_tp_conv_fwd_radial(plan, rowptr, src, x, Y, vec, RC, W1s, W2s, out=out)
+    res = oeq.oeq_tp_conv_bwd_radial(plan, rowptr, src, x, Y, vec, RC, W1s, W2s, g)
+    torch.cuda.synchronize()
+    assert not out.cpu().numpy().any()
+    assert not res["x"].cpu().numpy().any() and not res["W2"].cpu().numpy().any()
 
 
 @pytest.mark.slow
