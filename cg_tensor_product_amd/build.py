@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liboeq.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
-HOST_SOURCES = ["capi.cpp", "planner.cpp", "cg_tables.cpp", "codegen.cpp", "jit.cpp"]
+HOST_SOURCES = ["capi.cpp", "capi_graph.cpp", "capi_edge.cpp", "planner.cpp", "cg_tables.cpp", "codegen.cpp", "jit.cpp"]
 HIP_SOURCES = ["csr.hip"]
 ARCH = "gfx950"
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
