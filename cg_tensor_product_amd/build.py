@@ -32,13 +32,20 @@ def _run(cmd):
     return r
 
 
+# Parts of the kernel template, concatenated in this order after the planner's prelude.
+TEMPLATE_PARTS = ["kernels_common.tpl.hip", "kernels_conv.tpl.hip", "kernels_sender.tpl.hip",
+                  "kernels_gemm_radial.tpl.hip", "kernels_radial_fused.tpl.hip", "kernels_dbwd.tpl.hip"]
+
+
 def _embed_template() -> str:
-    with open(os.path.join(CSRC, "kernels.tpl.hip")) as f:
-        text = f.read()
+    text = ""
+    for part in TEMPLATE_PARTS:
+        with open(os.path.join(CSRC, part)) as f:
+            text += f.read() + "\n"
     delim = "OEQTPL"
     assert (")" + delim + '"') not in text
     out = os.path.join(BUILD, "kernel_template.cpp")
-    body = ("// generated from csrc/kernels.tpl.hip\nnamespace oeq {\nextern const char *kKernelTemplate;\n"
+    body = ("// generated from csrc/kernels_*.tpl.hip\nnamespace oeq {\nextern const char *kKernelTemplate;\n"
             f'const char *kKernelTemplate = R"{delim}(' + text + f'){delim}";\n}}\n')
     old = open(out).read() if os.path.exists(out) else None
     if old != body:

@@ -1,0 +1,291 @@
+// Receiver-stationary passes: forward, VJP (three x-gradient modes), the
+// ordered combination of partial rows and the per-sender sum of x-gradient rows.
+
+// ---------------------------------------------------------------------------
+// Forward: out[r] = sum over the receiver's edges of the per-edge messages.
+// ---------------------------------------------------------------------------
+template <int G, bool YV>
+__device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ rowptr,
+                                          const int *__restrict__ src, const real_t *__restrict__ x,
+                                          const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                          real_t *__restrict__ out, bool acc) {
+    using Gr = FG<G>;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;  // inactive lanes read channel 0 and store nothing
+    real_t sum[Gr::NO];
+    zero(sum);
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    if (e0 < e1) {
+        // software pipeline: the next edge's loads are in flight while this one computes
+        int s = uni(src[e0]);
+        real_t yv[YD], xv[Gr::NX], wv[Gr::NW];
+        edge_y<YV>(Y, e0, yv);
+        Gr::load_x(x + (i64)s * XD, uu, xv);
+        Gr::load_w(W + (i64)e0 * (P * U), uu, wv);
+        for (int e = e0; e < e1; ++e) {
+            real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            edge_y<YV>(Y, en, yn);
+            Gr::load_x(x + (i64)sn * XD, uu, xn);
+            Gr::load_w(W + (i64)en * (P * U), uu, wn);
+            // keep the next edge's loads ahead of this edge's arithmetic
+            PIN_FWD();
+            Gr::edge(xv, yv, wv, sum);
+#pragma unroll
+            for (int k = 0; k < YD; ++k) yv[k] = yn[k];
+#pragma unroll
+            for (int k = 0; k < Gr::NX; ++k) xv[k] = xn[k];
+#pragma unroll
+            for (int k = 0; k < Gr::NW; ++k) wv[k] = wn[k];
+        }
+    }
+    if (act) {
+        if (acc)
+            Gr::add_out(out + (i64)r * OD, u, sum);
+        else
+            Gr::store_out(out + (i64)r * OD, u, sum);
+    }
+}
+
+template <int G, bool YV>
+__device__ __forceinline__ void fwd_dispatch(int grp, int r, int u, const int *__restrict__ rowptr,
+                                             const int *__restrict__ src, const real_t *__restrict__ x,
+                                             const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                             real_t *__restrict__ out, bool acc) {
+    if (grp == G) {
+        fwd_group<G, YV>(r, u, rowptr, src, x, Y, W, out, acc);
+        return;
+    }
+    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1, YV>(grp, r, u, rowptr, src, x, Y, W, out, acc);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
+oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+        const real_t *__restrict__ Y, const real_t *__restrict__ W, real_t *__restrict__ out, int flags) {
+    // flags: bit0 add into out instead of overwriting it
+    const int w = uni(threadIdx.x >> 6);
+    const int grp = w / UCH, uc = w - grp * UCH;
+    fwd_dispatch<0, false>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out,
+                           (flags & 1) != 0);
+}
+
+// The forward with Y evaluated in the kernel from the edge vectors vec[E, 3]
+// (no Y tensor): each wave computes the harmonics of the edge it streams.
+extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
+oeq_fwd_vec(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+            const real_t *__restrict__ vec, const real_t *__restrict__ W, real_t *__restrict__ out) {
+    const int w = uni(threadIdx.x >> 6);
+    const int grp = w / UCH, uc = w - grp * UCH;
+    fwd_dispatch<0, true>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, vec, W, out, false);
+}
+
+// The atomic x-gradient is accumulated m-major inside each x block (so the
+// lanes of one atomic instruction address consecutive words); this restores the
+// u-major row layout in place, one node row per workgroup.
+extern "C" __global__ void __launch_bounds__(256)
+oeq_x_untranspose(real_t *__restrict__ gx) {
+    __shared__ real_t t[XT ? XD : 1];
+    real_t *row = gx + (i64)blockIdx.x * XD;
+    if (!XT) return;
+    for (int i = threadIdx.x; i < XD; i += 256) t[i] = row[i];
+    __syncthreads();
+    g_untranspose_row(t, row);
+}
+
+// ---------------------------------------------------------------------------
+// Y-gradient staging: per-wave lane-reduced rows in LDS, summed over the waves
+// of the workgroup (fixed order) every GY_TILE edges.  In the backward passes a
+// workgroup is one (receiver, path group); with several groups each writes its
+// partial Y-gradient rows to its own slice of the workspace and oeq_gy_combine
+// adds the slices in group order.
+// ---------------------------------------------------------------------------
+struct GyStage {
+    real_t red[UCH][GY_TILE][PY];
+};
+
+// Rows of width RW <= PY (default: the Y width); the radial VJP also stages its
+// 8-wide hidden-value gradients this way.
+template <int RW = YD>
+__device__ __forceinline__ void gy_push(GyStage &st, real_t *__restrict__ gY, int e, int j,
+                                        real_t (&gy)[RW], int lane, int wv, bool acc = false) {
+    static_assert(RW <= PY, "row wider than the reduction");
+    real_t v[PY];
+#pragma unroll
+    for (int k = 0; k < PY; ++k) v[k] = (k < RW) ? gy[k] : real_t(0);
+    wave_reduce_scatter(v, lane);
+    const int idx = lane >> (6 - LGPY);
+    const bool writer = (lane & ((1 << (6 - LGPY)) - 1)) == 0;
+    if (UCH == 1) {
+        if (writer && idx < RW) gY[(i64)e * RW + idx] = acc ? gY[(i64)e * RW + idx] + v[0] : v[0];
+    } else {
+        if (writer) st.red[wv][j][idx] = v[0];
+    }
+}
+
+template <int RW = YD>
+__device__ __forceinline__ void gy_flush(GyStage &st, real_t *__restrict__ gY, int base, int n, bool acc = false) {
+    if (UCH == 1) return;
+    __syncthreads();
+    for (int k = threadIdx.x; k < n * RW; k += UCH * 64) {
+        const int j = k / RW, m = k - j * RW;
+        real_t s = st.red[0][j][m];
+#pragma unroll
+        for (int w = 1; w < UCH; ++w) s += st.red[w][j][m];
+        real_t *dst = gY + (i64)(base + j) * RW + m;
+        *dst = acc ? *dst + s : s;
+    }
+    __syncthreads();
+}
+
+// flags: bit0 store grad_W, bit1 store grad_Y
+// GXMODE: 0 no x gradient, 1 atomic add into gx[src[e]], 2 store row h[e] (summed per sender later)
+template <int GXMODE, int G>
+__device__ __forceinline__ void bwd_group(GyStage &st, int r, int wv, int u, const int *__restrict__ rowptr,
+                                          const int *__restrict__ src, const real_t *__restrict__ x,
+                                          const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                          const real_t *__restrict__ g, real_t *__restrict__ gx,
+                                          real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
+    using Gr = BG<G>;
+    const int lane = threadIdx.x & 63;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;
+    const bool want_gw = (flags & 1) != 0, want_gy = (flags & 2) != 0;
+    real_t gv[Gr::NO];
+    Gr::load_g(g + (i64)r * OD, uu, gv);
+    if (!act) zero(gv);  // inactive lanes contribute nothing to the lane sums
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    if (e0 >= e1) return;
+    // software pipeline: the next edge's loads are in flight while this one computes
+    int s = uni(src[e0]);
+    real_t yv[YD], xv[Gr::NX], wv_[Gr::NW];
+    load_y(Y, e0, yv);
+    Gr::load_x(x + (i64)s * XD, uu, xv);
+    Gr::load_w(W + (i64)e0 * (P * U), uu, wv_);
+    for (int e = e0; e < e1; ++e) {
+        const int en = (e + 1 < e1) ? e + 1 : e;
+        const int sn = uni(src[en]);
+        real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
+        load_y(Y, en, yn);
+        Gr::load_x(x + (i64)sn * XD, uu, xn);
+        Gr::load_w(W + (i64)en * (P * U), uu, wn);
+        // keep the next edge's loads ahead of this edge's arithmetic
+        PIN_BWD();
+        const int j = uni((e - e0) % GY_TILE);
+        real_t gw[Gr::NW], gy[YD], gxp[Gr::NX];
+        zero(gw);
+        zero(gy);
+        zero(gxp);
+        Gr::template vjp<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
+        if (want_gw && act) Gr::store_w(gW + (i64)e * (P * U), u, gw);
+        if (want_gy) {
+            gy_push(st, gY, e, j, gy, lane, wv);
+            if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, gY, e - j, j + 1);
+        }
+        if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * XD, u, gxp);
+        if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * XD, u, gxp);
+        s = sn;
+#pragma unroll
+        for (int k = 0; k < YD; ++k) yv[k] = yn[k];
+#pragma unroll
+        for (int k = 0; k < Gr::NX; ++k) xv[k] = xn[k];
+#pragma unroll
+        for (int k = 0; k < Gr::NW; ++k) wv_[k] = wn[k];
+    }
+}
+
+template <int GXMODE, int G>
+__device__ __forceinline__ void bwd_dispatch(GyStage &st, int r, int grp, int wv, int u, const int *__restrict__ rowptr,
+                                             const int *__restrict__ src, const real_t *__restrict__ x,
+                                             const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                             const real_t *__restrict__ g, real_t *__restrict__ gx,
+                                             real_t *__restrict__ gY, real_t *__restrict__ gW, int flags) {
+    if (grp == G) {
+        bwd_group<GXMODE, G>(st, r, wv, u, rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+        return;
+    }
+    if constexpr (G + 1 < NGB)
+        bwd_dispatch<GXMODE, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, gx, gY, gW, flags);
+}
+
+template <int GXMODE>
+__device__ __forceinline__ void bwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
+                                         const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                         const real_t *__restrict__ W, const real_t *__restrict__ g,
+                                         real_t *__restrict__ gx, real_t *__restrict__ gY,
+                                         real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    __shared__ GyStage st;
+    const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
+    const int wv = uni(threadIdx.x >> 6);
+    bwd_dispatch<GXMODE, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, gx,
+                            gY + grp * gy_stride, gW, flags);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
+oeq_bwd_nogx(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+             const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
+             real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    bwd_body<0>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
+oeq_bwd_atomic(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+               const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
+               real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    bwd_body<1>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride);
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
+oeq_bwd_rows(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+             const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
+             real_t *__restrict__ h, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
+    bwd_body<2>(rowptr, src, x, Y, W, g, h, gY, gW, flags, gy_stride);
+}
+
+// Partial rows of several groups added in group order: out[i] = sum_g part[g n + i].
+extern "C" __global__ void __launch_bounds__(256)
+oeq_part_combine(const real_t *__restrict__ part, int groups, real_t *__restrict__ out, i64 n) {
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x) {
+        real_t s = part[i];
+        for (int gidx = 1; gidx < groups; ++gidx) s += part[gidx * n + i];
+        out[i] = s;
+    }
+}
+
+// Y-gradient of several path groups: gY = sum over groups of the partial rows,
+// in group order.
+extern "C" __global__ void __launch_bounds__(256)
+oeq_gy_combine(const real_t *__restrict__ part, real_t *__restrict__ gY, i64 n) {
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x) {
+        real_t s = part[i];
+#pragma unroll
+        for (int gidx = 1; gidx < NGB; ++gidx) s += part[gidx * n + i];
+        gY[i] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Deterministic x gradient: gx[s] = sum of h[e] over the sender's edges, in the
+// sender CSR's (increasing edge id) order.
+// ---------------------------------------------------------------------------
+extern "C" __global__ void __launch_bounds__(256)
+oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
+               const real_t *__restrict__ h, real_t *__restrict__ gx, int n_nodes) {
+    const int s = blockIdx.x;
+    if (s >= n_nodes) return;
+    const int k0 = uni(srowptr[s]), k1 = uni(srowptr[s + 1]);
+    for (i64 c = threadIdx.x; c < XD; c += 256) {
+        real_t acc = real_t(0);
+        int k = k0;
+        // eight rows in flight, added in edge order
+        for (; k + 8 <= k1; k += 8) {
+            real_t t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) t[j] = h[(i64)uni(sperm[k + j]) * XD + c];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc += t[j];
+        }
+        for (; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * XD + c];
+        gx[(i64)s * XD + c] = acc;
+    }
+}

@@ -1,0 +1,177 @@
+// Double backward.
+
+// ---------------------------------------------------------------------------
+// Double backward.  TM: which tangents are present (1 gg_x, 2 gg_Y, 4 gg_W).
+//   d_grad_out = f(ggx,Y,W) + f(x,ggY,W) + f(x,Y,ggW)      (receiver-local)
+//   d_W = BW(ggx,Y,g) + BW(x,ggY,g),  d_Y = BY(ggx,W,g) + BY(x,ggW,g)
+//   d_x = Bx(ggY,W,g) + Bx(Y,ggW,g)                         (to senders)
+// OUT: the outputs the kernel is built for (1 d_W, 2 d_Y, 4 d_grad_out, 8 d_x); a
+// kernel for a subset holds fewer live registers.
+// flags: bit0 d_W, bit1 d_Y, bit2 d_grad_out, bits 3-4 d_x mode (0 none, 1 atomic, 2 rows),
+//        bits 5-8 add into d_W / d_Y / d_grad_out / the d_x rows instead of overwriting
+// ---------------------------------------------------------------------------
+constexpr int DW = 1, DY = 2, DG = 4, DX = 8;
+
+template <int TM, int OUT, int G>
+__device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, const int *__restrict__ rowptr,
+                                           const int *__restrict__ src, const real_t *__restrict__ x,
+                                           const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                           const real_t *__restrict__ g, const real_t *__restrict__ ggx,
+                                           const real_t *__restrict__ ggY, const real_t *__restrict__ ggW,
+                                           real_t *__restrict__ dx, real_t *__restrict__ dY,
+                                           real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {
+    using Gr = BG<G>;
+    const int lane = threadIdx.x & 63;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;
+    const bool want_dw = (OUT & DW) && (flags & 1) != 0, want_dy = (OUT & DY) && (flags & 2) != 0,
+               want_dg = (OUT & DG) && (flags & 4) != 0;
+    const int dxmode = (OUT & DX) ? (flags >> 3) & 3 : 0;
+    // add into the outputs instead of overwriting (one pass per tangent)
+    const bool acc_dw = (flags & 32) != 0, acc_dy = (flags & 64) != 0, acc_dg = (flags & 128) != 0,
+               acc_h = (flags & 256) != 0;
+    constexpr bool HAS_DX = (TM & 6) != 0 && (OUT & DX) != 0;
+    constexpr bool GW_ = (OUT & DW) != 0, GY_ = (OUT & DY) != 0, GX_ = (OUT & DX) != 0;
+    real_t gv[Gr::NO];
+    Gr::load_g(g + (i64)r * OD, uu, gv);
+    if (!act) zero(gv);
+    real_t dgacc[(OUT & DG) ? Gr::NO : 1];
+    zero(dgacc);
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    // per-edge operands (unused ones are dropped by the compiler for a given TM)
+    struct Ops {
+        real_t y[YD], x[Gr::NX], w[Gr::NW], tx[Gr::NX], ty[YD], tw[Gr::NW];
+    };
+    auto load = [&](int e, int s, Ops &o) {
+        load_y(Y, e, o.y);
+        Gr::load_x(x + (i64)s * XD, uu, o.x);
+        Gr::load_w(W + (i64)e * (P * U), uu, o.w);
+        if (TM & 1) Gr::load_x(ggx + (i64)s * XD, uu, o.tx);
+        if (TM & 2) load_y(ggY, e, o.ty);
+        if (TM & 4) Gr::load_w(ggW + (i64)e * (P * U), uu, o.tw);
+    };
+    if (e0 < e1) {
+        int s = uni(src[e0]);
+        Ops cur;
+        load(e0, s, cur);
+        for (int e = e0; e < e1; ++e) {
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            Ops nxt;
+            load(en, sn, nxt);
+            // keep the next edge's loads ahead of this edge's arithmetic
+            PIN_BWD();
+            const int j = uni((e - e0) % GY_TILE);
+            real_t dw[Gr::NW], dy[YD], dxp[Gr::NX];
+            zero(dw);
+            zero(dy);
+            zero(dxp);
+            if constexpr ((TM & 1) != 0) {
+                if constexpr ((OUT & DG) != 0)
+                    if (want_dg) Gr::edge(cur.tx, cur.y, cur.w, dgacc);
+                if constexpr (GW_ || GY_) Gr::template vjp<GW_, GY_, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
+            }
+            if constexpr ((TM & 2) != 0) {
+                if constexpr ((OUT & DG) != 0)
+                    if (want_dg) Gr::edge(cur.x, cur.ty, cur.w, dgacc);
+                if constexpr (GW_ || GX_) Gr::template vjp<GW_, false, GX_>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
+            }
+            if constexpr ((TM & 4) != 0) {
+                if constexpr ((OUT & DG) != 0)
+                    if (want_dg) Gr::edge(cur.x, cur.y, cur.tw, dgacc);
+                if constexpr (GY_ || GX_) Gr::template vjp<false, GY_, GX_>(cur.x, cur.y, cur.tw, gv, dw, dy, dxp);
+            }
+            if (want_dw && act) {
+                if (acc_dw)
+                    Gr::add_w(dW + (i64)e * (P * U), u, dw);
+                else
+                    Gr::store_w(dW + (i64)e * (P * U), u, dw);
+            }
+            if (want_dy) {
+                gy_push(st, dY, e, j, dy, lane, wv, acc_dy);
+                if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, dY, e - j, j + 1, acc_dy);
+            }
+            if (HAS_DX && dxmode == 1 && act) Gr::atomic_x(dx + (i64)s * XD, u, dxp);
+            if (HAS_DX && dxmode == 2 && act) {
+                if (acc_h)
+                    Gr::add_x(dx + (i64)e * XD, u, dxp);
+                else
+                    Gr::store_x(dx + (i64)e * XD, u, dxp);
+            }
+            s = sn;
+            cur = nxt;
+        }
+    }
+    if constexpr ((OUT & DG) != 0)
+    if (want_dg && act) {
+        if (acc_dg)
+            Gr::add_out(dg + (i64)r * OD, u, dgacc);
+        else
+            Gr::store_out(dg + (i64)r * OD, u, dgacc);
+    }
+}
+
+template <int TM, int OUT, int G>
+__device__ __forceinline__ void dbwd_dispatch(GyStage &st, int r, int grp, int wv, int u, const int *__restrict__ rowptr,
+                                              const int *__restrict__ src, const real_t *__restrict__ x,
+                                              const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                              const real_t *__restrict__ g, const real_t *__restrict__ ggx,
+                                              const real_t *__restrict__ ggY, const real_t *__restrict__ ggW,
+                                              real_t *__restrict__ dx, real_t *__restrict__ dY,
+                                              real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {
+    if (grp == G) {
+        dbwd_group<TM, OUT, G>(st, r, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
+        return;
+    }
+    if constexpr (G + 1 < NGB)
+        dbwd_dispatch<TM, OUT, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg,
+                                      flags);
+}
+
+template <int TM, int OUT>
+__device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
+                                          const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                          const real_t *__restrict__ W, const real_t *__restrict__ g,
+                                          const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,
+                                          const real_t *__restrict__ ggW, real_t *__restrict__ dx,
+                                          real_t *__restrict__ dY, real_t *__restrict__ dW,
+                                          real_t *__restrict__ dg, int flags, i64 gy_stride) {
+    __shared__ GyStage st;
+    const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
+    const int wv = uni(threadIdx.x >> 6);
+    dbwd_dispatch<TM, OUT, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx,
+                         dY + grp * gy_stride, dW, dg, flags);
+}
+
+// oeq_dbwd_<TM>: every output in one pass.  oeq_dbwd_<TM>_<OUT>: the passes of
+// the split double backward (d_W; d_Y and d_x; d_grad_out is left to the
+// forward kernel, one accumulating launch per tangent).
+#define OEQ_DBWD_KERNEL(NAME, TM, OUT)                                                              \
+    extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY NAME(                      \
+        const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x, \
+        const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,  \
+        const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,                            \
+        const real_t *__restrict__ ggW, real_t *__restrict__ dx, real_t *__restrict__ dY,          \
+        real_t *__restrict__ dW, real_t *__restrict__ dg, int flags, i64 gy_stride) {              \
+        dbwd_body<TM, OUT>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags, gy_stride); \
+    }
+OEQ_DBWD_KERNEL(oeq_dbwd_1, 1, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_2, 2, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_3, 3, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_4, 4, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_5, 5, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_6, 6, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_7, 7, 15)
+// d_W = BW(gg_x,Y,g) + BW(x,gg_Y,g): reads no weights
+OEQ_DBWD_KERNEL(oeq_dbwd_1_1, 1, 1)
+OEQ_DBWD_KERNEL(oeq_dbwd_2_1, 2, 1)
+OEQ_DBWD_KERNEL(oeq_dbwd_3_1, 3, 1)
+// d_Y and d_x of several tangents in one pass over W and gg_W
+OEQ_DBWD_KERNEL(oeq_dbwd_3_10, 3, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_5_10, 5, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_6_10, 6, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_7_10, 7, 10)
+// one tangent: d_Y = BY(gg_x,W,g); d_x = Bx(gg_Y,W,g); d_Y, d_x = BY(x,gg_W,g), Bx(Y,gg_W,g)
+OEQ_DBWD_KERNEL(oeq_dbwd_1_2, 1, 2)
+OEQ_DBWD_KERNEL(oeq_dbwd_2_8, 2, 8)
+OEQ_DBWD_KERNEL(oeq_dbwd_4_10, 4, 10)
