@@ -49,6 +49,12 @@ EDGE_CASES = {
     "u1_l3_f64": synth.Workload("u1_l3_f64", 40, 9, synth._irr("1x3o+1x1e"), 3, 3, "f64", "unit", 32),
     # U = 8 with Y degrees 0..1 only (padded lane reduction) and outputs up to l=2
     "u8_l1_f32": synth.Workload("u8_l1_f32", 50, 12, synth._irr("8x0e+8x1o+8x2e"), 1, 2, "f32", "unit", 33),
+    # the largest multiplicity: 16 waves per workgroup (register-capped kernels)
+    "u1024_f32": synth.Workload("u1024_f32", 24, 5, synth._irr("1024x0e+1024x1o"), 2, 2, "f32", "unit", 34),
+    # one hub receiver with 3,000 distinct senders (a long edge loop, 94 Y tiles) among
+    # 3,099 receivers of one edge each
+    "hub_u32_f32": synth.Workload("hub_u32_f32", 3100, 0, synth._irr("32x0e+32x1o"), 3, 3, "f32", "unit", 35,
+                                  degrees=(3000,) + (1,) * 3099),
 }
 SMALL = {**REDUCED, **EDGE_CASES}
 
@@ -110,7 +116,8 @@ def test_bwd_partial_outputs(name):
 
 
 @pytest.mark.parametrize("mode", ["atomic", "deterministic"])
-@pytest.mark.parametrize("name", ["mace_large_fp32", "wide_proxy_fp32", "ragged_u96_f32", "tiny_fp64"])
+@pytest.mark.parametrize("name", ["mace_large_fp32", "wide_proxy_fp32", "ragged_u96_f32", "tiny_fp64", "u1024_f32",
+                                  "hub_u32_f32"])
 def test_hvp_parity(name, mode):
     """Double backward with a tangent on x only (the HVP of the workloads)."""
     wl, d, inp, g, plan = _case(name)
@@ -128,7 +135,7 @@ def test_hvp_parity(name, mode):
 
 @pytest.mark.parametrize("mode", ["atomic", "deterministic"])
 @pytest.mark.parametrize("mask", [1, 2, 3, 4, 5, 6, 7])
-@pytest.mark.parametrize("name", ["u8_l1_f32", "u1_l3_f64", "ragged_u96_f32"])
+@pytest.mark.parametrize("name", ["u8_l1_f32", "u1_l3_f64", "ragged_u96_f32", "u1024_f32"])
 def test_dbwd_all_tangents(name, mask, mode):
     wl, d, inp, g, plan = _case(name)
     tx = synth.extra_normal(wl, inp["x"].shape, 0)
@@ -198,7 +205,7 @@ def test_csr_check():
         oeq.oeq_csr_check(rp, bad)
 
 
-@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "ragged_u96_f32"])
+@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "ragged_u96_f32", "hub_u32_f32"])
 def test_bitwise_repeatable(name):
     """The forward and the deterministic backward are bitwise repeatable; the
     atomic backward agrees with them within the tolerance."""
