@@ -203,18 +203,20 @@ inline oeq_status gemm(oeq_plan *p, int M, int N, int K, const void *A, int64_t 
         splits = (K + kchunk - 1) / kchunk;
     }
     if (splits < 1) splits = 1;
-    int ta_i = ta ? 1 : 0, tb_i = tb ? 1 : 0;
+
     void *dst = splits > 1 ? part : C;
     int64_t ldd = splits > 1 ? N : ldc;
     int64_t stride = static_cast<int64_t>(M) * N;
     float af = static_cast<float>(alpha);
     void *ap = p->dtype == OEQ_F64 ? static_cast<void *>(&alpha) : static_cast<void *>(&af);
-    void *args[] = {&M, &N, &K, &A, &lda, &ta_i, &B, &ldb, &tb_i, &dst, &ldd, &stride, &kchunk, ap};
+    if (ta && tb) return fail(OEQ_ERR_UNSUPPORTED, "both operands transposed");
+    void *args[] = {&M, &N, &K, &A, &lda, &B, &ldb, &dst, &ldd, &stride, &kchunk, ap};
     // 128-wide tile sides where the matrix fills them; fp64 keeps 64 x 64 (its 128-wide tiles
     // hold one wave per SIMD and ran slower, as did 128 rows over a 64-row matrix)
     const bool wide = p->dtype == OEQ_F32;
     const int bm = wide && M >= 128 ? 128 : 64, bn = wide && N >= 128 ? 128 : 64;
-    const std::string kname = "oeq_gemm_" + std::to_string(bm) + "x" + std::to_string(bn);
+    const std::string kname = "oeq_gemm_" + std::to_string(bm) + "x" + std::to_string(bn) + "_" + (ta ? "1" : "0") +
+                              (tb ? "1" : "0");
     const char *name = kname.c_str();
     hipFunction_t fn = nullptr;
     std::string why;

@@ -3,7 +3,8 @@
 // ---------------------------------------------------------------------------
 // Dense matrix products on the matrix cores (the radial-weight MLP).
 //   C[M,N] = alpha op(A)[M,K] op(B)[K,N]   (row-major; op = identity or transpose)
-// A workgroup of 4 waves owns a BM x BN tile of C (oeq_gemm_<BM>x<BN>, 64 or 128 each);
+// A workgroup of 4 waves owns a BM x BN tile of C (oeq_gemm_<BM>x<BN>_<TA><TB>, sides 64 or 128,
+// TA / TB the transposed operands);
 // each wave a quarter, as blocks of the 16x16x4 MFMA (v_mfma_f32_16x16x4f32 /
 // v_mfma_f64_16x16x4f64).  K advances 32 at a time through LDS.  blockIdx.z splits K: split s covers
 // [s*kchunk, (s+1)*kchunk) and writes its tile to C + s*split_stride; with more
@@ -28,11 +29,12 @@ constexpr int GK = 32;
 
 // Workgroup tile GBM x BN (64 or 128 each): 4 waves as 2 x 2, each (GBM/2) x (BN/2) in
 // 16x16 blocks, K staged GK at a time through LDS with the next chunk's loads in registers.
-template <int GBM, int BN>
-__device__ __forceinline__ void gemm_body(int M, int N, int K, const real_t *__restrict__ A, i64 lda, int ta,
-                                          const real_t *__restrict__ B, i64 ldb, int tb, real_t *__restrict__ C,
+// TA / TB: A stored [K, M] / B stored [N, K] (transposed operands).
+template <int GBM, int BN, bool TA, bool TB>
+__device__ __forceinline__ void gemm_body(int M, int N, int K, const real_t *__restrict__ A, i64 lda,
+                                          const real_t *__restrict__ B, i64 ldb, real_t *__restrict__ C,
                                           i64 ldc, i64 split_stride, int kchunk, real_t alpha) {
-    constexpr int BI = GBM / 32, BJ = BN / 32;           // 16x16 blocks per wave
+    constexpr int BI = GBM / 32, BJ = BN / 32;              // 16x16 blocks per wave
     constexpr int LA = GBM * GK / 256, LB = BN * GK / 256;  // elements per thread per chunk
     __shared__ real_t As[GBM][GK + 1];
     __shared__ real_t Bs[GK][BN + 1];
@@ -46,49 +48,41 @@ __device__ __forceinline__ void gemm_body(int M, int N, int K, const real_t *__r
     for (int i = 0; i < BI; ++i)
 #pragma unroll
         for (int j = 0; j < BJ; ++j) acc[i][j] = mfma_acc{0, 0, 0, 0};
+    // Consecutive threads walk the contiguous dimension of each stored operand.  Element q
+    // of a thread sits at (row, k) = (am + q*AMS, ak + q*AKS) of the A tile and
+    // (bk + q*BKS, bn + q*BNS) of the B tile: affine in q, so no per-element state.
+    constexpr int AMS = TA ? 0 : 256 / GK, AKS = TA ? 256 / GBM : 0;
+    constexpr int BKS = TB ? 0 : 256 / BN, BNS = TB ? 256 / GK : 0;
+    const int am = TA ? t % GBM : t / GK, ak = TA ? t / GBM : t % GK;
+    const int bn = TB ? t / GK : t % BN, bk = TB ? t % GK : t / BN;
+    const i64 aoff = TA ? (i64)ak * lda + am : (i64)am * lda + ak;           // at q = 0
+    const i64 aq = TA ? (i64)AKS * lda : (i64)AMS * lda;                       // per q
+    const i64 boff = TB ? (i64)bn * ldb + bk : (i64)bk * ldb + bn;
+    const i64 bq = TB ? (i64)BNS * ldb : (i64)BKS * ldb;
     real_t ra[LA], rb[LB];
-    // consecutive threads walk the contiguous dimension of each stored operand
-    auto a_at = [&](int q, int &m, int &k) {
-        const int idx = t + q * 256;
-        if (ta) { k = idx / GBM; m = idx % GBM; } else { m = idx / GK; k = idx % GK; }
-    };
-    auto b_at = [&](int q, int &n, int &k) {
-        const int idx = t + q * 256;
-        if (tb) { n = idx / GK; k = idx % GK; } else { k = idx / BN; n = idx % BN; }
-    };
+    // Out-of-range elements read the chunk's first element (always valid); they are
+    // zeroed when stashed, so the loads themselves carry no dependence and stay in flight.
+    auto a_ok = [&](int q, int kl) { return (m0 + am + q * AMS < M) && (ak + q * AKS < kl); };
+    auto b_ok = [&](int q, int kl) { return (n0 + bn + q * BNS < N) && (bk + q * BKS < kl); };
     auto fetch = [&](int k0) {
+        const real_t *Ab = TA ? A + (i64)k0 * lda + m0 : A + (i64)m0 * lda + k0;
+        const real_t *Bb = TB ? B + (i64)n0 * ldb + k0 : B + (i64)k0 * ldb + n0;
+        const int kl = ke - k0;  // K values left in this chunk
 #pragma unroll
-        for (int q = 0; q < LA; ++q) {
-            int m, k;
-            a_at(q, m, k);
-            const int gm = m0 + m, gk = k0 + k;
-            ra[q] = (gm < M && gk < ke) ? (ta ? A[(i64)gk * lda + gm] : A[(i64)gm * lda + gk]) : real_t(0);
-        }
+        for (int q = 0; q < LA; ++q) ra[q] = Ab[a_ok(q, kl) ? aoff + q * aq : 0];
 #pragma unroll
-        for (int q = 0; q < LB; ++q) {
-            int n, k;
-            b_at(q, n, k);
-            const int gn = n0 + n, gk = k0 + k;
-            rb[q] = (gn < N && gk < ke) ? (tb ? B[(i64)gn * ldb + gk] : B[(i64)gk * ldb + gn]) : real_t(0);
-        }
+        for (int q = 0; q < LB; ++q) rb[q] = Bb[b_ok(q, kl) ? boff + q * bq : 0];
     };
-    auto stash = [&]() {
+    auto stash = [&](int k0) {
+        const int kl = ke - k0;
 #pragma unroll
-        for (int q = 0; q < LA; ++q) {
-            int m, k;
-            a_at(q, m, k);
-            As[m][k] = ra[q];
-        }
+        for (int q = 0; q < LA; ++q) As[am + q * AMS][ak + q * AKS] = a_ok(q, kl) ? ra[q] : real_t(0);
 #pragma unroll
-        for (int q = 0; q < LB; ++q) {
-            int n, k;
-            b_at(q, n, k);
-            Bs[k][n] = rb[q];
-        }
+        for (int q = 0; q < LB; ++q) Bs[bk + q * BKS][bn + q * BNS] = b_ok(q, kl) ? rb[q] : real_t(0);
     };
     if (kb < ke) fetch(kb);
     for (int k0 = kb; k0 < ke; k0 += GK) {
-        stash();
+        stash(k0);
         __syncthreads();
         if (k0 + GK < ke) fetch(k0 + GK);
 #pragma unroll
@@ -105,6 +99,16 @@ __device__ __forceinline__ void gemm_body(int M, int N, int K, const real_t *__r
         }
         __syncthreads();
     }
+    real_t *Ct = C + (i64)(m0 + wr) * ldc + n0 + wc + (l & 15);
+    if (m0 + GBM <= M && n0 + BN <= N) {  // interior tile: no bounds tests
+#pragma unroll
+        for (int i = 0; i < BI; ++i)
+#pragma unroll
+            for (int j = 0; j < BJ; ++j)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Ct[(i64)(16 * i + mfma_row(l, v)) * ldc + 16 * j] = alpha * acc[i][j][v];
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < BI; ++i)
 #pragma unroll
@@ -116,16 +120,20 @@ __device__ __forceinline__ void gemm_body(int M, int N, int K, const real_t *__r
             }
 }
 
-#define OEQ_GEMM_KERNEL(BM, BN)                                                                            \
-    extern "C" __global__ void __launch_bounds__(256) oeq_gemm_##BM##x##BN(                                \
-        int M, int N, int K, const real_t *__restrict__ A, i64 lda, int ta, const real_t *__restrict__ B,  \
-        i64 ldb, int tb, real_t *__restrict__ C, i64 ldc, i64 split_stride, int kchunk, real_t alpha) {    \
-        gemm_body<BM, BN>(M, N, K, A, lda, ta, B, ldb, tb, C, ldc, split_stride, kchunk, alpha);           \
+#define OEQ_GEMM_KERNEL(BM, BN, TA, TB)                                                                   \
+    extern "C" __global__ void __launch_bounds__(256) oeq_gemm_##BM##x##BN##_##TA##TB(                    \
+        int M, int N, int K, const real_t *__restrict__ A, i64 lda, const real_t *__restrict__ B, i64 ldb, \
+        real_t *__restrict__ C, i64 ldc, i64 split_stride, int kchunk, real_t alpha) {                     \
+        gemm_body<BM, BN, TA != 0, TB != 0>(M, N, K, A, lda, B, ldb, C, ldc, split_stride, kchunk, alpha); \
     }
-OEQ_GEMM_KERNEL(64, 64)
-OEQ_GEMM_KERNEL(64, 128)
-OEQ_GEMM_KERNEL(128, 64)
-OEQ_GEMM_KERNEL(128, 128)
+#define OEQ_GEMM_SHAPES(TA, TB)          \
+    OEQ_GEMM_KERNEL(64, 64, TA, TB)      \
+    OEQ_GEMM_KERNEL(64, 128, TA, TB)     \
+    OEQ_GEMM_KERNEL(128, 64, TA, TB)     \
+    OEQ_GEMM_KERNEL(128, 128, TA, TB)
+OEQ_GEMM_SHAPES(0, 0)
+OEQ_GEMM_SHAPES(0, 1)
+OEQ_GEMM_SHAPES(1, 0)
 
 // First stage of an ordered sum of many partial rows: part [rows, n] -> out
 // [ceil(rows / 32), n], chunk c holding rows 32c .. 32c+31 added in order.
