@@ -165,6 +165,36 @@ oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
     return launch(p, "oeq_fwd_radial", static_cast<unsigned>(N), fwd_block(p), s, args);
 }
 
+}  // extern "C"
+
+namespace {
+// the rest of the radial backward from dh (E x 8 in the workspace): dpre = dh silu'(pre) in
+// place, gW1 = B^T dpre / sqrt(8), dB = dpre W1^T / sqrt(8), then grad_vec through r = |vec|
+oeq_status radial_vjp_tail(oeq_plan *p, int64_t E, const void *vec, double r_cut, const void *W1, void *gvec,
+                           void *gW1, char *ws, const RadialWs &w, hipStream_t s) {
+    if (!gvec && !gW1) return OEQ_OK;
+    oeq_status st;
+    const int H = kFusedHidden, Ei = static_cast<int>(E);
+    const double s8 = 1.0 / std::sqrt(double(kRadialNB));
+    void *Bp = ws + w.B, *dh = ws + w.dh;
+    void *dargs[] = {&Bp, &W1, const_cast<int *>(&H), &dh, &E};
+    if ((st = edge_launch(p, "oeq_radial_dpre", E * H, dargs, s)) != OEQ_OK) return st;
+    if (gW1 && (st = gemm(p, kRadialNB, H, Ei, Bp, kRadialNB, true, dh, H, false, gW1, H, s8, w.splitsW1,
+                          ws + w.pW1, s)) != OEQ_OK)
+        return st;
+    if (!gvec) return OEQ_OK;
+    void *dB = ws + w.dB;
+    if ((st = gemm(p, Ei, kRadialNB, H, dh, H, false, W1, H, true, dB, kRadialNB, s8, 1, nullptr, s)) != OEQ_OK)
+        return st;
+    float rcf = static_cast<float>(r_cut);
+    void *rc = p->dtype == OEQ_F64 ? static_cast<void *>(&r_cut) : static_cast<void *>(&rcf);
+    void *gargs[] = {&vec, rc, &dB, &gvec, &E};
+    return edge_launch(p, "oeq_radial_gvec", E, gargs, s);
+}
+}  // namespace
+
+extern "C" {
+
 oeq_status oeq_workspace_size_radial(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, size_t *bytes) {
     if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
     if (N < 0 || E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
@@ -209,8 +239,26 @@ oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
     if ((st = radial_hidden(p, E, vec, r_cut, H, W1, ws, w.rad, s)) != OEQ_OK) return st;
     const int G = static_cast<int>(p->rad_groups.size());
     const bool want_dh = gvec || gW1;
+    const int Ei = static_cast<int>(E);
+    const double s8 = 1.0 / std::sqrt(double(kRadialNB));
+    void *hid = ws + w.rad.h, *dh = ws + w.rad.dh;
+    if (p->rad_compose) {
+        // W = h W2 / sqrt(8) per edge, the convolution VJP, then gW2 = h^T gW / sqrt(8) and
+        // dh = gW W2^T / sqrt(8): the same sums with W and its gradient held in the workspace
+        void *Wb = ws + w.wbuf, *gWb = (gW2 || want_dh) ? ws + w.gwbuf : nullptr;
+        if ((st = gemm(p, Ei, PU, H, hid, H, false, W2, PU, false, Wb, PU, s8, 1, nullptr, s)) != OEQ_OK) return st;
+        if ((st = oeq_tp_conv_bwd(plan, N, E, rowptr, src, x, Y, Wb, g, gx, gY, gWb, mode, ws + w.conv_off,
+                                  w.conv.bytes, stream)) != OEQ_OK)
+            return st;
+        if (gW2 && (st = gemm(p, H, PU, Ei, hid, H, true, gWb, PU, false, gW2, PU, s8, w.rad.splitsW2,
+                              ws + w.rad.pW2, s)) != OEQ_OK)
+            return st;
+        if (want_dh && (st = gemm(p, Ei, H, PU, gWb, PU, false, W2, PU, true, dh, H, s8, 1, nullptr, s)) != OEQ_OK)
+            return st;
+        return radial_vjp_tail(p, E, vec, r_cut, W1, gvec, gW1, ws, w.rad, s);
+    }
     int flags = (gW2 ? 1 : 0) | (gY ? 2 : 0) | (want_dh ? 4 : 0);
-    void *hid = ws + w.rad.h, *dh = ws + w.rad.dh, *w2p = ws + w.w2p;
+    void *w2p = ws + w.w2p;
     void *gy_target = G > 1 ? ws + w.gyp : gY, *dh_target = G > 1 ? ws + w.dhp : dh;
     int64_t gy_stride = G > 1 ? E * p->YD : 0, dh_stride = G > 1 ? E * H : 0;
     const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(G));
@@ -242,24 +290,7 @@ oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
     // sum of the receivers' partial rows, in receiver order
     if (gW2 && (st = ordered_sum(p, w2p, static_cast<int>(N), kFusedHidden, PU, gW2, PU, ws + w.w2s, s)) != OEQ_OK)
         return st;
-    if (!want_dh) return OEQ_OK;
-    // the rest of the radial backward from dh: dpre, gW1 = B^T dpre / sqrt(8), dB, grad_vec
-    void *Bp = ws + w.rad.B;
-    const int Ei = static_cast<int>(E);
-    const double s8 = 1.0 / std::sqrt(double(kRadialNB));
-    void *dargs[] = {&Bp, &W1, const_cast<int *>(&H), &dh, &E};
-    if ((st = edge_launch(p, "oeq_radial_dpre", E * H, dargs, s)) != OEQ_OK) return st;
-    if (gW1 && (st = gemm(p, kRadialNB, H, Ei, Bp, kRadialNB, true, dh, H, false, gW1, H, s8, w.rad.splitsW1,
-                          ws + w.rad.pW1, s)) != OEQ_OK)
-        return st;
-    if (!gvec) return OEQ_OK;
-    void *dB = ws + w.rad.dB;
-    if ((st = gemm(p, Ei, kRadialNB, H, dh, H, false, W1, H, true, dB, kRadialNB, s8, 1, nullptr, s)) != OEQ_OK)
-        return st;
-    float rcf = static_cast<float>(r_cut);
-    void *rc = p->dtype == OEQ_F64 ? static_cast<void *>(&r_cut) : static_cast<void *>(&rcf);
-    void *gargs[] = {&vec, rc, &dB, &gvec, &E};
-    return edge_launch(p, "oeq_radial_gvec", E, gargs, s);
+    return radial_vjp_tail(p, E, vec, r_cut, W1, gvec, gW1, ws, w.rad, s);
 }
 
 }  // extern "C"

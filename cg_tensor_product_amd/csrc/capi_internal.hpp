@@ -312,7 +312,7 @@ inline oeq_status radial_hidden(oeq_plan *p, int64_t E, const void *vec, double 
 struct RadVjpWs {
     RadialWs rad;
     Workspace conv;
-    size_t conv_off = 0, gyp = 0, dhp = 0, w2p = 0, w2s = 0, bytes = 0;
+    size_t conv_off = 0, gyp = 0, dhp = 0, w2p = 0, w2s = 0, wbuf = 0, gwbuf = 0, bytes = 0;
 };
 
 inline oeq_status radvjp_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, char *base, RadVjpWs *w) {
@@ -320,6 +320,17 @@ inline oeq_status radvjp_layout(const oeq_plan *p, int64_t N, int64_t E, bool de
     w->rad = radial_layout(p, E, kFusedHidden);
     size_t off = w->rad.bytes;
     w->conv_off = off;
+    if (p->rad_compose) {  // the convolution VJP's own workspace, then W and its gradient
+        oeq_status st = ws_layout(p, N, E, det, p->bwd_groups.size() > 1, base ? base + off : nullptr, &w->conv);
+        if (st != OEQ_OK) return st;
+        off += up(w->conv.bytes);
+        w->wbuf = off;
+        off += up(static_cast<size_t>(E) * PU * es);
+        w->gwbuf = off;
+        off += up(static_cast<size_t>(E) * PU * es);
+        w->bytes = off;
+        return OEQ_OK;
+    }
     oeq_status st = ws_layout(p, N, E, det, false, base ? base + off : nullptr, &w->conv);
     if (st != OEQ_OK) return st;
     off += up(w->conv.bytes);

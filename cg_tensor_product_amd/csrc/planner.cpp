@@ -267,16 +267,23 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         // estimate is under budget (estimates of 358 / 636 / 696 compiled to 394 registers /
         // spills / spills for the medium fp32 / large / medium fp64 configurations)
         const int max_g = std::max(1, 16 / p->uch), f = p->dtype == OEQ_F64 ? 2 : 1;
+        auto worst_of = [&](const std::vector<std::vector<int>> &groups) {
+            int worst = 0;
+            for (const auto &gr : groups)
+                worst = std::max(worst, group_registers(*p, gr, false) + 2 * 8 * static_cast<int>(gr.size()) * f);
+            return worst;
+        };
         for (int g = 1; g <= max_g; ++g) {
             auto cand = partition_paths(*p, false, g);
             p->rad_groups = cand;
-            int worst = 0;
-            for (const auto &gr : cand)
-                worst = std::max(worst, group_registers(*p, gr, false) + 2 * 8 * static_cast<int>(gr.size()) * f);
-            if (worst <= 400 || static_cast<int>(cand.size()) < g) break;
+            if (worst_of(cand) <= 400 || static_cast<int>(cand.size()) < g) break;
         }
         if (const char *e = std::getenv("OEQ_RAD_GROUPS"))
             p->rad_groups = partition_paths(*p, false, std::max(1, std::min(std::atoi(e), max_g)));
+        // a group that is still over the budget spills in the in-kernel pass (the medium fp64
+        // configuration's 9-path block: 12 ms against about 3 ms when composed)
+        p->rad_compose = worst_of(p->rad_groups) > 400;
+        if (const char *e = std::getenv("OEQ_RAD_COMPOSE")) p->rad_compose = std::atoi(e) != 0;
     }
     if (const char *s = std::getenv("OEQ_GY_TILE")) {
         const int v = std::atoi(s);

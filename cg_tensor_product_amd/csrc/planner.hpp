@@ -80,6 +80,9 @@ struct oeq_plan {
     // groups of the VJP that forms the radial weights in the kernel (it also holds the
     // hidden-width slices of W2 and of the W2 gradient per lane)
     std::vector<std::vector<int>> rad_groups;
+    // the VJP with in-kernel radial weights runs as W = h W2, the convolution VJP and two
+    // dense products instead (its groups do not fit registers)
+    bool rad_compose = false;
 
     std::string source;         // emitted HIP source
     std::vector<char> code;     // gfx950 code object

@@ -4,6 +4,8 @@ against the oracle (oracle/radial.py): the weights, and the gradients to the
 edge vectors and to both weight matrices, including hidden widths that are not
 multiples of the 16-wide matrix blocks, lengths beyond the cutoff and a zero
 vector."""
+import os
+
 import numpy as np
 import pytest
 
@@ -145,6 +147,19 @@ def test_fwd_radial_fused_parity(name):
     assert rel_l2(out.cpu().numpy(), ref) <= RTOL[wl.dtype]
 
 
+def _plan_with(wl, env):
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        return plan_for(wl)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
 @pytest.mark.parametrize("mode", ["atomic", "deterministic"])
 @pytest.mark.parametrize("name", ["tiny_fp64", "mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32",
                                   "ragged_u96_f32", "u1_l3_f64"])
@@ -152,9 +167,24 @@ def test_bwd_radial_fused_parity(name, mode):
     """The VJP with W formed in the kernel (hidden width 8) against the oracle:
     grad_x, grad_Y from the oracle VJP on the oracle's radial weights; grad_vec,
     grad_W1, grad_W2 from the oracle radial backward of the oracle's grad_W."""
+    _check_bwd_radial(name, mode, {})
+
+
+# the other route than the planned one: composed through W where the in-kernel pass
+# fits registers, in-kernel where the plan composes (the medium fp64 configuration)
+ROUTES = [("mace_medium_fp32", "1"), ("tiny_fp64", "1"), ("u1_l3_f64", "1"), ("mace_medium_fp64", "0")]
+
+
+@pytest.mark.parametrize("mode", ["atomic", "deterministic"])
+@pytest.mark.parametrize("name,compose", ROUTES)
+def test_bwd_radial_routes(name, compose, mode):
+    _check_bwd_radial(name, mode, {"OEQ_RAD_COMPOSE": compose})
+
+
+def _check_bwd_radial(name, mode, env):
     import oracle
     wl = SMALL[name]
-    plan = plan_for(wl)
+    plan = _plan_with(wl, env)
     d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
     inp = synth.generate(wl, d.P, d.out_dim, want=("x", "Y", "evec", "g"))
     rng = np.random.default_rng(22)
@@ -162,7 +192,7 @@ def test_bwd_radial_fused_parity(name, mode):
     W1 = rng.standard_normal((8, 8)).astype(dt)
     W2 = rng.standard_normal((8, plan.n_paths * plan.U)).astype(dt)
     dev = {k: to_dev(inp[k]) for k in ("rowptr", "src", "x", "Y", "evec", "g")}
-    print(f"[bwd radial] {name} {mode}", flush=True)
+    print(f"[bwd radial] {name} {mode} {env}", flush=True)
     res = oeq.oeq_tp_conv_bwd_radial(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["evec"], RC,
                                      to_dev(W1), to_dev(W2), dev["g"], mode=mode)
     again = oeq.oeq_tp_conv_bwd_radial(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["evec"], RC,
