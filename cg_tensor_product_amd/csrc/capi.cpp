@@ -211,7 +211,10 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
         const oeq_status r = oeq::get_kernel(*p, name.c_str(), &fn, &why);
         if (r != OEQ_OK) return fail(r, why);
         int scratch = 0;
-        *yes = hipFuncGetAttribute(&scratch, HIP_FUNC_ATTRIBUTE_LOCAL_SIZE_BYTES, fn) == hipSuccess && scratch > 0;
+        // a moderate spill costs less than a split. Measured on the fused kernels: 12, 144 and
+        // 196 bytes per lane ran as fast as or faster than their splits (fp64 gg_x+gg_Y, large
+        // gg_Y, fp64 gg_Y+gg_W); 276 bytes and up ran slower (large gg_x+gg_Y: 5.47 vs 4.85 ms)
+        *yes = hipFuncGetAttribute(&scratch, HIP_FUNC_ATTRIBUTE_LOCAL_SIZE_BYTES, fn) == hipSuccess && scratch > 200;
         return OEQ_OK;
     };
     const std::string T = std::to_string(tm);

@@ -111,6 +111,144 @@ void emit_row_move(std::ostringstream &o, const char *sig, const std::map<int, i
     o << "  }\n";
 }
 
+// All double-backward terms of one edge in one pass (TM: tangents present, 1 gg_x = tx,
+// 2 gg_Y = ty, 4 gg_W = tw), sharing what the separate forward and VJP calls would each
+// recompute:
+//   d_grad_out[m3] += w * sum C (tx y + x ty) + tw * sum C x y
+//   T[m1,m2] = sum_m3 C g[m3]  (once per path, not once per tangent)
+//   d_W += tx . (T y) + x . (T ty);  d_x[m1] += w (T ty)[m1] + tw (T y)[m1]
+//   d_Y[m2] += w (tx T)[m2] + tw (x T)[m2]
+void emit_dbwd_edge(std::ostringstream &o, const oeq_plan &p, const Local &L) {
+    o << "  template <int TM, bool GW, bool GY, bool GX>\n"
+         "  static __device__ __forceinline__ void dbwd_edge(const real_t (&x)[NX], const real_t (&y)[YD], "
+         "const real_t (&w)[NW], const real_t (&tx)[NX], const real_t (&ty)[YD], const real_t (&tw)[NW], "
+         "const real_t (&g)[NO], bool want_dg, real_t (&dg)[NO], real_t (&dw)[NW], real_t (&dy)[YD], "
+         "real_t (&dx)[NX]) {\n"
+         "    constexpr bool HX = (TM & 1) != 0, HY = (TM & 2) != 0, HW = (TM & 4) != 0;\n"
+         "    constexpr bool NQY = (HX && GW) || (HW && GX), NQT = HY && (GW || GX), NSX = HW && GY, NST = HX && GY;\n";
+    // d_grad_out
+    o << "    if (want_dg) {\n";
+    std::map<std::pair<int, int>, std::vector<int>> pairs;  // (x block, l2) -> paths
+    for (int k : L.paths) pairs[{p.paths[k].i1, p.paths[k].l2}].push_back(k);
+    for (const auto &gkv : pairs) {
+        const int i1 = gkv.first.first, l2 = gkv.first.second;
+        const int xo = L.xoff.at(i1);
+        std::set<std::pair<int, int>> used;
+        for (int k : gkv.second)
+            for (const auto &nz : p.paths[k].nz) used.insert({nz.m1, nz.m2});
+        o << "      { // x block " << i1 << " x Y l=" << l2 << "\n";
+        for (const auto &ab : used) {
+            const std::string xa = "[" + S(xo + ab.first) + "]", yb = "[" + S(l2 * l2 + ab.second) + "]";
+            const std::string nm = S(ab.first) + "_" + S(ab.second);
+            o << "        real_t z" << nm << ", u" << nm << ";";
+            o << " if constexpr (HW) z" << nm << " = x" << xa << " * y" << yb << ";";
+            o << " if constexpr (HX && HY) u" << nm << " = fmar(x" << xa << ", ty" << yb << ", tx" << xa << " * y" << yb
+              << "); else if constexpr (HX) u" << nm << " = tx" << xa << " * y" << yb << "; else if constexpr (HY) u"
+              << nm << " = x" << xa << " * ty" << yb << ";\n";
+        }
+        for (int k : gkv.second) {
+            const Path &pa = p.paths[k];
+            const int oo = L.ooff.at(pa.ob), wk = L.widx.at(k);
+            o << "        { // path " << k << "\n";
+            for (int m3 = 0; m3 < 2 * pa.l3 + 1; ++m3) {
+                bool first = true;
+                std::ostringstream l0, l1;
+                for (const auto &nz : pa.nz) {
+                    if (nz.m3 != m3) continue;
+                    const std::string nm = S(nz.m1) + "_" + S(nz.m2);
+                    l0 << " " << fma_term("s0", nz.c, "z" + nm, first);
+                    l1 << " " << fma_term("s1", nz.c, "u" + nm, first);
+                    first = false;
+                }
+                if (first) continue;
+                const std::string d = "dg[" + S(oo + m3) + "]";
+                o << "          if constexpr (HX || HY) { real_t s1;" << l1.str() << " " << d << " = fmar(w[" << wk
+                  << "], s1, " << d << "); }";
+                o << " if constexpr (HW) { real_t s0;" << l0.str() << " " << d << " = fmar(tw[" << wk << "], s0, " << d
+                  << "); }\n";
+            }
+            o << "        }\n";
+        }
+        o << "      }\n";
+    }
+    o << "    }\n";
+    // d_W, d_Y, d_x from T = C g
+    o << "    if constexpr (GW || GY || GX) {\n";
+    for (int k : L.paths) {
+        const Path &pa = p.paths[k];
+        const int xo = L.xoff.at(pa.i1), oo = L.ooff.at(pa.ob), wk = L.widx.at(k);
+        const int n1 = 2 * pa.l1 + 1, n2 = 2 * pa.l2 + 1, yo = pa.l2 * pa.l2;
+        o << "    { // path " << k << "\n";
+        std::map<std::pair<int, int>, std::vector<const NonZero *>> T;
+        for (const auto &nz : pa.nz) T[{nz.m1, nz.m2}].push_back(&nz);
+        for (const auto &tkv : T) {
+            const std::string nm = "T" + S(tkv.first.first) + "_" + S(tkv.first.second);
+            o << "      real_t " << nm << ";";
+            bool first = true;
+            for (const NonZero *nz : tkv.second) {
+                o << " " << fma_term(nm, nz->c, "g[" + S(oo + nz->m3) + "]", first);
+                first = false;
+            }
+            o << "\n";
+        }
+        o << "      if constexpr (GW || GX) {\n";
+        for (int a = 0; a < n1; ++a) {
+            std::ostringstream qy, qt;
+            bool first = true;
+            for (const auto &tkv : T) {
+                if (tkv.first.first != a) continue;
+                const std::string tn = "T" + S(a) + "_" + S(tkv.first.second);
+                const std::string yi = "[" + S(yo + tkv.first.second) + "]";
+                if (first) {
+                    qy << " qy = y" << yi << " * " << tn << ";";
+                    qt << " qt = ty" << yi << " * " << tn << ";";
+                } else {
+                    qy << " qy = fmar(y" << yi << ", " << tn << ", qy);";
+                    qt << " qt = fmar(ty" << yi << ", " << tn << ", qt);";
+                }
+                first = false;
+            }
+            if (first) continue;
+            const std::string xa = "[" + S(xo + a) + "]";
+            o << "        { real_t qy, qt; if constexpr (NQY) {" << qy.str() << " } if constexpr (NQT) {" << qt.str()
+              << " }";
+            o << " if constexpr (GW && HX) dw[" << wk << "] = fmar(tx" << xa << ", qy, dw[" << wk << "]);";
+            o << " if constexpr (GW && HY) dw[" << wk << "] = fmar(x" << xa << ", qt, dw[" << wk << "]);";
+            o << " if constexpr (GX && HY) dx" << xa << " = fmar(w[" << wk << "], qt, dx" << xa << ");";
+            o << " if constexpr (GX && HW) dx" << xa << " = fmar(tw[" << wk << "], qy, dx" << xa << "); }\n";
+        }
+        o << "      }\n";
+        o << "      if constexpr (GY) {\n";
+        for (int b = 0; b < n2; ++b) {
+            std::ostringstream sx, st;
+            bool first = true;
+            for (const auto &tkv : T) {
+                if (tkv.first.second != b) continue;
+                const std::string tn = "T" + S(tkv.first.first) + "_" + S(b);
+                const std::string xi = "[" + S(xo + tkv.first.first) + "]";
+                if (first) {
+                    sx << " sx = x" << xi << " * " << tn << ";";
+                    st << " st = tx" << xi << " * " << tn << ";";
+                } else {
+                    sx << " sx = fmar(x" << xi << ", " << tn << ", sx);";
+                    st << " st = fmar(tx" << xi << ", " << tn << ", st);";
+                }
+                first = false;
+            }
+            if (first) continue;
+            const std::string d = "dy[" + S(yo + b) + "]";
+            o << "        { real_t sx, st; if constexpr (NSX) {" << sx.str() << " } if constexpr (NST) {" << st.str()
+              << " }";
+            o << " if constexpr (HX) " << d << " = fmar(w[" << wk << "], st, " << d << ");";
+            o << " if constexpr (HW) " << d << " = fmar(tw[" << wk << "], sx, " << d << "); }\n";
+        }
+        o << "      }\n";
+        o << "    }\n";
+    }
+    o << "    }\n";
+    o << "  }\n";
+}
+
 void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int g, const std::vector<int> &paths) {
     const Local L = make_local(p, paths);
     o << "template <> struct " << name << "<" << g << "> {\n";
@@ -273,6 +411,7 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
         o << "    }\n";
     }
     o << "  }\n";
+    if (std::string(name) == "BG") emit_dbwd_edge(o, p, L);
     o << "};\n";
 }
 

@@ -35,7 +35,7 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
     real_t gv[Gr::NO];
     Gr::load_g(g + (i64)r * OD, uu, gv);
     if (!act) zero(gv);
-    real_t dgacc[(OUT & DG) ? Gr::NO : 1];
+    real_t dgacc[Gr::NO];  // dropped by the compiler when OUT has no DG
     zero(dgacc);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     // per-edge operands (unused ones are dropped by the compiler for a given TM)
@@ -66,20 +66,15 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
             zero(dw);
             zero(dy);
             zero(dxp);
-            if constexpr ((TM & 1) != 0) {
-                if constexpr ((OUT & DG) != 0)
-                    if (want_dg) Gr::edge(cur.tx, cur.y, cur.w, dgacc);
-                if constexpr (GW_ || GY_) Gr::template vjp<GW_, GY_, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
-            }
-            if constexpr ((TM & 2) != 0) {
-                if constexpr ((OUT & DG) != 0)
-                    if (want_dg) Gr::edge(cur.x, cur.ty, cur.w, dgacc);
-                if constexpr (GW_ || GX_) Gr::template vjp<GW_, false, GX_>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
-            }
-            if constexpr ((TM & 4) != 0) {
-                if constexpr ((OUT & DG) != 0)
-                    if (want_dg) Gr::edge(cur.x, cur.y, cur.tw, dgacc);
-                if constexpr (GY_ || GX_) Gr::template vjp<false, GY_, GX_>(cur.x, cur.y, cur.tw, gv, dw, dy, dxp);
+            if constexpr (OUT == DW) {
+                // the d_W-only pass, one tangent after the other: this order fits 256 registers
+                // in fp64 (two waves per SIMD) where the interleaved one needs 258
+                if constexpr ((TM & 1) != 0) Gr::template vjp<true, false, false>(cur.tx, cur.y, cur.w, gv, dw, dy, dxp);
+                if constexpr ((TM & 2) != 0) Gr::template vjp<true, false, false>(cur.x, cur.ty, cur.w, gv, dw, dy, dxp);
+            } else {
+                // every term of this edge in one pass (the g contraction is shared by the tangents)
+                Gr::template dbwd_edge<TM, GW_ && (TM & 3) != 0, GY_ && (TM & 5) != 0, GX_ && (TM & 6) != 0>(
+                    cur.x, cur.y, cur.w, cur.tx, cur.ty, cur.tw, gv, (OUT & DG) != 0 && want_dg, dgacc, dw, dy, dxp);
             }
             if (want_dw && act) {
                 if (acc_dw)
