@@ -150,7 +150,18 @@ def cpu_baseline(wl, d, inp, target_s=10.0):
         reps += 1
     return {"value": reps * inp["E"] / t, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"the whole workload ({inp['E']} edges): forward + VJP, {reps} repetition(s), "
-                      f"{t:.1f} s in total"}
+                      f"{t:.1f} s in total", "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():

@@ -101,7 +101,7 @@ oeq_status oeq_workspace_size(const oeq_plan *p, int64_t n_nodes, int64_t n_edge
     if (n_nodes < 0 || n_edges < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
     if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
     Workspace w;
-    oeq_status st = ws_layout(p, n_nodes, n_edges, mode == OEQ_BWD_DETERMINISTIC, p->bwd_groups.size() > 1,
+    oeq_status st = ws_layout(p, n_nodes, n_edges, mode == OEQ_BWD_DETERMINISTIC, gy_groups(p) > 1,
                               nullptr, &w);
     if (st != OEQ_OK) return st;
     *bytes = w.bytes;
@@ -180,31 +180,6 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
     // d_x = Bx(ggY,W,g) + Bx(Y,ggW,g) vanishes without a Y or W tangent
     const bool dx_live = dx && (tm & 6);
     const bool det = dx_live && mode == OEQ_BWD_DETERMINISTIC;
-    const bool gyp = dY && p->bwd_groups.size() > 1;
-    Workspace w;
-    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w)) != OEQ_OK) return st;
-    if (dx && !dx_live && (st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
-    int dxmode = 0;
-    void *dx_target = nullptr;
-    if (dx_live && !det) {
-        if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
-        dxmode = 1;
-        dx_target = dx;
-    } else if (det) {
-        if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
-        dxmode = 2;
-        dx_target = w.h;
-        if (p->x_unused && (st = fill_zero(p, w.h, E * p->XD, s)) != OEQ_OK) return st;
-    }
-    if (!dxmode && !dY && !dW && !dg) return OEQ_OK;
-    void *dy_target = gyp ? w.gy_part : dY;
-    int64_t gy_stride = gyp ? E * p->YD : 0;
-    const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(p->bwd_groups.size()));
-    auto pass = [&](const std::string &name, int flags) {
-        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dy_target, &dW, &dg, &flags,
-                        &gy_stride};
-        return launch(p, name.c_str(), grid, bwd_block(p), s, args);
-    };
     auto spills = [&](const std::string &name, bool *yes) {
         hipFunction_t fn = nullptr;
         std::string why;
@@ -224,15 +199,24 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
     //        level 1: oeq_dbwd_<tm>_10 in one pass; level 2: one pass per tangent
     //   d_grad_out = f(gg_x,Y,W) + f(x,gg_Y,W) + f(x,Y,gg_W)  forward kernel, accumulating
     const bool single = tm == 1 || tm == 2 || tm == 4;
-    const bool want_w = dW && (tm & 3), want_yx = (dY && (tm & 5)) || dxmode;
+    const bool want_w = dW && (tm & 3), want_yx = (dY && (tm & 5)) || dx_live;
     std::vector<std::string> yx1;  // level-1 d_Y / d_x pass
     if (want_yx) yx1.push_back(single ? (tm == 1 ? "oeq_dbwd_1_2" : tm == 2 ? "oeq_dbwd_2_8" : "oeq_dbwd_4_10")
                                       : "oeq_dbwd_" + T + "_10");
+    // One fused pass on the backward groups (oeq_dbwd_<t>) unless it spills; then the fused
+    // pass on the finer double-backward groups (oeq_dbwd_<t>_d), where those differ; then
+    // the split passes (on the double-backward groups).
+    const bool two_sets = p->dbwd_groups != p->bwd_groups;
+    std::string fused = "oeq_dbwd_" + T;
     int level = p->dbwd_split;  // 0 one fused pass, 1 or 2 split
     if (level < 0) {
         bool sp = false;
-        if ((st = spills("oeq_dbwd_" + T, &sp)) != OEQ_OK) return st;
+        if ((st = spills(fused, &sp)) != OEQ_OK) return st;
         level = 0;
+        if (sp && two_sets) {
+            fused = "oeq_dbwd_" + T + "_d";
+            if ((st = spills(fused, &sp)) != OEQ_OK) return st;
+        }
         if (sp) {
             level = 1;
             std::vector<std::string> k1 = yx1;
@@ -243,9 +227,46 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
             }
         }
     }
+    // Path groups of the kernels this call launches: oeq_dbwd_<t> is built on the backward
+    // groups; oeq_dbwd_<t>_d and every split pass on the double-backward groups. The grid
+    // must match: a kernel maps block b to receiver b / groups.
+    auto kernel_groups = [&](const std::string &name) {
+        const bool bwd_set = name.size() == 10 && name.compare(0, 9, "oeq_dbwd_") == 0;  // oeq_dbwd_<t>
+        return static_cast<int64_t>(bwd_set ? p->bwd_groups.size() : p->dbwd_groups.size());
+    };
+    const int64_t NG = level == 0 ? kernel_groups(fused) : static_cast<int64_t>(p->dbwd_groups.size());
+    const bool gyp = dY && NG > 1;
+    Workspace w;
+    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w)) != OEQ_OK) return st;
+    if (dx && !dx_live && (st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+    int dxmode = 0;
+    void *dx_target = nullptr;
+    if (dx_live && !det) {
+        if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+        dxmode = 1;
+        dx_target = dx;
+    } else if (det) {
+        if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
+        dxmode = 2;
+        dx_target = w.h;
+        if (p->x_unused && (st = fill_zero(p, w.h, E * p->XD, s)) != OEQ_OK) return st;
+    }
+    if (!dxmode && !dY && !dW && !dg) return OEQ_OK;
+    void *dy_target = gyp ? w.gy_part : dY;
+    int64_t gy_stride = gyp ? E * p->YD : 0;
+    const unsigned grid = static_cast<unsigned>(N * NG);
+    auto pass = [&](const std::string &name, int flags) {
+        // the kernel's own group count (the rule the kernel template applies); a grid of
+        // another size would map blocks past the last receiver
+        if (kernel_groups(name) != NG)
+            return fail(OEQ_ERR_UNSUPPORTED, "internal: " + name + " is built for another path-group count");
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dy_target, &dW, &dg, &flags,
+                        &gy_stride};
+        return launch(p, name.c_str(), grid, bwd_block(p), s, args);
+    };
     if (level == 0) {
         const int flags = (dW ? 1 : 0) | (dY ? 2 : 0) | (dg ? 4 : 0) | (dxmode << 3);
-        if ((st = pass("oeq_dbwd_" + T, flags)) != OEQ_OK) return st;
+        if ((st = pass(fused, flags)) != OEQ_OK) return st;
     } else {
         if (want_w && (st = pass("oeq_dbwd_" + std::to_string(tm & 3) + "_1", 1)) != OEQ_OK) return st;
         if (dW && !want_w && (st = fill_zero(p, dW, E * PU, s)) != OEQ_OK) return st;
@@ -271,7 +292,7 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
             }
         }
         if (dY && !(tm & 5) &&
-            (st = fill_zero(p, dy_target, E * p->YD * (gyp ? static_cast<int64_t>(p->bwd_groups.size()) : 1), s)) !=
+            (st = fill_zero(p, dy_target, E * p->YD * (gyp ? NG : 1), s)) !=
                 OEQ_OK)
             return st;
         if (dg) {
@@ -285,7 +306,7 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
     }
     if (dxmode == 2 && (st = det_finish(p, N, w, dx, s)) != OEQ_OK) return st;
     if (dxmode == 1 && (st = untranspose(p, N, dx, s)) != OEQ_OK) return st;
-    return gyp ? gy_combine(p, w, dY, E, s) : OEQ_OK;
+    return gyp ? combine_parts(p, w.gy_part, static_cast<int>(NG), dY, E * p->YD, s) : OEQ_OK;
 }
 
 }  // extern "C"

@@ -38,7 +38,8 @@ inline oeq_status check_graph(const oeq_plan *p, int64_t N, int64_t E, const int
     if (N >= std::numeric_limits<int32_t>::max() || E >= std::numeric_limits<int32_t>::max())
         return fail(OEQ_ERR_UNSUPPORTED, "node and edge counts must fit the int32 CSR");
     if (N == 0 && E != 0) return fail(OEQ_ERR_INVALID_ARG, "edges without nodes");
-    if (N * std::max<int64_t>(fwd_block(p), static_cast<int64_t>(bwd_block(p)) * p->bwd_groups.size()) >=
+    const int64_t groups = static_cast<int64_t>(std::max({p->bwd_groups.size(), p->dbwd_groups.size(), p->rad_groups.size()}));
+    if (N * std::max<int64_t>(fwd_block(p), static_cast<int64_t>(bwd_block(p)) * groups) >=
         (int64_t(1) << 32))
         return fail(OEQ_ERR_UNSUPPORTED, "too many nodes for one launch");
     if (N > 0 && !rowptr) return fail(OEQ_ERR_INVALID_ARG, "rowptr is NULL");
@@ -83,11 +84,15 @@ struct Workspace {
     size_t bytes = 0;
 };
 
+// per-group Y-gradient partials are sized for the larger of the VJP's and the double
+// backward's group counts, so that one workspace size serves both
+inline size_t gy_groups(const oeq_plan *p) { return std::max(p->bwd_groups.size(), p->dbwd_groups.size()); }
+
 inline oeq_status ws_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, bool gy_part, char *base, Workspace *w) {
     size_t off = 0;
     if (gy_part) {
         w->gy_part = base + off;
-        off += up(p->bwd_groups.size() * static_cast<size_t>(E) * p->YD * esize(p));
+        off += up(gy_groups(p) * static_cast<size_t>(E) * p->YD * esize(p));
     }
     if (det) {
         size_t csr_bytes = 0;
@@ -321,7 +326,7 @@ inline oeq_status radvjp_layout(const oeq_plan *p, int64_t N, int64_t E, bool de
     size_t off = w->rad.bytes;
     w->conv_off = off;
     if (p->rad_compose) {  // the convolution VJP's own workspace, then W and its gradient
-        oeq_status st = ws_layout(p, N, E, det, p->bwd_groups.size() > 1, base ? base + off : nullptr, &w->conv);
+        oeq_status st = ws_layout(p, N, E, det, gy_groups(p) > 1, base ? base + off : nullptr, &w->conv);
         if (st != OEQ_OK) return st;
         off += up(w->conv.bytes);
         w->wbuf = off;

@@ -411,7 +411,7 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
         o << "    }\n";
     }
     o << "  }\n";
-    if (std::string(name) == "BG") emit_dbwd_edge(o, p, L);
+    if (std::string(name) == "BG" || std::string(name) == "DG") emit_dbwd_edge(o, p, L);
     o << "};\n";
 }
 
@@ -458,6 +458,8 @@ std::string emit_source(const oeq_plan &p) {
     for (const auto &g : p.fwd_groups) o << " " << g.size();
     o << " paths, backward groups of";
     for (const auto &g : p.bwd_groups) o << " " << g.size();
+    o << ", double-backward groups of";
+    for (const auto &g : p.dbwd_groups) o << " " << g.size();
     o << ", radial backward groups of";
     for (const auto &g : p.rad_groups) o << " " << g.size();
     o << " paths\n";
@@ -488,6 +490,8 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr int UCH = " << p.uch << ";\n";
     o << "constexpr int NGF = " << p.fwd_groups.size() << ";\n";
     o << "constexpr int NGB = " << p.bwd_groups.size() << ";\n";
+    o << "constexpr int NGD = " << p.dbwd_groups.size() << ";\n";
+    o << "constexpr bool DBWD_TWO_SETS = " << (p.dbwd_groups != p.bwd_groups ? "true" : "false") << ";\n";
     o << "constexpr int P = " << p.paths.size() << ";\n";
     o << "constexpr int LY = " << p.L << ";\n";
     o << "constexpr int YD = " << p.YD << ";\n";
@@ -500,10 +504,17 @@ std::string emit_source(const oeq_plan &p) {
     o << "template <int G> struct FG;\n";
     o << "template <int G> struct BG;\n";
     o << "template <int G> struct RG;\n";
+    o << "template <int G> struct DG;\n";
     o << "constexpr int NGR = " << p.rad_groups.size() << ";\n";
     for (size_t g = 0; g < p.fwd_groups.size(); ++g) emit_group(o, p, "FG", static_cast<int>(g), p.fwd_groups[g]);
     for (size_t g = 0; g < p.bwd_groups.size(); ++g) emit_group(o, p, "BG", static_cast<int>(g), p.bwd_groups[g]);
     for (size_t g = 0; g < p.rad_groups.size(); ++g) emit_group(o, p, "RG", static_cast<int>(g), p.rad_groups[g]);
+    if (p.dbwd_groups == p.bwd_groups) {
+        o << "template <int G> struct DG : BG<G> {};\n";
+    } else {
+        for (size_t g = 0; g < p.dbwd_groups.size(); ++g)
+            emit_group(o, p, "DG", static_cast<int>(g), p.dbwd_groups[g]);
+    }
     emit_untranspose(o, p);
     o << kKernelTemplate;
     return o.str();

@@ -10,9 +10,19 @@
 // flags: bit0 d_W, bit1 d_Y, bit2 d_grad_out, bits 3-4 d_x mode (0 none, 1 atomic, 2 rows),
 //        bits 5-8 add into d_W / d_Y / d_grad_out / the d_x rows instead of overwriting
 // ---------------------------------------------------------------------------
-constexpr int DW = 1, DY = 2, DG = 4, DX = 8;
+constexpr int DW = 1, DY = 2, DGO = 4, DX = 8;
 
-template <int TM, int OUT, int G>
+// Path groups: DS = false runs on the backward groups (BG, NGB), DS = true on the
+// double-backward groups (DG, NGD), which the planner splits finer where the larger
+// kernels need the registers. The fused kernels exist for both sets (oeq_dbwd_<t> and
+// oeq_dbwd_<t>_d, the latter empty when the two sets are the same); the split passes run on
+// DG. The host sizes each launch's grid by the kernel's set.
+template <bool DS> struct DbwdSet { static constexpr int N = NGB; };
+template <> struct DbwdSet<true> { static constexpr int N = NGD; };
+template <bool DS, int G> struct DbwdGr { using T = BG<G>; };
+template <int G> struct DbwdGr<true, G> { using T = DG<G>; };
+
+template <int TM, int OUT, bool DS, int G>
 __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, const int *__restrict__ rowptr,
                                            const int *__restrict__ src, const real_t *__restrict__ x,
                                            const real_t *__restrict__ Y, const real_t *__restrict__ W,
@@ -20,12 +30,12 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
                                            const real_t *__restrict__ ggY, const real_t *__restrict__ ggW,
                                            real_t *__restrict__ dx, real_t *__restrict__ dY,
                                            real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {
-    using Gr = BG<G>;
+    using Gr = typename DbwdGr<DS, G>::T;
     const int lane = threadIdx.x & 63;
     const bool act = (U % 64 == 0) || (u < U);
     const int uu = act ? u : 0;
     const bool want_dw = (OUT & DW) && (flags & 1) != 0, want_dy = (OUT & DY) && (flags & 2) != 0,
-               want_dg = (OUT & DG) && (flags & 4) != 0;
+               want_dg = (OUT & DGO) && (flags & 4) != 0;
     const int dxmode = (OUT & DX) ? (flags >> 3) & 3 : 0;
     // add into the outputs instead of overwriting (one pass per tangent)
     const bool acc_dw = (flags & 32) != 0, acc_dy = (flags & 64) != 0, acc_dg = (flags & 128) != 0,
@@ -35,7 +45,7 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
     real_t gv[Gr::NO];
     Gr::load_g(g + (i64)r * OD, uu, gv);
     if (!act) zero(gv);
-    real_t dgacc[Gr::NO];  // dropped by the compiler when OUT has no DG
+    real_t dgacc[Gr::NO];  // dropped by the compiler when OUT has no DGO
     zero(dgacc);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     // per-edge operands (unused ones are dropped by the compiler for a given TM)
@@ -74,7 +84,7 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
             } else {
                 // every term of this edge in one pass (the g contraction is shared by the tangents)
                 Gr::template dbwd_edge<TM, GW_ && (TM & 3) != 0, GY_ && (TM & 5) != 0, GX_ && (TM & 6) != 0>(
-                    cur.x, cur.y, cur.w, cur.tx, cur.ty, cur.tw, gv, (OUT & DG) != 0 && want_dg, dgacc, dw, dy, dxp);
+                    cur.x, cur.y, cur.w, cur.tx, cur.ty, cur.tw, gv, (OUT & DGO) != 0 && want_dg, dgacc, dw, dy, dxp);
             }
             if (want_dw && act) {
                 if (acc_dw)
@@ -97,7 +107,7 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
             cur = nxt;
         }
     }
-    if constexpr ((OUT & DG) != 0)
+    if constexpr ((OUT & DGO) != 0)
     if (want_dg && act) {
         if (acc_dg)
             Gr::add_out(dg + (i64)r * OD, u, dgacc);
@@ -106,7 +116,7 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
     }
 }
 
-template <int TM, int OUT, int G>
+template <int TM, int OUT, bool DS, int G>
 __device__ __forceinline__ void dbwd_dispatch(GyStage &st, int r, int grp, int wv, int u, const int *__restrict__ rowptr,
                                               const int *__restrict__ src, const real_t *__restrict__ x,
                                               const real_t *__restrict__ Y, const real_t *__restrict__ W,
@@ -115,15 +125,15 @@ __device__ __forceinline__ void dbwd_dispatch(GyStage &st, int r, int grp, int w
                                               real_t *__restrict__ dx, real_t *__restrict__ dY,
                                               real_t *__restrict__ dW, real_t *__restrict__ dg, int flags) {
     if (grp == G) {
-        dbwd_group<TM, OUT, G>(st, r, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
+        dbwd_group<TM, OUT, DS, G>(st, r, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags);
         return;
     }
-    if constexpr (G + 1 < NGB)
-        dbwd_dispatch<TM, OUT, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg,
+    if constexpr (G + 1 < DbwdSet<DS>::N)
+        dbwd_dispatch<TM, OUT, DS, G + 1>(st, r, grp, wv, u, rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg,
                                       flags);
 }
 
-template <int TM, int OUT>
+template <int TM, int OUT, bool DS>
 __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const int *__restrict__ src,
                                           const real_t *__restrict__ x, const real_t *__restrict__ Y,
                                           const real_t *__restrict__ W, const real_t *__restrict__ g,
@@ -132,41 +142,52 @@ __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const 
                                           real_t *__restrict__ dY, real_t *__restrict__ dW,
                                           real_t *__restrict__ dg, int flags, i64 gy_stride) {
     __shared__ GyStage st;
-    const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
+    constexpr int NG = DbwdSet<DS>::N;
+    const int r = blockIdx.x / NG, grp = blockIdx.x - r * NG;
     const int wv = uni(threadIdx.x >> 6);
-    dbwd_dispatch<TM, OUT, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx,
+    dbwd_dispatch<TM, OUT, DS, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx,
                          dY + grp * gy_stride, dW, dg, flags);
 }
 
 // oeq_dbwd_<TM>: every output in one pass.  oeq_dbwd_<TM>_<OUT>: the passes of
 // the split double backward (d_W; d_Y and d_x; d_grad_out is left to the
 // forward kernel, one accumulating launch per tangent).
-#define OEQ_DBWD_KERNEL(NAME, TM, OUT)                                                              \
+#define OEQ_DBWD_KERNEL(NAME, TM, OUT, DS)                                                          \
     extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY NAME(                      \
         const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x, \
         const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,  \
         const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,                            \
         const real_t *__restrict__ ggW, real_t *__restrict__ dx, real_t *__restrict__ dY,          \
         real_t *__restrict__ dW, real_t *__restrict__ dg, int flags, i64 gy_stride) {              \
-        dbwd_body<TM, OUT>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags, gy_stride); \
+        if constexpr (!(DS && OUT == 15) || DBWD_TWO_SETS)                                         \
+            dbwd_body<TM, OUT, DS>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags,  \
+                                   gy_stride);                                                     \
     }
-OEQ_DBWD_KERNEL(oeq_dbwd_1, 1, 15)
-OEQ_DBWD_KERNEL(oeq_dbwd_2, 2, 15)
-OEQ_DBWD_KERNEL(oeq_dbwd_3, 3, 15)
-OEQ_DBWD_KERNEL(oeq_dbwd_4, 4, 15)
-OEQ_DBWD_KERNEL(oeq_dbwd_5, 5, 15)
-OEQ_DBWD_KERNEL(oeq_dbwd_6, 6, 15)
-OEQ_DBWD_KERNEL(oeq_dbwd_7, 7, 15)
+OEQ_DBWD_KERNEL(oeq_dbwd_1, 1, 15, false)
+OEQ_DBWD_KERNEL(oeq_dbwd_2, 2, 15, false)
+OEQ_DBWD_KERNEL(oeq_dbwd_3, 3, 15, false)
+OEQ_DBWD_KERNEL(oeq_dbwd_4, 4, 15, false)
+OEQ_DBWD_KERNEL(oeq_dbwd_5, 5, 15, false)
+OEQ_DBWD_KERNEL(oeq_dbwd_6, 6, 15, false)
+OEQ_DBWD_KERNEL(oeq_dbwd_7, 7, 15, false)
+// the same on the double-backward groups (empty when they are the backward groups)
+OEQ_DBWD_KERNEL(oeq_dbwd_1_d, 1, 15, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_2_d, 2, 15, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_3_d, 3, 15, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_4_d, 4, 15, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_5_d, 5, 15, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_6_d, 6, 15, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_7_d, 7, 15, true)
 // d_W = BW(gg_x,Y,g) + BW(x,gg_Y,g): reads no weights
-OEQ_DBWD_KERNEL(oeq_dbwd_1_1, 1, 1)
-OEQ_DBWD_KERNEL(oeq_dbwd_2_1, 2, 1)
-OEQ_DBWD_KERNEL(oeq_dbwd_3_1, 3, 1)
+OEQ_DBWD_KERNEL(oeq_dbwd_1_1, 1, 1, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_2_1, 2, 1, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_3_1, 3, 1, true)
 // d_Y and d_x of several tangents in one pass over W and gg_W
-OEQ_DBWD_KERNEL(oeq_dbwd_3_10, 3, 10)
-OEQ_DBWD_KERNEL(oeq_dbwd_5_10, 5, 10)
-OEQ_DBWD_KERNEL(oeq_dbwd_6_10, 6, 10)
-OEQ_DBWD_KERNEL(oeq_dbwd_7_10, 7, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_3_10, 3, 10, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_5_10, 5, 10, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_6_10, 6, 10, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_7_10, 7, 10, true)
 // one tangent: d_Y = BY(gg_x,W,g); d_x = Bx(gg_Y,W,g); d_Y, d_x = BY(x,gg_W,g), Bx(Y,gg_W,g)
-OEQ_DBWD_KERNEL(oeq_dbwd_1_2, 1, 2)
-OEQ_DBWD_KERNEL(oeq_dbwd_2_8, 2, 8)
-OEQ_DBWD_KERNEL(oeq_dbwd_4_10, 4, 10)
+OEQ_DBWD_KERNEL(oeq_dbwd_1_2, 1, 2, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_2_8, 2, 8, true)
+OEQ_DBWD_KERNEL(oeq_dbwd_4_10, 4, 10, true)

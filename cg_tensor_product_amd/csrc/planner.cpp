@@ -97,6 +97,45 @@ int group_registers(const oeq_plan &p, const std::vector<int> &paths, bool fwd) 
     return vals * (p.dtype == OEQ_F64 ? 2 : 1) + 20;
 }
 
+// Registers of the fused all-tangent double backward for one group: g and the d_grad_out
+// accumulators, the current and next edge's x, gg_x, W, gg_W, Y, gg_Y, the per-edge
+// d_Y, d_x, d_W and the largest per-path product block.
+int dbwd_registers(const oeq_plan &p, const std::vector<int> &paths) {
+    std::set<int> xs, os;
+    int transient = 0;
+    for (int k : paths) {
+        const Path &pa = p.paths[k];
+        xs.insert(pa.i1);
+        os.insert(pa.ob);
+        transient = std::max(transient, (2 * pa.l1 + 1) * (2 * pa.l2 + 1));
+    }
+    int nx = 0, no = 0;
+    for (int i : xs) nx += 2 * p.xb[i].l + 1;
+    for (int o : os) no += 2 * p.ob[o].l + 1;
+    const int nw = static_cast<int>(paths.size());
+    const int vals = 2 * no + 5 * nx + 5 * nw + 5 * p.YD + transient;
+    return vals * (p.dtype == OEQ_F64 ? 2 : 1) + 20;
+}
+
+// The double backward's groups: split until the all-tangent kernel's estimate is under
+// budget. Measured with all three tangents (ms, 1 / 2 / 3 groups): medium fp32 1.80 / 3.01 /
+// 3.03 (estimate 316 at 1 group), medium fp64 5.91 / 4.99 / 4.99, large 6.78 / 5.30 / 4.91,
+// wide 14.84 / 10.77 / 9.79 (estimate 512 at 1 group, 317 at 2).
+std::vector<std::vector<int>> choose_dbwd_groups(const oeq_plan &p) {
+    const int max_g = std::max(1, 16 / p.uch);
+    if (const char *e = std::getenv("OEQ_DBWD_GROUPS"))
+        return partition_paths(p, false, std::max(1, std::min(std::atoi(e), max_g)));
+    std::vector<std::vector<int>> best = partition_paths(p, false, 1);
+    for (int g = 1; g <= max_g; ++g) {
+        auto cand = partition_paths(p, false, g);
+        best = cand;
+        int worst = 0;
+        for (const auto &gr : cand) worst = std::max(worst, dbwd_registers(p, gr));
+        if (worst <= 400 || static_cast<int>(cand.size()) < g) break;
+    }
+    return best;
+}
+
 std::vector<std::vector<int>> choose_groups(const oeq_plan &p, bool fwd) {
     const char *env = std::getenv(fwd ? "OEQ_FWD_GROUPS" : "OEQ_BWD_GROUPS");
     const int max_g = std::max(1, 16 / p.uch);  // at most 16 waves per workgroup
@@ -262,6 +301,7 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     waves("OEQ_BWD_WAVES", p->bwd_waves);
     p->fwd_groups = choose_groups(*p, true);
     p->bwd_groups = choose_groups(*p, false);
+    p->dbwd_groups = choose_dbwd_groups(*p);
     {
         // the radial VJP keeps 2 x 8 x NW more values per lane than the VJP: split until the
         // estimate is under budget (estimates of 358 / 636 / 696 compiled to 394 registers /

@@ -77,6 +77,9 @@ struct oeq_plan {
     std::pair<int, int> fwd_waves{0, 0}, bwd_waves{0, 0};  // (min, max) waves per SIMD; 0 = compiler default
     // Path groups: one wave computes one group for 64 channels of a receiver.
     std::vector<std::vector<int>> fwd_groups, bwd_groups;
+    // path groups of the double-backward kernels with more than the gg_x tangent (the HVP,
+    // gg_x alone, keeps bwd_groups)
+    std::vector<std::vector<int>> dbwd_groups;
     // groups of the VJP that forms the radial weights in the kernel (it also holds the
     // hidden-width slices of W2 and of the W2 gradient per lane)
     std::vector<std::vector<int>> rad_groups;

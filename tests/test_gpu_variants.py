@@ -49,6 +49,11 @@ CASES = [
     ("mace_medium_fp32", {"OEQ_DBWD_SPLIT": "1"}),
     ("mace_medium_fp32", {"OEQ_DBWD_SPLIT": "2"}),
     ("mace_medium_fp32", {"OEQ_DBWD_SPLIT": "0"}),
+    # double-backward path groups other than the planned ones, with each split level
+    ("mace_medium_fp32", {"OEQ_DBWD_GROUPS": "2"}),
+    ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "1"}),
+    ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "3", "OEQ_DBWD_SPLIT": "1"}),
+    ("mace_medium_fp64", {"OEQ_DBWD_GROUPS": "2", "OEQ_DBWD_SPLIT": "2"}),
 ]
 
 
