@@ -131,8 +131,9 @@ oeq_status oeq_cg_table(int32_t l1, int32_t l2, int32_t l3, double *out);
 
 /* Workspace bytes a backward or double-backward call may need for `mode`
  * (per-group partial Y-gradients when the plan splits its paths over several
- * backward groups; per-edge x-gradient rows and the sender CSR for
- * DETERMINISTIC).  0 means no workspace is needed. */
+ * backward or double-backward groups, sized for the larger count; per-edge
+ * x-gradient rows and the sender CSR for DETERMINISTIC).  One size serves both
+ * calls.  0 means no workspace is needed. */
 oeq_status oeq_workspace_size(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                               oeq_bwd_mode mode, size_t *bytes);
 
