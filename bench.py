@@ -308,6 +308,8 @@ def main():
     if not args.no_side_rows:
         res["side_rows"] = side_rows(torch, oeq, plan, dev, N, E, ab)
     res["stream_reference"] = stream_reference(torch)
+    # the dominant kernel's algorithmic rate as a fraction of this box's plain copy rate
+    res["stream_reference"]["frac_of_copy"] = achieved / res["stream_reference"]["copy_GBps"]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wl, d, inp)
     print(json.dumps(res), flush=True)
