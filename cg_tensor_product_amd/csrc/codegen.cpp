@@ -249,7 +249,150 @@ void emit_dbwd_edge(std::ostringstream &o, const oeq_plan &p, const Local &L) {
     o << "  }\n";
 }
 
-void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int g, const std::vector<int> &paths) {
+
+// Y-contracted CG entries of one forward group: for every path and every (m1, m3) that a
+// non-zero reaches, M[m1][m3] = sum_{m2} C[m1][m2][m3] Y[l2, m2].  M depends on the edge
+// only (not on the channel), so it is built once per edge (one lane per edge) and read by
+// every channel lane from LDS.
+struct MEntry {
+    int path, m1, m3;
+    std::vector<std::pair<int, double>> terms;  // (index into the edge's Y row, coefficient)
+};
+
+std::vector<MEntry> m_entries(const oeq_plan &p, const Local &L) {
+    std::vector<MEntry> out;
+    for (int k : L.paths) {
+        const Path &pa = p.paths[k];
+        std::map<std::pair<int, int>, std::vector<std::pair<int, double>>> by;  // (m3, m1) -> terms
+        for (const auto &nz : pa.nz) by[{nz.m3, nz.m1}].push_back({pa.l2 * pa.l2 + nz.m2, nz.c});
+        for (const auto &kv : by) out.push_back({k, kv.first.second, kv.first.first, kv.second});
+    }
+    return out;
+}
+
+// Row stride of the M rows in elements: whole 16-byte vectors, an odd number of them, so
+// that lanes writing consecutive rows with 16-byte stores hit distinct banks.
+int m_stride(const oeq_plan &p, int entries) {
+    const int ve = p.dtype == OEQ_F64 ? 2 : 4;
+    int nv = (std::max(entries, 1) + ve - 1) / ve;
+    if (nv % 2 == 0) ++nv;
+    return nv * ve;
+}
+
+int group_m_stride(const oeq_plan &p, const std::vector<int> &paths) {
+    return m_stride(p, static_cast<int>(m_entries(p, make_local(p, paths)).size()));
+}
+
+void emit_m_functions(std::ostringstream &o, const oeq_plan &p, const Local &L, int moff) {
+    const std::vector<MEntry> ents = m_entries(p, L);
+    const int sm = m_stride(p, static_cast<int>(ents.size()));
+    const int ve = p.dtype == OEQ_F64 ? 2 : 4;
+    o << "  static constexpr int KM = " << ents.size() << ", SM = " << sm << ", MOFF = " << moff << ";\n";
+    // one edge's M row from its Y row, written to LDS with 16-byte stores
+    o << "  static __device__ __forceinline__ void make_m(const real_t (&y)[YD], real_t *__restrict__ row) {\n";
+    o << "    real_t m[SM];\n";
+    for (int j = 0; j < sm; ++j) {
+        if (j < static_cast<int>(ents.size())) {
+            bool first = true;
+            o << "   ";
+            for (const auto &t : ents[j].terms) {
+                o << " " << fma_term("m[" + S(j) + "]", t.second, "y[" + S(t.first) + "]", first);
+                first = false;
+            }
+            o << "\n";
+        } else {
+            o << "    m[" << j << "] = real_t(0);\n";
+        }
+        if (j % ve == ve - 1) {
+            // store each vector once formed; the fence keeps the row from being formed whole
+            // in registers first
+            const int k = j / ve;
+            o << "    { vec16_t v;";
+            for (int i = 0; i < ve; ++i) o << " v[" << i << "] = m[" << ve * k + i << "];";
+            o << " reinterpret_cast<vec16_t *>(row)[" << k << "] = v; } M_FENCE();\n";
+        }
+    }
+    o << "  }\n";
+    // forward of one edge from its M row (in LDS)
+    o << "  static __device__ __forceinline__ void edge_m(const real_t (&x)[NX], const real_t *__restrict__ row, "
+         "const real_t (&w)[NW], real_t (&acc)[NO]) {\n";
+    // each 16-byte vector of the row is read just before its first entry is used, so the
+    // row is never held in registers whole
+    o << "    const vec16_t *__restrict__ mv = reinterpret_cast<const vec16_t *>(row);\n";
+    int loaded = -1;
+    auto need = [&](size_t i) {
+        const int v = static_cast<int>(i) / ve;
+        std::string r;
+        while (loaded < v) {
+            ++loaded;
+            r += "    const vec16_t v" + S(loaded) + " = mv[" + S(loaded) + "];\n";
+        }
+        return r;
+    };
+    auto mref = [&](size_t i) { return "v" + S(static_cast<long long>(i) / ve) + "[" + S(static_cast<long long>(i) % ve) + "]"; };
+    // paths as [begin, end) ranges of entries
+    std::vector<std::pair<size_t, size_t>> ranges;
+    for (size_t a = 0; a < ents.size();) {
+        size_t b = a;
+        while (b < ents.size() && ents[b].path == ents[a].path) ++b;
+        ranges.push_back({a, b});
+        a = b;
+    }
+    // the vectors a path needs, declared one path ahead of its arithmetic (declaring the
+    // whole row first, or fencing the scheduler between paths, doubled the register count)
+    auto load_for = [&](size_t r) {
+        std::string out;
+        if (r < ranges.size())
+            for (size_t i = ranges[r].first; i < ranges[r].second; ++i) out += need(i);
+        return out;
+    };
+    o << load_for(0) << load_for(1);
+    for (size_t r = 0; r < ranges.size(); ++r) {
+        const size_t j = ranges[r].first, j1 = ranges[r].second;
+        const int k = ents[j].path;
+        if (r > 0) o << load_for(r + 1);
+        const Path &pa = p.paths[k];
+        const int xo = L.xoff.at(pa.i1), oo = L.ooff.at(pa.ob), wk = L.widx.at(k);
+        std::set<int> m1s, m3s;
+        for (size_t i = j; i < j1; ++i) {
+            m1s.insert(ents[i].m1);
+            m3s.insert(ents[i].m3);
+        }
+        // vectors are declared at function scope (a path's entries can share a vector
+        // with the next path's)
+        if (m1s.size() < m3s.size()) {
+            // weight applied to x first: acc[m3] += sum_m1 M[m1][m3] (w x[m1])
+            o << "    // path " << k << ": " << pa.l1 << " x " << pa.l2 << " -> " << pa.l3 << " (weight on x)\n";
+            for (int a : m1s) o << "    const real_t wx" << k << "_" << a << " = w[" << wk << "] * x[" << xo + a << "];\n";
+            for (size_t i = j; i < j1; ++i) {
+                const std::string d = "acc[" + S(oo + ents[i].m3) + "]";
+                o << need(i) << "    " << d << " = fmar(" << mref(i) << ", wx" << k << "_" << ents[i].m1 << ", " << d
+                  << ");\n";
+            }
+        } else {
+            // t[m3] = sum_m1 M[m1][m3] x[m1];  acc[m3] += w t[m3]
+            o << "    // path " << k << ": " << pa.l1 << " x " << pa.l2 << " -> " << pa.l3 << "\n";
+            size_t i = j;
+            while (i < j1) {
+                const int m3 = ents[i].m3;
+                std::string pre = need(i);
+                std::string line = "    { real_t t = " + mref(i) + " * x[" + S(xo + ents[i].m1) + "];";
+                ++i;
+                while (i < j1 && ents[i].m3 == m3) {
+                    pre += need(i);
+                    line += " t = fmar(" + mref(i) + ", x[" + S(xo + ents[i].m1) + "], t);";
+                    ++i;
+                }
+                const std::string d = "acc[" + S(oo + m3) + "]";
+                o << pre << line << " " << d << " = fmar(w[" << wk << "], t, " << d << "); }\n";
+            }
+        }
+    }
+    o << "  }\n";
+}
+
+void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int g, const std::vector<int> &paths,
+                int moff = 0) {
     const Local L = make_local(p, paths);
     o << "template <> struct " << name << "<" << g << "> {\n";
     o << "  static constexpr int NX = " << L.nx << ", NW = " << L.nw << ", NO = " << L.no << ";\n";
@@ -412,6 +555,7 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
     }
     o << "  }\n";
     if (std::string(name) == "BG" || std::string(name) == "DG") emit_dbwd_edge(o, p, L);
+    if (std::string(name) == "FG" && p.fwd_lds) emit_m_functions(o, p, L, moff);
     o << "};\n";
 }
 
@@ -443,6 +587,12 @@ void emit_untranspose(std::ostringstream &o, const oeq_plan &p) {
 }
 
 }  // namespace
+
+int fwd_m_elems(const oeq_plan &p) {
+    int n = 0;
+    for (const auto &g : p.fwd_groups) n += group_m_stride(p, g);
+    return n;
+}
 
 std::string emit_source(const oeq_plan &p) {
     std::ostringstream o;
@@ -506,7 +656,19 @@ std::string emit_source(const oeq_plan &p) {
     o << "template <int G> struct RG;\n";
     o << "template <int G> struct DG;\n";
     o << "constexpr int NGR = " << p.rad_groups.size() << ";\n";
-    for (size_t g = 0; g < p.fwd_groups.size(); ++g) emit_group(o, p, "FG", static_cast<int>(g), p.fwd_groups[g]);
+    o << "constexpr bool FWD_LDS = " << (p.fwd_lds ? "true" : "false") << ";\n";
+    o << "#define M_FENCE() __builtin_amdgcn_sched_barrier(0)\n";
+    o << "constexpr int FWD_MT = " << p.fwd_tile << ";\n";
+    o << "typedef real_t vec16_t __attribute__((ext_vector_type(" << (p.dtype == OEQ_F64 ? 2 : 4) << ")));\n";
+    {
+        int moff = 0;
+        for (size_t g = 0; g < p.fwd_groups.size(); ++g) {
+            emit_group(o, p, "FG", static_cast<int>(g), p.fwd_groups[g], moff);
+            moff += group_m_stride(p, p.fwd_groups[g]);
+        }
+        // elements of one edge's M rows over all forward groups
+        o << "constexpr int FWD_M_ELEMS = " << (p.fwd_lds ? moff : 0) << ";\n";
+    }
     for (size_t g = 0; g < p.bwd_groups.size(); ++g) emit_group(o, p, "BG", static_cast<int>(g), p.bwd_groups[g]);
     for (size_t g = 0; g < p.rad_groups.size(); ++g) emit_group(o, p, "RG", static_cast<int>(g), p.rad_groups[g]);
     if (p.dbwd_groups == p.bwd_groups) {

@@ -60,14 +60,91 @@ __device__ __forceinline__ void fwd_dispatch(int grp, int r, int u, const int *_
     if constexpr (G + 1 < NGF) fwd_dispatch<G + 1, YV>(grp, r, u, rowptr, src, x, Y, W, out, acc);
 }
 
+// Forward from Y-contracted CG rows: the receiver's edges are taken in tiles of FWD_MT.
+// For each tile the first waves of every group build the group's rows M[e] = C . Y[e] in
+// LDS (one lane per edge), and every channel lane streams the tile's edges reading M[e] by
+// broadcast.  Every wave of the workgroup has the same receiver, so all run the same tiles
+// and meet at the same barriers.
+template <int G>
+__device__ __forceinline__ void fwd_group_lds(real_t *__restrict__ mt, int r, int uc, int lane,
+                                              const int *__restrict__ rowptr, const int *__restrict__ src,
+                                              const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                              const real_t *__restrict__ W, real_t *__restrict__ out, bool acc) {
+    using Gr = FG<G>;
+    const int u = uc * 64 + lane;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;  // inactive lanes read channel 0 and store nothing
+    const int i = u;             // the tile row this lane builds (when < FWD_MT)
+    real_t sum[Gr::NO];
+    zero(sum);
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    if (e0 < e1) {
+        int s = uni(src[e0]);
+        real_t xv[Gr::NX], wv[Gr::NW];
+        Gr::load_x(x + (i64)s * XD, uu, xv);
+        Gr::load_w(W + (i64)e0 * (P * U), uu, wv);
+        int tb = e0;  // first edge of the tile whose rows are in LDS
+        for (int e = e0; e < e1; ++e) {
+            if (e == tb + FWD_MT || e == e0) {
+                tb = e;
+                __syncthreads();  // the previous tile's rows are no longer read
+                if (i < FWD_MT && e + i < e1) {
+                    real_t yv[YD];
+                    const real_t *yr = Y + (i64)(e + i) * YD;
+#pragma unroll
+                    for (int k = 0; k < YD; ++k) yv[k] = yr[k];
+                    Gr::make_m(yv, mt + i * Gr::SM);
+                }
+                __syncthreads();
+            }
+            real_t xn[Gr::NX], wn[Gr::NW];
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            Gr::load_x(x + (i64)sn * XD, uu, xn);
+            Gr::load_w(W + (i64)en * (P * U), uu, wn);
+            PIN_FWD();
+            Gr::edge_m(xv, mt + (e - tb) * Gr::SM, wv, sum);
+#pragma unroll
+            for (int k = 0; k < Gr::NX; ++k) xv[k] = xn[k];
+#pragma unroll
+            for (int k = 0; k < Gr::NW; ++k) wv[k] = wn[k];
+        }
+    }
+    if (act) {
+        if (acc)
+            Gr::add_out(out + (i64)r * OD, u, sum);
+        else
+            Gr::store_out(out + (i64)r * OD, u, sum);
+    }
+}
+
+template <int G>
+__device__ __forceinline__ void fwd_lds_dispatch(real_t *__restrict__ mbuf, int grp, int r, int uc, int lane,
+                                                 const int *__restrict__ rowptr, const int *__restrict__ src,
+                                                 const real_t *__restrict__ x, const real_t *__restrict__ Y,
+                                                 const real_t *__restrict__ W, real_t *__restrict__ out, bool acc) {
+    if constexpr (FWD_LDS) {
+        if (grp == G) {
+            fwd_group_lds<G>(mbuf + FG<G>::MOFF * FWD_MT, r, uc, lane, rowptr, src, x, Y, W, out, acc);
+            return;
+        }
+        if constexpr (G + 1 < NGF) fwd_lds_dispatch<G + 1>(mbuf, grp, r, uc, lane, rowptr, src, x, Y, W, out, acc);
+    }
+}
+
 extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
 oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
         const real_t *__restrict__ Y, const real_t *__restrict__ W, real_t *__restrict__ out, int flags) {
     // flags: bit0 add into out instead of overwriting it
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
-    fwd_dispatch<0, false>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out,
-                           (flags & 1) != 0);
+    if constexpr (FWD_LDS) {
+        __shared__ __attribute__((aligned(16))) real_t mbuf[FWD_M_ELEMS * FWD_MT > 0 ? FWD_M_ELEMS * FWD_MT : 1];
+        fwd_lds_dispatch<0>(mbuf, grp, blockIdx.x, uc, threadIdx.x & 63, rowptr, src, x, Y, W, out, (flags & 1) != 0);
+    } else {
+        fwd_dispatch<0, false>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out,
+                               (flags & 1) != 0);
+    }
 }
 
 // The forward with Y evaluated in the kernel from the edge vectors vec[E, 3]

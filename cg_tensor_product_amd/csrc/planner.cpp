@@ -300,6 +300,22 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     waves("OEQ_FWD_WAVES", p->fwd_waves);
     waves("OEQ_BWD_WAVES", p->bwd_waves);
     p->fwd_groups = choose_groups(*p, true);
+    // measured on MI355X: the tile form wins for fp64 (0.76 against 0.81 ms on the medium
+    // workload) and loses for fp32 where the literal form already keeps the forward near its
+    // bound (large workload 0.79 against 0.67 ms: its 172 registers leave two waves per SIMD)
+    p->fwd_lds = p->dtype == OEQ_F64;
+    if (const char *e = std::getenv("OEQ_FWD_LDS")) p->fwd_lds = std::atoi(e) != 0;
+    if (const char *e = std::getenv("OEQ_FWD_TILE")) {
+        const int v = std::atoi(e);
+        if (v >= 1) p->fwd_tile = v;
+    }
+    // one lane builds one edge's rows: a tile has at most one edge per lane of a group's waves
+    p->fwd_tile = std::min(p->fwd_tile, 64 * p->uch);
+    // and the tile's rows stay within 64 KB of LDS
+    {
+        const int row_bytes = fwd_m_elems(*p) * (p->dtype == OEQ_F64 ? 8 : 4);
+        while (p->fwd_tile > 1 && p->fwd_tile * row_bytes > 65536) p->fwd_tile /= 2;
+    }
     p->bwd_groups = choose_groups(*p, false);
     p->dbwd_groups = choose_dbwd_groups(*p);
     {

@@ -72,6 +72,11 @@ struct oeq_plan {
     int sched_fwd = 0, sched_bwd = 0;
     double move_fwd[2] = {0, 0}, move_bwd[2] = {0, 0};
     bool nt_w = true;           // non-temporal loads/stores for W and its gradients
+    // forward with the CG tables contracted with Y per edge tile in LDS (M[e] = C . Y[e],
+    // built with one lane per edge), so each lane does |M| + min(n1, n3) multiply-adds per
+    // path instead of the x-Y products plus every non-zero plus n3
+    bool fwd_lds = false;
+    int fwd_tile = 32;          // edges per LDS tile of M rows
     // keep the software-pipelined loads ahead of the arithmetic (forward, backward passes)
     bool pin_fwd = false, pin_bwd = false;
     std::pair<int, int> fwd_waves{0, 0}, bwd_waves{0, 0};  // (min, max) waves per SIMD; 0 = compiler default
@@ -100,6 +105,9 @@ namespace oeq {
 // Validates the descriptor and fills the structural part of the plan (paths,
 // tables, layouts).  Returns OEQ_OK or an error with a message in *why.
 oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why);
+
+// Elements of one edge's Y-contracted CG rows over all forward groups (the LDS forward).
+int fwd_m_elems(const oeq_plan &p);
 
 // Emits the HIP source of every kernel of the plan.
 std::string emit_source(const oeq_plan &p);

@@ -1,6 +1,7 @@
 """GPU parity of the kernel variants the planner can choose: path-group counts
-for the forward and backward passes, the x-gradient atomic layout and plain
-(temporal) weight accesses.  Each variant is a separate plan (the choice is made
+for the forward and backward passes, the x-gradient atomic layout, plain
+(temporal) weight accesses and the two forms of the forward (CG literals, or
+Y-contracted rows in LDS, with several tile sizes).  Each variant is a separate plan (the choice is made
 when the plan is compiled) and is compared with the oracle like the defaults."""
 import os
 
@@ -54,6 +55,14 @@ CASES = [
     ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "1"}),
     ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "3", "OEQ_DBWD_SPLIT": "1"}),
     ("mace_medium_fp64", {"OEQ_DBWD_GROUPS": "2", "OEQ_DBWD_SPLIT": "2"}),
+    # forward from Y-contracted CG rows in LDS (the fp64 default) and the literal form:
+    # tiles of one edge, of 7 (ragged), 32 and 50 (capped from 100 by the LDS budget)
+    ("mace_medium_fp64", {"OEQ_FWD_LDS": "0"}),
+    ("tiny_fp64", {"OEQ_FWD_LDS": "0"}),
+    ("mace_medium_fp32", {"OEQ_FWD_LDS": "1"}),
+    ("mace_medium_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "1"}),
+    ("mace_large_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "7", "OEQ_FWD_GROUPS": "3"}),
+    ("wide_proxy_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "100"}),
 ]
 
 
