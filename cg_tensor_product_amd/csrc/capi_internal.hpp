@@ -31,6 +31,19 @@ inline size_t esize(const oeq_plan *p) { return p->dtype == OEQ_F64 ? 8 : 4; }
 // Threads per workgroup: one wave per (64-channel chunk, path group).
 inline unsigned fwd_block(const oeq_plan *p) { return static_cast<unsigned>(p->uch * p->fwd_groups.size() * 64); }
 inline unsigned bwd_block(const oeq_plan *p) { return static_cast<unsigned>(p->uch * 64); }
+// oeq_fwd: one workgroup per receiver, or with fwd_xcd one per (receiver, chunk) in an order
+// that keeps each chunk on the same XCDs (the kernel maps the workgroup id back)
+inline unsigned fwd_wg(const oeq_plan *p) {
+    return static_cast<unsigned>((p->fwd_xcd ? 1 : p->uch) * p->fwd_groups.size() * 64);
+}
+inline unsigned fwd_grid(const oeq_plan *p, int64_t N) {
+    if (!p->fwd_xcd) return static_cast<unsigned>(N);
+    if (8 % p->uch == 0) {
+        const int64_t per = 8 / p->uch;  // XCDs of one chunk
+        return static_cast<unsigned>(8 * ((N + per - 1) / per));
+    }
+    return static_cast<unsigned>(N * p->uch);
+}
 
 inline oeq_status check_graph(const oeq_plan *p, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src) {
     if (!p) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
@@ -153,8 +166,9 @@ inline oeq_status gy_combine(oeq_plan *p, const Workspace &w, void *gY, int64_t 
 // flags bit0: add into out instead of overwriting it
 inline oeq_status fwd_launch(oeq_plan *p, int64_t N, const int32_t *rowptr, const int32_t *src, const void *x, const void *Y,
                       const void *W, void *out, int flags, hipStream_t s) {
-    void *args[] = {&rowptr, &src, &x, &Y, &W, &out, &flags};
-    return launch(p, "oeq_fwd", static_cast<unsigned>(N), fwd_block(p), s, args);
+    int n_nodes = static_cast<int>(N);
+    void *args[] = {&rowptr, &src, &x, &Y, &W, &out, &flags, &n_nodes};
+    return launch(p, "oeq_fwd", fwd_grid(p, N), fwd_wg(p), s, args);
 }
 
 // Grid-stride launch of a per-edge kernel (vec, a, b, n) over E edges.

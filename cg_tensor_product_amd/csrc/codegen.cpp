@@ -657,6 +657,7 @@ std::string emit_source(const oeq_plan &p) {
     o << "template <int G> struct DG;\n";
     o << "constexpr int NGR = " << p.rad_groups.size() << ";\n";
     o << "constexpr bool FWD_LDS = " << (p.fwd_lds ? "true" : "false") << ";\n";
+    o << "constexpr bool FWD_XCD = " << (p.fwd_xcd ? "true" : "false") << ";\n";
     o << "#define M_FENCE() __builtin_amdgcn_sched_barrier(0)\n";
     o << "constexpr int FWD_MT = " << p.fwd_tile << ";\n";
     o << "typedef real_t vec16_t __attribute__((ext_vector_type(" << (p.dtype == OEQ_F64 ? 2 : 4) << ")));\n";

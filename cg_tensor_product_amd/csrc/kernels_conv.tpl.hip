@@ -66,7 +66,7 @@ __device__ __forceinline__ void fwd_dispatch(int grp, int r, int u, const int *_
 // broadcast.  Every wave of the workgroup has the same receiver, so all run the same tiles
 // and meet at the same barriers.
 template <int G>
-__device__ __forceinline__ void fwd_group_lds(real_t *__restrict__ mt, int r, int uc, int lane,
+__device__ __forceinline__ void fwd_group_lds(real_t *__restrict__ mt, int r, int uc, int lane, int bi,
                                               const int *__restrict__ rowptr, const int *__restrict__ src,
                                               const real_t *__restrict__ x, const real_t *__restrict__ Y,
                                               const real_t *__restrict__ W, real_t *__restrict__ out, bool acc) {
@@ -74,7 +74,7 @@ __device__ __forceinline__ void fwd_group_lds(real_t *__restrict__ mt, int r, in
     const int u = uc * 64 + lane;
     const bool act = (U % 64 == 0) || (u < U);
     const int uu = act ? u : 0;  // inactive lanes read channel 0 and store nothing
-    const int i = u;             // the tile row this lane builds (when < FWD_MT)
+    const int i = bi;            // the tile row this lane builds (when < FWD_MT)
     real_t sum[Gr::NO];
     zero(sum);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
@@ -119,31 +119,57 @@ __device__ __forceinline__ void fwd_group_lds(real_t *__restrict__ mt, int r, in
 }
 
 template <int G>
-__device__ __forceinline__ void fwd_lds_dispatch(real_t *__restrict__ mbuf, int grp, int r, int uc, int lane,
+__device__ __forceinline__ void fwd_lds_dispatch(real_t *__restrict__ mbuf, int grp, int r, int uc, int lane, int bi,
                                                  const int *__restrict__ rowptr, const int *__restrict__ src,
                                                  const real_t *__restrict__ x, const real_t *__restrict__ Y,
                                                  const real_t *__restrict__ W, real_t *__restrict__ out, bool acc) {
     if constexpr (FWD_LDS) {
         if (grp == G) {
-            fwd_group_lds<G>(mbuf + FG<G>::MOFF * FWD_MT, r, uc, lane, rowptr, src, x, Y, W, out, acc);
+            fwd_group_lds<G>(mbuf + FG<G>::MOFF * FWD_MT, r, uc, lane, bi, rowptr, src, x, Y, W, out, acc);
             return;
         }
-        if constexpr (G + 1 < NGF) fwd_lds_dispatch<G + 1>(mbuf, grp, r, uc, lane, rowptr, src, x, Y, W, out, acc);
+        if constexpr (G + 1 < NGF) fwd_lds_dispatch<G + 1>(mbuf, grp, r, uc, lane, bi, rowptr, src, x, Y, W, out, acc);
     }
 }
 
-extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
+// Workgroup shape of oeq_fwd: all 64-channel chunks of a receiver (waves = chunks x path
+// groups), or with FWD_XCD one chunk per workgroup (waves = path groups).
+constexpr int FWD_WG = (FWD_XCD ? 1 : UCH) * NGF * 64;
+
+extern "C" __global__ void __launch_bounds__(FWD_WG) FWD_OCCUPANCY
 oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
-        const real_t *__restrict__ Y, const real_t *__restrict__ W, real_t *__restrict__ out, int flags) {
+        const real_t *__restrict__ Y, const real_t *__restrict__ W, real_t *__restrict__ out, int flags,
+        int n_nodes) {
     // flags: bit0 add into out instead of overwriting it
-    const int w = uni(threadIdx.x >> 6);
-    const int grp = w / UCH, uc = w - grp * UCH;
+    const int w = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    int r, grp, uc, wc;  // receiver, path group, channel chunk, chunk index inside the workgroup
+    if constexpr (FWD_XCD) {
+        // Workgroup b is dispatched to XCD b % 8.  With UCH dividing 8, chunk c runs only on
+        // the 8 / UCH XCDs with b % 8 % UCH == c, so each XCD's L2 holds the x rows of one
+        // chunk (x[:, chunk] rather than all of x).
+        const int b = blockIdx.x;
+        if constexpr (8 % UCH == 0) {
+            const int xcd = b & 7;
+            uc = xcd % UCH;
+            r = (b >> 3) * (8 / UCH) + xcd / UCH;
+        } else {
+            uc = b % UCH;
+            r = b / UCH;
+        }
+        if (r >= n_nodes) return;
+        grp = w;
+        wc = 0;
+    } else {
+        grp = w / UCH;
+        uc = w - grp * UCH;
+        r = blockIdx.x;
+        wc = uc;
+    }
     if constexpr (FWD_LDS) {
         __shared__ __attribute__((aligned(16))) real_t mbuf[FWD_M_ELEMS * FWD_MT > 0 ? FWD_M_ELEMS * FWD_MT : 1];
-        fwd_lds_dispatch<0>(mbuf, grp, blockIdx.x, uc, threadIdx.x & 63, rowptr, src, x, Y, W, out, (flags & 1) != 0);
+        fwd_lds_dispatch<0>(mbuf, grp, r, uc, lane, wc * 64 + lane, rowptr, src, x, Y, W, out, (flags & 1) != 0);
     } else {
-        fwd_dispatch<0, false>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, out,
-                               (flags & 1) != 0);
+        fwd_dispatch<0, false>(grp, r, uc * 64 + lane, rowptr, src, x, Y, W, out, (flags & 1) != 0);
     }
 }
 

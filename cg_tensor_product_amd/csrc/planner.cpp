@@ -309,8 +309,9 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         const int v = std::atoi(e);
         if (v >= 1) p->fwd_tile = v;
     }
+    if (const char *e = std::getenv("OEQ_FWD_XCD")) p->fwd_xcd = std::atoi(e) != 0;
     // one lane builds one edge's rows: a tile has at most one edge per lane of a group's waves
-    p->fwd_tile = std::min(p->fwd_tile, 64 * p->uch);
+    p->fwd_tile = std::min(p->fwd_tile, 64 * (p->fwd_xcd ? 1 : p->uch));
     // and the tile's rows stay within 64 KB of LDS
     {
         const int row_bytes = fwd_m_elems(*p) * (p->dtype == OEQ_F64 ? 8 : 4);

@@ -77,6 +77,9 @@ struct oeq_plan {
     // path instead of the x-Y products plus every non-zero plus n3
     bool fwd_lds = false;
     int fwd_tile = 32;          // edges per LDS tile of M rows
+    // forward workgroups of one 64-channel chunk, mapped so that each chunk stays on the
+    // same XCDs (their L2 caches then hold the x rows of one chunk)
+    bool fwd_xcd = false;
     // keep the software-pipelined loads ahead of the arithmetic (forward, backward passes)
     bool pin_fwd = false, pin_bwd = false;
     std::pair<int, int> fwd_waves{0, 0}, bwd_waves{0, 0};  // (min, max) waves per SIMD; 0 = compiler default

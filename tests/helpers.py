@@ -36,9 +36,23 @@ def to_dev(a, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def plan_for(wl: synth.Workload):
+def plan_for(wl: synth.Workload, env=None):
+    """The plan of a workload; `env` sets planner options (OEQ_* variables) while the
+    plan is built (the choices are fixed when it is compiled)."""
+    import os
+
     import cg_tensor_product_amd as oeq
-    return oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    env = env or {}
+    old = {k: os.environ.get(k) for k in env}
+    os.environ.update(env)
+    try:
+        return oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    finally:
+        for k, v in old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
 
 
 def sample(n: int, k: int, seed: int) -> np.ndarray:

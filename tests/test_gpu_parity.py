@@ -87,6 +87,31 @@ def test_fwd_parity(name):
     assert not out.cpu().numpy()[deg == 0].any()          # receivers without edges
 
 
+# The forward's other forms on every small case: the one the planner does not choose by
+# default (CG literals for fp64, Y-contracted rows in LDS for fp32; tiles of 32 edges, so
+# the hub's 3,000 edges run 94 tiles), and workgroups of one channel chunk in an XCD-affine
+# order (U = 96: a half-empty second chunk; U = 1024: 16 chunks, the mapping for chunk
+# counts that do not divide 8; U = 1: one chunk).
+OTHER_FORMS = [(n, {"OEQ_FWD_LDS": "0" if SMALL[n].dtype == "f64" else "1"}) for n in SMALL] + [
+    (n, {"OEQ_FWD_XCD": "1"}) for n in ("ragged_u96_f32", "u1024_f32", "hub_u32_f32", "u1_l3_f64")]
+
+
+@pytest.mark.parametrize("name,env", OTHER_FORMS,
+                         ids=[f"{n}-{'-'.join(f'{k[4:]}{v}' for k, v in e.items())}" for n, e in OTHER_FORMS])
+def test_fwd_parity_other_forms(name, env):
+    wl = SMALL[name]
+    d, inp = inputs(wl, want=("x", "Y", "W"))
+    g = _dev_inputs(inp, wl.dtype)
+    plan = plan_for(wl, env)
+    print(f"[fwd form] {name} {env} N={wl.n_nodes} E={inp['E']}", flush=True)
+    out = oeq.oeq_tp_conv_fwd(plan, g["rowptr"], g["src"], g["x"], g["Y"], g["W"])
+    torch.cuda.synchronize()
+    ref = oracle.fwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"])
+    assert rel_l2(out.cpu().numpy(), ref) <= RTOL[wl.dtype]
+    deg = np.diff(inp["rowptr"])
+    assert not out.cpu().numpy()[deg == 0].any()
+
+
 @pytest.mark.parametrize("mode", ["atomic", "deterministic"])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_bwd_parity(name, mode):

@@ -63,6 +63,13 @@ CASES = [
     ("mace_medium_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "1"}),
     ("mace_large_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "7", "OEQ_FWD_GROUPS": "3"}),
     ("wide_proxy_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "100"}),
+    # forward workgroups of one channel chunk in an XCD-affine order, both forms
+    ("mace_medium_fp32", {"OEQ_FWD_XCD": "1"}),
+    ("wide_proxy_fp32", {"OEQ_FWD_XCD": "1", "OEQ_FWD_LDS": "1"}),
+    ("mace_medium_fp64", {"OEQ_FWD_XCD": "1"}),
+    # the split double backward's accumulating forward launches in the tile form
+    ("mace_medium_fp64", {"OEQ_DBWD_SPLIT": "1"}),
+    ("mace_medium_fp32", {"OEQ_FWD_LDS": "1", "OEQ_DBWD_SPLIT": "2"}),
 ]
 
 
