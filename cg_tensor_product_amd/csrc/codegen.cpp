@@ -304,8 +304,8 @@ void emit_m_functions(std::ostringstream &o, const oeq_plan &p, const Local &L, 
             o << "    m[" << j << "] = real_t(0);\n";
         }
         if (j % ve == ve - 1) {
-            // store each vector once formed; the fence keeps the row from being formed whole
-            // in registers first
+            // store each vector once formed, with a scheduling fence after it (the kernel's
+            // register peak is in the edge loop, not in this build of the rows)
             const int k = j / ve;
             o << "    { vec16_t v;";
             for (int i = 0; i < ve; ++i) o << " v[" << i << "] = m[" << ve * k + i << "];";
@@ -339,7 +339,8 @@ void emit_m_functions(std::ostringstream &o, const oeq_plan &p, const Local &L, 
         a = b;
     }
     // the vectors a path needs, declared one path ahead of its arithmetic (declaring the
-    // whole row first, or fencing the scheduler between paths, doubled the register count)
+    // whole row first, or fencing the scheduler between paths, raised the medium config's
+    // forward from 131 to 202-215 registers)
     auto load_for = [&](size_t r) {
         std::string out;
         if (r < ranges.size())
