@@ -300,11 +300,16 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     waves("OEQ_FWD_WAVES", p->fwd_waves);
     waves("OEQ_BWD_WAVES", p->bwd_waves);
     p->fwd_groups = choose_groups(*p, true);
-    // measured on MI355X: the tile form wins for fp64 (0.76 against 0.81 ms on the medium
-    // workload) and loses for fp32 where the literal form already keeps the forward near its
-    // bound (large workload 0.79 against 0.67 ms: its 172 registers leave two waves per SIMD)
-    p->fwd_lds = p->dtype == OEQ_F64;
+    // measured on MI355X (tiles of 64 edges): the tile form wins for fp64 (medium workload
+    // 0.74 against 0.76 ms) and where four or more channel chunks share each edge's rows (wide
+    // workload, U = 256: 1.49 against 1.62 ms); with two chunks in fp32 the literal form is
+    // faster (large workload 0.67 against 0.78 ms: the tile form's 172 registers leave two
+    // waves per SIMD, and the waves wait while a tile's rows are built)
+    p->fwd_lds = p->dtype == OEQ_F64 || p->uch >= 4;
     if (const char *e = std::getenv("OEQ_FWD_LDS")) p->fwd_lds = std::atoi(e) != 0;
+    // tiles of 64 edges: one build of the rows per receiver of the degree-56 workloads (wide
+    // 1.49 against 1.56 ms with 32); the literal form does not use tiles
+    if (p->fwd_lds) p->fwd_tile = 64;
     if (const char *e = std::getenv("OEQ_FWD_TILE")) {
         const int v = std::atoi(e);
         if (v >= 1) p->fwd_tile = v;
@@ -312,10 +317,11 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     if (const char *e = std::getenv("OEQ_FWD_XCD")) p->fwd_xcd = std::atoi(e) != 0;
     // one lane builds one edge's rows: a tile has at most one edge per lane of a group's waves
     p->fwd_tile = std::min(p->fwd_tile, 64 * (p->fwd_xcd ? 1 : p->uch));
-    // and the tile's rows stay within 64 KB of LDS
+    // and the tile's rows stay within 80 KB of LDS (gfx950 gives a workgroup up to 160 KB;
+    // 80 KB leaves room for two workgroups per compute unit)
     {
         const int row_bytes = fwd_m_elems(*p) * (p->dtype == OEQ_F64 ? 8 : 4);
-        while (p->fwd_tile > 1 && p->fwd_tile * row_bytes > 65536) p->fwd_tile /= 2;
+        while (p->fwd_tile > 1 && p->fwd_tile * row_bytes > 81920) p->fwd_tile /= 2;
     }
     p->bwd_groups = choose_groups(*p, false);
     p->dbwd_groups = choose_dbwd_groups(*p);

@@ -76,7 +76,7 @@ struct oeq_plan {
     // built with one lane per edge), so each lane does |M| + min(n1, n3) multiply-adds per
     // path instead of the x-Y products plus every non-zero plus n3
     bool fwd_lds = false;
-    int fwd_tile = 32;          // edges per LDS tile of M rows
+    int fwd_tile = 32;          // edges per LDS tile of M rows (capped by the LDS budget)
     // forward workgroups of one 64-channel chunk, mapped so that each chunk stays on the
     // same XCDs (their L2 caches then hold the x rows of one chunk)
     bool fwd_xcd = false;

@@ -88,11 +88,15 @@ def test_fwd_parity(name):
 
 
 # The forward's other forms on every small case: the one the planner does not choose by
-# default (CG literals for fp64, Y-contracted rows in LDS for fp32; tiles of 32 edges, so
-# the hub's 3,000 edges run 94 tiles), and workgroups of one channel chunk in an XCD-affine
-# order (U = 96: a half-empty second chunk; U = 1024: 16 chunks, the mapping for chunk
-# counts that do not divide 8; U = 1: one chunk).
-OTHER_FORMS = [(n, {"OEQ_FWD_LDS": "0" if SMALL[n].dtype == "f64" else "1"}) for n in SMALL] + [
+# default (CG literals for fp64 and for four or more channel chunks, Y-contracted rows in
+# LDS otherwise; tiles of 64 edges, so the hub's 3,000 edges run 47 tiles), and workgroups
+# of one channel chunk in an XCD-affine order (U = 96: a half-empty second chunk; U = 1024:
+# 16 chunks, the mapping for chunk counts that do not divide 8; U = 1: one chunk).
+def _tile_form_default(wl):
+    return wl.dtype == "f64" or wl.x_irreps[0][0] > 192
+
+
+OTHER_FORMS = [(n, {"OEQ_FWD_LDS": "0" if _tile_form_default(SMALL[n]) else "1"}) for n in SMALL] + [
     (n, {"OEQ_FWD_XCD": "1"}) for n in ("ragged_u96_f32", "u1024_f32", "hub_u32_f32", "u1_l3_f64")]
 
 

@@ -55,11 +55,13 @@ CASES = [
     ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "1"}),
     ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "3", "OEQ_DBWD_SPLIT": "1"}),
     ("mace_medium_fp64", {"OEQ_DBWD_GROUPS": "2", "OEQ_DBWD_SPLIT": "2"}),
-    # forward from Y-contracted CG rows in LDS (the fp64 default) and the literal form:
-    # tiles of one edge, of 7 (ragged), 32 and 50 (capped from 100 by the LDS budget)
+    # forward from Y-contracted CG rows in LDS (the default for fp64 and for four or more
+    # channel chunks) and the literal form: tiles of one edge, of 7 (ragged), 32, 50 and 64
     ("mace_medium_fp64", {"OEQ_FWD_LDS": "0"}),
     ("tiny_fp64", {"OEQ_FWD_LDS": "0"}),
     ("mace_medium_fp32", {"OEQ_FWD_LDS": "1"}),
+    ("mace_medium_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "32"}),
+    ("wide_proxy_fp32", {"OEQ_FWD_LDS": "0"}),
     ("mace_medium_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "1"}),
     ("mace_large_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "7", "OEQ_FWD_GROUPS": "3"}),
     ("wide_proxy_fp32", {"OEQ_FWD_LDS": "1", "OEQ_FWD_TILE": "100"}),
