@@ -164,6 +164,37 @@ def test_generated_source_has_no_packed_fp32_and_caches(tmp_path, monkeypatch):
         assert "oeq_fwd" in dis.stdout and "oeq_bwd_atomic" in dis.stdout
 
 
+def test_tile_form_rows_match_the_tables(tmp_path):
+    """The tile-form forward stores, per edge and path, one Y-contracted entry for every
+    (m1, m3) that a non-zero CG coefficient reaches: the emitted row sizes equal that count
+    taken from the oracle's tables; rows are whole 16-byte vectors, an odd number of them;
+    a tile's rows fit the 80 KB LDS budget.  fp64 plans use the tile form by default."""
+    import re
+    import subprocess
+    import sys
+    env = dict(os.environ, OEQ_CACHE_DIR=str(tmp_path), OEQ_DUMP_SOURCE="1")
+    code = ("import sys; sys.path.insert(0, %r); import cg_tensor_product_amd as m; "
+            "m.Plan('4x0e+4x1o+4x2e', 2, 2, 'f64')" % ROOT)
+    subprocess.run([sys.executable, "-c", code], check=True, env=env)
+    src = next(tmp_path.glob("*.hip")).read_text()
+    assert "constexpr bool FWD_LDS = true;" in src
+    rows = [tuple(map(int, t)) for t in re.findall(r"static constexpr int KM = (\d+), SM = (\d+), MOFF = (\d+);", src)]
+    assert rows, "no tile-form rows emitted"
+    want = 0
+    xl = [0, 1, 2]
+    for (i1, l2, l3, _) in oracle.enumerate_paths(((4, 0, 1), (4, 1, -1), (4, 2, 1)), 2, 2):
+        c = oracle.cg_real(xl[i1], l2, l3)
+        want += len({(a, k) for a, _, k in np.argwhere(np.abs(c) > 1e-10)})
+    assert sum(km for km, _, _ in rows) == want
+    moff = 0
+    for km, sm, off in rows:
+        assert off == moff and sm >= km and sm % 2 == 0 and (sm // 2) % 2 == 1  # fp64: 2 per vector
+        moff += sm
+    tile = int(re.search(r"constexpr int FWD_MT = (\d+);", src).group(1))
+    assert tile == 64 and int(re.search(r"constexpr int FWD_M_ELEMS = (\d+);", src).group(1)) == moff
+    assert tile * moff * 8 <= 81920
+
+
 def test_schedule_model_prefers_moving_the_narrower_rows(monkeypatch):
     """The data-movement model of oeq_plan_schedule, in gathered elements per edge
     and channel, an atomic add counting 6: the receiver-stationary forward gathers
