@@ -22,7 +22,9 @@ const char *oeq_status_string(oeq_status s) {
 
 const char *oeq_last_error(void) { return g_last_error.c_str(); }
 
-oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan) {
+namespace {
+
+oeq_status plan_create(const oeq_tp_desc *desc, oeq_plan **plan, bool cache_only) {
     if (!plan) return fail(OEQ_ERR_INVALID_ARG, "plan output pointer is NULL");
     *plan = nullptr;
     oeq_plan *p = new oeq_plan();
@@ -30,7 +32,7 @@ oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan) {
     oeq_status st = oeq::plan_build(desc, p, &why);
     if (st == OEQ_OK) {
         p->source = oeq::emit_source(*p);
-        st = oeq::jit_compile(*p, &why);
+        st = oeq::jit_compile(*p, &why, cache_only);
     }
     if (st != OEQ_OK) {
         delete p;
@@ -39,6 +41,12 @@ oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan) {
     *plan = p;
     return OEQ_OK;
 }
+
+}  // namespace
+
+oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan) { return plan_create(desc, plan, false); }
+
+oeq_status oeq_plan_create_cached(const oeq_tp_desc *desc, oeq_plan **plan) { return plan_create(desc, plan, true); }
 
 void oeq_plan_destroy(oeq_plan *plan) {
     if (!plan) return;

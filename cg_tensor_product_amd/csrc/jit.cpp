@@ -81,7 +81,7 @@ void write_file_atomic(const std::string &path, const std::vector<char> &data) {
 
 }  // namespace
 
-oeq_status jit_compile(oeq_plan &p, std::string *why) {
+oeq_status jit_compile(oeq_plan &p, std::string *why, bool cache_only) {
     int ver_major = 0, ver_minor = 0;
     hiprtcVersion(&ver_major, &ver_minor);
     std::ostringstream key;
@@ -99,6 +99,10 @@ oeq_status jit_compile(oeq_plan &p, std::string *why) {
         std::ofstream(dir + "/" + p.code_key + ".hip") << p.source;
     }
     if (use_cache && read_file(path, p.code)) return OEQ_OK;
+    if (cache_only) {
+        if (why) *why = "code object " + p.code_key + " is not in the cache";
+        return OEQ_ERR_JIT;
+    }
 
     hiprtcProgram prog;
     if (hiprtcCreateProgram(&prog, p.source.c_str(), "oeq_tp_conv.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS) {

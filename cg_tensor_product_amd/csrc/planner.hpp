@@ -115,8 +115,9 @@ int fwd_m_elems(const oeq_plan &p);
 // Emits the HIP source of every kernel of the plan.
 std::string emit_source(const oeq_plan &p);
 
-// Compiles p.source with hipRTC (or loads it from the on-disk cache).
-oeq_status jit_compile(oeq_plan &p, std::string *why);
+// Compiles p.source with hipRTC (or loads it from the on-disk cache); with
+// cache_only, a code object missing from the cache is an OEQ_ERR_JIT instead.
+oeq_status jit_compile(oeq_plan &p, std::string *why, bool cache_only = false);
 
 // Loads the module on the current device (once) and returns the kernel.
 oeq_status get_kernel(oeq_plan &p, const char *name, hipFunction_t *fn, std::string *why);

@@ -108,6 +108,14 @@ typedef struct oeq_plan oeq_plan; /* opaque, host-owned */
  * beside the library).  Host-only; the code object is loaded on a device at the
  * first compute call there.  *plan is set to NULL on failure. */
 oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan);
+
+/* As oeq_plan_create, but never runs the runtime compiler: returns OEQ_ERR_JIT
+ * (with *plan = NULL) when the plan's code object is not in the cache.  For
+ * callers that compile in another process and load the result here: on MI355X
+ * a forward launched from a process that had run the runtime compiler took
+ * 0.95 ms where the byte-identical code object loaded from the cache took
+ * 0.35 ms (cause not found). */
+oeq_status oeq_plan_create_cached(const oeq_tp_desc *desc, oeq_plan **plan);
 void oeq_plan_destroy(oeq_plan *plan);
 
 /* Row widths: x_dim = XD, y_dim = (L+1)^2, out_dim = OD, w_per_edge = P*U. */

@@ -164,6 +164,36 @@ def test_generated_source_has_no_packed_fp32_and_caches(tmp_path, monkeypatch):
         assert "oeq_fwd" in dis.stdout and "oeq_bwd_atomic" in dis.stdout
 
 
+def test_plan_from_cache_only_and_compiled_in_a_child(tmp_path):
+    """oeq_plan_create_cached never compiles: with an empty cache it fails with
+    OEQ_ERR_JIT and leaves the plan NULL.  Plan() then compiles in a child process, and the
+    code object it leaves in the cache loads here without compiling."""
+    import subprocess
+    import sys
+    code = r"""
+import ctypes, os, sys
+sys.path.insert(0, %r)
+import cg_tensor_product_amd as m
+L = m.lib()
+d = m._Desc()
+xs = (m._Irrep * 2)(m._Irrep(4, 0, 1), m._Irrep(4, 1, -1))
+d.x_irreps, d.n_x, d.y_lmax, d.lmax_out, d.dtype = xs, 2, 1, 1, m.OEQ_F32
+h = ctypes.c_void_p()
+assert L.oeq_plan_create_cached(ctypes.byref(d), ctypes.byref(h)) == 5 and not h.value
+assert b"not in the cache" in L.oeq_last_error()
+assert os.listdir(os.environ["OEQ_CACHE_DIR"]) == [] if os.path.isdir(os.environ["OEQ_CACHE_DIR"]) else True
+p = m.Plan("4x0e+4x1o", 1, 1, "f32")
+assert [f for f in os.listdir(os.environ["OEQ_CACHE_DIR"]) if f.endswith(".hsaco")] == [p.code_key + ".hsaco"]
+assert L.oeq_plan_create_cached(ctypes.byref(d), ctypes.byref(h)) == 0 and h.value
+L.oeq_plan_destroy(h)
+print("ok")
+""" % ROOT
+    env = dict(os.environ, OEQ_CACHE_DIR=str(tmp_path / "cache"))
+    env.pop("OEQ_PLAN_IN_PROCESS", None)
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
 def test_tile_form_rows_match_the_tables(tmp_path):
     """The tile-form forward stores, per edge and path, one Y-contracted entry for every
     (m1, m3) that a non-zero CG coefficient reaches: the emitted row sizes equal that count
