@@ -26,22 +26,27 @@ from numpy.polynomial import polynomial as _poly
 from . import real_basis
 
 
-def assoc_legendre(l: int, m: int, t: np.ndarray) -> np.ndarray:
+def assoc_legendre(l: int, m: int, t: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """P_l^m(t) = (1 - t^2)^(m/2) d^m P_l/dt^m (no Condon-Shortley phase), with
+    s = sqrt(1 - t^2) = sin(theta) passed in (taken from the vector's components,
+    which keeps it accurate near the z axis)."""
     c = np.zeros(l + 1)
     c[l] = 1.0
     p = _leg.leg2poly(c)
     dp = _poly.polyder(p, m) if m > 0 else p
-    return (1.0 - t * t) ** (m / 2.0) * _poly.polyval(t, dp)
+    return s ** m * _poly.polyval(t, dp)
 
 
 def sh_complex(l: int, vec: np.ndarray) -> np.ndarray:
+    """Complex harmonics of unit vectors: cos(theta) = z, sin(theta) = sqrt(x^2 + y^2)."""
     x, y, z = vec[:, 0], vec[:, 1], vec[:, 2]
-    theta = np.arccos(np.clip(z, -1.0, 1.0))
+    t = np.clip(z, -1.0, 1.0)
+    s = np.hypot(x, y)
     phi = np.arctan2(y, x)
     out = np.zeros((len(vec), 2 * l + 1), dtype=complex)
     for m in range(0, l + 1):
         n = math.sqrt((2 * l + 1) / (4 * math.pi) * math.factorial(l - m) / math.factorial(l + m))
-        v = n * (-1) ** m * assoc_legendre(l, m, np.cos(theta)) * np.exp(1j * m * phi)
+        v = n * (-1) ** m * assoc_legendre(l, m, t, s) * np.exp(1j * m * phi)
         out[:, m + l] = v
         if m > 0:
             out[:, -m + l] = (-1) ** m * np.conj(v)
@@ -80,7 +85,7 @@ def _legendre_parts(l: int, m: int):
     return q, _poly.polyder(q)
 
 
-def sh_grad_of_vectors(L: int, vec: np.ndarray) -> np.ndarray:
+def _sh_grad_polar(L: int, vec: np.ndarray) -> np.ndarray:
     """Gradient of sh_of_vectors with respect to the vector, [E, (L+1)^2, 3], by
     the chain rule through the polar angles:
         grad Y = (dY/dtheta) e_theta / r + (dY/dphi) e_phi / (r sin theta),
@@ -94,8 +99,7 @@ def sh_grad_of_vectors(L: int, vec: np.ndarray) -> np.ndarray:
     live = r > 0
     x, y, z = (vec[:, k] / np.where(live, r, 1.0) for k in range(3))
     ct = np.clip(z, -1.0, 1.0)
-    theta = np.arccos(ct)
-    st = np.sin(theta)
+    st = np.hypot(x, y)
     phi = np.arctan2(y, x)
     e_theta = np.stack([ct * np.cos(phi), ct * np.sin(phi), -st], axis=1)
     e_phi = np.stack([-np.sin(phi), np.cos(phi), np.zeros(E)], axis=1)
@@ -126,6 +130,40 @@ def sh_grad_of_vectors(L: int, vec: np.ndarray) -> np.ndarray:
         cols.append(gl.real)
     G = np.concatenate(cols, axis=1)
     G[~live] = 0.0
+    return G
+
+
+# Rotation used to carry vectors off the z axis: R = Ry(pi/2) takes the z axis to the x axis.
+_OFF_AXIS = (0.0, math.pi / 2, 0.0)
+
+
+def sh_grad_of_vectors(L: int, vec: np.ndarray) -> np.ndarray:
+    """Gradient of sh_of_vectors with respect to the vector, [E, (L+1)^2, 3],
+    defined for every vector.
+
+    Away from the z axis it is the polar-angle chain rule (_sh_grad_polar).  Within
+    sin(theta) < 0.5 of the axis it comes from the rotation identity instead: the
+    harmonics satisfy Y(R v) = D(R) Y(v), so Y(v) = D(R)^T Y(R v) and
+        grad Y(v) = D(R)^T grad Y(R v) R,
+    with R = Ry(pi/2), which takes every such vector to sin(theta) > 0.85, where
+    the polar form is regular.  D is the real Wigner-D of this module.  Zero for a
+    zero vector."""
+    vec = np.asarray(vec, dtype=np.float64)
+    G = _sh_grad_polar(L, vec)
+    r = np.linalg.norm(vec, axis=1)
+    live = r > 0
+    sin_t = np.zeros(len(vec))
+    sin_t[live] = np.hypot(vec[live, 0], vec[live, 1]) / r[live]
+    near = live & (sin_t < 0.5)
+    if near.any():
+        R = rotation(*_OFF_AXIS)
+        GR = _sh_grad_polar(L, vec[near] @ R.T)
+        o = 0
+        for l in range(L + 1):
+            D = wigner_d_real(l, *_OFF_AXIS)
+            blk = slice(o, o + 2 * l + 1)
+            G[near, blk, :] = np.einsum("ba,ebk,kj->eaj", D, GR[:, blk, :], R)
+            o += 2 * l + 1
     return G
 
 
