@@ -145,12 +145,13 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     int64_t gy_stride = gyp ? E * p->YD : 0;
     const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(p->bwd_groups.size()));
     const unsigned block = bwd_block(p);
+    int n_nodes = static_cast<int>(N);
     if (!gx) {
-        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride};
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
         st = launch(p, "oeq_bwd_nogx", grid, block, s, args);
     } else if (mode == OEQ_BWD_ATOMIC) {
         if ((st = fill_zero(p, gx, N * p->XD, s)) != OEQ_OK) return st;
-        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride};
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
         if ((st = launch(p, "oeq_bwd_atomic", grid, block, s, args)) != OEQ_OK) return st;
         st = untranspose(p, N, gx, s);
     } else {
@@ -158,7 +159,7 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
         void *h = w.h;
         // an x block that feeds no path is never written into the per-edge rows
         if (p->x_unused && (st = fill_zero(p, h, E * p->XD, s)) != OEQ_OK) return st;
-        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &h, &gy_target, &gW, &flags, &gy_stride};
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &h, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
         if ((st = launch(p, "oeq_bwd_rows", grid, block, s, args)) != OEQ_OK) return st;
         st = det_finish(p, N, w, gx, s);
     }
@@ -268,8 +269,9 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
         // another size would map blocks past the last receiver
         if (kernel_groups(name) != NG)
             return fail(OEQ_ERR_UNSUPPORTED, "internal: " + name + " is built for another path-group count");
+        int n_nodes = static_cast<int>(N);
         void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &ggx, &ggY, &ggW, &dx_target, &dy_target, &dW, &dg, &flags,
-                        &gy_stride};
+                        &gy_stride, &n_nodes};
         return launch(p, name.c_str(), grid, bwd_block(p), s, args);
     };
     if (level == 0) {

@@ -36,7 +36,8 @@ oeq_status oeq_tp_conv_fwd_vec(const oeq_plan *plan, int64_t N, int64_t E, const
     if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
     if (E > 0 && (!x || !vec || !W)) return fail(OEQ_ERR_INVALID_ARG, "x, vec or W is NULL");
     oeq_plan *p = const_cast<oeq_plan *>(plan);
-    void *args[] = {&rowptr, &src, &x, &vec, &W, &out};
+    int n_nodes = static_cast<int>(N);
+    void *args[] = {&rowptr, &src, &x, &vec, &W, &out, &n_nodes};
     return launch(p, "oeq_fwd_vec", static_cast<unsigned>(N), fwd_block(p), static_cast<hipStream_t>(stream), args);
 }
 
@@ -161,7 +162,8 @@ oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
     char *ws = static_cast<char *>(workspace);
     if ((st = radial_hidden(p, E, vec, r_cut, kFusedHidden, W1, ws, w, s)) != OEQ_OK) return st;
     void *hid = ws + w.h;
-    void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &out};
+    int n_nodes = static_cast<int>(N);
+    void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &out, &n_nodes};
     return launch(p, "oeq_fwd_radial", static_cast<unsigned>(N), fwd_block(p), s, args);
 }
 
@@ -263,14 +265,15 @@ oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
     int64_t gy_stride = G > 1 ? E * p->YD : 0, dh_stride = G > 1 ? E * H : 0;
     const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(G));
     const unsigned block = bwd_block(p);
+    int n_nodes = static_cast<int>(N);
     if (!gx) {
         void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &g, &gx, &gy_target, &dh_target, &w2p, &flags, &gy_stride,
-                        &dh_stride};
+                        &dh_stride, &n_nodes};
         if ((st = launch(p, "oeq_bwd_radial_nogx", grid, block, s, args)) != OEQ_OK) return st;
     } else if (!det) {
         if ((st = fill_zero(p, gx, N * p->XD, s)) != OEQ_OK) return st;
         void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &g, &gx, &gy_target, &dh_target, &w2p, &flags, &gy_stride,
-                        &dh_stride};
+                        &dh_stride, &n_nodes};
         if ((st = launch(p, "oeq_bwd_radial_atomic", grid, block, s, args)) != OEQ_OK) return st;
         if ((st = untranspose(p, N, gx, s)) != OEQ_OK) return st;
     } else {
@@ -279,7 +282,7 @@ oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
         // each group writes the x blocks of its own paths; a block no path uses stays zero
         if (p->x_unused && (st = fill_zero(p, hrows, E * p->XD, s)) != OEQ_OK) return st;
         void *args[] = {&rowptr, &src, &x, &Y, &hid, &W2, &g, &hrows, &gy_target, &dh_target, &w2p, &flags,
-                        &gy_stride, &dh_stride};
+                        &gy_stride, &dh_stride, &n_nodes};
         if ((st = launch(p, "oeq_bwd_radial_rows", grid, block, s, args)) != OEQ_OK) return st;
         if ((st = det_finish(p, N, w.conv, gx, s)) != OEQ_OK) return st;
     }

@@ -71,7 +71,8 @@ oeq_status oeq_tp_conv_fwd_sender(const oeq_plan *plan, int64_t N, int64_t E, co
     oeq_plan *p = const_cast<oeq_plan *>(plan);
     hipStream_t s = static_cast<hipStream_t>(stream);
     if ((st = fill_zero(p, out, N * p->OD, s)) != OEQ_OK || E == 0) return st;
-    void *args[] = {&srowptr, &sperm, &sdst, &x, &Y, &W, &out};
+    int n_nodes = static_cast<int>(N);
+    void *args[] = {&srowptr, &sperm, &sdst, &x, &Y, &W, &out, &n_nodes};
     if ((st = launch(p, "oeq_fwd_sender", static_cast<unsigned>(N), fwd_block(p), s, args)) != OEQ_OK) return st;
     void *uargs[] = {&out};
     return launch(p, "oeq_out_untranspose", static_cast<unsigned>(N), 256, s, uargs);
@@ -98,7 +99,8 @@ oeq_status oeq_tp_conv_bwd_sender(const oeq_plan *plan, int64_t N, int64_t E, co
     void *gy_target = gyp ? w.gy_part : gY;
     int64_t gy_stride = gyp ? E * p->YD : 0;
     const unsigned grid = static_cast<unsigned>(N * static_cast<int64_t>(p->bwd_groups.size()));
-    void *args[] = {&srowptr, &sperm, &sdst, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride};
+    int n_nodes = static_cast<int>(N);
+    void *args[] = {&srowptr, &sperm, &sdst, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
     if ((st = launch(p, "oeq_bwd_sender", grid, bwd_block(p), s, args)) != OEQ_OK) return st;
     return gyp ? gy_combine(p, w, gY, E, s) : OEQ_OK;
 }

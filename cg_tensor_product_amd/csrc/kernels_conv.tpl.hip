@@ -163,6 +163,7 @@ oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_
         grp = w / UCH;
         uc = w - grp * UCH;
         r = blockIdx.x;
+        if (r >= n_nodes) return;
         wc = uc;
     }
     if constexpr (FWD_LDS) {
@@ -177,7 +178,8 @@ oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_
 // (no Y tensor): each wave computes the harmonics of the edge it streams.
 extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
 oeq_fwd_vec(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
-            const real_t *__restrict__ vec, const real_t *__restrict__ W, real_t *__restrict__ out) {
+            const real_t *__restrict__ vec, const real_t *__restrict__ W, real_t *__restrict__ out, int n_nodes) {
+    if ((int)blockIdx.x >= n_nodes) return;
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
     fwd_dispatch<0, true>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, vec, W, out, false);
@@ -316,9 +318,10 @@ __device__ __forceinline__ void bwd_body(const int *__restrict__ rowptr, const i
                                          const real_t *__restrict__ x, const real_t *__restrict__ Y,
                                          const real_t *__restrict__ W, const real_t *__restrict__ g,
                                          real_t *__restrict__ gx, real_t *__restrict__ gY,
-                                         real_t *__restrict__ gW, int flags, i64 gy_stride) {
+                                         real_t *__restrict__ gW, int flags, i64 gy_stride, int n_nodes) {
     __shared__ GyStage st;
     const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
+    if (r >= n_nodes) return;  // a grid larger than the plan's groups x nodes reads nothing
     const int wv = uni(threadIdx.x >> 6);
     bwd_dispatch<GXMODE, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, gx,
                             gY + grp * gy_stride, gW, flags);
@@ -327,22 +330,25 @@ __device__ __forceinline__ void bwd_body(const int *__restrict__ rowptr, const i
 extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
 oeq_bwd_nogx(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
              const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
-             real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
-    bwd_body<0>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride);
+             real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride,
+             int n_nodes) {
+    bwd_body<0>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride, n_nodes);
 }
 
 extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
 oeq_bwd_atomic(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
                const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
-               real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
-    bwd_body<1>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride);
+               real_t *__restrict__ gx, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride,
+               int n_nodes) {
+    bwd_body<1>(rowptr, src, x, Y, W, g, gx, gY, gW, flags, gy_stride, n_nodes);
 }
 
 extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
 oeq_bwd_rows(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
              const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,
-             real_t *__restrict__ h, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride) {
-    bwd_body<2>(rowptr, src, x, Y, W, g, h, gY, gW, flags, gy_stride);
+             real_t *__restrict__ h, real_t *__restrict__ gY, real_t *__restrict__ gW, int flags, i64 gy_stride,
+             int n_nodes) {
+    bwd_body<2>(rowptr, src, x, Y, W, g, h, gY, gW, flags, gy_stride, n_nodes);
 }
 
 // Partial rows of several groups added in group order: out[i] = sum_g part[g n + i].

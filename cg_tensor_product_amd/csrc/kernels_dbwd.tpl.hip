@@ -140,10 +140,11 @@ __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const 
                                           const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,
                                           const real_t *__restrict__ ggW, real_t *__restrict__ dx,
                                           real_t *__restrict__ dY, real_t *__restrict__ dW,
-                                          real_t *__restrict__ dg, int flags, i64 gy_stride) {
+                                          real_t *__restrict__ dg, int flags, i64 gy_stride, int n_nodes) {
     __shared__ GyStage st;
     constexpr int NG = DbwdSet<DS>::N;
     const int r = blockIdx.x / NG, grp = blockIdx.x - r * NG;
+    if (r >= n_nodes) return;  // a grid larger than the kernel's groups x nodes reads nothing
     const int wv = uni(threadIdx.x >> 6);
     dbwd_dispatch<TM, OUT, DS, 0>(st, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx,
                          dY + grp * gy_stride, dW, dg, flags);
@@ -158,10 +159,10 @@ __device__ __forceinline__ void dbwd_body(const int *__restrict__ rowptr, const 
         const real_t *__restrict__ Y, const real_t *__restrict__ W, const real_t *__restrict__ g,  \
         const real_t *__restrict__ ggx, const real_t *__restrict__ ggY,                            \
         const real_t *__restrict__ ggW, real_t *__restrict__ dx, real_t *__restrict__ dY,          \
-        real_t *__restrict__ dW, real_t *__restrict__ dg, int flags, i64 gy_stride) {              \
+        real_t *__restrict__ dW, real_t *__restrict__ dg, int flags, i64 gy_stride, int n_nodes) { \
         if constexpr (!(DS && OUT == 15) || DBWD_TWO_SETS)                                         \
             dbwd_body<TM, OUT, DS>(rowptr, src, x, Y, W, g, ggx, ggY, ggW, dx, dY, dW, dg, flags,  \
-                                   gy_stride);                                                     \
+                                   gy_stride, n_nodes);                                            \
     }
 OEQ_DBWD_KERNEL(oeq_dbwd_1, 1, 15, false)
 OEQ_DBWD_KERNEL(oeq_dbwd_2, 2, 15, false)

@@ -78,7 +78,8 @@ __device__ __forceinline__ void fwd_radial_dispatch(int grp, int r, int u, const
 extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
 oeq_fwd_radial(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
                const real_t *__restrict__ Y, const real_t *__restrict__ hid, const real_t *__restrict__ W2,
-               real_t *__restrict__ out) {
+               real_t *__restrict__ out, int n_nodes) {
+    if ((int)blockIdx.x >= n_nodes) return;
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
     fwd_radial_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, Y, hid, W2, out);
@@ -218,9 +219,11 @@ __device__ __forceinline__ void bwd_radial_dispatch(GyStage &st, GyStage &sth, i
         const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,      \
         const real_t *__restrict__ Y, const real_t *__restrict__ hid, const real_t *__restrict__ W2,    \
         const real_t *__restrict__ g, real_t *__restrict__ gx, real_t *__restrict__ gY,                 \
-        real_t *__restrict__ dh, real_t *__restrict__ dw2p, int flags, i64 gy_stride, i64 dh_stride) {  \
+        real_t *__restrict__ dh, real_t *__restrict__ dw2p, int flags, i64 gy_stride, i64 dh_stride,    \
+        int n_nodes) {                                                                                  \
         __shared__ GyStage st, sth;                                                                     \
         const int r = blockIdx.x / NGR, grp = blockIdx.x - r * NGR;                                     \
+        if (r >= n_nodes) return;                                                                       \
         const int wv = uni(threadIdx.x >> 6);                                                           \
         bwd_radial_dispatch<GXMODE, 0>(st, sth, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, x, Y, \
                                        hid, W2, g, gx, gY + grp * gy_stride, dh + grp * dh_stride, dw2p,  \

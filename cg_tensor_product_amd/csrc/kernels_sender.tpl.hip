@@ -62,7 +62,8 @@ __device__ __forceinline__ void fwd_sender_dispatch(int grp, int s, int u, const
 extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
 oeq_fwd_sender(const int *__restrict__ srowptr, const int *__restrict__ sperm, const int *__restrict__ sdst,
                const real_t *__restrict__ x, const real_t *__restrict__ Y, const real_t *__restrict__ W,
-               real_t *__restrict__ out) {
+               real_t *__restrict__ out, int n_nodes) {
+    if ((int)blockIdx.x >= n_nodes) return;
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
     fwd_sender_dispatch<0>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), srowptr, sperm, sdst, x, Y, W, out);
@@ -170,9 +171,10 @@ extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
 oeq_bwd_sender(const int *__restrict__ srowptr, const int *__restrict__ sperm, const int *__restrict__ sdst,
                const real_t *__restrict__ x, const real_t *__restrict__ Y, const real_t *__restrict__ W,
                const real_t *__restrict__ g, real_t *__restrict__ gx, real_t *__restrict__ gY,
-               real_t *__restrict__ gW, int flags, i64 gy_stride) {
+               real_t *__restrict__ gW, int flags, i64 gy_stride, int n_nodes) {
     __shared__ GyStage st;
     const int s = blockIdx.x / NGB, grp = blockIdx.x - s * NGB;
+    if (s >= n_nodes) return;
     const int wv = uni(threadIdx.x >> 6);
     bwd_sender_dispatch<0>(st, s, grp, wv, wv * 64 + (threadIdx.x & 63), srowptr, sperm, sdst, x, Y, W, g, gx,
                            gY + grp * gy_stride, gW, flags);

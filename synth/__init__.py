@@ -12,7 +12,9 @@ other sizes are the small cases used for parity tests.
 Recipe (every tensor from its own child of one SeedSequence):
   * graph:  each receiver r draws its in-degree's worth of distinct senders
             uniformly from {0..N-1} minus {r}, sorted ascending inside the row;
-            the edge id is the position in that receiver-major order.
+            the edge id is the position in that receiver-major order.  Multigraph
+            workloads (edge-case tests) draw with replacement from all N nodes
+            instead: self-loops and repeated (s, r) edges.
   * edge vectors: z ~ N(0, I3), normalised; Y = real spherical harmonics of
             them with component normalisation (sum over m of Y^2 = 2l+1),
             degrees 0..L, m = -l..l, l=1 ordered (y, z, x).
@@ -46,6 +48,7 @@ class Workload:
     seed: int
     ops: tuple = ("fwd", "bwd")
     degrees: Optional[tuple] = None  # per-receiver in-degree (non-uniform graphs)
+    multi: bool = False              # senders drawn with replacement, the receiver included
 
     @property
     def U(self) -> int:
@@ -108,11 +111,15 @@ WORKLOADS = {
 # Graph
 # ---------------------------------------------------------------------------
 
-def make_graph(n_nodes: int, degrees: Sequence[int], rng: np.random.Generator):
-    """Receiver-sorted CSR: rowptr[N+1] (int32), src[E] (int32)."""
+def make_graph(n_nodes: int, degrees: Sequence[int], rng: np.random.Generator, multi: bool = False):
+    """Receiver-sorted CSR: rowptr[N+1] (int32), src[E] (int32).
+
+    multi=False: distinct senders other than the receiver (a neighbour list).
+    multi=True: senders drawn uniformly with replacement from all N nodes, so a row
+    may hold self-loops (s = r) and repeated (s, r) edges; still sorted in the row."""
     degrees = np.asarray(degrees, dtype=np.int64)
     assert degrees.shape == (n_nodes,)
-    if n_nodes > 0 and degrees.max(initial=0) > n_nodes - 1:
+    if not multi and n_nodes > 0 and degrees.max(initial=0) > n_nodes - 1:
         raise ValueError("in-degree larger than N-1 cannot have distinct senders")
     rowptr = np.zeros(n_nodes + 1, dtype=np.int64)
     np.cumsum(degrees, out=rowptr[1:])
@@ -124,8 +131,11 @@ def make_graph(n_nodes: int, degrees: Sequence[int], rng: np.random.Generator):
         d = int(degrees[r])
         if d == 0:
             continue
-        v = rng.choice(n_nodes - 1, size=d, replace=False)
-        v = v + (v >= r)             # skip the receiver itself
+        if multi:
+            v = rng.integers(0, n_nodes, size=d)
+        else:
+            v = rng.choice(n_nodes - 1, size=d, replace=False)
+            v = v + (v >= r)         # skip the receiver itself
         v.sort()
         src[rowptr[r]:rowptr[r + 1]] = v
     return rowptr.astype(np.int32), src
@@ -211,7 +221,7 @@ def generate(wl: Workload, n_paths: int, out_dim: int, want=("x", "Y", "W", "g")
     (they follow from the path list, which this module does not compute)."""
     rngs = _children(wl.seed)
     degrees = wl.degrees if wl.degrees is not None else [wl.degree] * wl.n_nodes
-    rowptr, src = make_graph(wl.n_nodes, degrees, rngs[_GRAPH])
+    rowptr, src = make_graph(wl.n_nodes, degrees, rngs[_GRAPH], multi=wl.multi)
     E = int(rowptr[-1])
     dt = wl.np_dtype()
     out = {"rowptr": rowptr, "src": src, "N": wl.n_nodes, "E": E}

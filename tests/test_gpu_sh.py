@@ -26,10 +26,16 @@ def _need_gpu():
     torch.cuda.set_device(0)
 
 
-def _case(name):
+def _case(name, special=False):
     wl = SMALL[name]
     d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
     inp = synth.generate(wl, d.P, d.out_dim, want=("x", "evec", "W", "g"))
+    if special:
+        # the first edges carry the zero vector, the six axis directions (+-z included), a
+        # tiny and a huge vector
+        sv = _special_vectors(wl.np_dtype())
+        k = min(len(sv), inp["E"])
+        inp["evec"][:k] = sv[:k]
     inp["Y"] = sphere.sh_of_vectors(wl.y_lmax, inp["evec"])       # the oracle's Y of the same vectors
     return wl, d, inp, plan_for(wl)
 
@@ -56,19 +62,23 @@ def test_sph_harm_parity(name):
 @pytest.mark.parametrize("name", NAMES)
 def test_sph_harm_bwd_parity(name):
     wl, d, inp, plan = _case(name)
-    vec = np.concatenate([inp["evec"], np.zeros((1, 3), dtype=wl.np_dtype())])
+    special = _special_vectors(wl.np_dtype())
+    vec = np.concatenate([inp["evec"], special])
     gY = synth.extra_normal(wl, (len(vec), plan.y_dim), 3)
     gvec = oeq.oeq_sph_harm_bwd(plan, to_dev(vec), to_dev(gY))
     torch.cuda.synchronize()
     ref = np.einsum("em,emk->ek", gY.astype(np.float64), sphere.sh_grad_of_vectors(wl.y_lmax, vec))
     got = gvec.cpu().numpy()
     assert rel_l2(got, ref) <= RTOL[wl.dtype]
-    assert not got[-1].any()                                        # zero vector: zero gradient
+    # the special vectors alone (the six axis directions, +-z included; tiny and huge)
+    n = len(inp["evec"])
+    assert rel_l2(got[n + 1:], ref[n + 1:]) <= RTOL[wl.dtype]
+    assert not got[n].any()                                         # zero vector: zero gradient
 
 
 @pytest.mark.parametrize("name", NAMES)
 def test_fwd_vec_parity(name):
-    wl, d, inp, plan = _case(name)
+    wl, d, inp, plan = _case(name, special=True)
     print(f"[fwd vec] {name}", flush=True)
     dev = {k: to_dev(inp[k]) for k in ("rowptr", "src", "x", "evec", "W")}
     out = oeq.oeq_tp_conv_fwd_vec(plan, dev["rowptr"], dev["src"], dev["x"], dev["evec"], dev["W"])
@@ -80,7 +90,7 @@ def test_fwd_vec_parity(name):
 @pytest.mark.parametrize("mode", ["atomic", "deterministic"])
 @pytest.mark.parametrize("name", NAMES)
 def test_bwd_vec_parity(name, mode):
-    wl, d, inp, plan = _case(name)
+    wl, d, inp, plan = _case(name, special=True)
     print(f"[bwd vec] {name} {mode}", flush=True)
     dev = {k: to_dev(inp[k]) for k in ("rowptr", "src", "x", "evec", "W", "g")}
     gx, gvec, gW = oeq.oeq_tp_conv_bwd_vec(plan, dev["rowptr"], dev["src"], dev["x"], dev["evec"], dev["W"],
@@ -92,6 +102,8 @@ def test_bwd_vec_parity(name, mode):
     assert rel_l2(gx.cpu().numpy(), rx) <= tol
     assert rel_l2(gW.cpu().numpy(), rW) <= tol
     assert rel_l2(gvec.cpu().numpy(), rvec) <= tol
+    k = min(len(_special_vectors(wl.np_dtype())), inp["E"])
+    assert rel_l2(gvec[:k].cpu().numpy(), rvec[:k]) <= tol            # the special vectors' edges alone
     # partial request: the vector gradient alone
     _, gv2, _ = oeq.oeq_tp_conv_bwd_vec(plan, dev["rowptr"], dev["src"], dev["x"], dev["evec"], dev["W"], dev["g"],
                                         mode=mode, want=("vec",))
