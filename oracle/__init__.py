@@ -60,6 +60,8 @@ def lib():
         L.oracle_cg_real.argtypes = [i, i, i, p]
         L.oracle_enumerate_paths.restype = i
         L.oracle_enumerate_paths.argtypes = [i, p, p, i, i, p, i]
+        L.oracle_enumerate_paths_y.restype = i
+        L.oracle_enumerate_paths_y.argtypes = [i, p, p, i, p, p, i, p, i]
         L.oracle_sender_csr.restype = None
         L.oracle_sender_csr.argtypes = [i64, i64, p, p, p]
         L.oracle_fwd.restype = i
@@ -130,14 +132,22 @@ def cg_real(l1, l2, l3) -> np.ndarray:
     return C
 
 
-def enumerate_paths(x_irreps, y_lmax: int, l3_max: int):
-    """[(i1, l2, l3, p3), ...] for x irreps ((mul, l, parity), ...)."""
+def enumerate_paths(x_irreps, y_lmax: int, l3_max: int, y_irreps=None):
+    """[(i1, j, l3, p3), ...] for x irreps ((mul, l, parity), ...): j is the Y
+    block, which for the default Y (degrees 0..y_lmax with parity (-1)^l) is the
+    degree l2 itself."""
     xl = _i32([l for _, l, _ in x_irreps])
     xp = _i32([p for _, _, p in x_irreps])
     cap = 256
     out = np.zeros(4 * cap, dtype=np.int32)
-    n = lib().oracle_enumerate_paths(len(xl), _ptr(xl), _ptr(xp), y_lmax, l3_max,
-                                     _ptr(out), cap)
+    if y_irreps is None:
+        n = lib().oracle_enumerate_paths(len(xl), _ptr(xl), _ptr(xp), y_lmax, l3_max,
+                                         _ptr(out), cap)
+    else:
+        yl = _i32([l for _, l, _ in y_irreps])
+        yp = _i32([p for _, _, p in y_irreps])
+        n = lib().oracle_enumerate_paths_y(len(xl), _ptr(xl), _ptr(xp), len(yl), _ptr(yl),
+                                           _ptr(yp), l3_max, _ptr(out), cap)
     assert n <= cap
     return [tuple(int(v) for v in out[4 * k:4 * k + 4]) for k in range(n)]
 
@@ -148,46 +158,63 @@ def enumerate_paths(x_irreps, y_lmax: int, l3_max: int):
 
 class _CDesc(ctypes.Structure):
     _fields_ = [("nx", ctypes.c_int), ("xl", ctypes.c_void_p), ("U", ctypes.c_int),
-                ("L", ctypes.c_int), ("np", ctypes.c_int), ("p_i1", ctypes.c_void_p),
-                ("p_l2", ctypes.c_void_p), ("p_l3", ctypes.c_void_p),
+                ("ny", ctypes.c_int), ("yl", ctypes.c_void_p),
+                ("np", ctypes.c_int), ("p_i1", ctypes.c_void_p),
+                ("p_iy", ctypes.c_void_p), ("p_l3", ctypes.c_void_p),
                 ("p_ob", ctypes.c_void_p), ("nob", ctypes.c_int),
                 ("ob_l", ctypes.c_void_p)]
 
 
 class Desc:
-    """x irreps (uniform multiplicity U), Y degrees 0..L, a path list and the
-    output blocks.  Default: all triangle-allowed paths up to l3_max, one output
+    """x irreps (uniform multiplicity U), Y blocks, a path list and the output
+    blocks.  Y: y_irreps ((1, l, parity), ...) in row order, or by default the
+    harmonics of degrees 0..y_lmax with parity (-1)^l.  Paths are
+    (x block, Y block, l3, output block); with the default Y the Y block index is
+    the degree.  Default paths: all triangle-allowed ones up to l3_max, one output
     block per path, in enumeration order."""
 
     def __init__(self, x_irreps, y_lmax: int, l3_max: int = 3,
-                 paths: Optional[Sequence] = None, out_l: Optional[Sequence[int]] = None):
+                 paths: Optional[Sequence] = None, out_l: Optional[Sequence[int]] = None,
+                 y_irreps=None):
         self.x_irreps = tuple(tuple(t) for t in x_irreps)
         muls = {m for m, _, _ in self.x_irreps}
         if len(muls) != 1:
             raise ValueError("channel-wise product needs one multiplicity")
         self.U = muls.pop()
-        self.L = y_lmax
+        if y_irreps is None:
+            y_irreps = tuple((1, l, 1 if l % 2 == 0 else -1) for l in range(y_lmax + 1))
+        self.y_irreps = tuple(tuple(t) for t in y_irreps)
+        if any(m != 1 for m, _, _ in self.y_irreps):
+            raise ValueError("Y blocks carry one channel each")
+        self.yl = [l for _, l, _ in self.y_irreps]
+        self.yoff = [int(v) for v in np.cumsum([0] + [2 * l + 1 for l in self.yl])[:-1]]
+        self.L = max(self.yl)
         if paths is None:
-            en = enumerate_paths(self.x_irreps, y_lmax, l3_max)
-            paths = [(i1, l2, l3, k) for k, (i1, l2, l3, _) in enumerate(en)]
+            en = enumerate_paths(self.x_irreps, y_lmax, l3_max, y_irreps=self.y_irreps)
+            paths = [(i1, j, l3, k) for k, (i1, j, l3, _) in enumerate(en)]
             out_l = [l3 for (_, _, l3, _) in en]
         self.paths = [tuple(p) for p in paths]
         self.out_l = list(out_l)
         self.xl = [l for _, l, _ in self.x_irreps]
         self.P = len(self.paths)
         self.x_dim = self.U * sum(2 * l + 1 for l in self.xl)
-        self.y_dim = (y_lmax + 1) ** 2
+        self.y_dim = sum(2 * l + 1 for l in self.yl)
         self.out_dim = self.U * sum(2 * l + 1 for l in self.out_l)
         # keep the arrays alive for the C struct
         self._xl = _i32(self.xl)
+        self._yl = _i32(self.yl)
         self._i1 = _i32([p[0] for p in self.paths])
-        self._l2 = _i32([p[1] for p in self.paths])
+        self._iy = _i32([p[1] for p in self.paths])
         self._l3 = _i32([p[2] for p in self.paths])
         self._ob = _i32([p[3] for p in self.paths])
         self._obl = _i32(self.out_l)
-        self._c = _CDesc(len(self.xl), _ptr(self._xl), self.U, y_lmax, self.P,
-                         _ptr(self._i1), _ptr(self._l2), _ptr(self._l3), _ptr(self._ob),
+        self._c = _CDesc(len(self.xl), _ptr(self._xl), self.U, len(self.yl), _ptr(self._yl), self.P,
+                         _ptr(self._i1), _ptr(self._iy), _ptr(self._l3), _ptr(self._ob),
                          len(self.out_l), _ptr(self._obl))
+
+    def path_l2(self, p: int) -> int:
+        """Degree of path p's Y block."""
+        return self.yl[self.paths[p][1]]
 
     @property
     def cptr(self):

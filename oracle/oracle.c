@@ -32,7 +32,9 @@
  *
  * Layouts (one convention, stated once):
  *   x  [N, XD]  block i (degree l_i, U channels) at xoff_i, element u*(2l_i+1)+(m+l_i)
- *   Y  [E, (L+1)^2]  element l2*l2 + (m2+l2)
+ *   Y  [E, YD]  Y block j (degree l_j, one channel) at yoff_j = sum of (2l+1) over the
+ *               blocks before it, element yoff_j + (m2+l_j); with the blocks 0e, 1o,
+ *               2e, .. L this is element l2*l2 + (m2+l2)
  *   W  [E, P, U]
  *   out[N, OD]  output block o (degree l_o) at ooff_o, element u*(2l_o+1)+(m+l_o)
  * Edge e lies in receiver row r when rowptr[r] <= e < rowptr[r+1]; its sender
@@ -195,28 +197,42 @@ int oracle_cg_real(int l1, int l2, int l3, double *C) {
 /* Path enumeration (all triangle-allowed outputs up to l3max).        */
 /* ------------------------------------------------------------------ */
 
-/* x blocks in descriptor order, then l2 = 0..L, then l3 = |l1-l2|..min(l1+l2, l3max).
- * Output parity p3 = p1 * (-1)^l2.  Writes rows (i1, l2, l3, p3) into out[4*k];
- * returns the number of paths (or the number that would be written, if larger
- * than max_paths). */
-int oracle_enumerate_paths(int nx, const int *xl, const int *xpar, int L,
-                           int l3max, int *out, int max_paths) {
+/* x blocks in descriptor order, then the Y blocks in their order, then
+ * l3 = |l1-l2|..min(l1+l2, l3max), l2 the Y block's degree.  Output parity
+ * p3 = p1 * pY (the product of the two inputs' parities).  Writes rows
+ * (i1, Y block, l3, p3) into out[4*k]; returns the number of paths (or the number
+ * that would be written, if larger than max_paths). */
+int oracle_enumerate_paths_y(int nx, const int *xl, const int *xpar, int ny, const int *yl,
+                             const int *ypar, int l3max, int *out, int max_paths) {
     int k = 0;
     for (int i = 0; i < nx; ++i)
-        for (int l2 = 0; l2 <= L; ++l2) {
+        for (int j = 0; j < ny; ++j) {
+            int l2 = yl[j];
             int lo = abs(xl[i] - l2), hi = xl[i] + l2;
             if (hi > l3max) hi = l3max;
             for (int l3 = lo; l3 <= hi; ++l3) {
                 if (k < max_paths) {
                     out[4 * k + 0] = i;
-                    out[4 * k + 1] = l2;
+                    out[4 * k + 1] = j;
                     out[4 * k + 2] = l3;
-                    out[4 * k + 3] = xpar[i] * ((l2 & 1) ? -1 : 1);
+                    out[4 * k + 3] = xpar[i] * ypar[j];
                 }
                 ++k;
             }
         }
     return k;
+}
+
+/* The spherical harmonics of degrees 0..L as Y blocks (degree l, parity (-1)^l). */
+int oracle_enumerate_paths(int nx, const int *xl, const int *xpar, int L,
+                           int l3max, int *out, int max_paths) {
+    int yl[ORACLE_LMAX + 1], ypar[ORACLE_LMAX + 1];
+    if (L < 0 || L > ORACLE_LMAX) return 0;
+    for (int l = 0; l <= L; ++l) {
+        yl[l] = l;
+        ypar[l] = (l & 1) ? -1 : 1;
+    }
+    return oracle_enumerate_paths_y(nx, xl, xpar, L + 1, yl, ypar, l3max, out, max_paths);
 }
 
 /* ------------------------------------------------------------------ */
@@ -227,10 +243,11 @@ typedef struct {
     int nx;            /* number of x blocks                                */
     const int *xl;     /* degree of each x block (all with U channels)      */
     int U;             /* channels                                          */
-    int L;             /* Y carries degrees 0..L                            */
+    int ny;            /* number of Y blocks (one channel each)             */
+    const int *yl;     /* degree of each Y block, in row order              */
     int np;            /* number of paths                                   */
     const int *p_i1;   /* x block of each path                              */
-    const int *p_l2;   /* Y degree of each path                             */
+    const int *p_iy;   /* Y block of each path                              */
     const int *p_l3;   /* output degree of each path                        */
     const int *p_ob;   /* output block of each path                         */
     int nob;           /* number of output blocks                           */
@@ -244,18 +261,18 @@ typedef struct {
     int m3[ORACLE_NM * ORACLE_NM * ORACLE_NM];
     double c[ORACLE_NM * ORACLE_NM * ORACLE_NM];
     int64_t xoff, ooff; /* block offsets within a node row                 */
-    int n1, n3;         /* 2l1+1, 2l3+1                                   */
-    int yoff;           /* l2*l2                                          */
+    int n1, n2, n3;     /* 2l1+1, 2l2+1, 2l3+1                            */
+    int yoff;           /* offset of the path's Y block in a Y row        */
 } oracle_path;
 
 /* Returns 0 on success, -1 on an invalid description.  Fills the per-path
  * tables and the row widths. */
 static int build_paths(const oracle_desc *d, oracle_path *pt, int64_t *xd,
                        int64_t *od, int *yd) {
-    if (d->nx <= 0 || d->U <= 0 || d->L < 0 || d->L > ORACLE_LMAX || d->np < 0 ||
-        d->nob < 0)
+    if (d->nx <= 0 || d->U <= 0 || d->ny <= 0 || d->ny > 64 || d->np < 0 || d->nob < 0)
         return -1;
     int64_t xoff[64], ooff[64];
+    int yoff[64];
     if (d->nx > 64 || d->nob > 64) return -1;
     int64_t acc = 0;
     for (int i = 0; i < d->nx; ++i) {
@@ -271,11 +288,18 @@ static int build_paths(const oracle_desc *d, oracle_path *pt, int64_t *xd,
         acc += (int64_t)d->U * (2 * d->ob_l[o] + 1);
     }
     *od = acc;
-    *yd = (d->L + 1) * (d->L + 1);
+    int ya = 0;
+    for (int j = 0; j < d->ny; ++j) {
+        if (d->yl[j] < 0 || d->yl[j] > ORACLE_LMAX) return -1;
+        yoff[j] = ya;
+        ya += 2 * d->yl[j] + 1;
+    }
+    *yd = ya;
     for (int p = 0; p < d->np; ++p) {
-        int i1 = d->p_i1[p], l2 = d->p_l2[p], l3 = d->p_l3[p], ob = d->p_ob[p];
-        if (i1 < 0 || i1 >= d->nx || l2 < 0 || l2 > d->L || ob < 0 || ob >= d->nob)
+        int i1 = d->p_i1[p], iy = d->p_iy[p], l3 = d->p_l3[p], ob = d->p_ob[p];
+        if (i1 < 0 || i1 >= d->nx || iy < 0 || iy >= d->ny || ob < 0 || ob >= d->nob)
             return -1;
+        int l2 = d->yl[iy];
         if (d->ob_l[ob] != l3) return -1;
         int l1 = d->xl[i1];
         double C[ORACLE_NM * ORACLE_NM * ORACLE_NM];
@@ -296,8 +320,9 @@ static int build_paths(const oracle_desc *d, oracle_path *pt, int64_t *xd,
         pt[p].xoff = xoff[i1];
         pt[p].ooff = ooff[ob];
         pt[p].n1 = n1;
+        pt[p].n2 = n2;
         pt[p].n3 = n3;
-        pt[p].yoff = l2 * l2;
+        pt[p].yoff = yoff[iy];
     }
     return 0;
 }

@@ -26,11 +26,12 @@ def _dense_fwd(d, rowptr, src, x, Y, W):
     xoff = np.cumsum([0] + [d.U * (2 * l + 1) for l in d.xl])
     ooff = np.cumsum([0] + [d.U * (2 * l + 1) for l in d.out_l])
     out = np.zeros((N, d.out_dim))
-    for p, (i1, l2, l3, ob) in enumerate(d.paths):
-        l1 = d.xl[i1]
+    yoff = np.cumsum([0] + [2 * l + 1 for l in d.yl])
+    for p, (i1, iy, l3, ob) in enumerate(d.paths):
+        l1, l2 = d.xl[i1], d.yl[iy]
         C = oracle.cg_real(l1, l2, l3)
         xb = xs[:, xoff[i1]:xoff[i1 + 1]].reshape(E, d.U, 2 * l1 + 1)
-        yb = Y[:, l2 * l2:(l2 + 1) ** 2]
+        yb = Y[:, yoff[iy]:yoff[iy + 1]]
         msg = np.einsum("eua,eb,abc,eu->euc", xb, yb, C, W[:, p, :])
         out[:, ooff[ob]:ooff[ob + 1]] += A_recv.T @ msg.reshape(E, -1)
     return out
@@ -334,3 +335,80 @@ def test_generator_graph_properties():
     assert inp["W"].shape == (1024, 6, 8) and inp["x"].dtype == np.float64
     again = synth.generate(wl, d.P, d.out_dim)
     assert np.array_equal(again["W"], inp["W"]) and np.array_equal(again["src"], src)
+
+
+# ---------------------------------------------------------------------------
+# Y given as a list of irreps (any degrees, in any order, with either parity)
+# ---------------------------------------------------------------------------
+
+Y_SUBSET = ((1, 2, 1), (1, 0, 1), (1, 1, 1))      # 2e + 0e + 1e: no degree 3, a pseudovector, unsorted
+
+
+def test_path_enumeration_with_y_irreps():
+    # x = 1o; Y = 0e + 1e: 1o x 0e -> 1o; 1o x 1e -> 0o, 1o, 2o (parity -1 * +1)
+    en = oracle.enumerate_paths(((4, 1, -1),), 0, 3, y_irreps=((1, 0, 1), (1, 1, 1)))
+    assert en == [(0, 0, 1, -1), (0, 1, 0, -1), (0, 1, 1, -1), (0, 1, 2, -1)]
+    # the default Y is the harmonics 0e, 1o, 2e, 3o: the same list as y_lmax alone
+    x = synth.WORKLOADS["mace_large_fp32"].x_irreps
+    assert oracle.enumerate_paths(x, 3, 3) == oracle.enumerate_paths(
+        x, 0, 3, y_irreps=((1, 0, 1), (1, 1, -1), (1, 2, 1), (1, 3, -1)))
+    d = oracle.Desc(((3, 0, 1), (3, 1, -1)), 0, 2, y_irreps=Y_SUBSET)
+    assert d.y_dim == 9 and d.yoff == [0, 5, 6]
+    # 0e x (2e, 0e, 1e) -> 2, 0, 1; 1o x 2e -> 1, 2 (l3 <= 2); 1o x 0e -> 1; 1o x 1e -> 0, 1, 2
+    assert [d.path_l2(p) for p in range(d.P)] == [2, 0, 1, 2, 2, 0, 1, 1, 1]
+    assert [p[2] for p in d.paths] == [2, 0, 1, 1, 2, 1, 0, 1, 2]
+
+
+def test_fwd_with_y_irreps_matches_dense_einsum():
+    rng = np.random.default_rng(40)
+    d = oracle.Desc(((3, 0, 1), (3, 1, -1), (3, 2, 1)), 0, 3, y_irreps=Y_SUBSET)
+    rowptr, src = _tiny_graph(rng)
+    N, E = len(rowptr) - 1, len(src)
+    x = rng.standard_normal((N, d.x_dim))
+    Y = rng.standard_normal((E, d.y_dim))
+    W = rng.standard_normal((E, d.P, d.U))
+    ref = _dense_fwd(d, rowptr, src, x, Y, W)
+    got = oracle.fwd(d, rowptr, src, x, Y, W)
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
+
+
+def test_y_subset_equals_full_y_on_the_matching_paths():
+    """Y = 2e + 0e (a subset, reordered) gives what Y = 0e + 1o + 2e gives on the paths of
+    degrees 0 and 2, whatever the degree-1 columns hold; every output of the VJP too."""
+    rng = np.random.default_rng(41)
+    xi = ((2, 1, -1), (2, 2, 1))
+    sub = oracle.Desc(xi, 0, 3, y_irreps=((1, 2, 1), (1, 0, 1)))
+    full_all = oracle.Desc(xi, 2, 3)
+    # the full descriptor restricted to the subset's paths, in the subset's order
+    to_full = {0: 2, 1: 0}
+    paths = [(i1, to_full[iy], l3, k) for k, (i1, iy, l3, _) in enumerate(sub.paths)]
+    full = oracle.Desc(xi, 2, 3, paths=paths, out_l=sub.out_l)
+    assert full.P == sub.P < full_all.P
+    rowptr, src = _tiny_graph(rng)
+    N, E = len(rowptr) - 1, len(src)
+    x = rng.standard_normal((N, sub.x_dim))
+    Ys = rng.standard_normal((E, sub.y_dim))
+    Yf = rng.standard_normal((E, full.y_dim))        # degree-1 columns: anything
+    Yf[:, 4:9], Yf[:, 0:1] = Ys[:, 0:5], Ys[:, 5:6]
+    W = rng.standard_normal((E, sub.P, sub.U))
+    g = rng.standard_normal((N, sub.out_dim))
+    assert np.allclose(oracle.fwd(sub, rowptr, src, x, Ys, W), oracle.fwd(full, rowptr, src, x, Yf, W), atol=1e-13)
+    gs, gf = oracle.bwd(sub, rowptr, src, x, Ys, W, g), oracle.bwd(full, rowptr, src, x, Yf, W, g)
+    assert np.allclose(gs[0], gf[0], atol=1e-13) and np.allclose(gs[2], gf[2], atol=1e-13)
+    assert np.allclose(gs[1][:, 0:5], gf[1][:, 4:9], atol=1e-13)
+    assert np.allclose(gs[1][:, 5:6], gf[1][:, 0:1], atol=1e-13)
+    assert not gf[1][:, 1:4].any()                   # no path uses degree 1
+
+
+def test_vjp_adjoint_with_y_irreps():
+    """<g, f(x, Y, W)> = <gx, x> = <gY, Y> = <gW, W> with a Y subset (trilinearity)."""
+    rng = np.random.default_rng(42)
+    d = oracle.Desc(((3, 0, 1), (3, 1, -1)), 0, 3, y_irreps=Y_SUBSET)
+    rowptr, src = _tiny_graph(rng)
+    N, E = len(rowptr) - 1, len(src)
+    x, Y = rng.standard_normal((N, d.x_dim)), rng.standard_normal((E, d.y_dim))
+    W, g = rng.standard_normal((E, d.P, d.U)), rng.standard_normal((N, d.out_dim))
+    f = np.vdot(g, oracle.fwd(d, rowptr, src, x, Y, W))
+    gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
+    for a, b in ((gx, x), (gY, Y), (gW, W)):
+        assert abs(np.vdot(a, b) - f) <= 1e-12 * max(1.0, abs(f))

@@ -24,9 +24,9 @@ MUTANTS = {
     "no_sign_canon": ("sign = src[i] > 0 ? 1.0 : -1.0;", "sign = 1.0;"),
     "conj_missing": ("double pi = -(a1r[i][a] * a2i[j][b] + a1i[i][a] * a2r[j][b]);",
                      "double pi = (a1r[i][a] * a2i[j][b] + a1i[i][a] * a2r[j][b]);"),
-    "path_parity": ("out[4 * k + 3] = xpar[i] * ((l2 & 1) ? -1 : 1);", "out[4 * k + 3] = xpar[i];"),
+    "path_parity": ("out[4 * k + 3] = xpar[i] * ypar[j];", "out[4 * k + 3] = xpar[i];"),
     "fwd_y_index": ("double yv = Y[e * YD + q->yoff + q->m2[t]];\n                        o[",
-                    "double yv = Y[e * YD + q->yoff + q->m3[t] % (2 * d->p_l2[p] + 1)];\n                        o["),
+                    "double yv = Y[e * YD + q->yoff + q->m3[t] % q->n2];\n                        o["),
     "fwd_w_transposed": ("double w = W[(e * P + p) * U + u];\n                    for (int t = 0; t < q->nnz; ++t) {\n                        double xv",
                          "double w = W[(e * U + u) * P + p];\n                    for (int t = 0; t < q->nnz; ++t) {\n                        double xv"),
     "gy_without_w": ("gy[q->yoff + q->m2[t]] += q->c[t] * xv * w * gv;", "gy[q->yoff + q->m2[t]] += q->c[t] * xv * gv;"),
