@@ -55,6 +55,7 @@ class _Path(ctypes.Structure):
 
 class _Desc(ctypes.Structure):
     _fields_ = [("x_irreps", ctypes.POINTER(_Irrep)), ("n_x", ctypes.c_int32),
+                ("y_irreps", ctypes.POINTER(_Irrep)), ("n_y", ctypes.c_int32),
                 ("y_lmax", ctypes.c_int32), ("out_irreps", ctypes.POINTER(_Irrep)),
                 ("n_out", ctypes.c_int32), ("paths", ctypes.POINTER(_Path)),
                 ("n_paths", ctypes.c_int32), ("lmax_out", ctypes.c_int32), ("dtype", ctypes.c_int)]
@@ -158,15 +159,15 @@ def _irreps(seq) -> tuple:
     return tuple(tuple(int(v) for v in t) for t in seq)
 
 
-def _compile_in_child(x_irreps, y_lmax, lmax_out, dtype, paths, out_irreps):
+def _compile_in_child(x_irreps, y_lmax, lmax_out, dtype, paths, out_irreps, y_irreps=None):
     """Creates the plan in a child Python process (compiling its kernels into the code-object
     cache); the child inherits the OEQ_* planner options of this process."""
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     code = ("import sys; sys.path.insert(0, %r); import cg_tensor_product_amd as m; "
-            "m.Plan(%r, %r, %r, %r, paths=%r, out_irreps=%r)"
-            % (root, list(x_irreps), y_lmax, lmax_out, dtype, paths, out_irreps))
+            "m.Plan(%r, %r, %r, %r, paths=%r, out_irreps=%r, y_irreps=%r)"
+            % (root, list(x_irreps), y_lmax, lmax_out, dtype, paths, out_irreps, y_irreps))
     env = dict(os.environ, OEQ_PLAN_IN_PROCESS="1")
     subprocess.run([sys.executable, "-c", code], env=env, check=False,
                    stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
@@ -175,12 +176,16 @@ def _compile_in_child(x_irreps, y_lmax, lmax_out, dtype, paths, out_irreps):
 class Plan:
     """oeq_plan_create for an irreps descriptor.  dtype: "f32" or "f64".
 
-    paths=None enumerates every triangle-allowed path up to lmax_out; an explicit
-    list holds (x block, l2, output block) triples and needs out_irreps."""
+    Y: y_irreps (one-channel irreps in row order, e.g. "1x0e+1x2e+1x1e"), or by
+    default the spherical harmonics of degrees 0..y_lmax.  paths=None enumerates
+    every triangle-allowed path up to lmax_out; an explicit list holds
+    (x block, Y block, output block) triples and needs out_irreps (with the default
+    Y the Y block index is the degree)."""
 
     def __init__(self, x_irreps, y_lmax: int, lmax_out: int = 3, dtype: str = "f32",
-                 paths: Optional[Sequence] = None, out_irreps=None):
+                 paths: Optional[Sequence] = None, out_irreps=None, y_irreps=None):
         self.x_irreps = _irreps(x_irreps)
+        self.y_irreps = None if y_irreps is None else _irreps(y_irreps)
         self.y_lmax = int(y_lmax)
         self.lmax_out = int(lmax_out)
         self.dtype = dtype
@@ -194,6 +199,10 @@ class Plan:
         if dtype not in ("f32", "f64"):
             d.dtype = 7  # rejected by the library
         keep = [xs]
+        if self.y_irreps is not None:
+            ys = (_Irrep * len(self.y_irreps))(*[_Irrep(*t) for t in self.y_irreps])
+            d.y_irreps, d.n_y = ys, len(self.y_irreps)
+            keep.append(ys)
         if out_irreps is not None:
             oi = _irreps(out_irreps)
             os_ = (_Irrep * len(oi))(*[_Irrep(*t) for t in oi])
@@ -213,7 +222,7 @@ class Plan:
         if st == 5 and not os.environ.get("OEQ_PLAN_IN_PROCESS") and not os.environ.get("OEQ_NO_CACHE"):
             _compile_in_child(self.x_irreps, self.y_lmax, self.lmax_out, dtype,
                               None if paths is None else [tuple(int(v) for v in t) for t in paths],
-                              None if out_irreps is None else _irreps(out_irreps))
+                              None if out_irreps is None else _irreps(out_irreps), self.y_irreps)
             st = lib().oeq_plan_create_cached(ctypes.byref(d), ctypes.byref(h))
         if st == 5:
             st = lib().oeq_plan_create(ctypes.byref(d), ctypes.byref(h))

@@ -5,10 +5,23 @@
 
 using namespace oeq::capi;
 
+namespace {
+
+// Harmonics of an edge vector have parity (-1)^l: a Y block of the other parity (a
+// pseudotensor) cannot come from one.
+oeq_status check_y_from_vectors(const oeq_plan *p) {
+    if (!p) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (!p->y_natural)
+        return fail(OEQ_ERR_UNSUPPORTED, "Y blocks of parity other than (-1)^l cannot be harmonics of vectors");
+    return OEQ_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 oeq_status oeq_sph_harm(const oeq_plan *plan, int64_t E, const void *vec, void *Y, void *stream) {
-    if (!plan) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (oeq_status st = check_y_from_vectors(plan); st != OEQ_OK) return st;
     if (E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative edge count");
     if (E == 0) return OEQ_OK;
     if (!vec || !Y) return fail(OEQ_ERR_INVALID_ARG, "vec or Y is NULL");
@@ -19,7 +32,7 @@ oeq_status oeq_sph_harm(const oeq_plan *plan, int64_t E, const void *vec, void *
 
 oeq_status oeq_sph_harm_bwd(const oeq_plan *plan, int64_t E, const void *vec, const void *gY, void *gvec,
                             void *stream) {
-    if (!plan) return fail(OEQ_ERR_INVALID_ARG, "plan is NULL");
+    if (oeq_status st = check_y_from_vectors(plan); st != OEQ_OK) return st;
     if (E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative edge count");
     if (E == 0) return OEQ_OK;
     if (!vec || !gY || !gvec) return fail(OEQ_ERR_INVALID_ARG, "vec, grad_Y or grad_vec is NULL");
@@ -33,6 +46,7 @@ oeq_status oeq_tp_conv_fwd_vec(const oeq_plan *plan, int64_t N, int64_t E, const
                                void *stream) {
     oeq_status st = check_graph(plan, N, E, rowptr, src);
     if (st != OEQ_OK) return st;
+    if ((st = check_y_from_vectors(plan)) != OEQ_OK) return st;
     if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
     if (E > 0 && (!x || !vec || !W)) return fail(OEQ_ERR_INVALID_ARG, "x, vec or W is NULL");
     oeq_plan *p = const_cast<oeq_plan *>(plan);
@@ -56,6 +70,7 @@ oeq_status oeq_tp_conv_bwd_vec(const oeq_plan *plan, int64_t N, int64_t E, const
                                size_t workspace_bytes, void *stream) {
     oeq_status st = check_graph(plan, N, E, rowptr, src);
     if (st != OEQ_OK) return st;
+    if ((st = check_y_from_vectors(plan)) != OEQ_OK) return st;
     if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
     if (E > 0 && (!x || !vec || !W || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, vec, W or grad_out is NULL");
     oeq_plan *p = const_cast<oeq_plan *>(plan);

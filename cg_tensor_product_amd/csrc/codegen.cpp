@@ -128,17 +128,17 @@ void emit_dbwd_edge(std::ostringstream &o, const oeq_plan &p, const Local &L) {
          "    constexpr bool NQY = (HX && GW) || (HW && GX), NQT = HY && (GW || GX), NSX = HW && GY, NST = HX && GY;\n";
     // d_grad_out
     o << "    if (want_dg) {\n";
-    std::map<std::pair<int, int>, std::vector<int>> pairs;  // (x block, l2) -> paths
-    for (int k : L.paths) pairs[{p.paths[k].i1, p.paths[k].l2}].push_back(k);
+    std::map<std::pair<int, int>, std::vector<int>> pairs;  // (x block, Y block) -> paths
+    for (int k : L.paths) pairs[{p.paths[k].i1, p.paths[k].iy}].push_back(k);
     for (const auto &gkv : pairs) {
-        const int i1 = gkv.first.first, l2 = gkv.first.second;
+        const int i1 = gkv.first.first, iy = gkv.first.second, yo0 = p.yb[iy].lane_off;
         const int xo = L.xoff.at(i1);
         std::set<std::pair<int, int>> used;
         for (int k : gkv.second)
             for (const auto &nz : p.paths[k].nz) used.insert({nz.m1, nz.m2});
-        o << "      { // x block " << i1 << " x Y l=" << l2 << "\n";
+        o << "      { // x block " << i1 << " x Y block " << iy << "\n";
         for (const auto &ab : used) {
-            const std::string xa = "[" + S(xo + ab.first) + "]", yb = "[" + S(l2 * l2 + ab.second) + "]";
+            const std::string xa = "[" + S(xo + ab.first) + "]", yb = "[" + S(yo0 + ab.second) + "]";
             const std::string nm = S(ab.first) + "_" + S(ab.second);
             o << "        real_t z" << nm << ", u" << nm << ";";
             o << " if constexpr (HW) z" << nm << " = x" << xa << " * y" << yb << ";";
@@ -177,7 +177,7 @@ void emit_dbwd_edge(std::ostringstream &o, const oeq_plan &p, const Local &L) {
     for (int k : L.paths) {
         const Path &pa = p.paths[k];
         const int xo = L.xoff.at(pa.i1), oo = L.ooff.at(pa.ob), wk = L.widx.at(k);
-        const int n1 = 2 * pa.l1 + 1, n2 = 2 * pa.l2 + 1, yo = pa.l2 * pa.l2;
+        const int n1 = 2 * pa.l1 + 1, n2 = 2 * pa.l2 + 1, yo = pa.yoff;
         o << "    { // path " << k << "\n";
         std::map<std::pair<int, int>, std::vector<const NonZero *>> T;
         for (const auto &nz : pa.nz) T[{nz.m1, nz.m2}].push_back(&nz);
@@ -264,7 +264,7 @@ std::vector<MEntry> m_entries(const oeq_plan &p, const Local &L) {
     for (int k : L.paths) {
         const Path &pa = p.paths[k];
         std::map<std::pair<int, int>, std::vector<std::pair<int, double>>> by;  // (m3, m1) -> terms
-        for (const auto &nz : pa.nz) by[{nz.m3, nz.m1}].push_back({pa.l2 * pa.l2 + nz.m2, nz.c});
+        for (const auto &nz : pa.nz) by[{nz.m3, nz.m1}].push_back({pa.yoff + nz.m2, nz.c});
         for (const auto &kv : by) out.push_back({k, kv.first.second, kv.first.first, kv.second});
     }
     return out;
@@ -456,18 +456,19 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
     // forward of one edge
     o << "  static __device__ __forceinline__ void edge(const real_t (&x)[NX], const real_t (&y)[YD], "
          "const real_t (&w)[NW], real_t (&acc)[NO]) {\n";
-    std::map<std::pair<int, int>, std::vector<int>> pairs;  // (x block, l2) -> paths
-    for (int k : L.paths) pairs[{p.paths[k].i1, p.paths[k].l2}].push_back(k);
+    std::map<std::pair<int, int>, std::vector<int>> pairs;  // (x block, Y block) -> paths
+    for (int k : L.paths) pairs[{p.paths[k].i1, p.paths[k].iy}].push_back(k);
     for (const auto &gkv : pairs) {
-        const int i1 = gkv.first.first, l2 = gkv.first.second;
+        const int i1 = gkv.first.first, iy = gkv.first.second;
         const int xo = L.xoff.at(i1);
         std::set<std::pair<int, int>> used;
         for (int k : gkv.second)
             for (const auto &nz : p.paths[k].nz) used.insert({nz.m1, nz.m2});
-        o << "    { // x block " << i1 << " (l=" << p.xb[i1].l << ") x Y l=" << l2 << "\n";
+        o << "    { // x block " << i1 << " (l=" << p.xb[i1].l << ") x Y block " << iy << " (l=" << p.yb[iy].l
+          << ")\n";
         for (const auto &ab : used)
             o << "      const real_t z" << ab.first << "_" << ab.second << " = x[" << xo + ab.first << "] * y["
-              << l2 * l2 + ab.second << "];\n";
+              << p.yb[iy].lane_off + ab.second << "];\n";
         for (int k : gkv.second) {
             const Path &pa = p.paths[k];
             const int oo = L.ooff.at(pa.ob);
@@ -499,7 +500,7 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
         const Path &pa = p.paths[k];
         const int xo = L.xoff.at(pa.i1), oo = L.ooff.at(pa.ob), wk = L.widx.at(k);
         const int n1 = 2 * pa.l1 + 1, n2 = 2 * pa.l2 + 1;
-        const int yo = pa.l2 * pa.l2;
+        const int yo = pa.yoff;
         o << "    { // path " << k << ": " << pa.l1 << " x " << pa.l2 << " -> " << pa.l3 << "\n";
         std::map<std::pair<int, int>, std::vector<const NonZero *>> T;
         for (const auto &nz : pa.nz) T[{nz.m1, nz.m2}].push_back(&nz);
@@ -604,7 +605,9 @@ std::string emit_source(const oeq_plan &p) {
     }
     o << "// Generated for: U=" << p.U << ", x blocks";
     for (const auto &b : p.xb) o << " " << b.l << (b.parity > 0 ? "e" : "o");
-    o << ", Y degrees 0.." << p.L << ", " << p.paths.size() << " paths, " << p.total_nnz
+    o << ", Y blocks";
+    for (const auto &b : p.yb) o << " " << b.l << (b.parity > 0 ? "e" : "o");
+    o << ", " << p.paths.size() << " paths, " << p.total_nnz
       << " CG non-zeros, dtype " << (p.dtype == OEQ_F64 ? "f64" : "f32") << "; forward groups of";
     for (const auto &g : p.fwd_groups) o << " " << g.size();
     o << " paths, backward groups of";
@@ -646,6 +649,18 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr int P = " << p.paths.size() << ";\n";
     o << "constexpr int LY = " << p.L << ";\n";
     o << "constexpr int YD = " << p.YD << ";\n";
+    // element k of a Y row is element YSEL[k] of the harmonics of degrees 0..LY (the
+    // forward and VJP from edge vectors evaluate those and keep the plan's blocks)
+    o << "constexpr int YSEL[YD] = {";
+    {
+        bool first = true;
+        for (const auto &b : p.yb)
+            for (int m = 0; m < 2 * b.l + 1; ++m) {
+                o << (first ? "" : ", ") << b.l * b.l + m;
+                first = false;
+            }
+    }
+    o << "};\n";
     o << "constexpr int PY = " << py << ";\n";
     o << "constexpr int LGPY = " << lgpy << ";\n";
     o << "constexpr int GY_TILE = " << p.gy_tile << ";\n";

@@ -5,7 +5,8 @@
 // It is compiled at plan time with hipRTC, after a prelude emitted by the
 // planner that defines, for one descriptor and dtype: real_t; U, UCH (64-channel
 // chunks), NGF / NGB / NGR (forward / backward / radial-backward path groups),
-// P (paths), LY and YD ((LY+1)^2), PY (YD rounded up to a power of two), LGPY
+// P (paths), LY (largest Y degree), YD (Y row width), YSEL (the harmonic of degrees
+// 0..LY behind each Y element), PY (YD rounded up to a power of two), LGPY
 // (log2 PY), GY_TILE, XD, OD, XT; LDW / STW (loads and stores of W and its
 // gradients); and the group structs FG<g> / BG<g> / RG<g> (see the planner's code
 // generator) holding the unrolled sparse CG streams of one group of paths.
@@ -48,7 +49,9 @@ __device__ __forceinline__ real_t rsqrt_or_zero(real_t r2) {
     return r2 > real_t(0) ? real_t(1) / sqrt_r(r2) : real_t(0);
 }
 
-__device__ __forceinline__ void sh_eval(real_t vx, real_t vy, real_t vz, real_t (&Yv)[YD]) {
+constexpr int YF = (LY + 1) * (LY + 1);  // harmonics of degrees 0..LY
+
+__device__ __forceinline__ void sh_eval_full(real_t vx, real_t vy, real_t vz, real_t (&Yv)[YF]) {
     const real_t inv = rsqrt_or_zero(vx * vx + vy * vy + vz * vz);
     const real_t x = vx * inv, y = vy * inv, z = vz * inv;
     const bool live = inv > real_t(0);
@@ -85,8 +88,8 @@ __device__ __forceinline__ void sh_eval(real_t vx, real_t vy, real_t vz, real_t 
 
 // Vector gradient of sum_m gy[m] Y_m(v): with P_m the Cartesian polynomials above
 // (any smooth extension off the sphere), grad = (I - n n^T) (sum_m gy[m] grad P_m(n)) / |v|.
-__device__ __forceinline__ void sh_grad(real_t vx, real_t vy, real_t vz, const real_t (&gy)[YD], real_t &gvx,
-                                        real_t &gvy, real_t &gvz) {
+__device__ __forceinline__ void sh_grad_full(real_t vx, real_t vy, real_t vz, const real_t (&gy)[YF], real_t &gvx,
+                                             real_t &gvy, real_t &gvz) {
     const real_t inv = rsqrt_or_zero(vx * vx + vy * vy + vz * vz);
     const real_t x = vx * inv, y = vy * inv, z = vz * inv;
     real_t ax = real_t(0), ay = real_t(0), az = real_t(0);
@@ -124,6 +127,25 @@ __device__ __forceinline__ void sh_grad(real_t vx, real_t vy, real_t vz, const r
     gvx = (ax - dot * x) * inv;
     gvy = (ay - dot * y) * inv;
     gvz = (az - dot * z) * inv;
+}
+
+// The plan's Y row from the harmonics of degrees 0..LY (the planner accepts vectors only
+// for Y blocks of parity (-1)^l), and the gradient through it.
+__device__ __forceinline__ void sh_eval(real_t vx, real_t vy, real_t vz, real_t (&Yv)[YD]) {
+    real_t f[YF];
+    sh_eval_full(vx, vy, vz, f);
+#pragma unroll
+    for (int k = 0; k < YD; ++k) Yv[k] = f[YSEL[k]];
+}
+
+__device__ __forceinline__ void sh_grad(real_t vx, real_t vy, real_t vz, const real_t (&gy)[YD], real_t &gvx,
+                                        real_t &gvy, real_t &gvz) {
+    real_t f[YF];
+#pragma unroll
+    for (int k = 0; k < YF; ++k) f[k] = real_t(0);
+#pragma unroll
+    for (int k = 0; k < YD; ++k) f[YSEL[k]] += gy[k];
+    sh_grad_full(vx, vy, vz, f, gvx, gvy, gvz);
 }
 
 // Y row of edge e from its vector (YV) or from memory

@@ -48,7 +48,7 @@ std::vector<std::vector<int>> partition_paths(const oeq_plan &p, bool fwd, int w
     for (int a = 0; a < n; ++a)
         for (int b = a + 1; b < n; ++b) {
             const Path &pa = p.paths[a], &pb = p.paths[b];
-            const bool same = fwd ? (pa.i1 == pb.i1 && pa.l2 == pb.l2) : (pa.i1 == pb.i1);
+            const bool same = fwd ? (pa.i1 == pb.i1 && pa.iy == pb.iy) : (pa.i1 == pb.i1);
             if (same || pa.ob == pb.ob) unite(a, b);
         }
     std::map<int, std::vector<int>> units;
@@ -162,11 +162,32 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         return fail(why, OEQ_ERR_UNSUPPORTED, "dtype must be OEQ_F32 or OEQ_F64");
     if (!d->x_irreps || d->n_x <= 0 || d->n_x > 16)
         return fail(why, OEQ_ERR_INVALID_ARG, "x_irreps must hold 1..16 blocks");
-    if (d->y_lmax < 0 || d->y_lmax > kLMax)
-        return fail(why, OEQ_ERR_UNSUPPORTED, "y_lmax must be in 0..3");
     p->dtype = d->dtype;
-    p->L = d->y_lmax;
-    p->YD = (d->y_lmax + 1) * (d->y_lmax + 1);
+    // Y blocks: the given irreps, or the spherical harmonics 0..y_lmax (parity (-1)^l)
+    if (d->y_irreps) {
+        if (d->n_y <= 0 || d->n_y > 16) return fail(why, OEQ_ERR_INVALID_ARG, "y_irreps must hold 1..16 blocks");
+        int off = 0;
+        for (int j = 0; j < d->n_y; ++j) {
+            const oeq_irrep &ir = d->y_irreps[j];
+            if (ir.mul != 1) return fail(why, OEQ_ERR_UNSUPPORTED, "Y blocks must have multiplicity 1");
+            if (ir.l < 0 || ir.l > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "Y degree must be in 0..3");
+            if (ir.parity != 1 && ir.parity != -1) return fail(why, OEQ_ERR_INVALID_ARG, "parity must be +1 or -1");
+            p->yb.push_back({ir.l, ir.parity, off, off});
+            off += 2 * ir.l + 1;
+        }
+    } else {
+        if (d->y_lmax < 0 || d->y_lmax > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "y_lmax must be in 0..3");
+        for (int l = 0; l <= d->y_lmax; ++l) p->yb.push_back({l, (l % 2) ? -1 : 1, l * l, l * l});
+    }
+    p->YD = 0;
+    p->L = 0;
+    for (const Block &b : p->yb) {
+        p->YD += 2 * b.l + 1;
+        p->L = std::max(p->L, b.l);
+        if (b.parity != ((b.l % 2) ? -1 : 1)) p->y_natural = false;
+    }
+    // the lane reduction of the Y gradient handles rows of up to 16 values
+    if (p->YD > 16) return fail(why, OEQ_ERR_UNSUPPORTED, "Y rows wider than 16 values");
     p->U = d->x_irreps[0].mul;
     if (p->U <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "multiplicity must be >= 1");
     if (p->U > 1024) return fail(why, OEQ_ERR_UNSUPPORTED, "multiplicity above 1024");
@@ -184,7 +205,7 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     p->XD = static_cast<int64_t>(p->U) * lane;
 
     // Output blocks and the path list.
-    struct Raw { int i1, l2, ob; };
+    struct Raw { int i1, iy, ob; };
     std::vector<Raw> raw;
     std::vector<std::pair<int, int>> out_lp;  // (l, parity) of each output block
     if (d->paths == nullptr) {
@@ -203,8 +224,9 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         }
         for (int i = 0; i < d->n_x; ++i) {
             const int l1 = d->x_irreps[i].l, p1 = d->x_irreps[i].parity;
-            for (int l2 = 0; l2 <= d->y_lmax; ++l2) {
-                const int p3 = p1 * ((l2 % 2) ? -1 : 1);
+            for (int j = 0; j < static_cast<int>(p->yb.size()); ++j) {
+                const int l2 = p->yb[j].l;
+                const int p3 = p1 * p->yb[j].parity;
                 const int hi = std::min(l1 + l2, static_cast<int>(d->lmax_out));
                 for (int l3 = std::abs(l1 - l2); l3 <= hi; ++l3) {
                     if (d->out_irreps) {
@@ -215,9 +237,9 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
                                 ob = static_cast<int>(o);
                                 break;
                             }
-                        if (ob >= 0) raw.push_back({i, l2, ob});
+                        if (ob >= 0) raw.push_back({i, j, ob});
                     } else {
-                        raw.push_back({i, l2, static_cast<int>(out_lp.size())});
+                        raw.push_back({i, j, static_cast<int>(out_lp.size())});
                         out_lp.push_back({l3, p3});
                     }
                 }
@@ -237,12 +259,13 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         for (int k = 0; k < d->n_paths; ++k) {
             const oeq_path &pa = d->paths[k];
             if (pa.in1 < 0 || pa.in1 >= d->n_x) return fail(why, OEQ_ERR_INVALID_ARG, "path in1 out of range");
-            if (pa.in2 < 0 || pa.in2 > d->y_lmax) return fail(why, OEQ_ERR_INVALID_ARG, "path l2 out of range");
+            if (pa.in2 < 0 || pa.in2 >= static_cast<int>(p->yb.size()))
+                return fail(why, OEQ_ERR_INVALID_ARG, "path Y block out of range");
             if (pa.out < 0 || pa.out >= d->n_out) return fail(why, OEQ_ERR_INVALID_ARG, "path out out of range");
-            const int l1 = d->x_irreps[pa.in1].l, l3 = out_lp[pa.out].first;
-            if (l3 < std::abs(l1 - pa.in2) || l3 > l1 + pa.in2)
+            const int l1 = d->x_irreps[pa.in1].l, l2 = p->yb[pa.in2].l, l3 = out_lp[pa.out].first;
+            if (l3 < std::abs(l1 - l2) || l3 > l1 + l2)
                 return fail(why, OEQ_ERR_INVALID_ARG, "path violates the triangle rule");
-            const int p3 = d->x_irreps[pa.in1].parity * ((pa.in2 % 2) ? -1 : 1);
+            const int p3 = d->x_irreps[pa.in1].parity * p->yb[pa.in2].parity;
             if (p3 != out_lp[pa.out].second) return fail(why, OEQ_ERR_INVALID_ARG, "path violates parity");
             raw.push_back({pa.in1, pa.in2, pa.out});
         }
@@ -262,8 +285,10 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     for (const Raw &r : raw) {
         Path pa;
         pa.i1 = r.i1;
+        pa.iy = r.iy;
+        pa.yoff = p->yb[r.iy].lane_off;
         pa.l1 = p->xb[r.i1].l;
-        pa.l2 = r.l2;
+        pa.l2 = p->yb[r.iy].l;
         pa.l3 = p->ob[r.ob].l;
         pa.ob = r.ob;
         pa.parity3 = p->ob[r.ob].parity;

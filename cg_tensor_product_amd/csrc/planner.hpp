@@ -28,6 +28,8 @@ struct NonZero {
 
 struct Path {
     int i1;          // x block
+    int iy;          // Y block
+    int yoff;        // offset of the Y block in a Y row
     int l1, l2, l3;
     int ob;          // output block
     int parity3;
@@ -53,11 +55,12 @@ struct oeq_plan_impl;
 struct oeq_plan {
     oeq_dtype dtype;
     int U = 0;
-    int L = 0;                  // Y degrees 0..L
-    int YD = 0;                 // (L+1)^2
+    int L = 0;                  // largest Y degree
+    int YD = 0;                 // Y row width: sum of 2l+1 over the Y blocks
+    bool y_natural = true;      // every Y block has parity (-1)^l (spherical harmonics can fill it)
     int NXC = 0, NOC = 0;       // per-channel x and output widths
     int64_t XD = 0, OD = 0;     // node row widths
-    std::vector<oeq::Block> xb, ob;
+    std::vector<oeq::Block> xb, ob, yb;  // yb: lane_off = offset in a Y row
     std::vector<oeq::Path> paths;
     int total_nnz = 0;
 

@@ -23,7 +23,9 @@
  *   src    [E]   int32   sender of edge e; edge e belongs to receiver r when
  *                        rowptr[r] <= e < rowptr[r+1]
  *   x      [N, XD]       x block i at xoff_i, element u*(2 l_i + 1) + (m + l_i)
- *   Y      [E, (L+1)^2]  element l2*l2 + (m2 + l2)
+ *   Y      [E, YD]       Y block j (one channel) at yoff_j = the widths 2l+1 of the
+ *                        blocks before it, element yoff_j + (m2 + l_j); for the
+ *                        default Y (degrees 0..L) element l2*l2 + (m2 + l2)
  *   W      [E, P, U]
  *   out    [N, OD]       output block o at ooff_o, element u*(2 l_o + 1) + (m + l_o)
  * Gradients use the layout of the tensor they belong to.
@@ -82,21 +84,29 @@ typedef struct {
 
 typedef struct {
     int32_t in1; /* index into the x irreps                              */
-    int32_t in2; /* Y degree l2 (Y holds every degree 0..L)              */
+    int32_t in2; /* index into the Y irreps (default Y: the degree l2)   */
     int32_t out; /* index into the output irreps                         */
 } oeq_path;
 
+/* Irreps descriptor of one tensor product ("Receiver-streaming convolutions for
+ * channel-wise UVU tensor products", maintainer replies: the convolution is one
+ * interface over irreps descriptors of its inputs and outputs).  All arrays are
+ * host memory, read during oeq_plan_create only. */
 typedef struct {
-    const oeq_irrep *x_irreps; /* host memory                                   */
+    const oeq_irrep *x_irreps;   /* x blocks, each with the same multiplicity U     */
     int32_t n_x;
-    int32_t y_lmax;            /* L: Y carries degrees 0..L, multiplicity 1 each */
-    const oeq_irrep *out_irreps; /* NULL: one output block per path, in path order */
+    const oeq_irrep *y_irreps;   /* Y blocks in row order, multiplicity 1 each, any */
+    int32_t n_y;                 /*   degrees 0..3 in any order and either parity,  */
+                                 /*   total width sum(2l+1) <= 16.  NULL: the       */
+                                 /*   spherical harmonics 0..y_lmax, parity (-1)^l  */
+    int32_t y_lmax;              /* used when y_irreps == NULL                      */
+    const oeq_irrep *out_irreps; /* NULL: one output block per path, in path order  */
     int32_t n_out;
-    const oeq_path *paths;     /* NULL: enumerate every triangle-allowed path:   */
-    int32_t n_paths;           /*   x blocks in order, l2 = 0..L,                */
-                               /*   l3 = |l1-l2|..min(l1+l2, lmax_out),          */
-                               /*   output parity p1 * (-1)^l2                   */
-    int32_t lmax_out;          /* used when paths == NULL                        */
+    const oeq_path *paths;       /* NULL: enumerate every triangle-allowed path:    */
+    int32_t n_paths;             /*   x blocks in order, then Y blocks in order,    */
+                                 /*   l3 = |l1-l2|..min(l1+l2, lmax_out),           */
+                                 /*   output parity p1 * pY                         */
+    int32_t lmax_out;            /* used when paths == NULL                         */
     oeq_dtype dtype;
 } oeq_tp_desc;
 
@@ -105,8 +115,18 @@ typedef struct oeq_plan oeq_plan; /* opaque, host-owned */
 /* Builds the path list and the real-basis CG tables, emits the specialised HIP
  * kernels and compiles them for gfx950 (runtime compilation, cached on disk by a
  * hash of the generated source in $OEQ_CACHE_DIR, default: a "jitcache" folder
- * beside the library).  Host-only; the code object is loaded on a device at the
- * first compute call there.  *plan is set to NULL on failure. */
+ * beside the library).  The kernels are specialised per descriptor when the
+ * model is set up, as the CG kernel generator analyses each tensor product
+ * before its kernels are built ("An Efficient Sparse Kernel Generator for
+ * O(3)-Equivariant Deep Networks", abstract), and the streaming convolution is
+ * its own template, chosen when the kernels are compiled at run time
+ * ("Receiver-streaming convolutions ...", first maintainer reply).  Host-only;
+ * the code object is loaded on a device at
+ * the first compute call there.  *plan is set to NULL on failure.
+ * Errors: OEQ_ERR_INVALID_ARG (NULL pointers, bad parity, a path outside the
+ * triangle rule or with the wrong output parity), OEQ_ERR_UNSUPPORTED (degree
+ * above 3, mixed x multiplicities, Y wider than 16, more than 128 paths, an
+ * unknown dtype), OEQ_ERR_JIT (the runtime compiler failed). */
 oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan);
 
 /* As oeq_plan_create, but never runs the runtime compiler: returns OEQ_ERR_JIT
@@ -118,7 +138,10 @@ oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan);
 oeq_status oeq_plan_create_cached(const oeq_tp_desc *desc, oeq_plan **plan);
 void oeq_plan_destroy(oeq_plan *plan);
 
-/* Row widths: x_dim = XD, y_dim = (L+1)^2, out_dim = OD, w_per_edge = P*U. */
+/* Row widths of the tensors of the layouts above ("Receiver-streaming
+ * convolutions ...", opening post: x per node, Y and W per edge, outputs per
+ * receiver): x_dim = XD, y_dim = YD, out_dim = OD, w_per_edge = P*U.
+ * Any output pointer may be NULL.  OEQ_ERR_INVALID_ARG for a NULL plan. */
 oeq_status oeq_plan_dims(const oeq_plan *plan, int64_t *x_dim, int64_t *y_dim,
                          int64_t *out_dim, int64_t *n_paths, int64_t *w_per_edge);
 
@@ -140,8 +163,12 @@ oeq_status oeq_cg_table(int32_t l1, int32_t l2, int32_t l3, double *out);
 /* Workspace bytes a backward or double-backward call may need for `mode`
  * (per-group partial Y-gradients when the plan splits its paths over several
  * backward or double-backward groups, sized for the larger count; per-edge
- * x-gradient rows and the sender CSR for DETERMINISTIC).  One size serves both
- * calls.  0 means no workspace is needed. */
+ * x-gradient rows and the sender CSR for DETERMINISTIC: the materialised
+ * per-edge tensor reduced in a fixed order of the deterministic fallback in
+ * "Optimize UMA SO2 and Wigner inference kernels").  One size serves both
+ * calls.  0 means no workspace is needed; the caller allocates it (the library
+ * never allocates in a compute call).  OEQ_ERR_INVALID_ARG for a NULL plan or
+ * output, negative sizes or an unknown mode. */
 oeq_status oeq_workspace_size(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                               oeq_bwd_mode mode, size_t *bytes);
 
@@ -251,14 +278,16 @@ oeq_status oeq_tp_conv_bwd_sender(const oeq_plan *plan, int64_t n_nodes, int64_t
 
 /* ---- Y from edge vectors ---------------------------------------------------
  * The step before the tensor product: Y[e] = the real spherical harmonics of the
- * direction of the edge vector vec[e] = (x, y, z) (the pages' receiver-major edges
- * are built from atom positions; "Receiver-streaming convolutions ...", opening
- * post), and the gradient carried back from Y to the vectors.  Convention as for
- * Y everywhere in this library: degrees 0..L of the plan, m = -l..l, degree 1
- * ordered (y, z, x), Condon-Shortley phase, component normalisation (the squares
- * of degree l sum to 2l+1).  The vector need not be unit length; a zero vector
- * gives Y_00 = 1, all other degrees 0, and a zero gradient.  vec is [E, 3] in the
- * plan's dtype. */
+ * direction of the edge vector vec[e] = (x, y, z) (receiver-major edges are built
+ * from atom positions; "Receiver-streaming convolutions ...", opening post), and
+ * the gradient carried back from Y to the vectors.  Convention as for Y
+ * everywhere in this library: the plan's Y blocks (each filled with the harmonics
+ * of its degree), m = -l..l, degree 1 ordered (y, z, x), Condon-Shortley phase,
+ * component normalisation (the squares of degree l sum to 2l+1).  The vector need
+ * not be unit length; a zero vector gives Y_00 = 1, all other degrees 0, and a
+ * zero gradient.  vec is [E, 3] in the plan's dtype.  Every entry point that
+ * takes vectors returns OEQ_ERR_UNSUPPORTED for a plan with a Y block whose
+ * parity is not (-1)^l (harmonics of a vector cannot fill it). */
 oeq_status oeq_sph_harm(const oeq_plan *plan, int64_t n_edges, const void *vec, void *Y,
                         void *stream);
 

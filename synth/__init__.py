@@ -17,7 +17,8 @@ Recipe (every tensor from its own child of one SeedSequence):
             instead: self-loops and repeated (s, r) edges.
   * edge vectors: z ~ N(0, I3), normalised; Y = real spherical harmonics of
             them with component normalisation (sum over m of Y^2 = 2l+1),
-            degrees 0..L, m = -l..l, l=1 ordered (y, z, x).
+            degrees 0..L, m = -l..l, l=1 ordered (y, z, x); a workload with
+            listed Y blocks gets the harmonics of each block's degree.
   * x, g, v ~ N(0,1); W ~ N(0,1) * w_scale.
   * values are drawn in fp64 and rounded to nearest-even for fp32 workloads,
     so the fp64 twin of a workload sees the same draws.
@@ -49,6 +50,7 @@ class Workload:
     ops: tuple = ("fwd", "bwd")
     degrees: Optional[tuple] = None  # per-receiver in-degree (non-uniform graphs)
     multi: bool = False              # senders drawn with replacement, the receiver included
+    y_irreps: Optional[tuple] = None # Y blocks ((1, l, parity), ...); None: degrees 0..y_lmax
 
     @property
     def U(self) -> int:
@@ -65,8 +67,14 @@ class Workload:
         return sum(mul * (2 * l + 1) for mul, l, _ in self.x_irreps)
 
     @property
+    def y_degrees(self) -> tuple:
+        if self.y_irreps is None:
+            return tuple(range(self.y_lmax + 1))
+        return tuple(l for _, l, _ in self.y_irreps)
+
+    @property
     def y_dim(self) -> int:
-        return (self.y_lmax + 1) ** 2
+        return sum(2 * l + 1 for l in self.y_degrees)
 
     def np_dtype(self):
         return np.float64 if self.dtype == "f64" else np.float32
@@ -228,7 +236,9 @@ def generate(wl: Workload, n_paths: int, out_dim: int, want=("x", "Y", "W", "g")
     if "Y" in want or "vec" in want:
         vec = unit_vectors(E, rngs[_VEC])
         out["vec"] = vec
-        out["Y"] = real_sh_cartesian(wl.y_lmax, vec).astype(dt)
+        full = real_sh_cartesian(max(wl.y_degrees), vec)
+        # each Y block holds the harmonics of its degree (whatever parity it is labelled with)
+        out["Y"] = np.concatenate([full[:, l * l:(l + 1) ** 2] for l in wl.y_degrees], axis=1).astype(dt)
     if "evec" in want:
         # edge vectors with lengths: the unit vectors above times lengths uniform in [0.5, 5)
         unit = out["vec"] if "vec" in out else unit_vectors(E, _children(wl.seed)[_VEC])

@@ -23,7 +23,7 @@ def rel_l2(got, ref) -> float:
 
 
 def oracle_desc(wl: synth.Workload) -> oracle.Desc:
-    return oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    return oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max, y_irreps=wl.y_irreps)
 
 
 def inputs(wl: synth.Workload, want=("x", "Y", "W", "g")):
@@ -46,7 +46,7 @@ def plan_for(wl: synth.Workload, env=None):
     old = {k: os.environ.get(k) for k in env}
     os.environ.update(env)
     try:
-        return oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+        return oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype, y_irreps=wl.y_irreps)
     finally:
         for k, v in old.items():
             if v is None:

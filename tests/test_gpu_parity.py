@@ -66,8 +66,15 @@ EDGE_CASES = {
                                     36, degrees=_multi_deg[:60], multi=True),
     "multi_u40_f64": synth.Workload("multi_u40_f64", 50, 0, synth._irr("40x0e+40x1o"), 2, 2, "f64", "unit", 37,
                                     degrees=_multi_deg[60:], multi=True),
+    # Y given as irreps: unsorted degrees with a pseudovector block (2e + 0e + 1e) in fp32,
+    # and the odd degrees only (1o + 3o) in fp64
+    "ysub_u48_f32": synth.Workload("ysub_u48_f32", 80, 20, synth._irr("48x0e+48x1o+48x2e"), 0, 3, "f32", "unit", 38,
+                                   y_irreps=synth._irr("1x2e+1x0e+1x1e")),
+    "ysub_u16_f64": synth.Workload("ysub_u16_f64", 60, 14, synth._irr("16x0e+16x1o+16x2e"), 0, 3, "f64", "unit", 39,
+                                   y_irreps=synth._irr("1x1o+1x3o")),
 }
 MULTI = ["multi_u64_f32", "multi_u40_f64"]
+YSUB = ["ysub_u48_f32", "ysub_u16_f64"]
 SMALL = {**REDUCED, **EDGE_CASES}
 
 
@@ -158,7 +165,7 @@ def test_bwd_partial_outputs(name):
 
 @pytest.mark.parametrize("mode", ["atomic", "deterministic"])
 @pytest.mark.parametrize("name", ["mace_large_fp32", "wide_proxy_fp32", "ragged_u96_f32", "tiny_fp64", "u1024_f32",
-                                  "hub_u32_f32"] + MULTI)
+                                  "hub_u32_f32"] + MULTI + YSUB)
 def test_hvp_parity(name, mode):
     """Double backward with a tangent on x only (the HVP of the workloads)."""
     wl, d, inp, g, plan = _case(name)
@@ -176,7 +183,7 @@ def test_hvp_parity(name, mode):
 
 @pytest.mark.parametrize("mode", ["atomic", "deterministic"])
 @pytest.mark.parametrize("mask", [1, 2, 3, 4, 5, 6, 7])
-@pytest.mark.parametrize("name", ["u8_l1_f32", "u1_l3_f64", "ragged_u96_f32", "u1024_f32"] + MULTI)
+@pytest.mark.parametrize("name", ["u8_l1_f32", "u1_l3_f64", "ragged_u96_f32", "u1024_f32"] + MULTI + YSUB)
 def test_dbwd_all_tangents(name, mask, mode):
     wl, d, inp, g, plan = _case(name)
     tx = synth.extra_normal(wl, inp["x"].shape, 0)

@@ -16,7 +16,20 @@ torch = pytest.importorskip("torch")
 oeq = pytest.importorskip("cg_tensor_product_amd")
 
 NAMES = ["tiny_fp64", "mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32", "u1_l3_f64", "u8_l1_f32",
-         "ragged_u96_f32"]
+         "ragged_u96_f32", "ysub_u16_f64"]
+
+
+def _cols(wl):
+    """Columns of the harmonics of degrees 0..max that make up the workload's Y row."""
+    return np.concatenate([np.arange(l * l, (l + 1) ** 2) for l in wl.y_degrees])
+
+
+def _sh(wl, vec):
+    return sphere.sh_of_vectors(max(wl.y_degrees), vec)[:, _cols(wl)]
+
+
+def _sh_grad(wl, vec):
+    return sphere.sh_grad_of_vectors(max(wl.y_degrees), vec)[:, _cols(wl), :]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,7 +41,7 @@ def _need_gpu():
 
 def _case(name, special=False):
     wl = SMALL[name]
-    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max, y_irreps=wl.y_irreps)
     inp = synth.generate(wl, d.P, d.out_dim, want=("x", "evec", "W", "g"))
     if special:
         # the first edges carry the zero vector, the six axis directions (+-z included), a
@@ -36,7 +49,7 @@ def _case(name, special=False):
         sv = _special_vectors(wl.np_dtype())
         k = min(len(sv), inp["E"])
         inp["evec"][:k] = sv[:k]
-    inp["Y"] = sphere.sh_of_vectors(wl.y_lmax, inp["evec"])       # the oracle's Y of the same vectors
+    inp["Y"] = _sh(wl, inp["evec"])                                # the oracle's Y of the same vectors
     return wl, d, inp, plan_for(wl)
 
 
@@ -53,10 +66,10 @@ def test_sph_harm_parity(name):
     vec = np.concatenate([inp["evec"], _special_vectors(wl.np_dtype())])
     Y = oeq.oeq_sph_harm(plan, to_dev(vec))
     torch.cuda.synchronize()
-    ref = sphere.sh_of_vectors(wl.y_lmax, vec)
+    ref = _sh(wl, vec)
     got = Y.cpu().numpy()
     assert rel_l2(got, ref) <= RTOL[wl.dtype]
-    assert np.array_equal(got[len(inp["evec"])], np.eye(plan.y_dim)[0])  # zero vector: Y_00 = 1, rest 0
+    assert np.array_equal(got[len(inp["evec"])], ref[len(inp["evec"])])  # zero vector: Y_00 = 1, rest 0
 
 
 @pytest.mark.parametrize("name", NAMES)
@@ -67,7 +80,7 @@ def test_sph_harm_bwd_parity(name):
     gY = synth.extra_normal(wl, (len(vec), plan.y_dim), 3)
     gvec = oeq.oeq_sph_harm_bwd(plan, to_dev(vec), to_dev(gY))
     torch.cuda.synchronize()
-    ref = np.einsum("em,emk->ek", gY.astype(np.float64), sphere.sh_grad_of_vectors(wl.y_lmax, vec))
+    ref = np.einsum("em,emk->ek", gY.astype(np.float64), _sh_grad(wl, vec))
     got = gvec.cpu().numpy()
     assert rel_l2(got, ref) <= RTOL[wl.dtype]
     # the special vectors alone (the six axis directions, +-z included; tiny and huge)
@@ -97,7 +110,7 @@ def test_bwd_vec_parity(name, mode):
                                            dev["g"], mode=mode)
     torch.cuda.synchronize()
     rx, rY, rW = oracle.bwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"])
-    rvec = np.einsum("em,emk->ek", rY, sphere.sh_grad_of_vectors(wl.y_lmax, inp["evec"]))
+    rvec = np.einsum("em,emk->ek", rY, _sh_grad(wl, inp["evec"]))
     tol = RTOL[wl.dtype]
     assert rel_l2(gx.cpu().numpy(), rx) <= tol
     assert rel_l2(gW.cpu().numpy(), rW) <= tol

@@ -290,3 +290,59 @@ def test_radial_argument_errors_before_any_device_work():
     assert g(p.handle, 100, P(16), 6.0, 16, P(16), P(16), None, P(16), None, None, ws, nb, None) == 1  # grad_W
     # nothing requested: returns without work
     assert g(p.handle, 100, P(16), 6.0, 16, P(16), P(16), P(16), None, None, None, ws, nb, None) == 0
+
+
+# ---------------------------------------------------------------------------
+# Y described by its irreps
+# ---------------------------------------------------------------------------
+
+Y_CASES = [
+    ("32x0e+32x1o", "1x0e+1x2e", 3),               # a missing degree (no 1, no 3)
+    ("16x0e+16x1o+16x2e", "1x2e+1x0e+1x1e", 3),    # unsorted, with a pseudovector block
+    ("8x1o", "1x3o+1x1o", 2),                      # the odd degrees only
+]
+
+
+@pytest.mark.parametrize("xi,yi,l3", Y_CASES)
+def test_plan_with_y_irreps_equals_oracle(xi, yi, l3):
+    p = oeq.Plan(xi, 0, l3, "f32", y_irreps=yi)
+    xt, yt = oeq._irreps(xi), oeq._irreps(yi)
+    d = oracle.Desc(xt, 0, l3, y_irreps=yt)
+    en = oracle.enumerate_paths(xt, 0, l3, y_irreps=yt)
+    got = p.paths()
+    # (x block, l1, l2, l3, output block, output parity) against (x block, Y block, l3, parity)
+    assert [(i1, l3_, p3) for (i1, _, _, l3_, _, p3) in got] == [(i1, l3_, p3) for (i1, _, l3_, p3) in en]
+    assert [l2 for (_, _, l2, *_) in got] == [yt[j][1] for (_, j, _, _) in en]
+    assert (p.x_dim, p.y_dim, p.out_dim, p.n_paths) == (d.x_dim, d.y_dim, d.out_dim, d.P)
+
+
+def test_default_y_equals_the_natural_harmonics():
+    a = oeq.Plan("8x0e+8x1o", 3, 3, "f32")
+    b = oeq.Plan("8x0e+8x1o", 0, 3, "f32", y_irreps="1x0e+1x1o+1x2e+1x3o")
+    assert a.paths() == b.paths() and a.code_key == b.code_key
+
+
+def test_y_irreps_rejected():
+    def status(**kw):
+        with pytest.raises(oeq.OeqError) as e:
+            oeq.Plan("8x1o", 0, 3, "f32", **kw)
+        return e.value.status
+    assert status(y_irreps="2x1o") == 2                          # multiplicity above 1
+    assert status(y_irreps="1x4e") == 2                          # degree above 3
+    assert status(y_irreps="1x3o+1x3o+1x1o") == 2                # 17 values per row
+    # an explicit path must respect the product of the parities: 1o x 1e -> 1o, not 1e
+    assert status(y_irreps="1x1e", paths=[(0, 0, 0)], out_irreps="8x1e") == 1
+    p = oeq.Plan("8x1o", 0, 3, "f32", y_irreps="1x1e", paths=[(0, 0, 0)], out_irreps="8x1o")
+    assert p.paths() == [(0, 1, 1, 1, 0, -1)]
+    assert status(y_irreps="1x0e", paths=[(0, 1, 0)], out_irreps="8x1o") == 1   # no Y block 1
+
+
+def test_vector_entry_points_reject_pseudotensor_y():
+    # harmonics of a vector cannot fill a 1e block: refused on the host, before any launch
+    p = oeq.Plan("8x1o", 0, 2, "f32", y_irreps="1x0e+1x1e")
+    fake = ctypes.c_void_p(0x1000)
+    st = oeq.lib().oeq_sph_harm(p.handle, 4, fake, fake, None)
+    assert st == 2 and b"parity" in oeq.lib().oeq_last_error()
+    assert oeq.lib().oeq_sph_harm_bwd(p.handle, 4, fake, fake, fake, None) == 2
+    rp = ctypes.c_void_p(0x2000)
+    assert oeq.lib().oeq_tp_conv_fwd_vec(p.handle, 2, 4, rp, fake, fake, fake, fake, fake, None) == 2
