@@ -30,7 +30,7 @@ STATUS = {0: "OEQ_OK", 1: "OEQ_ERR_INVALID_ARG", 2: "OEQ_ERR_UNSUPPORTED", 3: "O
 
 EXPORTED = ["oeq_plan_create", "oeq_plan_create_cached", "oeq_plan_destroy", "oeq_plan_dims", "oeq_plan_paths", "oeq_plan_code_key",
             "oeq_cg_table",
-            "oeq_workspace_size", "oeq_tp_conv_fwd", "oeq_tp_conv_bwd", "oeq_tp_conv_dbwd",
+            "oeq_workspace_size", "oeq_tp_conv_fwd", "oeq_tp_conv_bwd", "oeq_tp_conv_bwd_noalloc", "oeq_tp_conv_dbwd",
             "oeq_csr_workspace_size", "oeq_sender_csr", "oeq_csr_check", "oeq_status_string",
             "oeq_last_error", "oeq_plan_schedule", "oeq_sender_view", "oeq_tp_conv_fwd_sender",
             "oeq_tp_conv_bwd_sender", "oeq_sph_harm", "oeq_sph_harm_bwd", "oeq_tp_conv_fwd_vec",
@@ -95,6 +95,8 @@ def lib():
     L.oeq_tp_conv_fwd.restype = st
     L.oeq_tp_conv_bwd.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, SZ, P]
     L.oeq_tp_conv_bwd.restype = st
+    L.oeq_tp_conv_bwd_noalloc.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P]
+    L.oeq_tp_conv_bwd_noalloc.restype = st
     L.oeq_tp_conv_dbwd.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, SZ, P]
     L.oeq_tp_conv_dbwd.restype = st
     L.oeq_csr_workspace_size.argtypes = [I64, I64, ctypes.POINTER(SZ)]
@@ -371,6 +373,22 @@ def oeq_tp_conv_bwd(plan: Plan, rowptr, src, x, Y, W, grad_out, mode: str = "ato
     _check(lib().oeq_tp_conv_bwd(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W),
                                  _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gW), _MODES[mode], _ptr(ws), nbytes,
                                  _stream()))
+    return gx, gY, gW
+
+
+def oeq_tp_conv_bwd_noalloc(plan: Plan, rowptr, src, x, Y, W, grad_out, out, mode: str = "atomic"):
+    """oeq_tp_conv_bwd into preallocated (grad_x, grad_Y, grad_W) (None: not computed),
+    with the library's fixed device scratch in place of a workspace."""
+    N, E = _graph(rowptr, src)
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(Y, (E, plan.y_dim), dt, "Y")
+    _want(W, (E, plan.n_paths, plan.U), dt, "W")
+    _want(grad_out, (N, plan.out_dim), dt, "grad_out")
+    shapes = ((N, plan.x_dim), (E, plan.y_dim), (E, plan.n_paths, plan.U))
+    gx, gY, gW = (_want(t, s, dt, n) for t, s, n in zip(out, shapes, ("grad_x", "grad_Y", "grad_W")))
+    _check(lib().oeq_tp_conv_bwd_noalloc(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(Y), _ptr(W),
+                                         _ptr(grad_out), _ptr(gx), _ptr(gY), _ptr(gW), _MODES[mode], _stream()))
     return gx, gY, gW
 
 

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "liboeq.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HOST_SOURCES = ["capi.cpp", "capi_graph.cpp", "capi_edge.cpp", "planner.cpp", "cg_tables.cpp", "codegen.cpp", "jit.cpp"]
-HIP_SOURCES = ["csr.hip"]
+HIP_SOURCES = ["csr.hip", "noalloc.hip"]
 ARCH = "gfx950"
 NO_PACKED_FP32 = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -1,7 +1,10 @@
 // C ABI entry points of the plans and the receiver-stationary convolution passes
 // (forward, VJP, double backward): argument checks on the host only (no device
 // reads, no synchronisation), workspace carving and stream-ordered launches.
+#include <cstdio>
+
 #include "capi_internal.hpp"
+#include "noalloc.hpp"
 
 using namespace oeq::capi;
 
@@ -165,6 +168,39 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     }
     if (st != OEQ_OK) return st;
     return gyp ? gy_combine(p, w, gY, E, s) : OEQ_OK;
+}
+
+oeq_status oeq_tp_conv_bwd_noalloc(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr,
+                                   const int32_t *src, const void *x, const void *Y, const void *W, const void *g,
+                                   void *gx, void *gY, void *gW, oeq_bwd_mode mode, void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    // the scratch this call binds: exactly what oeq_tp_conv_bwd carves from its workspace
+    const bool det = gx && mode == OEQ_BWD_DETERMINISTIC && E > 0;
+    const bool gyp = gY && p->bwd_groups.size() > 1 && E > 0;
+    Workspace w;
+    if ((st = ws_layout(p, N, E, det, gyp, nullptr, &w)) != OEQ_OK) return st;
+    if (w.bytes > oeq::kNoAllocScratchBytes) {
+        char msg[160];
+        std::snprintf(msg, sizeof msg, "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu",
+                      w.bytes, oeq::kNoAllocScratchBytes);
+        return fail(OEQ_ERR_WORKSPACE, msg);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    // loading the plan's kernels on a device allocates device memory: an ordinary call
+    // with this plan on this device must come first
+    if (!oeq::module_loaded(*p, dev))
+        return fail(OEQ_ERR_INVALID_ARG, "the plan's kernels are not loaded on this device yet (make one ordinary "
+                                         "call with the plan on this device first)");
+    void *ws = nullptr;
+    if (w.bytes > 0 && (e = oeq::noalloc_scratch(&ws)) != hipSuccess)
+        return fail(OEQ_ERR_HIP, std::string("scratch address: ") + hipGetErrorString(e));
+    return oeq_tp_conv_bwd(plan, N, E, rowptr, src, x, Y, W, g, gx, gY, gW, mode, ws,
+                           ws ? oeq::kNoAllocScratchBytes : 0, stream);
 }
 
 oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,

@@ -133,6 +133,12 @@ oeq_status jit_compile(oeq_plan &p, std::string *why, bool cache_only) {
     return OEQ_OK;
 }
 
+bool module_loaded(oeq_plan &p, int dev) {
+    std::lock_guard<std::mutex> lock(p.mu);
+    const auto it = p.modules.find(dev);
+    return it != p.modules.end() && it->second.module != nullptr;
+}
+
 oeq_status get_kernel(oeq_plan &p, const char *name, hipFunction_t *fn, std::string *why) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);

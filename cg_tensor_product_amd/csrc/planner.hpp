@@ -125,4 +125,7 @@ oeq_status jit_compile(oeq_plan &p, std::string *why, bool cache_only = false);
 // Loads the module on the current device (once) and returns the kernel.
 oeq_status get_kernel(oeq_plan &p, const char *name, hipFunction_t *fn, std::string *why);
 
+// Whether the plan's module is already loaded on device `dev` (a load allocates device memory).
+bool module_loaded(oeq_plan &p, int dev);
+
 }  // namespace oeq

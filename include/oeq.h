@@ -196,6 +196,25 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edge
                            void *grad_x, void *grad_Y, void *grad_W, oeq_bwd_mode mode,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* oeq_tp_conv_bwd without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.  Its scratch (the per-edge
+ * x-gradient rows and the sender CSR of DETERMINISTIC mode, the per-group partial
+ * Y-gradients of a plan with several backward groups) lives in a file-scope device
+ * array of 64 MiB that each device the library runs on holds until the process
+ * ends; a call needing more returns OEQ_ERR_WORKSPACE with the size in
+ * oeq_last_error(), before any device work.  The plan must already have run an
+ * ordinary call on the current device (loading its kernels allocates), else
+ * OEQ_ERR_INVALID_ARG.  Every call on a device shares that device's array:
+ * calls that overlap on one device (several streams or threads at once) race
+ * and must be ordered by the caller.  Results equal oeq_tp_conv_bwd's (bitwise
+ * in DETERMINISTIC mode). */
+oeq_status oeq_tp_conv_bwd_noalloc(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                   const int32_t *rowptr, const int32_t *src, const void *x,
+                                   const void *Y, const void *W, const void *grad_out,
+                                   void *grad_x, void *grad_Y, void *grad_W, oeq_bwd_mode mode,
+                                   void *stream);
+
 /* Double backward: gradients of
  *   S = <gg_x, grad_x> + <gg_Y, grad_Y> + <gg_W, grad_W>
  * (grad_* the VJP above) with respect to x, Y, W and grad_out.  Since f is

@@ -346,3 +346,17 @@ def test_vector_entry_points_reject_pseudotensor_y():
     assert oeq.lib().oeq_sph_harm_bwd(p.handle, 4, fake, fake, fake, None) == 2
     rp = ctypes.c_void_p(0x2000)
     assert oeq.lib().oeq_tp_conv_fwd_vec(p.handle, 2, 4, rp, fake, fake, fake, fake, fake, None) == 2
+
+
+def test_noalloc_bwd_rejects_scratch_beyond_its_limit():
+    # the deterministic VJP of the 5,000-node / 280,000-edge workload needs ~0.58 GB of
+    # per-edge rows: refused on the host with the size, before any device call
+    wl = synth.WORKLOADS["mace_medium_fp32"]
+    p = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    fake = ctypes.c_void_p(0x1000)
+    st = oeq.lib().oeq_tp_conv_bwd_noalloc(p.handle, 5000, 280000, fake, fake, fake, fake, fake, fake, fake, fake,
+                                            fake, 1, None)
+    assert st == 3
+    msg = oeq.lib().oeq_last_error().decode()
+    need = int(re.search(r"needs (\d+) bytes", msg).group(1))
+    assert "67108864" in msg and need >= 280000 * 512 * 4
