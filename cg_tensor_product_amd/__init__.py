@@ -35,7 +35,8 @@ EXPORTED = ["oeq_plan_create", "oeq_plan_create_cached", "oeq_plan_destroy", "oe
             "oeq_last_error", "oeq_plan_schedule", "oeq_sender_view", "oeq_tp_conv_fwd_sender",
             "oeq_tp_conv_bwd_sender", "oeq_sph_harm", "oeq_sph_harm_bwd", "oeq_tp_conv_fwd_vec",
             "oeq_workspace_size_vec", "oeq_tp_conv_bwd_vec", "oeq_radial_workspace_size", "oeq_radial_fwd",
-            "oeq_radial_bwd", "oeq_tp_conv_fwd_radial", "oeq_workspace_size_radial", "oeq_tp_conv_bwd_radial"]
+            "oeq_radial_bwd", "oeq_tp_conv_fwd_radial", "oeq_workspace_size_radial", "oeq_tp_conv_bwd_radial",
+            "oeq_tp_conv_fwd_pos", "oeq_workspace_size_pos", "oeq_tp_conv_bwd_pos"]
 SCHEDULES = {0: "receiver", 1: "sender"}
 
 
@@ -124,6 +125,12 @@ def lib():
     L.oeq_workspace_size_vec.restype = st
     L.oeq_tp_conv_bwd_vec.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, SZ, P]
     L.oeq_tp_conv_bwd_vec.restype = st
+    L.oeq_tp_conv_fwd_pos.argtypes = [P, I64, I64, P, P, P, P, P, P, P]
+    L.oeq_tp_conv_fwd_pos.restype = st
+    L.oeq_workspace_size_pos.argtypes = [P, I64, I64, ctypes.c_int, ctypes.POINTER(SZ)]
+    L.oeq_workspace_size_pos.restype = st
+    L.oeq_tp_conv_bwd_pos.argtypes = [P, I64, I64, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, SZ, P]
+    L.oeq_tp_conv_bwd_pos.restype = st
     D = ctypes.c_double
     L.oeq_radial_workspace_size.argtypes = [P, I64, I32, ctypes.POINTER(SZ)]
     L.oeq_radial_workspace_size.restype = st
@@ -566,6 +573,53 @@ def oeq_tp_conv_bwd_vec(plan: Plan, rowptr, src, x, vec, W, grad_out, mode: str 
         raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=x.device)
         workspace = raw[(-raw.data_ptr()) % 256:][:nbytes]
     _check(lib().oeq_tp_conv_bwd_vec(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(vec), _ptr(W),
+                                     _ptr(grad_out), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _MODES[mode],
+                                     _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def oeq_tp_conv_fwd_pos(plan: Plan, rowptr, src, x, pos, W, out=None):
+    """Forward with Y evaluated in the kernel from atom positions pos[N, 3]
+    (vec[e] = pos[src[e]] - pos[receiver])."""
+    N, E = _graph(rowptr, src)
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(pos, (N, 3), dt, "pos")
+    _want(W, (E, plan.n_paths, plan.U), dt, "W")
+    if out is None:
+        out = _empty((N, plan.out_dim), dt, rowptr.device)
+    _want(out, (N, plan.out_dim), dt, "out")
+    _check(lib().oeq_tp_conv_fwd_pos(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(pos), _ptr(W),
+                                     _ptr(out), _stream()))
+    return out
+
+
+def oeq_workspace_size_pos(plan: Plan, n_nodes: int, n_edges: int, mode: str = "atomic") -> int:
+    b = ctypes.c_size_t()
+    _check(lib().oeq_workspace_size_pos(plan.handle, n_nodes, n_edges, _MODES[mode], ctypes.byref(b)))
+    return b.value
+
+
+def oeq_tp_conv_bwd_pos(plan: Plan, rowptr, src, x, pos, W, grad_out, mode: str = "atomic",
+                        want=("x", "pos", "W"), out=None, workspace=None):
+    """VJP to (x, pos, W) of the forward from atom positions."""
+    import torch
+    N, E = _graph(rowptr, src)
+    dt = plan.torch_dtype()
+    _want(x, (N, plan.x_dim), dt, "x")
+    _want(pos, (N, 3), dt, "pos")
+    _want(W, (E, plan.n_paths, plan.U), dt, "W")
+    _want(grad_out, (N, plan.out_dim), dt, "grad_out")
+    shapes = ((N, plan.x_dim), (N, 3), (E, plan.n_paths, plan.U))
+    if out is None:
+        out = tuple(_empty(shp, dt, x.device) if k in want else None for k, shp in zip(("x", "pos", "W"), shapes))
+    for t, shp, k in zip(out, shapes, ("grad_x", "grad_pos", "grad_W")):
+        _want(t, shp, dt, k)
+    if workspace is None:
+        nbytes = oeq_workspace_size_pos(plan, N, E, mode)
+        raw = torch.empty(nbytes + 256, dtype=torch.uint8, device=x.device)
+        workspace = raw[(-raw.data_ptr()) % 256:][:nbytes]
+    _check(lib().oeq_tp_conv_bwd_pos(plan.handle, N, E, _ptr(rowptr), _ptr(src), _ptr(x), _ptr(pos), _ptr(W),
                                      _ptr(grad_out), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _MODES[mode],
                                      _ptr(workspace), workspace.numel(), _stream()))
     return out

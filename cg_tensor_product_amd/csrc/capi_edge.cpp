@@ -92,6 +92,116 @@ oeq_status oeq_tp_conv_bwd_vec(const oeq_plan *plan, int64_t N, int64_t E, const
     return gvec ? oeq_sph_harm_bwd(p, E, vec, gYw, gvec, stream) : OEQ_OK;
 }
 
+oeq_status oeq_tp_conv_fwd_pos(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr,
+                               const int32_t *src, const void *x, const void *pos, const void *W, void *out,
+                               void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if ((st = check_y_from_vectors(plan)) != OEQ_OK) return st;
+    if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
+    if (E > 0 && (!x || !pos || !W)) return fail(OEQ_ERR_INVALID_ARG, "x, pos or W is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    int n_nodes = static_cast<int>(N);
+    void *args[] = {&rowptr, &src, &x, &pos, &W, &out, &n_nodes};
+    return launch(p, "oeq_fwd_pos", static_cast<unsigned>(N), fwd_block(p), static_cast<hipStream_t>(stream), args);
+}
+
+namespace {
+
+// Workspace of the VJP from positions: edge vectors [E, 3], Y rows, Y-gradient rows,
+// vector gradients [E, 3], the sender CSR (deterministic mode), then the VJP's own.
+struct PosWs {
+    size_t vec = 0, Y = 0, gY = 0, gvec = 0, srowptr = 0, sperm = 0, csr = 0, vjp = 0, bytes = 0;
+};
+
+oeq_status pos_layout(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, PosWs *w) {
+    const size_t es = esize(p), e = static_cast<size_t>(E);
+    size_t off = 0;
+    w->vec = off;
+    off += up(e * 3 * es);
+    w->Y = off;
+    off += up(e * p->YD * es);
+    w->gY = off;
+    off += up(e * p->YD * es);
+    w->gvec = off;
+    off += up(e * 3 * es);
+    if (mode == OEQ_BWD_DETERMINISTIC) {
+        size_t csr = 0;
+        const hipError_t he = oeq::sender_csr_workspace(N, E, &csr);
+        if (he != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR workspace: ") + hipGetErrorString(he));
+        w->srowptr = off;
+        off += up(sizeof(int32_t) * static_cast<size_t>(N + 1));
+        w->sperm = off;
+        off += up(sizeof(int32_t) * (e > 0 ? e : 1));
+        w->csr = off;
+        off += up(csr);
+    }
+    size_t base = 0;
+    oeq_status st = oeq_workspace_size(p, N, E, mode, &base);
+    if (st != OEQ_OK) return st;
+    w->vjp = off;
+    w->bytes = off + base;
+    return OEQ_OK;
+}
+
+}  // namespace
+
+oeq_status oeq_workspace_size_pos(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, size_t *bytes) {
+    if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
+    if (N < 0 || E < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    PosWs w;
+    oeq_status st = pos_layout(p, N, E, mode, &w);
+    if (st != OEQ_OK) return st;
+    *bytes = w.bytes;
+    return OEQ_OK;
+}
+
+oeq_status oeq_tp_conv_bwd_pos(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr,
+                               const int32_t *src, const void *x, const void *pos, const void *W, const void *g,
+                               void *gx, void *gpos, void *gW, oeq_bwd_mode mode, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    oeq_status st = check_graph(plan, N, E, rowptr, src);
+    if (st != OEQ_OK) return st;
+    if ((st = check_y_from_vectors(plan)) != OEQ_OK) return st;
+    if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
+    if (E > 0 && (!x || !pos || !W || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, pos, W or grad_out is NULL");
+    oeq_plan *p = const_cast<oeq_plan *>(plan);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (E == 0) {
+        if (gx && (st = fill_zero(p, gx, N * p->XD, s)) != OEQ_OK) return st;
+        return gpos ? fill_zero(p, gpos, N * 3, s) : OEQ_OK;
+    }
+    if (!gx && !gpos && !gW) return OEQ_OK;
+    PosWs w;
+    if ((st = pos_layout(p, N, E, mode, &w)) != OEQ_OK) return st;
+    if (!workspace || workspace_bytes < w.bytes) return fail(OEQ_ERR_WORKSPACE, "workspace smaller than oeq_workspace_size_pos");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+        return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    char *ws = static_cast<char *>(workspace);
+    void *vec = ws + w.vec, *Yw = ws + w.Y, *gYw = gpos ? ws + w.gY : nullptr, *gvec = ws + w.gvec;
+    int n_nodes = static_cast<int>(N);
+    void *yargs[] = {&rowptr, &src, &pos, &Yw, &vec, &n_nodes};
+    if ((st = launch(p, "oeq_sph_harm_pos", static_cast<unsigned>(N), 64, s, yargs)) != OEQ_OK) return st;
+    if ((st = oeq_tp_conv_bwd(p, N, E, rowptr, src, x, Yw, W, g, gx, gYw, gW, mode, ws + w.vjp,
+                              workspace_bytes - w.vjp, stream)) != OEQ_OK)
+        return st;
+    if (!gpos) return OEQ_OK;
+    void *gargs[] = {&vec, &gYw, &gvec, &E};
+    if ((st = edge_launch(p, "oeq_sph_harm_bwd", E, gargs, s)) != OEQ_OK) return st;
+    if (mode == OEQ_BWD_ATOMIC) {
+        if ((st = fill_zero(p, gpos, N * 3, s)) != OEQ_OK) return st;
+        void *args[] = {&rowptr, &src, &gvec, &gpos, &n_nodes};
+        return launch(p, "oeq_pos_scatter_atomic", static_cast<unsigned>(N), 64, s, args);
+    }
+    int32_t *srp = reinterpret_cast<int32_t *>(ws + w.srowptr), *spm = reinterpret_cast<int32_t *>(ws + w.sperm);
+    const hipError_t he = oeq::sender_csr(N, E, src, srp, spm, ws + w.csr, s);
+    if (he != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR: ") + hipGetErrorString(he));
+    void *args[] = {&rowptr, &srp, &spm, &gvec, &gpos, &n_nodes};
+    const unsigned blocks = static_cast<unsigned>(std::min<int64_t>((N + 255) / 256, 65536));
+    return launch(p, "oeq_pos_scatter_det", blocks, 256, s, args);
+}
+
 oeq_status oeq_radial_workspace_size(const oeq_plan *p, int64_t E, int32_t hidden, size_t *bytes) {
     if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
     if (E < 0 || hidden < 1 || hidden > 1024) return fail(OEQ_ERR_INVALID_ARG, "bad size");

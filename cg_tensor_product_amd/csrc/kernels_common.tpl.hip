@@ -148,14 +148,88 @@ __device__ __forceinline__ void sh_grad(real_t vx, real_t vy, real_t vz, const r
     sh_grad_full(vx, vy, vz, f, gvx, gvy, gvz);
 }
 
-// Y row of edge e from its vector (YV) or from memory
-template <bool YV>
-__device__ __forceinline__ void edge_y(const real_t *__restrict__ Ysrc, int e, real_t (&yv)[YD]) {
-    if constexpr (YV) {
+// Where a pass takes edge e's Y row from: YM_TENSOR the Y tensor, YM_VEC the harmonics
+// of the edge vector vec[e], YM_POS the harmonics of pos[s] - pos[r] (the sender's
+// position relative to the receiver; pr holds the receiver's position).
+constexpr int YM_TENSOR = 0, YM_VEC = 1, YM_POS = 2;
+
+template <int YM>
+__device__ __forceinline__ void edge_y(const real_t *__restrict__ Ysrc, int e, int s, const real_t (&pr)[3],
+                                       real_t (&yv)[YD]) {
+    if constexpr (YM == YM_VEC) {
         const real_t *v = Ysrc + (i64)e * 3;
         sh_eval(v[0], v[1], v[2], yv);
+    } else if constexpr (YM == YM_POS) {
+        const real_t *ps = Ysrc + (i64)s * 3;
+        sh_eval(ps[0] - pr[0], ps[1] - pr[1], ps[2] - pr[2], yv);
     } else {
         load_y(Ysrc, e, yv);
+    }
+}
+
+// Edge vectors from positions, vec[e] = pos[src[e]] - pos[r], and their harmonics Y[e],
+// one workgroup per receiver row r.
+extern "C" __global__ void __launch_bounds__(64)
+oeq_sph_harm_pos(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ pos,
+                 real_t *__restrict__ Y, real_t *__restrict__ vec, int n_nodes) {
+    const int r = blockIdx.x;
+    if (r >= n_nodes) return;
+    const real_t px = pos[(i64)r * 3], py = pos[(i64)r * 3 + 1], pz = pos[(i64)r * 3 + 2];
+    const int e1 = rowptr[r + 1];
+    for (int e = rowptr[r] + (int)threadIdx.x; e < e1; e += 64) {
+        const i64 s = src[e];
+        const real_t vx = pos[s * 3] - px, vy = pos[s * 3 + 1] - py, vz = pos[s * 3 + 2] - pz;
+        vec[(i64)e * 3] = vx;
+        vec[(i64)e * 3 + 1] = vy;
+        vec[(i64)e * 3 + 2] = vz;
+        real_t yv[YD];
+        sh_eval(vx, vy, vz, yv);
+#pragma unroll
+        for (int k = 0; k < YD; ++k) Y[(i64)e * YD + k] = yv[k];
+    }
+}
+
+// The position gradient from the edge-vector gradient gvec[E, 3]: each edge adds gvec[e]
+// to its sender and subtracts it from its receiver (vec = pos[s] - pos[r]).  Atomic form:
+// one workgroup per receiver row, gpos zeroed beforehand.
+extern "C" __global__ void __launch_bounds__(64)
+oeq_pos_scatter_atomic(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ gvec,
+                       real_t *__restrict__ gpos, int n_nodes) {
+    const int r = blockIdx.x;
+    if (r >= n_nodes) return;
+    const int e1 = rowptr[r + 1];
+    for (int e = rowptr[r] + (int)threadIdx.x; e < e1; e += 64) {
+        const i64 s = src[e];
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+            const real_t v = gvec[(i64)e * 3 + c];
+            atomicAdd(gpos + s * 3 + c, v);
+            atomicAdd(gpos + (i64)r * 3 + c, -v);
+        }
+    }
+}
+
+// Deterministic form: one thread per node n sums its out-edges in increasing edge id
+// (the sender CSR) and then subtracts its own row's edges in order.
+extern "C" __global__ void __launch_bounds__(256)
+oeq_pos_scatter_det(const int *__restrict__ rowptr, const int *__restrict__ srowptr, const int *__restrict__ sperm,
+                    const real_t *__restrict__ gvec, real_t *__restrict__ gpos, int n_nodes) {
+    for (int n = blockIdx.x * blockDim.x + threadIdx.x; n < n_nodes; n += gridDim.x * blockDim.x) {
+        real_t a0 = real_t(0), a1 = real_t(0), a2 = real_t(0);
+        for (int k = srowptr[n]; k < srowptr[n + 1]; ++k) {
+            const i64 e = sperm[k];
+            a0 += gvec[e * 3];
+            a1 += gvec[e * 3 + 1];
+            a2 += gvec[e * 3 + 2];
+        }
+        for (int e = rowptr[n]; e < rowptr[n + 1]; ++e) {
+            a0 -= gvec[(i64)e * 3];
+            a1 -= gvec[(i64)e * 3 + 1];
+            a2 -= gvec[(i64)e * 3 + 2];
+        }
+        gpos[(i64)n * 3] = a0;
+        gpos[(i64)n * 3 + 1] = a1;
+        gpos[(i64)n * 3 + 2] = a2;
     }
 }
 

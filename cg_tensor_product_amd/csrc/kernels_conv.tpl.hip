@@ -4,7 +4,7 @@
 // ---------------------------------------------------------------------------
 // Forward: out[r] = sum over the receiver's edges of the per-edge messages.
 // ---------------------------------------------------------------------------
-template <int G, bool YV>
+template <int G, int YM>
 __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ rowptr,
                                           const int *__restrict__ src, const real_t *__restrict__ x,
                                           const real_t *__restrict__ Y, const real_t *__restrict__ W,
@@ -16,17 +16,22 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
     zero(sum);
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     if (e0 < e1) {
+        real_t pr[3] = {real_t(0), real_t(0), real_t(0)};  // the receiver's position (YM_POS)
+        if constexpr (YM == YM_POS) {
+#pragma unroll
+            for (int c = 0; c < 3; ++c) pr[c] = Y[(i64)r * 3 + c];
+        }
         // software pipeline: the next edge's loads are in flight while this one computes
         int s = uni(src[e0]);
         real_t yv[YD], xv[Gr::NX], wv[Gr::NW];
-        edge_y<YV>(Y, e0, yv);
+        edge_y<YM>(Y, e0, s, pr, yv);
         Gr::load_x(x + (i64)s * XD, uu, xv);
         Gr::load_w(W + (i64)e0 * (P * U), uu, wv);
         for (int e = e0; e < e1; ++e) {
             real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
             const int en = (e + 1 < e1) ? e + 1 : e;
             const int sn = uni(src[en]);
-            edge_y<YV>(Y, en, yn);
+            edge_y<YM>(Y, en, sn, pr, yn);
             Gr::load_x(x + (i64)sn * XD, uu, xn);
             Gr::load_w(W + (i64)en * (P * U), uu, wn);
             // keep the next edge's loads ahead of this edge's arithmetic
@@ -48,16 +53,16 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
     }
 }
 
-template <int G, bool YV>
+template <int G, int YM>
 __device__ __forceinline__ void fwd_dispatch(int grp, int r, int u, const int *__restrict__ rowptr,
                                              const int *__restrict__ src, const real_t *__restrict__ x,
                                              const real_t *__restrict__ Y, const real_t *__restrict__ W,
                                              real_t *__restrict__ out, bool acc) {
     if (grp == G) {
-        fwd_group<G, YV>(r, u, rowptr, src, x, Y, W, out, acc);
+        fwd_group<G, YM>(r, u, rowptr, src, x, Y, W, out, acc);
         return;
     }
-    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1, YV>(grp, r, u, rowptr, src, x, Y, W, out, acc);
+    if constexpr (G + 1 < NGF) fwd_dispatch<G + 1, YM>(grp, r, u, rowptr, src, x, Y, W, out, acc);
 }
 
 // Forward from Y-contracted CG rows: the receiver's edges are taken in tiles of FWD_MT.
@@ -170,7 +175,7 @@ oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_
         __shared__ __attribute__((aligned(16))) real_t mbuf[FWD_M_ELEMS * FWD_MT > 0 ? FWD_M_ELEMS * FWD_MT : 1];
         fwd_lds_dispatch<0>(mbuf, grp, r, uc, lane, wc * 64 + lane, rowptr, src, x, Y, W, out, (flags & 1) != 0);
     } else {
-        fwd_dispatch<0, false>(grp, r, uc * 64 + lane, rowptr, src, x, Y, W, out, (flags & 1) != 0);
+        fwd_dispatch<0, YM_TENSOR>(grp, r, uc * 64 + lane, rowptr, src, x, Y, W, out, (flags & 1) != 0);
     }
 }
 
@@ -182,7 +187,18 @@ oeq_fwd_vec(const int *__restrict__ rowptr, const int *__restrict__ src, const r
     if ((int)blockIdx.x >= n_nodes) return;
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
-    fwd_dispatch<0, true>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, vec, W, out, false);
+    fwd_dispatch<0, YM_VEC>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, vec, W, out, false);
+}
+
+// The forward from atom positions pos[N, 3]: the harmonics of edge e are those of
+// pos[src[e]] - pos[r], evaluated in the kernel (no vector or Y tensor).
+extern "C" __global__ void __launch_bounds__(UCH * NGF * 64) FWD_OCCUPANCY
+oeq_fwd_pos(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ x,
+            const real_t *__restrict__ pos, const real_t *__restrict__ W, real_t *__restrict__ out, int n_nodes) {
+    if ((int)blockIdx.x >= n_nodes) return;
+    const int w = uni(threadIdx.x >> 6);
+    const int grp = w / UCH, uc = w - grp * UCH;
+    fwd_dispatch<0, YM_POS>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, pos, W, out, false);
 }
 
 // The atomic x-gradient is accumulated m-major inside each x block (so the

@@ -333,6 +333,32 @@ oeq_status oeq_tp_conv_bwd_vec(const oeq_plan *plan, int64_t n_nodes, int64_t n_
                                void *grad_x, void *grad_vec, void *grad_W, oeq_bwd_mode mode,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---- Y from atom positions ---------------------------------------------------
+ * The same with the edges' vectors formed from atom positions pos[N, 3] (plan
+ * dtype): vec[e] = pos[src[e]] - pos[r] for edge e of receiver row r, the
+ * neighbour's position relative to the central atom of a neighbour list
+ * ("Receiver-streaming convolutions ...", opening post: receiver-major edges come
+ * from the neighbour lists of atom positions).  The VJP returns, in place of
+ * grad_Y, the gradient of <grad_out, f> with respect to the positions:
+ *   grad_pos[n] = sum_{e: src[e] = n} grad_vec[e] - sum_{e in row n} grad_vec[e],
+ * scattered with floating-point atomics (ATOMIC) or summed per node in a fixed
+ * order, out-edges in increasing edge id then the node's own row
+ * (DETERMINISTIC: bitwise repeatable).  The forward evaluates the harmonics
+ * inside the kernel; the VJP forms vectors and Y into the workspace, runs the VJP,
+ * then the harmonic gradient and the scatter.  A self-loop has a zero vector and
+ * contributes nothing to grad_pos.  `workspace` (256-byte aligned) must hold
+ * oeq_workspace_size_pos(mode) bytes.  Errors as for the vector entry points. */
+oeq_status oeq_tp_conv_fwd_pos(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                               const int32_t *rowptr, const int32_t *src, const void *x,
+                               const void *pos, const void *W, void *out, void *stream);
+oeq_status oeq_workspace_size_pos(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                                  oeq_bwd_mode mode, size_t *bytes);
+oeq_status oeq_tp_conv_bwd_pos(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
+                               const int32_t *rowptr, const int32_t *src, const void *x,
+                               const void *pos, const void *W, const void *grad_out,
+                               void *grad_x, void *grad_pos, void *grad_W, oeq_bwd_mode mode,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---- Radial weights from edge lengths ---------------------------------------
  * The pages realise W outside the convolution, and fusing its realisation would be
  * a new operation ("Receiver-streaming convolutions ...", maintainer replies).  They

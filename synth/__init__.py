@@ -245,6 +245,11 @@ def generate(wl: Workload, n_paths: int, out_dim: int, want=("x", "Y", "W", "g")
         lrng = np.random.Generator(np.random.PCG64(
             np.random.SeedSequence(wl.seed).spawn(_NCHILD)[_EXTRA].spawn(100)[99]))
         out["evec"] = (unit * (0.5 + 4.5 * lrng.random((E, 1)))).astype(dt)
+    if "pos" in want:
+        # atom positions uniform in a 10 x 10 x 10 box (the graph is drawn independently of them)
+        prng = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence(wl.seed).spawn(_NCHILD)[_EXTRA].spawn(100)[98]))
+        out["pos"] = (10.0 * prng.random((wl.n_nodes, 3))).astype(dt)
     if "x" in want:
         out["x"] = normal(rngs[_X], (wl.n_nodes, wl.x_dim), dt)
     if "W" in want:

@@ -37,7 +37,7 @@ def _launch_sites():
             continue
         src = open(os.path.join(CSRC, fn)).read()
         arrays = {}
-        for m in re.finditer(r"void \*(\w+)\[\] = \{([^}]*)\};|launch\(p, \"(\w+)\", [^;]*?, (\w*args)\)", src, re.S):
+        for m in re.finditer(r"void \*(\w+)\[\] = \{([^}]*)\};|launch\(p, \"(\w+)\", [^;]*?, (\w*args)(?:, \w+)?\)", src, re.S):
             if m.group(1):
                 arrays[m.group(1)] = len([a for a in m.group(2).split(",") if a.strip()])
             else:
