@@ -168,20 +168,6 @@ def _irreps(seq) -> tuple:
     return tuple(tuple(int(v) for v in t) for t in seq)
 
 
-def _compile_in_child(x_irreps, y_lmax, lmax_out, dtype, paths, out_irreps, y_irreps=None):
-    """Creates the plan in a child Python process (compiling its kernels into the code-object
-    cache); the child inherits the OEQ_* planner options of this process."""
-    import subprocess
-    import sys
-    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    code = ("import sys; sys.path.insert(0, %r); import cg_tensor_product_amd as m; "
-            "m.Plan(%r, %r, %r, %r, paths=%r, out_irreps=%r, y_irreps=%r)"
-            % (root, list(x_irreps), y_lmax, lmax_out, dtype, paths, out_irreps, y_irreps))
-    env = dict(os.environ, OEQ_PLAN_IN_PROCESS="1")
-    subprocess.run([sys.executable, "-c", code], env=env, check=False,
-                   stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
-
-
 class Plan:
     """oeq_plan_create for an irreps descriptor.  dtype: "f32" or "f64".
 
@@ -222,19 +208,9 @@ class Plan:
             d.paths, d.n_paths = ps, len(paths)
             keep.append(ps)
         h = ctypes.c_void_p()
-        # The runtime compiler runs in a child process, which leaves the code object in the
-        # cache; this process then loads it from there.  A forward launched from a process
-        # that had run the compiler itself measured 0.95 ms where the same code object from
-        # the cache took 0.35 ms (MI355X, medium workload).  OEQ_PLAN_IN_PROCESS=1 compiles
-        # here instead; so does a failure of the child (no writable cache, for example).
-        st = lib().oeq_plan_create_cached(ctypes.byref(d), ctypes.byref(h))
-        if st == 5 and not os.environ.get("OEQ_PLAN_IN_PROCESS") and not os.environ.get("OEQ_NO_CACHE"):
-            _compile_in_child(self.x_irreps, self.y_lmax, self.lmax_out, dtype,
-                              None if paths is None else [tuple(int(v) for v in t) for t in paths],
-                              None if out_irreps is None else _irreps(out_irreps), self.y_irreps)
-            st = lib().oeq_plan_create_cached(ctypes.byref(d), ctypes.byref(h))
-        if st == 5:
-            st = lib().oeq_plan_create(ctypes.byref(d), ctypes.byref(h))
+        # the library compiles a plan missing from its code-object cache in its compiler
+        # helper (a child process), so the kernels do not depend on what this process loaded
+        st = lib().oeq_plan_create(ctypes.byref(d), ctypes.byref(h))
         _check(st)
         self._h = h
         dims = [ctypes.c_int64() for _ in range(5)]

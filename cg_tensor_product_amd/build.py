@@ -17,6 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liboeq.so")
+JITC = os.path.join(PKG, "oeq_jitc")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 HOST_SOURCES = ["capi.cpp", "capi_graph.cpp", "capi_edge.cpp", "planner.cpp", "cg_tables.cpp", "codegen.cpp", "jit.cpp"]
@@ -78,6 +79,12 @@ def build_library(verbose: bool = False) -> str:
     _run([os.path.join(ROCM, "bin", "hipcc"), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs,
           "-L" + os.path.join(ROCM, "lib"), "-lhiprtc", "-lamdhip64", "-Wl,-rpath," + os.path.join(ROCM, "lib")])
     os.replace(tmp, LIB)
+    # the runtime-compiler helper (a separate program: see csrc/jitc_main.cpp); DT_RPATH so
+    # that it loads this installation's runtime compiler whatever LD_LIBRARY_PATH holds
+    rocm_lib = os.path.join(ROCM, "lib")
+    _run(["g++", *common, os.path.join(CSRC, "jitc_main.cpp"), "-o", JITC + ".tmp", "-L" + rocm_lib, "-lhiprtc",
+          "-ldl", "-Wl,--disable-new-dtags", "-Wl,-rpath," + rocm_lib])
+    os.replace(JITC + ".tmp", JITC)
     return LIB
 
 

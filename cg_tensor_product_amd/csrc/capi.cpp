@@ -116,6 +116,11 @@ oeq_status oeq_workspace_size(const oeq_plan *p, int64_t n_nodes, int64_t n_edge
                               nullptr, &w);
     if (st != OEQ_OK) return st;
     *bytes = w.bytes;
+    if (bwd_by_sender(p, n_edges)) {  // the VJP's sender-stationary route needs the sender view
+        SenderWs sw;
+        if ((st = sender_ws_layout(p, n_nodes, n_edges, &sw)) != OEQ_OK) return st;
+        *bytes = std::max(*bytes, sw.bytes);
+    }
     return OEQ_OK;
 }
 
@@ -139,6 +144,23 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (E == 0) return gx ? fill_zero(p, gx, N * p->XD, s) : OEQ_OK;
     if (!gx && !gY && !gW) return OEQ_OK;
+    if (bwd_by_sender(p, E)) {
+        // the plan's data-movement model prefers the sender-stationary pass ("source
+        // stationary"): the sender view goes into the workspace, then the pass runs
+        SenderWs sw;
+        if ((st = sender_ws_layout(p, N, E, &sw)) != OEQ_OK) return st;
+        if (!workspace || workspace_bytes < sw.bytes)
+            return fail(OEQ_ERR_WORKSPACE, "workspace smaller than oeq_workspace_size");
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
+            return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+        char *ws = static_cast<char *>(workspace);
+        int32_t *srp = reinterpret_cast<int32_t *>(ws + sw.srowptr), *spm = reinterpret_cast<int32_t *>(ws + sw.sperm),
+                *sdst = reinterpret_cast<int32_t *>(ws + sw.sdst);
+        const hipError_t he = oeq::sender_view(N, E, rowptr, src, srp, spm, sdst, ws + sw.csr, s);
+        if (he != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender view: ") + hipGetErrorString(he));
+        return oeq_tp_conv_bwd_sender(plan, N, E, srp, spm, sdst, x, Y, W, g, gx, gY, gW, ws + sw.vjp,
+                                      workspace_bytes - sw.vjp, stream);
+    }
     const bool det = gx && mode == OEQ_BWD_DETERMINISTIC;
     const bool gyp = gY && p->bwd_groups.size() > 1;
     Workspace w;
@@ -178,14 +200,12 @@ oeq_status oeq_tp_conv_bwd_noalloc(const oeq_plan *plan, int64_t N, int64_t E, c
     if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
     oeq_plan *p = const_cast<oeq_plan *>(plan);
     // the scratch this call binds: exactly what oeq_tp_conv_bwd carves from its workspace
-    const bool det = gx && mode == OEQ_BWD_DETERMINISTIC && E > 0;
-    const bool gyp = gY && p->bwd_groups.size() > 1 && E > 0;
-    Workspace w;
-    if ((st = ws_layout(p, N, E, det, gyp, nullptr, &w)) != OEQ_OK) return st;
-    if (w.bytes > oeq::kNoAllocScratchBytes) {
+    size_t need = 0;
+    if ((st = bwd_ws_bytes(p, N, E, mode, gx != nullptr, gY != nullptr, &need)) != OEQ_OK) return st;
+    if (need > oeq::kNoAllocScratchBytes) {
         char msg[160];
         std::snprintf(msg, sizeof msg, "this call needs %zu bytes of scratch; the allocation-free entry point holds %zu",
-                      w.bytes, oeq::kNoAllocScratchBytes);
+                      need, oeq::kNoAllocScratchBytes);
         return fail(OEQ_ERR_WORKSPACE, msg);
     }
     int dev = 0;
@@ -197,7 +217,7 @@ oeq_status oeq_tp_conv_bwd_noalloc(const oeq_plan *plan, int64_t N, int64_t E, c
         return fail(OEQ_ERR_INVALID_ARG, "the plan's kernels are not loaded on this device yet (make one ordinary "
                                          "call with the plan on this device first)");
     void *ws = nullptr;
-    if (w.bytes > 0 && (e = oeq::noalloc_scratch(&ws)) != hipSuccess)
+    if (need > 0 && (e = oeq::noalloc_scratch(&ws)) != hipSuccess)
         return fail(OEQ_ERR_HIP, std::string("scratch address: ") + hipGetErrorString(e));
     return oeq_tp_conv_bwd(plan, N, E, rowptr, src, x, Y, W, g, gx, gY, gW, mode, ws,
                            ws ? oeq::kNoAllocScratchBytes : 0, stream);

@@ -124,6 +124,54 @@ inline oeq_status ws_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, b
     return OEQ_OK;
 }
 
+// Workspace of a VJP that the plan's data-movement model sends to the sender-stationary
+// pass: the sender view (srowptr[N+1], sperm[E], sdst[E]) and its build scratch, then the
+// pass's own partial Y-gradient rows (several backward groups).
+struct SenderWs {
+    size_t srowptr = 0, sperm = 0, sdst = 0, csr = 0, vjp = 0, bytes = 0;
+};
+
+inline oeq_status sender_ws_layout(const oeq_plan *p, int64_t N, int64_t E, SenderWs *w) {
+    size_t csr_bytes = 0;
+    const hipError_t e = oeq::sender_csr_workspace(N, E, &csr_bytes);
+    if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR workspace: ") + hipGetErrorString(e));
+    const size_t ne = static_cast<size_t>(E > 0 ? E : 1);
+    size_t off = 0;
+    w->srowptr = off;
+    off += up(sizeof(int32_t) * static_cast<size_t>(N + 1));
+    w->sperm = off;
+    off += up(sizeof(int32_t) * ne);
+    w->sdst = off;
+    off += up(sizeof(int32_t) * ne);
+    w->csr = off;
+    off += up(csr_bytes);
+    w->vjp = off;
+    if (p->bwd_groups.size() > 1) off += up(gy_groups(p) * static_cast<size_t>(E) * p->YD * esize(p));
+    w->bytes = off;
+    return OEQ_OK;
+}
+
+// Whether oeq_tp_conv_bwd takes the sender-stationary pass (the model's choice; a graph
+// without edges needs no pass).
+inline bool bwd_by_sender(const oeq_plan *p, int64_t E) { return p->sched_bwd == 1 && E > 0; }
+
+// Bytes of workspace an oeq_tp_conv_bwd call binds for these requested outputs.
+inline oeq_status bwd_ws_bytes(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, bool gx, bool gY,
+                               size_t *bytes) {
+    *bytes = 0;
+    if (E <= 0) return OEQ_OK;
+    if (bwd_by_sender(p, E)) {
+        SenderWs sw;
+        oeq_status st = sender_ws_layout(p, N, E, &sw);
+        if (st == OEQ_OK) *bytes = sw.bytes;
+        return st;
+    }
+    Workspace w;
+    oeq_status st = ws_layout(p, N, E, gx && mode == OEQ_BWD_DETERMINISTIC, gY && p->bwd_groups.size() > 1, nullptr, &w);
+    if (st == OEQ_OK) *bytes = w.bytes;
+    return st;
+}
+
 // Carves the workspace a call needs; fails before any device work if it is
 // missing, misaligned or too small.
 inline oeq_status ws_bind(const oeq_plan *p, int64_t N, int64_t E, bool det, bool gy_part, void *workspace,

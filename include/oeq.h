@@ -120,7 +120,13 @@ typedef struct oeq_plan oeq_plan; /* opaque, host-owned */
  * before its kernels are built ("An Efficient Sparse Kernel Generator for
  * O(3)-Equivariant Deep Networks", abstract), and the streaming convolution is
  * its own template, chosen when the kernels are compiled at run time
- * ("Receiver-streaming convolutions ...", first maintainer reply).  Host-only;
+ * ("Receiver-streaming convolutions ...", first maintainer reply).  The compile
+ * runs in the helper program oeq_jitc beside the library (a child process with
+ * this ROCm installation's compiler): compiled inside a process that had already
+ * loaded another ROCm release's compiler library (a framework wheel that bundles
+ * its own), the runtime compiler would use that release's LLVM, and on MI355X
+ * its forward took 0.95 ms against 0.36 ms.  OEQ_JIT_IN_PROCESS=1, or a missing
+ * or failing helper, compiles in the calling process instead.  Host-only;
  * the code object is loaded on a device at
  * the first compute call there.  *plan is set to NULL on failure.
  * Errors: OEQ_ERR_INVALID_ARG (NULL pointers, bad parity, a path outside the
@@ -130,11 +136,8 @@ typedef struct oeq_plan oeq_plan; /* opaque, host-owned */
 oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan);
 
 /* As oeq_plan_create, but never runs the runtime compiler: returns OEQ_ERR_JIT
- * (with *plan = NULL) when the plan's code object is not in the cache.  For
- * callers that compile in another process and load the result here: on MI355X
- * a forward launched from a process that had run the runtime compiler took
- * 0.95 ms where the byte-identical code object loaded from the cache took
- * 0.35 ms (cause not found). */
+ * (with *plan = NULL) when the plan's code object is not in the cache (for
+ * callers that must not compile, or compile ahead of time elsewhere). */
 oeq_status oeq_plan_create_cached(const oeq_tp_desc *desc, oeq_plan **plan);
 void oeq_plan_destroy(oeq_plan *plan);
 
@@ -175,7 +178,9 @@ oeq_status oeq_workspace_size(const oeq_plan *plan, int64_t n_nodes, int64_t n_e
 /* Forward: out = f(x, Y, W).  Receiver-stationary: one lane owns one
  * (receiver, channel), streams the receiver's edges and writes its output row
  * once, without atomics ("Receiver-streaming convolutions ...", opening post,
- * forward ownership).  Bitwise repeatable. */
+ * forward ownership).  Bitwise repeatable.  The forward takes no workspace, so it
+ * always runs receiver-stationary; where oeq_plan_schedule prefers the
+ * sender-stationary forward, oeq_tp_conv_fwd_sender runs it on a sender view. */
 oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                            const int32_t *rowptr, const int32_t *src, const void *x,
                            const void *Y, const void *W, void *out, void *stream);
@@ -188,6 +193,13 @@ oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edge
  * ownership): a wave owns an edge at a time, lanes span channels, grad_W is
  * written directly, grad_Y is reduced across lanes, grad_x is scattered per
  * `mode`.  Any of grad_x, grad_Y, grad_W may be NULL (not computed).
+ * When the plan's data-movement model prefers the sender-stationary VJP
+ * (oeq_plan_schedule; the choice is made once, at plan creation, as the
+ * maintainers' reply in "Receiver-streaming convolutions ..." proposes), the call
+ * builds the sender view of the graph in the workspace and runs
+ * oeq_tp_conv_bwd_sender instead: no atomics, so every output is bitwise
+ * repeatable in either mode.  Callers that keep a sender view across calls can
+ * call oeq_tp_conv_bwd_sender directly and skip the view build.
  * `workspace` (256-byte aligned) must hold oeq_workspace_size(mode) bytes when
  * that size is not 0; a missing or small workspace gives OEQ_ERR_WORKSPACE. */
 oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,

@@ -170,3 +170,29 @@ def test_sender_full_size_sampled(name):
     assert rel_l2(gY[edges_t].cpu().numpy(), rY) <= tol
     rx = _sampled_gx_ref(d, inp, senders, inp["Y"], inp["W"])
     assert rel_l2(gx[send_t].cpu().numpy(), rx) <= tol
+
+
+def _schedule_bwd(wl):
+    return plan_for(wl).schedule()["bwd"]
+
+
+@pytest.mark.parametrize("mode", ["atomic", "deterministic"])
+@pytest.mark.parametrize("name", ["invariant_fp32", "u8_l1_f32", "tiny_fp64", "ysub_u16_f64"])
+def test_bwd_follows_the_plans_schedule(name, mode):
+    """oeq_tp_conv_bwd runs the pass the plan's data-movement model prefers: on these plans
+    the sender-stationary one, whose results (built on a sender view it makes in the
+    workspace) equal the explicit sender-stationary call bit for bit in either mode.  A
+    plan forced to the receiver-stationary VJP (OEQ_SCHEDULE=rr) agrees within tolerance."""
+    wl, d, inp, dev, plan = _case(name)
+    assert plan.schedule()["bwd"] == "sender"
+    args = (dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"])
+    auto = oeq.oeq_tp_conv_bwd(plan, *args, mode=mode)
+    view = oeq.oeq_sender_view(dev["rowptr"], dev["src"])
+    explicit = oeq.oeq_tp_conv_bwd_sender(plan, view, dev["x"], dev["Y"], dev["W"], dev["g"])
+    forced = oeq.oeq_tp_conv_bwd(plan_for(wl, {"OEQ_SCHEDULE": "rr"}), *args, mode=mode)
+    torch.cuda.synchronize()
+    ref = oracle.bwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"])
+    for a, b, c, r in zip(auto, explicit, forced, ref):
+        assert torch.equal(a, b)
+        assert rel_l2(a.cpu().numpy(), r) <= RTOL[wl.dtype]
+        assert rel_l2(c.cpu().numpy(), r) <= RTOL[wl.dtype]

@@ -52,7 +52,7 @@ def counts(tmp_path_factory):
     if not os.path.exists(READELF):
         pytest.skip("llvm-readelf not found")
     d = tmp_path_factory.mktemp("cache")
-    env = dict(os.environ, OEQ_CACHE_DIR=str(d), OEQ_PLAN_IN_PROCESS="1")
+    env = dict(os.environ, OEQ_CACHE_DIR=str(d))
     code = ("import sys; sys.path.insert(0, %r); import cg_tensor_product_amd as m; "
             "m.Plan('16x0e+16x1o+16x2e', 3, 3, 'f32')" % ROOT)
     subprocess.run([sys.executable, "-c", code], check=True, env=env)

@@ -133,12 +133,15 @@ def test_compute_argument_errors_before_any_device_work():
 
 
 def test_workspace_size_atomic(monkeypatch):
+    # the receiver-stationary VJP (forced: this plan's model prefers the sender-stationary one)
+    monkeypatch.setenv("OEQ_SCHEDULE", "rr")
     # one backward path group -> no scratch in atomic mode
     assert oeq.oeq_workspace_size(oeq.Plan("8x0e+8x1o", 2, 1, "f64"), 64, 1024, "atomic") == 0
     # two groups -> per-group partial Y-gradient rows
     monkeypatch.setenv("OEQ_BWD_GROUPS", "2")
     p = oeq.Plan("8x0e+8x1o", 2, 1, "f64")
     monkeypatch.delenv("OEQ_BWD_GROUPS")
+    monkeypatch.delenv("OEQ_SCHEDULE")
     assert oeq.oeq_workspace_size(p, 64, 1024, "atomic") == 2 * 1024 * 9 * 8
     assert oeq.oeq_workspace_size(p, 64, 1024, "deterministic") > 1024 * 32 * 8
     b = ctypes.c_size_t()
@@ -164,10 +167,11 @@ def test_generated_source_has_no_packed_fp32_and_caches(tmp_path, monkeypatch):
         assert "oeq_fwd" in dis.stdout and "oeq_bwd_atomic" in dis.stdout
 
 
-def test_plan_from_cache_only_and_compiled_in_a_child(tmp_path):
+def test_plan_from_cache_only_and_compiled_in_the_helper(tmp_path):
     """oeq_plan_create_cached never compiles: with an empty cache it fails with
-    OEQ_ERR_JIT and leaves the plan NULL.  Plan() then compiles in a child process, and the
-    code object it leaves in the cache loads here without compiling."""
+    OEQ_ERR_JIT and leaves the plan NULL.  Plan() (oeq_plan_create) then compiles in the
+    compiler helper, and the code object it leaves in the cache loads here without
+    compiling."""
     import subprocess
     import sys
     code = r"""
@@ -189,9 +193,30 @@ L.oeq_plan_destroy(h)
 print("ok")
 """ % ROOT
     env = dict(os.environ, OEQ_CACHE_DIR=str(tmp_path / "cache"))
-    env.pop("OEQ_PLAN_IN_PROCESS", None)
+    env.pop("OEQ_JIT_IN_PROCESS", None)
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
+def test_plans_compile_the_same_whatever_the_process_loaded(tmp_path):
+    """A framework that bundles another ROCm release's compiler library (this PyTorch wheel
+    does) loads it into the process; compiled in that process, the runtime compiler used it
+    and produced other (on MI355X, slower) code.  oeq_plan_create compiles in its helper, so
+    a plan made after importing torch gets exactly the code object of a plan made in a
+    process that loaded nothing else."""
+    import subprocess
+    import sys
+    code = ("import sys; sys.path.insert(0, %r)\n%s\nimport cg_tensor_product_amd as m\n"
+            "print(m.Plan('32x0e+32x1o', 3, 3, 'f32').code_key)")
+    objs = []
+    for k, pre in enumerate(("import torch", "")):
+        d = tmp_path / f"c{k}"
+        env = dict(os.environ, OEQ_CACHE_DIR=str(d))
+        env.pop("OEQ_JIT_IN_PROCESS", None)
+        r = subprocess.run([sys.executable, "-c", code % (ROOT, pre)], env=env, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+        objs.append((d / (r.stdout.strip() + ".hsaco")).read_bytes())
+    assert objs[0] == objs[1]
 
 
 def test_tile_form_rows_match_the_tables(tmp_path):
@@ -360,3 +385,15 @@ def test_noalloc_bwd_rejects_scratch_beyond_its_limit():
     msg = oeq.lib().oeq_last_error().decode()
     need = int(re.search(r"needs (\d+) bytes", msg).group(1))
     assert "67108864" in msg and need >= 280000 * 512 * 4
+
+
+def test_workspace_covers_the_sender_view_when_the_vjp_routes_there():
+    # the invariant plan's model prefers the sender-stationary VJP: oeq_tp_conv_bwd builds
+    # the sender view (srowptr, sperm, sdst and the counting-sort scratch) in its workspace
+    wl = synth.WORKLOADS["invariant_fp32"]
+    p = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    assert p.schedule()["bwd"] == "sender"
+    N, E = 5000, 280000
+    for mode in ("atomic", "deterministic"):
+        assert oeq.oeq_workspace_size(p, N, E, mode) >= 4 * (N + 1 + 2 * E)
+    assert oeq.oeq_workspace_size(p, N, 0, "atomic") == 0
