@@ -131,11 +131,13 @@ def side_rows(torch, oeq, plan, dev, N, E, ab, reps=10):
     return res
 
 
-def cpu_baseline(wl, d, inp, target_s=10.0):
+def cpu_baseline(wl, d, inp, target_s=10.0, single_s=4.0):
     """The oracle (fp64 loops, OpenMP over independent rows) on the same
     workload: forward of every receiver and the full VJP (W and Y gradients of
     every edge, x gradient of every sender), repeated until about target_s of
-    CPU time.  Inputs are converted to fp64 before the clock starts."""
+    CPU time, on all the threads the oracle uses.  Then the forward alone on one
+    thread over the first receivers' rows, about single_s.  Inputs are converted
+    to fp64 before the clock starts."""
     import oracle
 
     x, Y, W, g = (np.ascontiguousarray(inp[k], dtype=np.float64) for k in ("x", "Y", "W", "g"))
@@ -148,9 +150,25 @@ def cpu_baseline(wl, d, inp, target_s=10.0):
         oracle.bwd_gx(d, rp, sr, Y, W, g)
         t += time.perf_counter() - t0
         reps += 1
-    return {"value": reps * inp["E"] / t, "unit": "edges/s", "cores": oracle.num_threads(), "kind": "oracle",
+    threads = oracle.num_threads()
+    # one thread: the forward over the first receivers' rows (a prefix of the CSR)
+    oracle.set_num_threads(1)
+    rows, t1, e1 = 250, 0.0, 0
+    while t1 < single_s and rows <= wl.n_nodes:
+        rpp = rp[:rows + 1]
+        ne = int(rpp[-1])
+        t0 = time.perf_counter()
+        oracle.fwd(d, rpp, sr[:ne], x, Y[:ne], W[:ne])
+        t1 += time.perf_counter() - t0
+        e1 += ne
+        rows *= 2
+    oracle.set_num_threads(threads)
+    return {"value": reps * inp["E"] / t, "unit": "edges/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole workload ({inp['E']} edges): forward + VJP, {reps} repetition(s), "
-                      f"{t:.1f} s in total", "cpu_model": cpu_model()}
+                      f"{t:.1f} s in total", "cpu_model": cpu_model(),
+            "cpus_in_affinity": len(os.sched_getaffinity(0)),
+            "single_thread_fwd": {"value": e1 / t1, "unit": "edges/s", "edges": e1, "seconds": t1,
+                                  "sample": "the forward over the first 250, 500, ... receivers' rows, one thread"}}
 
 
 def cpu_model() -> str:
@@ -191,7 +209,7 @@ def main():
     import oracle
     import synth
 
-    wl = synth.WORKLOADS[args.workload]
+    wl = synth.WORKLOADS[args.workload] if args.workload in synth.WORKLOADS else synth.CALIBRATION[args.workload]
     d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
     inp = synth.generate(wl, d.P, d.out_dim, want=("x", "Y", "W", "g"))
     E, N = inp["E"], wl.n_nodes

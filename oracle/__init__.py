@@ -75,6 +75,8 @@ def lib():
                                   p, i64, p, i64, p, i64, p, p, p, p]
         L.oracle_num_threads.restype = i
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [i]
         _lib = L
     return _lib
 
@@ -97,6 +99,10 @@ def _i64(a):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(n)
 
 
 # ---------------------------------------------------------------------------
@@ -162,12 +168,13 @@ class _CDesc(ctypes.Structure):
                 ("np", ctypes.c_int), ("p_i1", ctypes.c_void_p),
                 ("p_iy", ctypes.c_void_p), ("p_l3", ctypes.c_void_p),
                 ("p_ob", ctypes.c_void_p), ("nob", ctypes.c_int),
-                ("ob_l", ctypes.c_void_p)]
+                ("ob_l", ctypes.c_void_p), ("xm", ctypes.c_void_p), ("om", ctypes.c_void_p)]
 
 
 class Desc:
-    """x irreps (uniform multiplicity U), Y blocks, a path list and the output
-    blocks.  Y: y_irreps ((1, l, parity), ...) in row order, or by default the
+    """x irreps (multiplicity U, or 1 for a block broadcast against the U channels),
+    Y blocks, a path list and the output blocks (multiplicity U, or 1 for a block
+    that sums the channels: out_mul).  Y: y_irreps ((1, l, parity), ...) in row order, or by default the
     harmonics of degrees 0..y_lmax with parity (-1)^l.  Paths are
     (x block, Y block, l3, output block); with the default Y the Y block index is
     the degree.  Default paths: all triangle-allowed ones up to l3_max, one output
@@ -175,12 +182,11 @@ class Desc:
 
     def __init__(self, x_irreps, y_lmax: int, l3_max: int = 3,
                  paths: Optional[Sequence] = None, out_l: Optional[Sequence[int]] = None,
-                 y_irreps=None):
+                 y_irreps=None, out_mul: Optional[Sequence[int]] = None):
         self.x_irreps = tuple(tuple(t) for t in x_irreps)
-        muls = {m for m, _, _ in self.x_irreps}
-        if len(muls) != 1:
-            raise ValueError("channel-wise product needs one multiplicity")
-        self.U = muls.pop()
+        self.U = max(m for m, _, _ in self.x_irreps)
+        if any(m not in (1, self.U) for m, _, _ in self.x_irreps):
+            raise ValueError("x blocks have U channels or one (broadcast)")
         if y_irreps is None:
             y_irreps = tuple((1, l, 1 if l % 2 == 0 else -1) for l in range(y_lmax + 1))
         self.y_irreps = tuple(tuple(t) for t in y_irreps)
@@ -195,11 +201,15 @@ class Desc:
             out_l = [l3 for (_, _, l3, _) in en]
         self.paths = [tuple(p) for p in paths]
         self.out_l = list(out_l)
+        self.out_mul = [self.U] * len(self.out_l) if out_mul is None else list(out_mul)
+        if len(self.out_mul) != len(self.out_l) or any(m not in (1, self.U) for m in self.out_mul):
+            raise ValueError("output blocks have U channels or one (a sum over channels)")
         self.xl = [l for _, l, _ in self.x_irreps]
+        self.xm = [m for m, _, _ in self.x_irreps]
         self.P = len(self.paths)
-        self.x_dim = self.U * sum(2 * l + 1 for l in self.xl)
+        self.x_dim = sum(m * (2 * l + 1) for m, l, _ in self.x_irreps)
         self.y_dim = sum(2 * l + 1 for l in self.yl)
-        self.out_dim = self.U * sum(2 * l + 1 for l in self.out_l)
+        self.out_dim = sum(m * (2 * l + 1) for m, l in zip(self.out_mul, self.out_l))
         # keep the arrays alive for the C struct
         self._xl = _i32(self.xl)
         self._yl = _i32(self.yl)
@@ -208,9 +218,11 @@ class Desc:
         self._l3 = _i32([p[2] for p in self.paths])
         self._ob = _i32([p[3] for p in self.paths])
         self._obl = _i32(self.out_l)
+        self._xm = _i32(self.xm)
+        self._om = _i32(self.out_mul)
         self._c = _CDesc(len(self.xl), _ptr(self._xl), self.U, len(self.yl), _ptr(self._yl), self.P,
                          _ptr(self._i1), _ptr(self._iy), _ptr(self._l3), _ptr(self._ob),
-                         len(self.out_l), _ptr(self._obl))
+                         len(self.out_l), _ptr(self._obl), _ptr(self._xm), _ptr(self._om))
 
     def path_l2(self, p: int) -> int:
         """Degree of path p's Y block."""

@@ -37,6 +37,12 @@
  *               2e, .. L this is element l2*l2 + (m2+l2)
  *   W  [E, P, U]
  *   out[N, OD]  output block o (degree l_o) at ooff_o, element u*(2l_o+1)+(m+l_o)
+ * A block of multiplicity 1 (x or output) has one channel: element (m+l) at its
+ * offset.  Channel u of a path reads channel u of its x block, or the single
+ * channel of a multiplicity-1 x block (broadcast), and adds into channel u of its
+ * output block, or into the single channel of a multiplicity-1 output block (a sum
+ * over the channels): a UVW product whose weight is diagonal in (u, w) up to such a
+ * broadcast or sum, which reduces to the channel-wise one.
  * Edge e lies in receiver row r when rowptr[r] <= e < rowptr[r+1]; its sender
  * is src[e].
  */
@@ -251,7 +257,9 @@ typedef struct {
     const int *p_l3;   /* output degree of each path                        */
     const int *p_ob;   /* output block of each path                         */
     int nob;           /* number of output blocks                           */
-    const int *ob_l;   /* degree of each output block (U channels each)     */
+    const int *ob_l;   /* degree of each output block                       */
+    const int *xm;     /* channels of each x block: U, or 1 (NULL: all U)   */
+    const int *om;     /* channels of each output block: U or 1 (NULL: U)   */
 } oracle_desc;
 
 typedef struct {
@@ -262,6 +270,7 @@ typedef struct {
     double c[ORACLE_NM * ORACLE_NM * ORACLE_NM];
     int64_t xoff, ooff; /* block offsets within a node row                 */
     int n1, n2, n3;     /* 2l1+1, 2l2+1, 2l3+1                            */
+    int xu, ou;         /* 1 when the x / output block has U channels, 0 for one channel */
     int yoff;           /* offset of the path's Y block in a Y row        */
 } oracle_path;
 
@@ -277,15 +286,19 @@ static int build_paths(const oracle_desc *d, oracle_path *pt, int64_t *xd,
     int64_t acc = 0;
     for (int i = 0; i < d->nx; ++i) {
         if (d->xl[i] < 0 || d->xl[i] > ORACLE_LMAX) return -1;
+        const int m = d->xm ? d->xm[i] : d->U;
+        if (m != d->U && m != 1) return -1;
         xoff[i] = acc;
-        acc += (int64_t)d->U * (2 * d->xl[i] + 1);
+        acc += (int64_t)m * (2 * d->xl[i] + 1);
     }
     *xd = acc;
     acc = 0;
     for (int o = 0; o < d->nob; ++o) {
         if (d->ob_l[o] < 0 || d->ob_l[o] > ORACLE_LMAX) return -1;
+        const int m = d->om ? d->om[o] : d->U;
+        if (m != d->U && m != 1) return -1;
         ooff[o] = acc;
-        acc += (int64_t)d->U * (2 * d->ob_l[o] + 1);
+        acc += (int64_t)m * (2 * d->ob_l[o] + 1);
     }
     *od = acc;
     int ya = 0;
@@ -322,6 +335,8 @@ static int build_paths(const oracle_desc *d, oracle_path *pt, int64_t *xd,
         pt[p].n1 = n1;
         pt[p].n2 = n2;
         pt[p].n3 = n3;
+        pt[p].xu = (d->xm ? d->xm[i1] : d->U) == d->U;
+        pt[p].ou = (d->om ? d->om[ob] : d->U) == d->U;
         pt[p].yoff = yoff[iy];
     }
     return 0;
@@ -379,9 +394,9 @@ int oracle_fwd(const oracle_desc *d, int64_t N, int64_t E, const int32_t *rowptr
                 for (int u = 0; u < U; ++u) {
                     double w = W[(e * P + p) * U + u];
                     for (int t = 0; t < q->nnz; ++t) {
-                        double xv = x[s * XD + q->xoff + (int64_t)u * q->n1 + q->m1[t]];
+                        double xv = x[s * XD + q->xoff + (int64_t)(u * q->xu) * q->n1 + q->m1[t]];
                         double yv = Y[e * YD + q->yoff + q->m2[t]];
-                        o[q->ooff + (int64_t)u * q->n3 + q->m3[t]] += q->c[t] * xv * yv * w;
+                        o[q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m3[t]] += q->c[t] * xv * yv * w;
                     }
                 }
             }
@@ -426,9 +441,9 @@ int oracle_bwd_edges(const oracle_desc *d, int64_t N, int64_t E,
                 for (int u = 0; u < U; ++u) {
                     double acc = 0.0;
                     for (int t = 0; t < q->nnz; ++t) {
-                        double xv = x[s * XD + q->xoff + (int64_t)u * q->n1 + q->m1[t]];
+                        double xv = x[s * XD + q->xoff + (int64_t)(u * q->xu) * q->n1 + q->m1[t]];
                         double yv = Y[e * YD + q->yoff + q->m2[t]];
-                        double gv = g[r * OD + q->ooff + (int64_t)u * q->n3 + q->m3[t]];
+                        double gv = g[r * OD + q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m3[t]];
                         acc += q->c[t] * xv * yv * gv;
                     }
                     gW_rows[k * P * U + (int64_t)p * U + u] = acc;
@@ -443,8 +458,8 @@ int oracle_bwd_edges(const oracle_desc *d, int64_t N, int64_t E,
                 for (int u = 0; u < U; ++u) {
                     double w = W[(e * P + p) * U + u];
                     for (int t = 0; t < q->nnz; ++t) {
-                        double xv = x[s * XD + q->xoff + (int64_t)u * q->n1 + q->m1[t]];
-                        double gv = g[r * OD + q->ooff + (int64_t)u * q->n3 + q->m3[t]];
+                        double xv = x[s * XD + q->xoff + (int64_t)(u * q->xu) * q->n1 + q->m1[t]];
+                        double gv = g[r * OD + q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m3[t]];
                         gy[q->yoff + q->m2[t]] += q->c[t] * xv * w * gv;
                     }
                 }
@@ -488,8 +503,8 @@ int oracle_bwd_gx(const oracle_desc *d, int64_t N, int64_t E, const int32_t *row
                     double w = W[(e * P + p) * U + u];
                     for (int t = 0; t < q->nnz; ++t) {
                         double yv = Y[e * YD + q->yoff + q->m2[t]];
-                        double gv = g[r * OD + q->ooff + (int64_t)u * q->n3 + q->m3[t]];
-                        gx[q->xoff + (int64_t)u * q->n1 + q->m1[t]] += q->c[t] * yv * w * gv;
+                        double gv = g[r * OD + q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m3[t]];
+                        gx[q->xoff + (int64_t)(u * q->xu) * q->n1 + q->m1[t]] += q->c[t] * yv * w * gv;
                     }
                 }
             }
@@ -575,5 +590,15 @@ int oracle_num_threads(void) {
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Sets that number (for timing the oracle on one thread); results do not depend on it. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

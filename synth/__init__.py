@@ -51,6 +51,7 @@ class Workload:
     degrees: Optional[tuple] = None  # per-receiver in-degree (non-uniform graphs)
     multi: bool = False              # senders drawn with replacement, the receiver included
     y_irreps: Optional[tuple] = None # Y blocks ((1, l, parity), ...); None: degrees 0..y_lmax
+    one_sender: bool = False         # every edge leaves node 0 (counter calibration: x is one row)
 
     @property
     def U(self) -> int:
@@ -112,6 +113,15 @@ WORKLOADS = {
     # output rows (sender-stationary) is cheaper than moving x rows.
     "invariant_fp32": Workload("invariant_fp32", 5000, 56, _irr("128x0e+128x1o+128x2e+128x3o"), 3, 0,
                                "f32", "inv_sqrt_paths", 6006),
+}
+
+
+# Counter calibration: the medium workload's sizes with every edge leaving node 0, so the
+# forward's HBM reads are the non-temporal W stream, Y and the CSR (x is a single cached
+# row); FETCH_SIZE of that forward checks the counter's scale for the kernels' own loads.
+CALIBRATION = {
+    "nt_read_calibration_fp32": Workload("nt_read_calibration_fp32", 5000, 56, _irr("128x0e+128x1o"), 3, 3,
+                                         "f32", "inv_sqrt_paths", 2002, one_sender=True),
 }
 
 
@@ -229,7 +239,11 @@ def generate(wl: Workload, n_paths: int, out_dim: int, want=("x", "Y", "W", "g")
     (they follow from the path list, which this module does not compute)."""
     rngs = _children(wl.seed)
     degrees = wl.degrees if wl.degrees is not None else [wl.degree] * wl.n_nodes
-    rowptr, src = make_graph(wl.n_nodes, degrees, rngs[_GRAPH], multi=wl.multi)
+    if wl.one_sender:
+        rowptr = np.concatenate([[0], np.cumsum(degrees)]).astype(np.int32)
+        src = np.zeros(int(rowptr[-1]), dtype=np.int32)
+    else:
+        rowptr, src = make_graph(wl.n_nodes, degrees, rngs[_GRAPH], multi=wl.multi)
     E = int(rowptr[-1])
     dt = wl.np_dtype()
     out = {"rowptr": rowptr, "src": src, "N": wl.n_nodes, "E": E}

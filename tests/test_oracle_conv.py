@@ -27,12 +27,19 @@ def _dense_fwd(d, rowptr, src, x, Y, W):
     ooff = np.cumsum([0] + [d.U * (2 * l + 1) for l in d.out_l])
     out = np.zeros((N, d.out_dim))
     yoff = np.cumsum([0] + [2 * l + 1 for l in d.yl])
+    xm = getattr(d, "xm", [d.U] * len(d.xl))
+    om = getattr(d, "out_mul", [d.U] * len(d.out_l))
+    xoff = np.cumsum([0] + [m * (2 * l + 1) for m, l in zip(xm, d.xl)])
+    ooff = np.cumsum([0] + [m * (2 * l + 1) for m, l in zip(om, d.out_l)])
     for p, (i1, iy, l3, ob) in enumerate(d.paths):
         l1, l2 = d.xl[i1], d.yl[iy]
         C = oracle.cg_real(l1, l2, l3)
-        xb = xs[:, xoff[i1]:xoff[i1 + 1]].reshape(E, d.U, 2 * l1 + 1)
+        xb = xs[:, xoff[i1]:xoff[i1 + 1]].reshape(E, xm[i1], 2 * l1 + 1)
+        xb = np.broadcast_to(xb, (E, d.U, 2 * l1 + 1))       # a one-channel block feeds every channel
         yb = Y[:, yoff[iy]:yoff[iy + 1]]
         msg = np.einsum("eua,eb,abc,eu->euc", xb, yb, C, W[:, p, :])
+        if om[ob] == 1:
+            msg = msg.sum(axis=1, keepdims=True)              # a one-channel output sums the channels
         out[:, ooff[ob]:ooff[ob + 1]] += A_recv.T @ msg.reshape(E, -1)
     return out
 
@@ -409,6 +416,108 @@ def test_vjp_adjoint_with_y_irreps():
     x, Y = rng.standard_normal((N, d.x_dim)), rng.standard_normal((E, d.y_dim))
     W, g = rng.standard_normal((E, d.P, d.U)), rng.standard_normal((N, d.out_dim))
     f = np.vdot(g, oracle.fwd(d, rowptr, src, x, Y, W))
+    gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
+    for a, b in ((gx, x), (gY, Y), (gW, W)):
+        assert abs(np.vdot(a, b) - f) <= 1e-12 * max(1.0, abs(f))
+
+
+# ---------------------------------------------------------------------------
+# UVW products that reduce to the channel-wise one: a one-channel x block broadcast
+# against the U channels, and one-channel output blocks that sum the channels
+# ---------------------------------------------------------------------------
+
+def _mixed(seed, U=3):
+    rng = np.random.default_rng(seed)
+    rowptr, src = _tiny_graph(rng)
+    N, E = len(rowptr) - 1, len(src)
+    return rng, rowptr, src, N, E
+
+
+def _expand_x(d_one, d_full, x):
+    """x of d_one (one-channel blocks) as the x of d_full (those blocks with U channels),
+    every channel a copy."""
+    out = []
+    o = 0
+    for (m, l, _p) in d_one.x_irreps:
+        n = 2 * l + 1
+        blk = x[:, o:o + m * n].reshape(len(x), m, n)
+        out.append(np.broadcast_to(blk, (len(x), d_full.U, n)).reshape(len(x), -1))
+        o += m * n
+    return np.concatenate(out, axis=1)
+
+
+def _fold_x(d_one, d_full, gx_full):
+    """The gradient of d_full's x folded back onto d_one's layout: summed over the channels
+    of the blocks that d_one has with one channel."""
+    out = []
+    o = 0
+    for (m, l, _p) in d_one.x_irreps:
+        n = 2 * l + 1
+        blk = gx_full[:, o:o + d_full.U * n].reshape(len(gx_full), d_full.U, n)
+        out.append((blk.sum(axis=1, keepdims=True) if m == 1 else blk).reshape(len(gx_full), -1))
+        o += d_full.U * n
+    return np.concatenate(out, axis=1)
+
+
+def test_one_channel_x_is_the_channel_wise_product_of_its_copies():
+    rng, rowptr, src, N, E = _mixed(90)
+    one = oracle.Desc(((1, 1, -1), (3, 0, 1)), 2, 2)
+    full = oracle.Desc(((3, 1, -1), (3, 0, 1)), 2, 2)
+    assert one.P == full.P and one.out_dim == full.out_dim and one.x_dim == 3 + 3
+    x = rng.standard_normal((N, one.x_dim))
+    Y = synth.real_sh_cartesian(2, synth.unit_vectors(E, rng))
+    W = rng.standard_normal((E, one.P, one.U))
+    g = rng.standard_normal((N, one.out_dim))
+    xf = _expand_x(one, full, x)
+    assert np.allclose(oracle.fwd(one, rowptr, src, x, Y, W), oracle.fwd(full, rowptr, src, xf, Y, W), atol=1e-13)
+    a, b = oracle.bwd(one, rowptr, src, x, Y, W, g), oracle.bwd(full, rowptr, src, xf, Y, W, g)
+    assert np.allclose(a[0], _fold_x(one, full, b[0]), atol=1e-13)        # gx: a sum over the copies
+    assert np.allclose(a[1], b[1], atol=1e-13) and np.allclose(a[2], b[2], atol=1e-13)
+    assert np.allclose(oracle.fwd(one, rowptr, src, x, Y, W), _dense_fwd(one, rowptr, src, x, Y, W), atol=1e-13)
+
+
+def test_one_channel_output_is_the_sum_of_the_channel_wise_outputs():
+    rng, rowptr, src, N, E = _mixed(91)
+    xi = ((3, 0, 1), (3, 1, -1))
+    base = oracle.Desc(xi, 2, 2)
+    summed = [1 if l3 % 2 == 0 else base.U for l3 in base.out_l]            # the even-degree outputs summed
+    one = oracle.Desc(xi, 2, 2, paths=base.paths, out_l=base.out_l, out_mul=summed)
+    assert one.out_dim < base.out_dim
+    x = rng.standard_normal((N, one.x_dim))
+    Y = synth.real_sh_cartesian(2, synth.unit_vectors(E, rng))
+    W = rng.standard_normal((E, one.P, one.U))
+    out_b = oracle.fwd(base, rowptr, src, x, Y, W)
+    out_o = oracle.fwd(one, rowptr, src, x, Y, W)
+    # fold base's output onto one's layout, and broadcast one's cotangent onto base's layout
+    fold, g_o = [], rng.standard_normal((N, one.out_dim))
+    g_b = []
+    ob = oo = 0
+    for m, l in zip(summed, base.out_l):
+        n = 2 * l + 1
+        blk = out_b[:, ob:ob + base.U * n].reshape(N, base.U, n)
+        fold.append((blk.sum(axis=1) if m == 1 else blk.reshape(N, -1)))
+        gblk = g_o[:, oo:oo + m * n].reshape(N, m, n)
+        g_b.append(np.broadcast_to(gblk, (N, base.U, n)).reshape(N, -1))
+        ob += base.U * n
+        oo += m * n
+    assert np.allclose(out_o, np.concatenate(fold, axis=1), atol=1e-13)
+    assert np.allclose(out_o, _dense_fwd(one, rowptr, src, x, Y, W), atol=1e-13)
+    a = oracle.bwd(one, rowptr, src, x, Y, W, g_o)
+    b = oracle.bwd(base, rowptr, src, x, Y, W, np.concatenate(g_b, axis=1))
+    for u, v in zip(a, b):
+        assert np.allclose(u, v, atol=1e-12)
+
+
+def test_mixed_multiplicities_adjoint_and_dense():
+    rng, rowptr, src, N, E = _mixed(92, U=4)
+    d = oracle.Desc(((1, 0, 1), (4, 1, -1), (1, 2, 1)), 3, 3)
+    om = [1 if k % 3 == 0 else d.U for k in range(len(d.out_l))]
+    d = oracle.Desc(((1, 0, 1), (4, 1, -1), (1, 2, 1)), 3, 3, paths=d.paths, out_l=d.out_l, out_mul=om)
+    x, Y = rng.standard_normal((N, d.x_dim)), rng.standard_normal((E, d.y_dim))
+    W, g = rng.standard_normal((E, d.P, d.U)), rng.standard_normal((N, d.out_dim))
+    out = oracle.fwd(d, rowptr, src, x, Y, W)
+    assert np.abs(out - _dense_fwd(d, rowptr, src, x, Y, W)).max() <= 1e-12 * np.abs(out).max()
+    f = np.vdot(g, out)
     gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
     for a, b in ((gx, x), (gY, Y), (gW, W)):
         assert abs(np.vdot(a, b) - f) <= 1e-12 * max(1.0, abs(f))

@@ -31,8 +31,8 @@ MUTANTS = {
                          "double w = W[(e * U + u) * P + p];\n                    for (int t = 0; t < q->nnz; ++t) {\n                        double xv"),
     "gy_without_w": ("gy[q->yoff + q->m2[t]] += q->c[t] * xv * w * gv;", "gy[q->yoff + q->m2[t]] += q->c[t] * xv * gv;"),
     "gx_wrong_receiver": ("int64_t e = sperm[j], r = recv[e];", "int64_t e = sperm[j], r = src[e];"),
-    "gw_wrong_g_index": ("double gv = g[r * OD + q->ooff + (int64_t)u * q->n3 + q->m3[t]];\n                        acc +=",
-                         "double gv = g[r * OD + q->ooff + (int64_t)u * q->n3 + q->m2[t] % q->n3];\n                        acc +="),
+    "gw_wrong_g_index": ("double gv = g[r * OD + q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m3[t]];\n                        acc +=",
+                         "double gv = g[r * OD + q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m2[t] % q->n3];\n                        acc +="),
     "dbwd_term_dropped": ("if (ggY) { oracle_fwd(d, N, E, rowptr, src, x, ggY, W, rows, nrows, to); axpy(dg, to, nrows * OD); }",
                           "(void)0;"),
     "sender_csr_unstable": ("for (int64_t e = 0; e < E; ++e) sperm[fill[src[e]]++] = (int32_t)e;",
