@@ -171,6 +171,10 @@ def _irreps(seq) -> tuple:
 class Plan:
     """oeq_plan_create for an irreps descriptor.  dtype: "f32" or "f64".
 
+    x and output blocks have U channels (the largest x multiplicity) or one: a
+    one-channel x block is broadcast against the U channels, a one-channel output
+    block (out_irreps) receives their sum.
+
     Y: y_irreps (one-channel irreps in row order, e.g. "1x0e+1x2e+1x1e"), or by
     default the spherical harmonics of degrees 0..y_lmax.  paths=None enumerates
     every triangle-allowed path up to lmax_out; an explicit list holds
@@ -216,7 +220,7 @@ class Plan:
         dims = [ctypes.c_int64() for _ in range(5)]
         _check(lib().oeq_plan_dims(h, *[ctypes.byref(v) for v in dims]))
         self.x_dim, self.y_dim, self.out_dim, self.n_paths, self.w_per_edge = (int(v.value) for v in dims)
-        self.U = self.x_irreps[0][0]
+        self.U = self.w_per_edge // self.n_paths  # channels: the largest x multiplicity
 
     @property
     def handle(self):

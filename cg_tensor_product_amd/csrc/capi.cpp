@@ -111,17 +111,8 @@ oeq_status oeq_workspace_size(const oeq_plan *p, int64_t n_nodes, int64_t n_edge
     if (!p || !bytes) return fail(OEQ_ERR_INVALID_ARG, "plan or output is NULL");
     if (n_nodes < 0 || n_edges < 0) return fail(OEQ_ERR_INVALID_ARG, "negative size");
     if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
-    Workspace w;
-    oeq_status st = ws_layout(p, n_nodes, n_edges, mode == OEQ_BWD_DETERMINISTIC, gy_groups(p) > 1,
-                              nullptr, &w);
-    if (st != OEQ_OK) return st;
-    *bytes = w.bytes;
-    if (bwd_by_sender(p, n_edges)) {  // the VJP's sender-stationary route needs the sender view
-        SenderWs sw;
-        if ((st = sender_ws_layout(p, n_nodes, n_edges, &sw)) != OEQ_OK) return st;
-        *bytes = std::max(*bytes, sw.bytes);
-    }
-    return OEQ_OK;
+    // the VJP's sender-stationary route (when the plan takes it) needs the sender view
+    return vjp_ws_bytes(p, n_nodes, n_edges, mode, bytes);
 }
 
 oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t N, int64_t E, const int32_t *rowptr, const int32_t *src,
@@ -163,8 +154,9 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     }
     const bool det = gx && mode == OEQ_BWD_DETERMINISTIC;
     const bool gyp = gY && p->bwd_groups.size() > 1;
+    const bool gxe = gx && !det && needs_gxe(p);
     Workspace w;
-    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w)) != OEQ_OK) return st;
+    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w, gxe)) != OEQ_OK) return st;
     int flags = (gW ? 1 : 0) | (gY ? 2 : 0);
     void *gy_target = gyp ? w.gy_part : gY;
     int64_t gy_stride = gyp ? E * p->YD : 0;
@@ -175,15 +167,17 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
         void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
         st = launch(p, "oeq_bwd_nogx", grid, block, s, args);
     } else if (mode == OEQ_BWD_ATOMIC) {
-        if ((st = fill_zero(p, gx, N * p->XD, s)) != OEQ_OK) return st;
-        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gx, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
+        void *gxr = gxe ? w.gxe : gx;  // rows of GXD values
+        if ((st = fill_zero(p, gxr, N * p->GXD, s)) != OEQ_OK) return st;
+        void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &gxr, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
         if ((st = launch(p, "oeq_bwd_atomic", grid, block, s, args)) != OEQ_OK) return st;
-        st = untranspose(p, N, gx, s);
+        if ((st = untranspose(p, N, gxr, s)) != OEQ_OK) return st;
+        if (gxe) st = fold_x(p, N, gxr, gx, s);
     } else {
         if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
         void *h = w.h;
         // an x block that feeds no path is never written into the per-edge rows
-        if (p->x_unused && (st = fill_zero(p, h, E * p->XD, s)) != OEQ_OK) return st;
+        if (p->x_unused && (st = fill_zero(p, h, E * p->GXD, s)) != OEQ_OK) return st;
         void *args[] = {&rowptr, &src, &x, &Y, &W, &g, &h, &gy_target, &gW, &flags, &gy_stride, &n_nodes};
         if ((st = launch(p, "oeq_bwd_rows", grid, block, s, args)) != OEQ_OK) return st;
         st = det_finish(p, N, w, gx, s);
@@ -292,6 +286,9 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
             }
         }
     }
+    // the fused passes write d_grad_out with U channels per block: a plan with one-channel
+    // output blocks takes d_grad_out from the forward kernel (its channel sum) instead
+    if (p->sum_out && level == 0) level = 1;
     // Path groups of the kernels this call launches: oeq_dbwd_<t> is built on the backward
     // groups; oeq_dbwd_<t>_d and every split pass on the double-backward groups. The grid
     // must match: a kernel maps block b to receiver b / groups.
@@ -301,20 +298,21 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
     };
     const int64_t NG = level == 0 ? kernel_groups(fused) : static_cast<int64_t>(p->dbwd_groups.size());
     const bool gyp = dY && NG > 1;
+    const bool gxe = dx_live && !det && needs_gxe(p);
     Workspace w;
-    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w)) != OEQ_OK) return st;
+    if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w, gxe)) != OEQ_OK) return st;
     if (dx && !dx_live && (st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
     int dxmode = 0;
     void *dx_target = nullptr;
     if (dx_live && !det) {
-        if ((st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+        dx_target = gxe ? w.gxe : dx;  // rows of GXD values
+        if ((st = fill_zero(p, dx_target, N * p->GXD, s)) != OEQ_OK) return st;
         dxmode = 1;
-        dx_target = dx;
     } else if (det) {
         if ((st = sender_csr_into(N, E, src, w, s)) != OEQ_OK) return st;
         dxmode = 2;
         dx_target = w.h;
-        if (p->x_unused && (st = fill_zero(p, w.h, E * p->XD, s)) != OEQ_OK) return st;
+        if (p->x_unused && (st = fill_zero(p, w.h, E * p->GXD, s)) != OEQ_OK) return st;
     }
     if (!dxmode && !dY && !dW && !dg) return OEQ_OK;
     void *dy_target = gyp ? w.gy_part : dY;
@@ -371,7 +369,8 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
         }
     }
     if (dxmode == 2 && (st = det_finish(p, N, w, dx, s)) != OEQ_OK) return st;
-    if (dxmode == 1 && (st = untranspose(p, N, dx, s)) != OEQ_OK) return st;
+    if (dxmode == 1 && (st = untranspose(p, N, dx_target, s)) != OEQ_OK) return st;
+    if (dxmode == 1 && gxe && (st = fold_x(p, N, dx_target, dx, s)) != OEQ_OK) return st;
     return gyp ? combine_parts(p, w.gy_part, static_cast<int>(NG), dY, E * p->YD, s) : OEQ_OK;
 }
 

@@ -276,6 +276,7 @@ oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
                                   void *stream) {
     oeq_status st = check_graph(plan, N, E, rowptr, src);
     if (st != OEQ_OK) return st;
+    if ((st = check_channelwise(plan, "the forward with in-kernel radial weights")) != OEQ_OK) return st;
     if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
     if (E > 0 && (!x || !Y)) return fail(OEQ_ERR_INVALID_ARG, "x or Y is NULL");
     RadialWs w;
@@ -340,6 +341,7 @@ oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t N, int64_t E, co
                                   void *stream) {
     oeq_status st = check_graph(plan, N, E, rowptr, src);
     if (st != OEQ_OK) return st;
+    if ((st = check_channelwise(plan, "the VJP with in-kernel radial weights")) != OEQ_OK) return st;
     if (mode != OEQ_BWD_ATOMIC && mode != OEQ_BWD_DETERMINISTIC) return fail(OEQ_ERR_INVALID_ARG, "unknown mode");
     if (E > 0 && (!x || !Y || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, Y or grad_out is NULL");
     oeq_plan *p = const_cast<oeq_plan *>(plan);

@@ -65,6 +65,7 @@ oeq_status oeq_tp_conv_fwd_sender(const oeq_plan *plan, int64_t N, int64_t E, co
                                   const void *W, void *out, void *stream) {
     oeq_status st = check_graph(plan, N, E, srowptr, sperm);
     if (st != OEQ_OK) return st;
+    if ((st = check_channelwise(plan, "the sender forward")) != OEQ_OK) return st;
     if (E > 0 && !sdst) return fail(OEQ_ERR_INVALID_ARG, "sdst is NULL");
     if (N > 0 && !out) return fail(OEQ_ERR_INVALID_ARG, "out is NULL");
     if (E > 0 && (!x || !Y || !W)) return fail(OEQ_ERR_INVALID_ARG, "x, Y or W is NULL");
@@ -84,6 +85,7 @@ oeq_status oeq_tp_conv_bwd_sender(const oeq_plan *plan, int64_t N, int64_t E, co
                                   size_t workspace_bytes, void *stream) {
     oeq_status st = check_graph(plan, N, E, srowptr, sperm);
     if (st != OEQ_OK) return st;
+    if ((st = check_channelwise(plan, "the sender VJP")) != OEQ_OK) return st;
     if (E > 0 && !sdst) return fail(OEQ_ERR_INVALID_ARG, "sdst is NULL");
     if (E > 0 && (!x || !Y || !W || !g)) return fail(OEQ_ERR_INVALID_ARG, "x, Y, W or grad_out is NULL");
     oeq_plan *p = const_cast<oeq_plan *>(plan);

@@ -88,21 +88,40 @@ inline oeq_status untranspose(oeq_plan *p, int64_t N, void *gx, hipStream_t stre
 
 // Caller-provided scratch, carved in 256-byte aligned pieces:
 //   gy_part  partial Y-gradient rows of each backward path group (several groups only)
-//   h, srowptr, sperm, csr_scratch   deterministic x-gradient (per-edge rows, sender CSR)
+//   h, srowptr, sperm, csr_scratch   deterministic x-gradient (per-edge rows of GXD values,
+//            sender CSR)
+//   gxe      atomic x-gradient rows of GXD values (plans with one-channel x blocks: the
+//            channels are summed into the caller's rows afterwards)
 struct Workspace {
     void *gy_part = nullptr;
     void *h = nullptr;
     int32_t *srowptr = nullptr, *sperm = nullptr;
     void *csr_scratch = nullptr;
+    void *gxe = nullptr;
     size_t bytes = 0;
 };
+
+// Whether an atomic x-gradient of this plan goes through GXD-wide rows in the workspace.
+inline bool needs_gxe(const oeq_plan *p) { return p->GXD != p->XD; }
+
+// Plans with one-channel x or output blocks run the receiver-stationary passes only.
+inline oeq_status check_channelwise(const oeq_plan *p, const char *what) {
+    if (p && (p->bcast_x || p->sum_out))
+        return fail(OEQ_ERR_UNSUPPORTED, std::string(what) + " needs U channels in every x and output block");
+    return OEQ_OK;
+}
 
 // per-group Y-gradient partials are sized for the larger of the VJP's and the double
 // backward's group counts, so that one workspace size serves both
 inline size_t gy_groups(const oeq_plan *p) { return std::max(p->bwd_groups.size(), p->dbwd_groups.size()); }
 
-inline oeq_status ws_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, bool gy_part, char *base, Workspace *w) {
+inline oeq_status ws_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, bool gy_part, char *base, Workspace *w,
+                            bool gxe = false) {
     size_t off = 0;
+    if (gxe) {
+        w->gxe = base + off;
+        off += up(static_cast<size_t>(N) * static_cast<size_t>(p->GXD) * esize(p));
+    }
     if (gy_part) {
         w->gy_part = base + off;
         off += up(gy_groups(p) * static_cast<size_t>(E) * p->YD * esize(p));
@@ -112,7 +131,7 @@ inline oeq_status ws_layout(const oeq_plan *p, int64_t N, int64_t E, bool det, b
         const hipError_t e = oeq::sender_csr_workspace(N, E, &csr_bytes);
         if (e != hipSuccess) return fail(OEQ_ERR_HIP, std::string("sender CSR workspace: ") + hipGetErrorString(e));
         w->h = base + off;
-        off += up(static_cast<size_t>(E) * static_cast<size_t>(p->XD) * esize(p));
+        off += up(static_cast<size_t>(E) * static_cast<size_t>(p->GXD) * esize(p));
         w->srowptr = reinterpret_cast<int32_t *>(base + off);
         off += up(sizeof(int32_t) * static_cast<size_t>(N + 1));
         w->sperm = reinterpret_cast<int32_t *>(base + off);
@@ -167,20 +186,37 @@ inline oeq_status bwd_ws_bytes(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_
         return st;
     }
     Workspace w;
-    oeq_status st = ws_layout(p, N, E, gx && mode == OEQ_BWD_DETERMINISTIC, gY && p->bwd_groups.size() > 1, nullptr, &w);
+    oeq_status st = ws_layout(p, N, E, gx && mode == OEQ_BWD_DETERMINISTIC, gY && p->bwd_groups.size() > 1, nullptr, &w,
+                              gx && mode == OEQ_BWD_ATOMIC && needs_gxe(p));
     if (st == OEQ_OK) *bytes = w.bytes;
     return st;
+}
+
+// Bytes of workspace oeq_tp_conv_bwd may bind for a mode, whatever outputs are requested:
+// the receiver-stationary layout, or the sender view when the plan routes the VJP there.
+inline oeq_status vjp_ws_bytes(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, size_t *bytes) {
+    Workspace w;
+    oeq_status st = ws_layout(p, N, E, mode == OEQ_BWD_DETERMINISTIC, gy_groups(p) > 1, nullptr, &w,
+                              mode == OEQ_BWD_ATOMIC && needs_gxe(p));
+    if (st != OEQ_OK) return st;
+    *bytes = w.bytes;
+    if (bwd_by_sender(p, E)) {
+        SenderWs sw;
+        if ((st = sender_ws_layout(p, N, E, &sw)) != OEQ_OK) return st;
+        *bytes = std::max(*bytes, sw.bytes);
+    }
+    return OEQ_OK;
 }
 
 // Carves the workspace a call needs; fails before any device work if it is
 // missing, misaligned or too small.
 inline oeq_status ws_bind(const oeq_plan *p, int64_t N, int64_t E, bool det, bool gy_part, void *workspace,
-                   size_t ws_bytes, Workspace *w) {
-    if (!det && !gy_part) return OEQ_OK;
+                   size_t ws_bytes, Workspace *w, bool gxe = false) {
+    if (!det && !gy_part && !gxe) return OEQ_OK;
     if (!workspace) return fail(OEQ_ERR_WORKSPACE, "this call needs a workspace (see oeq_workspace_size)");
     if (reinterpret_cast<uintptr_t>(workspace) % kAlign)
         return fail(OEQ_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    oeq_status st = ws_layout(p, N, E, det, gy_part, static_cast<char *>(workspace), w);
+    oeq_status st = ws_layout(p, N, E, det, gy_part, static_cast<char *>(workspace), w, gxe);
     if (st != OEQ_OK) return st;
     if (ws_bytes < w->bytes) return fail(OEQ_ERR_WORKSPACE, "workspace smaller than oeq_workspace_size");
     return OEQ_OK;
@@ -199,6 +235,15 @@ inline oeq_status det_finish(oeq_plan *p, int64_t N, const Workspace &w, void *g
     int n = static_cast<int>(N);
     void *args[] = {&srp, &spm, &h, &gx, &n};
     return launch(p, "oeq_sender_sum", static_cast<unsigned>(N), 256, stream, args);
+}
+
+// The caller's x-gradient rows from the GXD-wide rows of the atomic passes.
+inline oeq_status fold_x(oeq_plan *p, int64_t N, const void *gxe, void *gx, hipStream_t stream) {
+    int64_t n = N * p->XD;
+    if (n <= 0) return OEQ_OK;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 65536);
+    void *args[] = {&gxe, &gx, &n};
+    return launch(p, "oeq_fold_x", static_cast<unsigned>(blocks), 256, stream, args);
 }
 
 inline oeq_status gy_combine(oeq_plan *p, const Workspace &w, void *gY, int64_t E, hipStream_t stream) {
@@ -388,7 +433,7 @@ inline oeq_status radvjp_layout(const oeq_plan *p, int64_t N, int64_t E, bool de
     size_t off = w->rad.bytes;
     w->conv_off = off;
     if (p->rad_compose) {  // the convolution VJP's own workspace, then W and its gradient
-        oeq_status st = ws_layout(p, N, E, det, gy_groups(p) > 1, base ? base + off : nullptr, &w->conv);
+        oeq_status st = vjp_ws_bytes(p, N, E, det ? OEQ_BWD_DETERMINISTIC : OEQ_BWD_ATOMIC, &w->conv.bytes);
         if (st != OEQ_OK) return st;
         off += up(w->conv.bytes);
         w->wbuf = off;

@@ -70,7 +70,9 @@ struct Local {
     int nx = 0, nw = 0, no = 0;
 };
 
-Local make_local(const oeq_plan &p, const std::vector<int> &paths) {
+// first: the plan's first group, which also owns the output blocks that no path writes
+// (it stores their zeros, so that every output element is written)
+Local make_local(const oeq_plan &p, const std::vector<int> &paths, bool first = false) {
     Local L;
     L.paths = paths;
     std::sort(L.paths.begin(), L.paths.end());
@@ -78,6 +80,12 @@ Local make_local(const oeq_plan &p, const std::vector<int> &paths) {
     for (int k : L.paths) {
         xs.insert(p.paths[k].i1);
         os.insert(p.paths[k].ob);
+    }
+    if (first) {
+        std::vector<bool> fed(p.ob.size(), false);
+        for (const Path &pa : p.paths) fed[pa.ob] = true;
+        for (size_t o = 0; o < p.ob.size(); ++o)
+            if (!fed[o]) os.insert(static_cast<int>(o));
     }
     for (int i : xs) {
         L.xoff[i] = L.nx;
@@ -91,15 +99,28 @@ Local make_local(const oeq_plan &p, const std::vector<int> &paths) {
     return L;
 }
 
+// How a row move addresses a node row:
+//   kRowLoad      an input row (x, gg_x, grad_out): blocks at row_off; a one-channel
+//                 block is read by every lane (broadcast)
+//   kRowGradient  an x-gradient row: U channels in every block, at exp_off
+//   kRowOut       an output row: blocks at row_off; one-channel blocks are left out
+//                 (the forward sums their channels separately)
+enum RowKind { kRowLoad, kRowGradient, kRowOut };
+
 // Moves between a node row (u-major blocks) and a lane's compact registers.
-void emit_row_move(std::ostringstream &o, const char *sig, const std::map<int, int> &blocks,
-                   const std::vector<Block> &bl, bool load, const char *ptr, bool add = false) {
+void emit_row_move(std::ostringstream &o, const oeq_plan &p, const char *sig, const std::map<int, int> &blocks,
+                   const std::vector<Block> &bl, RowKind kind, const char *ptr, bool add = false) {
+    const bool load = kind == kRowLoad;
     o << "  static __device__ __forceinline__ void " << sig << " {\n";
     for (const auto &kv : blocks) {
         const Block &b = bl[kv.first];
         const int n = 2 * b.l + 1;
-        o << "    { " << (load ? "const " : "") << "real_t *q = " << ptr << " + " << b.row_off << "LL + (i64)u * " << n
-          << ";";
+        const bool single = b.mul != p.U;  // one channel against U > 1
+        if (kind == kRowOut && single) continue;
+        const int64_t off = kind == kRowGradient ? b.exp_off : b.row_off;
+        o << "    { " << (load ? "const " : "") << "real_t *q = " << ptr << " + " << off << "LL";
+        if (!(load && single)) o << " + (i64)u * " << n;
+        o << ";";
         for (int m = 0; m < n; ++m) {
             if (load)
                 o << " v[" << kv.second + m << "] = q[" << m << "];";
@@ -392,19 +413,44 @@ void emit_m_functions(std::ostringstream &o, const oeq_plan &p, const Local &L, 
     o << "  }\n";
 }
 
+// Elements of the one-channel output blocks that a group writes.
+int group_nsum(const oeq_plan &p, const std::vector<int> &paths, bool first) {
+    int n = 0;
+    for (const auto &kv : make_local(p, paths, first).ooff)
+        if (p.ob[kv.first].mul != p.U) n += 2 * p.ob[kv.first].l + 1;
+    return n;
+}
+
 void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int g, const std::vector<int> &paths,
-                int moff = 0) {
-    const Local L = make_local(p, paths);
+                int moff = 0, int soff = 0) {
+    const Local L = make_local(p, paths, g == 0);
     o << "template <> struct " << name << "<" << g << "> {\n";
     o << "  static constexpr int NX = " << L.nx << ", NW = " << L.nw << ", NO = " << L.no << ";\n";
-    emit_row_move(o, "load_x(const real_t *__restrict__ xr, int u, real_t (&v)[NX])", L.xoff, p.xb, true, "xr");
-    emit_row_move(o, "store_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX])", L.xoff, p.xb, false, "xr");
-    emit_row_move(o, "load_g(const real_t *__restrict__ gr, int u, real_t (&v)[NO])", L.ooff, p.ob, true, "gr");
-    emit_row_move(o, "store_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO])", L.ooff, p.ob, false, "orow");
+    emit_row_move(o, p, "load_x(const real_t *__restrict__ xr, int u, real_t (&v)[NX])", L.xoff, p.xb, kRowLoad, "xr");
+    emit_row_move(o, p, "store_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX])", L.xoff, p.xb, kRowGradient,
+                  "xr");
+    emit_row_move(o, p, "load_g(const real_t *__restrict__ gr, int u, real_t (&v)[NO])", L.ooff, p.ob, kRowLoad, "gr");
+    emit_row_move(o, p, "store_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO])", L.ooff, p.ob, kRowOut,
+                  "orow");
     // accumulating variants (double backward split into one pass per tangent)
-    emit_row_move(o, "add_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX])", L.xoff, p.xb, false, "xr", true);
-    emit_row_move(o, "add_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO])", L.ooff, p.ob, false, "orow",
+    emit_row_move(o, p, "add_x(real_t *__restrict__ xr, int u, const real_t (&v)[NX])", L.xoff, p.xb, kRowGradient, "xr",
                   true);
+    emit_row_move(o, p, "add_out(real_t *__restrict__ orow, int u, const real_t (&v)[NO])", L.ooff, p.ob, kRowOut,
+                  "orow", true);
+    // output blocks of one channel: this group's elements of them (the forward sums them
+    // over the channels), at SOFF in the plan's list of such elements
+    {
+        int nsum = 0;
+        std::ostringstream pick;
+        for (const auto &kv : L.ooff) {
+            const Block &b = p.ob[kv.first];
+            if (b.mul == p.U) continue;
+            for (int m = 0; m < 2 * b.l + 1; ++m) pick << " s[" << nsum++ << "] = v[" << kv.second + m << "];";
+        }
+        o << "  static constexpr int NSUM = " << nsum << ", SOFF = " << soff << ";\n";
+        o << "  static __device__ __forceinline__ void sum_pick(const real_t (&v)[NO], real_t (&s)[NSUM > 0 ? NSUM : 1]) {"
+          << (nsum ? pick.str() : std::string(" s[0] = real_t(0);")) << " }\n";
+    }
     // x-gradient scatter: with XT the block is addressed m-major (element m*U + u),
     // so consecutive lanes hit consecutive words; oeq_x_untranspose restores the
     // u-major layout afterwards.
@@ -413,11 +459,11 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
         const Block &b = p.xb[kv.first];
         const int n = 2 * b.l + 1;
         if (p.xt) {
-            o << "    { real_t *q = xr + " << b.row_off << "LL + u;";
+            o << "    { real_t *q = xr + " << b.exp_off << "LL + u;";
             for (int m = 0; m < n; ++m)
                 o << " atomicAdd(q + " << S(static_cast<long long>(m) * p.U) << ", v[" << kv.second + m << "]);";
         } else {
-            o << "    { real_t *q = xr + " << b.row_off << "LL + (i64)u * " << n << ";";
+            o << "    { real_t *q = xr + " << b.exp_off << "LL + (i64)u * " << n << ";";
             for (int m = 0; m < n; ++m) o << " atomicAdd(q + " << m << ", v[" << kv.second + m << "]);";
         }
         o << " }\n";
@@ -567,8 +613,8 @@ void emit_untranspose(std::ostringstream &o, const oeq_plan &p) {
     for (const auto &b : p.xb) {
         const int n = 2 * b.l + 1;
         o << "  for (int i = threadIdx.x; i < " << S(static_cast<long long>(n) * p.U)
-          << "; i += blockDim.x) { const int u = i / " << n << ", m = i - u * " << n << "; row[" << b.row_off
-          << "LL + i] = t[" << b.row_off << "LL + m * " << p.U << " + u]; }\n";
+          << "; i += blockDim.x) { const int u = i / " << n << ", m = i - u * " << n << "; row[" << b.exp_off
+          << "LL + i] = t[" << b.exp_off << "LL + m * " << p.U << " + u]; }\n";
     }
     o << "}\n";
     // the same for an output row, one block at a time through a buffer of the largest block
@@ -586,6 +632,24 @@ void emit_untranspose(std::ostringstream &o, const oeq_plan &p) {
         o << "  __syncthreads();\n";
     }
     o << "}\n";
+}
+
+// Element c of a node's x-gradient row from its row with U channels in every block: a
+// one-channel block's element is the sum of its U channel copies, added in channel order.
+void emit_fold_x(std::ostringstream &o, const oeq_plan &p) {
+    o << "__device__ __forceinline__ real_t fold_x_elem(const real_t *__restrict__ re, int c) {\n";
+    for (const auto &b : p.xb) {
+        const int n = 2 * b.l + 1;
+        const int64_t end = b.row_off + static_cast<int64_t>(b.mul) * n;
+        if (b.mul == p.U) {
+            o << "  if (c < " << end << ") return re[c + " << b.exp_off - b.row_off << "LL];\n";
+        } else {
+            o << "  if (c < " << end << ") { const int m = c - " << b.row_off << "; real_t s = re[" << b.exp_off
+              << "LL + m]; for (int u = 1; u < U; ++u) s += re[" << b.exp_off << "LL + (i64)u * " << n
+              << " + m]; return s; }\n";
+        }
+    }
+    o << "  return real_t(0);\n}\n";
 }
 
 }  // namespace
@@ -666,6 +730,8 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr int GY_TILE = " << p.gy_tile << ";\n";
     o << "constexpr i64 XD = " << p.XD << "LL;\n";
     o << "constexpr i64 OD = " << p.OD << "LL;\n";
+    // x-gradient rows carry U channels in every block (GXD > XD with one-channel x blocks)
+    o << "constexpr i64 GXD = " << p.GXD << "LL;\n";
     o << "constexpr bool XT = " << (p.xt ? "true" : "false") << ";\n";
     o << "template <int G> struct FG;\n";
     o << "template <int G> struct BG;\n";
@@ -678,13 +744,31 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr int FWD_MT = " << p.fwd_tile << ";\n";
     o << "typedef real_t vec16_t __attribute__((ext_vector_type(" << (p.dtype == OEQ_F64 ? 2 : 4) << ")));\n";
     {
-        int moff = 0;
+        int moff = 0, soff = 0;
         for (size_t g = 0; g < p.fwd_groups.size(); ++g) {
-            emit_group(o, p, "FG", static_cast<int>(g), p.fwd_groups[g], moff);
+            emit_group(o, p, "FG", static_cast<int>(g), p.fwd_groups[g], moff, soff);
             moff += group_m_stride(p, p.fwd_groups[g]);
+            soff += group_nsum(p, p.fwd_groups[g], g == 0);
         }
         // elements of one edge's M rows over all forward groups
         o << "constexpr int FWD_M_ELEMS = " << (p.fwd_lds ? moff : 0) << ";\n";
+        // elements of the one-channel output blocks (in forward-group order) and their
+        // offsets in an output row
+        o << "constexpr int NSUMT = " << soff << ";\n";
+        o << "__device__ __forceinline__ i64 sum_off(int t) {";
+        if (soff > 0) {
+            o << " switch (t) {";
+            int t = 0;
+            for (size_t g = 0; g < p.fwd_groups.size(); ++g) {
+                for (const auto &kv : make_local(p, p.fwd_groups[g], g == 0).ooff) {
+                    const Block &b = p.ob[kv.first];
+                    if (b.mul == p.U) continue;
+                    for (int m = 0; m < 2 * b.l + 1; ++m) o << " case " << t++ << ": return " << b.row_off + m << ";";
+                }
+            }
+            o << " }";
+        }
+        o << " return 0; }\n";
     }
     for (size_t g = 0; g < p.bwd_groups.size(); ++g) emit_group(o, p, "BG", static_cast<int>(g), p.bwd_groups[g]);
     for (size_t g = 0; g < p.rad_groups.size(); ++g) emit_group(o, p, "RG", static_cast<int>(g), p.rad_groups[g]);
@@ -695,6 +779,7 @@ std::string emit_source(const oeq_plan &p) {
             emit_group(o, p, "DG", static_cast<int>(g), p.dbwd_groups[g]);
     }
     emit_untranspose(o, p);
+    emit_fold_x(o, p);
     o << kKernelTemplate;
     return o.str();
 }

@@ -365,6 +365,22 @@ __device__ __forceinline__ void wave_reduce_scatter(real_t (&v)[PY], int lane) {
     v[0] = v[0] + dpp<kQxor1>(v[0]);
 }
 
+// Sum of one value over the 64 lanes of a wave, in a fixed order; every lane gets it.
+__device__ __forceinline__ real_t wave_sum(real_t v) {
+    real_t a = v, b = v;
+    swap32(a, b);
+    v = a + b;
+    a = v;
+    b = v;
+    swap16(a, b);
+    v = a + b;
+    v = v + dpp<kRor8>(v);
+    v = v + xor4(v);
+    v = v + dpp<kQxor2>(v);
+    v = v + dpp<kQxor1>(v);
+    return v;
+}
+
 extern "C" __global__ void __launch_bounds__(256)
 oeq_fill_zero(real_t *__restrict__ p, i64 n) {
     for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x)

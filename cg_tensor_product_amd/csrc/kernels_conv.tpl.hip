@@ -4,6 +4,44 @@
 // ---------------------------------------------------------------------------
 // Forward: out[r] = sum over the receiver's edges of the per-edge messages.
 // ---------------------------------------------------------------------------
+
+// Output blocks of one channel receive the sum over the U channels.  Each wave adds its
+// 64 lanes (inactive lanes give zero) and puts the total in LDS, slot [chunk][element];
+// after every wave of the workgroup (all chunks of one receiver) has done so, the
+// chunks are added in chunk order and the element is written.
+__device__ __forceinline__ real_t *fwd_red() {
+    __shared__ real_t red[NSUMT > 0 ? UCH * NSUMT : 1];
+    return red;
+}
+
+template <class Gr>
+__device__ __forceinline__ void fwd_sum_partial(const real_t (&sum)[Gr::NO], bool act, int uc, int lane) {
+    real_t s[Gr::NSUM > 0 ? Gr::NSUM : 1];
+    Gr::sum_pick(sum, s);
+    real_t *red = fwd_red();
+#pragma unroll
+    for (int j = 0; j < Gr::NSUM; ++j) {
+        const real_t t = wave_sum(act ? s[j] : real_t(0));
+        if (lane == 0) red[uc * NSUMT + Gr::SOFF + j] = t;
+    }
+}
+
+static_assert(NSUMT == 0 || !FWD_XCD, "the channel sum needs every chunk of a receiver in one workgroup");
+
+// Every wave of the workgroup calls this once, after its group's partials.
+__device__ __forceinline__ void fwd_sum_finish(int r, real_t *__restrict__ out, bool acc) {
+    if constexpr (NSUMT > 0) {
+        __syncthreads();
+        const real_t *red = fwd_red();
+        for (int t = threadIdx.x; t < NSUMT; t += blockDim.x) {
+            real_t s = red[t];
+            for (int c = 1; c < UCH; ++c) s += red[c * NSUMT + t];
+            real_t *q = out + (i64)r * OD + sum_off(t);
+            *q = acc ? *q + s : s;
+        }
+    }
+}
+
 template <int G, int YM>
 __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ rowptr,
                                           const int *__restrict__ src, const real_t *__restrict__ x,
@@ -51,6 +89,7 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
         else
             Gr::store_out(out + (i64)r * OD, u, sum);
     }
+    if constexpr (Gr::NSUM > 0) fwd_sum_partial<Gr>(sum, act, u >> 6, u & 63);
 }
 
 template <int G, int YM>
@@ -121,6 +160,7 @@ __device__ __forceinline__ void fwd_group_lds(real_t *__restrict__ mt, int r, in
         else
             Gr::store_out(out + (i64)r * OD, u, sum);
     }
+    if constexpr (Gr::NSUM > 0) fwd_sum_partial<Gr>(sum, act, uc, lane);
 }
 
 template <int G>
@@ -177,6 +217,7 @@ oeq_fwd(const int *__restrict__ rowptr, const int *__restrict__ src, const real_
     } else {
         fwd_dispatch<0, YM_TENSOR>(grp, r, uc * 64 + lane, rowptr, src, x, Y, W, out, (flags & 1) != 0);
     }
+    fwd_sum_finish(r, out, (flags & 1) != 0);
 }
 
 // The forward with Y evaluated in the kernel from the edge vectors vec[E, 3]
@@ -188,6 +229,7 @@ oeq_fwd_vec(const int *__restrict__ rowptr, const int *__restrict__ src, const r
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
     fwd_dispatch<0, YM_VEC>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, vec, W, out, false);
+    fwd_sum_finish(blockIdx.x, out, false);
 }
 
 // The forward from atom positions pos[N, 3]: the harmonics of edge e are those of
@@ -199,6 +241,7 @@ oeq_fwd_pos(const int *__restrict__ rowptr, const int *__restrict__ src, const r
     const int w = uni(threadIdx.x >> 6);
     const int grp = w / UCH, uc = w - grp * UCH;
     fwd_dispatch<0, YM_POS>(grp, blockIdx.x, uc * 64 + (threadIdx.x & 63), rowptr, src, x, pos, W, out, false);
+    fwd_sum_finish(blockIdx.x, out, false);
 }
 
 // The atomic x-gradient is accumulated m-major inside each x block (so the
@@ -206,10 +249,10 @@ oeq_fwd_pos(const int *__restrict__ rowptr, const int *__restrict__ src, const r
 // u-major row layout in place, one node row per workgroup.
 extern "C" __global__ void __launch_bounds__(256)
 oeq_x_untranspose(real_t *__restrict__ gx) {
-    __shared__ real_t t[XT ? XD : 1];
-    real_t *row = gx + (i64)blockIdx.x * XD;
+    __shared__ real_t t[XT ? GXD : 1];
+    real_t *row = gx + (i64)blockIdx.x * GXD;
     if (!XT) return;
-    for (int i = threadIdx.x; i < XD; i += 256) t[i] = row[i];
+    for (int i = threadIdx.x; i < GXD; i += 256) t[i] = row[i];
     __syncthreads();
     g_untranspose_row(t, row);
 }
@@ -303,8 +346,8 @@ __device__ __forceinline__ void bwd_group(GyStage &st, int r, int wv, int u, con
             gy_push(st, gY, e, j, gy, lane, wv);
             if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, gY, e - j, j + 1);
         }
-        if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * XD, u, gxp);
-        if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * XD, u, gxp);
+        if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * GXD, u, gxp);
+        if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * GXD, u, gxp);
         s = sn;
 #pragma unroll
         for (int k = 0; k < YD; ++k) yv[k] = yn[k];
@@ -391,7 +434,8 @@ oeq_gy_combine(const real_t *__restrict__ part, real_t *__restrict__ gY, i64 n) 
 
 // ---------------------------------------------------------------------------
 // Deterministic x gradient: gx[s] = sum of h[e] over the sender's edges, in the
-// sender CSR's (increasing edge id) order.
+// sender CSR's (increasing edge id) order.  The per-edge rows h carry U channels
+// in every block; a one-channel x block takes the sum of its channels per edge.
 // ---------------------------------------------------------------------------
 extern "C" __global__ void __launch_bounds__(256)
 oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
@@ -402,15 +446,29 @@ oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
     for (i64 c = threadIdx.x; c < XD; c += 256) {
         real_t acc = real_t(0);
         int k = k0;
-        // eight rows in flight, added in edge order
-        for (; k + 8 <= k1; k += 8) {
-            real_t t[8];
+        if constexpr (GXD == XD) {
+            // eight rows in flight, added in edge order
+            for (; k + 8 <= k1; k += 8) {
+                real_t t[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) t[j] = h[(i64)uni(sperm[k + j]) * XD + c];
+                for (int j = 0; j < 8; ++j) t[j] = h[(i64)uni(sperm[k + j]) * XD + c];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc += t[j];
+                for (int j = 0; j < 8; ++j) acc += t[j];
+            }
+            for (; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * XD + c];
+        } else {
+            for (; k < k1; ++k) acc += fold_x_elem(h + (i64)uni(sperm[k]) * GXD, (int)c);
         }
-        for (; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * XD + c];
         gx[(i64)s * XD + c] = acc;
+    }
+}
+
+// x gradient of the atomic passes: rows with U channels in every block (gxe) to the
+// x layout, a one-channel block taking the sum of its channels.
+extern "C" __global__ void __launch_bounds__(256)
+oeq_fold_x(const real_t *__restrict__ gxe, real_t *__restrict__ gx, i64 n) {
+    for (i64 i = (i64)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (i64)gridDim.x * blockDim.x) {
+        const i64 r = i / XD;
+        gx[i] = fold_x_elem(gxe + r * GXD, (int)(i - r * XD));
     }
 }

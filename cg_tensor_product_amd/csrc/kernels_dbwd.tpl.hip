@@ -96,12 +96,12 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
                 gy_push(st, dY, e, j, dy, lane, wv, acc_dy);
                 if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, dY, e - j, j + 1, acc_dy);
             }
-            if (HAS_DX && dxmode == 1 && act) Gr::atomic_x(dx + (i64)s * XD, u, dxp);
+            if (HAS_DX && dxmode == 1 && act) Gr::atomic_x(dx + (i64)s * GXD, u, dxp);
             if (HAS_DX && dxmode == 2 && act) {
                 if (acc_h)
-                    Gr::add_x(dx + (i64)e * XD, u, dxp);
+                    Gr::add_x(dx + (i64)e * GXD, u, dxp);
                 else
-                    Gr::store_x(dx + (i64)e * XD, u, dxp);
+                    Gr::store_x(dx + (i64)e * GXD, u, dxp);
             }
             s = sn;
             cur = nxt;

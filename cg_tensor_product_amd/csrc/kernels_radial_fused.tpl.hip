@@ -175,8 +175,8 @@ __device__ __forceinline__ void bwd_radial_group(GyStage &st, GyStage &sth, int 
                     gy_push(st, gY, e, jt, gy, lane, wv);
                     if (jt == GY_TILE - 1 || e + 1 == e1) gy_flush(st, gY, e - jt, jt + 1);
                 }
-                if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * XD, u, gxp);
-                if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * XD, u, gxp);
+                if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * GXD, u, gxp);
+                if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * GXD, u, gxp);
                 s = sn;
 #pragma unroll
                 for (int q = 0; q < YD; ++q) yv[q] = yn[q];

@@ -188,26 +188,38 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     }
     // the lane reduction of the Y gradient handles rows of up to 16 values
     if (p->YD > 16) return fail(why, OEQ_ERR_UNSUPPORTED, "Y rows wider than 16 values");
-    p->U = d->x_irreps[0].mul;
-    if (p->U <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "multiplicity must be >= 1");
+    // U: the largest x multiplicity.  A block of one channel (x or output) reduces a UVW
+    // product to the channel-wise one: an x block broadcast against the U channels, an
+    // output block that receives their sum.
+    p->U = 0;
+    for (int i = 0; i < d->n_x; ++i) {
+        if (d->x_irreps[i].mul <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "multiplicity must be >= 1");
+        p->U = std::max(p->U, d->x_irreps[i].mul);
+    }
     if (p->U > 1024) return fail(why, OEQ_ERR_UNSUPPORTED, "multiplicity above 1024");
     int lane = 0;
+    int64_t row = 0;
     for (int i = 0; i < d->n_x; ++i) {
         const oeq_irrep &ir = d->x_irreps[i];
-        if (ir.mul != p->U)
-            return fail(why, OEQ_ERR_UNSUPPORTED, "channel-wise product needs one multiplicity for all x blocks");
+        if (ir.mul != p->U && ir.mul != 1)
+            return fail(why, OEQ_ERR_UNSUPPORTED,
+                        "x blocks must have U channels (the largest multiplicity) or one (broadcast)");
         if (ir.l < 0 || ir.l > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "x degree must be in 0..3");
         if (ir.parity != 1 && ir.parity != -1) return fail(why, OEQ_ERR_INVALID_ARG, "parity must be +1 or -1");
-        p->xb.push_back({ir.l, ir.parity, lane, static_cast<int64_t>(p->U) * lane});
+        p->xb.push_back({ir.l, ir.parity, lane, row, ir.mul, static_cast<int64_t>(p->U) * lane});
+        if (ir.mul != p->U) p->bcast_x = true;
         lane += 2 * ir.l + 1;
+        row += static_cast<int64_t>(ir.mul) * (2 * ir.l + 1);
     }
     p->NXC = lane;
-    p->XD = static_cast<int64_t>(p->U) * lane;
+    p->XD = row;
+    p->GXD = static_cast<int64_t>(p->U) * lane;
 
     // Output blocks and the path list.
     struct Raw { int i1, iy, ob; };
     std::vector<Raw> raw;
     std::vector<std::pair<int, int>> out_lp;  // (l, parity) of each output block
+    std::vector<int> out_mul;                 // channels of each given output block
     if (d->paths == nullptr) {
         if (d->lmax_out < 0 || d->lmax_out > kLMax)
             return fail(why, OEQ_ERR_UNSUPPORTED, "lmax_out must be in 0..3");
@@ -215,11 +227,13 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
             if (d->n_out <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "n_out must be positive");
             for (int o = 0; o < d->n_out; ++o) {
                 const oeq_irrep &ir = d->out_irreps[o];
-                if (ir.mul != p->U) return fail(why, OEQ_ERR_UNSUPPORTED, "output multiplicity must equal U");
+                if (ir.mul != p->U && ir.mul != 1)
+                    return fail(why, OEQ_ERR_UNSUPPORTED, "output blocks must have U channels or one (a channel sum)");
                 if (ir.l < 0 || ir.l > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "output degree must be in 0..3");
                 if (ir.parity != 1 && ir.parity != -1)
                     return fail(why, OEQ_ERR_INVALID_ARG, "parity must be +1 or -1");
                 out_lp.push_back({ir.l, ir.parity});
+                out_mul.push_back(ir.mul);
             }
         }
         for (int i = 0; i < d->n_x; ++i) {
@@ -241,6 +255,7 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
                     } else {
                         raw.push_back({i, j, static_cast<int>(out_lp.size())});
                         out_lp.push_back({l3, p3});
+                        out_mul.push_back(p->U);
                     }
                 }
             }
@@ -251,10 +266,12 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         if (d->n_paths <= 0) return fail(why, OEQ_ERR_INVALID_ARG, "n_paths must be positive");
         for (int o = 0; o < d->n_out; ++o) {
             const oeq_irrep &ir = d->out_irreps[o];
-            if (ir.mul != p->U) return fail(why, OEQ_ERR_UNSUPPORTED, "output multiplicity must equal U");
+            if (ir.mul != p->U && ir.mul != 1)
+                return fail(why, OEQ_ERR_UNSUPPORTED, "output blocks must have U channels or one (a channel sum)");
             if (ir.l < 0 || ir.l > kLMax) return fail(why, OEQ_ERR_UNSUPPORTED, "output degree must be in 0..3");
             if (ir.parity != 1 && ir.parity != -1) return fail(why, OEQ_ERR_INVALID_ARG, "parity must be +1 or -1");
             out_lp.push_back({ir.l, ir.parity});
+            out_mul.push_back(ir.mul);
         }
         for (int k = 0; k < d->n_paths; ++k) {
             const oeq_path &pa = d->paths[k];
@@ -274,12 +291,17 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     if (raw.size() > 128) return fail(why, OEQ_ERR_UNSUPPORTED, "more than 128 paths");
 
     lane = 0;
-    for (const auto &lp : out_lp) {
-        p->ob.push_back({lp.first, lp.second, lane, static_cast<int64_t>(p->U) * lane});
-        lane += 2 * lp.first + 1;
+    row = 0;
+    for (size_t o = 0; o < out_lp.size(); ++o) {
+        const int l = out_lp[o].first, m = out_mul[o];
+        p->ob.push_back({l, out_lp[o].second, lane, row, m, static_cast<int64_t>(p->U) * lane});
+        if (m != p->U) p->sum_out = true;
+        lane += 2 * l + 1;
+        row += static_cast<int64_t>(m) * (2 * l + 1);
     }
     p->NOC = lane;
-    p->OD = static_cast<int64_t>(p->U) * lane;
+    p->OD = row;
+    p->GOD = static_cast<int64_t>(p->U) * lane;
 
     p->total_nnz = 0;
     for (const Raw &r : raw) {
@@ -307,7 +329,7 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
 
     p->uch = (p->U + 63) / 64;
     // m-major atomics need one node row in LDS for the final reorder
-    p->xt = p->XD * (p->dtype == OEQ_F64 ? 8 : 4) <= 65536 && std::getenv("OEQ_NO_XT") == nullptr;
+    p->xt = p->GXD * (p->dtype == OEQ_F64 ? 8 : 4) <= 65536 && std::getenv("OEQ_NO_XT") == nullptr;
     p->nt_w = std::getenv("OEQ_NO_NT") == nullptr;
     // measured on MI355X: pinning pays for the fp64 forward, not for fp32 or the backward passes
     p->pin_fwd = p->dtype == OEQ_F64;
@@ -340,6 +362,8 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         if (v >= 1) p->fwd_tile = v;
     }
     if (const char *e = std::getenv("OEQ_FWD_XCD")) p->fwd_xcd = std::atoi(e) != 0;
+    // an output channel sum adds the chunks of a receiver in the workgroup's LDS
+    if (p->sum_out) p->fwd_xcd = false;
     // one lane builds one edge's rows: a tile has at most one edge per lane of a group's waves
     p->fwd_tile = std::min(p->fwd_tile, 64 * (p->fwd_xcd ? 1 : p->uch));
     // and the tile's rows stay within 80 KB of LDS (gfx950 gives a workgroup up to 160 KB;
@@ -409,6 +433,8 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
             p->sched_bwd = s[1] == 's';
         }
     }
+    // the sender-stationary passes take U channels in every block
+    if (p->bcast_x || p->sum_out) p->sched_fwd = p->sched_bwd = 0;
     return OEQ_OK;
 }
 

@@ -39,7 +39,10 @@ struct Path {
 struct Block {
     int l, parity;
     int lane_off;    // offset of this block among one channel's values (sum of 2l+1 before it)
-    int64_t row_off; // offset of this block in a node row (U * lane_off)
+    int64_t row_off; // offset of this block in a node row (the sum of mul * (2l+1) before it)
+    int mul = 0;     // channels: U, or 1 for an x block broadcast against the U channels or an
+                     // output block that sums them
+    int64_t exp_off = 0;  // offset in a row with U channels in every block (U * lane_off)
 };
 
 // Kernels of one compiled module, on one device.
@@ -60,6 +63,12 @@ struct oeq_plan {
     bool y_natural = true;      // every Y block has parity (-1)^l (spherical harmonics can fill it)
     int NXC = 0, NOC = 0;       // per-channel x and output widths
     int64_t XD = 0, OD = 0;     // node row widths
+    // Rows with U channels in every block: the kernels write x-gradient rows this way and a
+    // fold sums the channels of the one-channel x blocks (GXD > XD only then).  An output
+    // block of one channel is summed over the channels in the forward itself.
+    int64_t GXD = 0, GOD = 0;
+    bool bcast_x = false;       // some x block has one channel and U > 1
+    bool sum_out = false;       // some output block has one channel and U > 1
     std::vector<oeq::Block> xb, ob, yb;  // yb: lane_off = offset in a Y row
     std::vector<oeq::Path> paths;
     int total_nnz = 0;

@@ -22,12 +22,15 @@
  *   rowptr [N+1] int32   receiver CSR, rowptr[0] = 0, rowptr[N] = E, non-decreasing
  *   src    [E]   int32   sender of edge e; edge e belongs to receiver r when
  *                        rowptr[r] <= e < rowptr[r+1]
- *   x      [N, XD]       x block i at xoff_i, element u*(2 l_i + 1) + (m + l_i)
+ *   x      [N, XD]       x block i at xoff_i (the widths mul*(2l+1) of the blocks
+ *                        before it), element u*(2 l_i + 1) + (m + l_i); a block of
+ *                        one channel holds (m + l_i) only
  *   Y      [E, YD]       Y block j (one channel) at yoff_j = the widths 2l+1 of the
  *                        blocks before it, element yoff_j + (m2 + l_j); for the
  *                        default Y (degrees 0..L) element l2*l2 + (m2 + l2)
  *   W      [E, P, U]
- *   out    [N, OD]       output block o at ooff_o, element u*(2 l_o + 1) + (m + l_o)
+ *   out    [N, OD]       output block o at ooff_o, element u*(2 l_o + 1) + (m + l_o);
+ *                        a block of one channel holds (m + l_o) only
  * Gradients use the layout of the tensor they belong to.
  *
  * Conventions shared by every entry point:
@@ -46,8 +49,18 @@
  *     during kernel execution surface at the caller's next synchronisation.
  *   - A plan is immutable after creation and may be used from several threads
  *     and streams at once.
- *   - Supported: degrees l <= 3 for x, Y and outputs; every x block with the
- *     same multiplicity U >= 1; dtype float32 or float64.
+ *   - Supported: degrees l <= 3 for x, Y and outputs; U = the largest x
+ *     multiplicity (1..1024), every x and output block with U channels or one;
+ *     dtype float32 or float64.
+ *
+ * UVW products that reduce to this one ("Receiver-streaming convolutions ...",
+ * maintainer replies: the streaming path also takes UVW convolutions reducible to
+ * UVU).  Read here as a weight diagonal in (u, w) up to a broadcast or a sum: an x
+ * block of one channel feeds every channel u (x[s, i1, 0, m1] in place of
+ * x[s, i1, u, m1]), and an output block of one channel receives the sum over u
+ * (out[r, blk, 0, m3] += the sum over u of the terms above).  Such plans run the
+ * receiver-stationary passes; the sender-stationary passes and the passes that
+ * form W in the kernel refuse them with OEQ_ERR_UNSUPPORTED.
  */
 #ifndef OEQ_H
 #define OEQ_H
@@ -62,7 +75,7 @@ extern "C" {
 typedef enum {
     OEQ_OK = 0,
     OEQ_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad enum        */
-    OEQ_ERR_UNSUPPORTED = 2, /* l > 3, mixed multiplicities, unknown dtype   */
+    OEQ_ERR_UNSUPPORTED = 2, /* l > 3, a multiplicity neither U nor 1, dtype */
     OEQ_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required   */
     OEQ_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed   */
     OEQ_ERR_JIT = 5          /* runtime compilation of the kernels failed    */
@@ -93,14 +106,17 @@ typedef struct {
  * interface over irreps descriptors of its inputs and outputs).  All arrays are
  * host memory, read during oeq_plan_create only. */
 typedef struct {
-    const oeq_irrep *x_irreps;   /* x blocks, each with the same multiplicity U     */
+    const oeq_irrep *x_irreps;   /* x blocks: U channels (the largest multiplicity) */
+                                 /*   or one (broadcast against the U channels)     */
     int32_t n_x;
     const oeq_irrep *y_irreps;   /* Y blocks in row order, multiplicity 1 each, any */
     int32_t n_y;                 /*   degrees 0..3 in any order and either parity,  */
                                  /*   total width sum(2l+1) <= 16.  NULL: the       */
                                  /*   spherical harmonics 0..y_lmax, parity (-1)^l  */
     int32_t y_lmax;              /* used when y_irreps == NULL                      */
-    const oeq_irrep *out_irreps; /* NULL: one output block per path, in path order  */
+    const oeq_irrep *out_irreps; /* NULL: one output block of U channels per path,  */
+                                 /*   in path order; given: U channels or one (the  */
+                                 /*   sum over the channels) per block              */
     int32_t n_out;
     const oeq_path *paths;       /* NULL: enumerate every triangle-allowed path:    */
     int32_t n_paths;             /*   x blocks in order, then Y blocks in order,    */
@@ -131,8 +147,8 @@ typedef struct oeq_plan oeq_plan; /* opaque, host-owned */
  * the first compute call there.  *plan is set to NULL on failure.
  * Errors: OEQ_ERR_INVALID_ARG (NULL pointers, bad parity, a path outside the
  * triangle rule or with the wrong output parity), OEQ_ERR_UNSUPPORTED (degree
- * above 3, mixed x multiplicities, Y wider than 16, more than 128 paths, an
- * unknown dtype), OEQ_ERR_JIT (the runtime compiler failed). */
+ * above 3, an x or output multiplicity other than U or 1, Y wider than 16, more
+ * than 128 paths, an unknown dtype), OEQ_ERR_JIT (the runtime compiler failed). */
 oeq_status oeq_plan_create(const oeq_tp_desc *desc, oeq_plan **plan);
 
 /* As oeq_plan_create, but never runs the runtime compiler: returns OEQ_ERR_JIT
@@ -168,7 +184,9 @@ oeq_status oeq_cg_table(int32_t l1, int32_t l2, int32_t l3, double *out);
  * backward or double-backward groups, sized for the larger count; per-edge
  * x-gradient rows and the sender CSR for DETERMINISTIC: the materialised
  * per-edge tensor reduced in a fixed order of the deterministic fallback in
- * "Optimize UMA SO2 and Wigner inference kernels").  One size serves both
+ * "Optimize UMA SO2 and Wigner inference kernels"); for ATOMIC with one-channel
+ * x blocks, x-gradient rows of U channels in every block, whose channels the call
+ * then sums into grad_x.  One size serves both
  * calls.  0 means no workspace is needed; the caller allocates it (the library
  * never allocates in a compute call).  OEQ_ERR_INVALID_ARG for a NULL plan or
  * output, negative sizes or an unknown mode. */

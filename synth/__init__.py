@@ -52,10 +52,11 @@ class Workload:
     multi: bool = False              # senders drawn with replacement, the receiver included
     y_irreps: Optional[tuple] = None # Y blocks ((1, l, parity), ...); None: degrees 0..y_lmax
     one_sender: bool = False         # every edge leaves node 0 (counter calibration: x is one row)
+    out_irreps: Optional[tuple] = None  # output blocks ((mul, l, parity), ...), mul U or 1; None: one per path
 
     @property
     def U(self) -> int:
-        return self.x_irreps[0][0]
+        return max(m for m, _, _ in self.x_irreps)
 
     @property
     def n_edges(self) -> int:

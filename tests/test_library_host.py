@@ -397,3 +397,57 @@ def test_workspace_covers_the_sender_view_when_the_vjp_routes_there():
     for mode in ("atomic", "deterministic"):
         assert oeq.oeq_workspace_size(p, N, E, mode) >= 4 * (N + 1 + 2 * E)
     assert oeq.oeq_workspace_size(p, N, 0, "atomic") == 0
+
+
+# UVW products that reduce to the channel-wise one: one-channel x blocks (broadcast)
+# and one-channel output blocks (channel sums)
+from test_gpu_uvw import CASES as UVW_CASES  # noqa: E402
+
+
+@pytest.mark.parametrize("name", list(UVW_CASES))
+def test_reducible_plans_equal_oracle(name):
+    wl = UVW_CASES[name]
+    d = oracle_desc(wl)
+    p = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype, out_irreps=wl.out_irreps)
+    assert [(i1, l2, l3, ob) for (i1, _, l2, l3, ob, _) in p.paths()] == [
+        (i1, d.path_l2(k), l3, ob) for k, (i1, _j, l3, ob) in enumerate(d.paths)]
+    assert (p.x_dim, p.y_dim, p.out_dim, p.n_paths, p.U) == (d.x_dim, d.y_dim, d.out_dim, d.P, d.U)
+
+
+def test_reducible_plans_take_the_receiver_passes_only(monkeypatch):
+    monkeypatch.setenv("OEQ_SCHEDULE", "ss")
+    for xi, oi in (("1x0e+16x1o", None), ("16x0e+16x1o", "1x0e+16x1o+1x1e")):
+        p = oeq.Plan(xi, 2, 2, "f32", out_irreps=oi)
+        assert (p.schedule()["fwd"], p.schedule()["bwd"]) == ("receiver", "receiver")
+        lib, P = oeq.lib(), ctypes.c_void_p
+        assert lib.oeq_tp_conv_fwd_sender(p.handle, 0, 0, P(16), None, None, None, None, None, None, None) == 2
+        assert b"U channels" in lib.oeq_last_error()
+        assert lib.oeq_tp_conv_bwd_sender(p.handle, 0, 0, P(16), None, None, None, None, None, None, None, None,
+                                          None, None, 0, None) == 2
+        assert lib.oeq_tp_conv_fwd_radial(p.handle, 0, 0, P(16), None, None, None, None, 5.0, None, None, None,
+                                          None, 0, None) == 2
+        assert lib.oeq_tp_conv_bwd_radial(p.handle, 0, 0, P(16), None, None, None, None, 5.0, None, None, None,
+                                          None, None, None, None, None, 0, None, 0, None) == 2
+
+
+def test_reducible_workspace_holds_the_wide_x_gradient_rows():
+    # atomic VJP of a plan with a broadcast x block: x-gradient rows of U channels in every
+    # block (64 x (1 + 3) values per node) in the workspace, summed into the caller's rows
+    p = oeq.Plan("1x0e+64x1o", 2, 2, "f32")
+    assert p.x_dim == 1 + 64 * 3
+    assert oeq.oeq_workspace_size(p, 64, 1024, "atomic") == 64 * 256 * 4
+    # per-edge rows of the deterministic VJP have the same width
+    assert oeq.oeq_workspace_size(p, 64, 1024, "deterministic") >= 1024 * 256 * 4
+    # channel sums alone need no x-gradient rows of their own
+    q = oeq.Plan("64x0e+64x1o", 2, 2, "f32", out_irreps="1x0e+64x1o+1x1e")
+    assert oeq.oeq_workspace_size(q, 64, 1024, "atomic") == 0
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x_irreps="8x0e+4x1o", y_lmax=2),                      # neither U nor one channel
+    dict(x_irreps="8x0e+8x1o", y_lmax=2, out_irreps="4x1o"),  # output of 4 channels against U = 8
+])
+def test_reducible_plan_errors(kw):
+    with pytest.raises(oeq.OeqError) as e:
+        oeq.Plan(**kw)
+    assert e.value.status == 2
