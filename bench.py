@@ -64,20 +64,25 @@ def measured_traffic(workload, kernel, code_key):
 
 def stream_reference(torch, nbytes=2 << 30):
     """Same-box context for the HBM figures: a plain device-to-device copy of
-    2 GiB (bytes read + written per second), best of 5."""
+    2 GiB (bytes read + written per second), best of 6."""
     a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
-    best = float("inf")
-    for _ in range(6):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        b.copy_(a)
-        e1.record()
-        torch.cuda.synchronize()
-        best = min(best, e0.elapsed_time(e1))
+
+    def best_ms(fn):
+        best = float("inf")
+        for _ in range(6):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    copy_ms = best_ms(lambda: b.copy_(a))
     del a, b
     torch.cuda.empty_cache()
-    return {"copy_GBps": 2 * nbytes / (best * 1e-3) / 1e9, "bytes": 2 * nbytes}
+    return {"copy_GBps": 2 * nbytes / (copy_ms * 1e-3) / 1e9, "bytes": 2 * nbytes}
 
 
 def side_rows(torch, oeq, plan, dev, N, E, ab, reps=10):
@@ -171,6 +176,56 @@ def cpu_baseline(wl, d, inp, target_s=10.0, single_s=4.0):
                                   "sample": "the forward over the first 250, 500, ... receivers' rows, one thread"}}
 
 
+def fresh_plan_check(torch, oeq, wl, plan, dev, out, reps=20):
+    """Forward time of the plan compiled again by oeq_plan_create in this process (a
+    process that has loaded torch and its own ROCm libraries), against the plan loaded
+    from the code-object cache; once through the compiler helper and once with the
+    compiler in this process.  Both timed with HIP events, interleaved."""
+    import shutil
+    import tempfile
+
+    def fwd_ms(p):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in ev:
+            a.record()
+            oeq.oeq_tp_conv_fwd(p, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], out=out)
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+    res = {}
+    for name, env in (("helper", {}), ("in_process", {"OEQ_JIT_IN_PROCESS": "1"})):
+        tmp = tempfile.mkdtemp(prefix="oeq_fresh_")
+        old = {k: os.environ.get(k) for k in ("OEQ_CACHE_DIR", "OEQ_JIT_IN_PROCESS")}
+        os.environ.update({"OEQ_CACHE_DIR": tmp, **env})
+        try:
+            t0 = time.perf_counter()
+            p2 = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+            compile_s = time.perf_counter() - t0
+        finally:
+            for k, v in old.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        fwd_ms(p2), fwd_ms(plan)  # load and warm both
+        fresh_ms, cached_ms = [], []
+        for _ in range(3):
+            fresh_ms.append(fwd_ms(p2))
+            cached_ms.append(fwd_ms(plan))
+        cached_file = os.path.join(ROOT, "cg_tensor_product_amd", "jitcache", plan.code_key + ".hsaco")
+        fresh_file = os.path.join(tmp, p2.code_key + ".hsaco")
+        same = (os.path.exists(cached_file) and os.path.exists(fresh_file)
+                and open(cached_file, "rb").read() == open(fresh_file, "rb").read())
+        res[name] = {"compile_s": compile_s, "fwd_ms": float(np.median(fresh_ms)),
+                     "cached_fwd_ms": float(np.median(cached_ms)),
+                     "ratio": float(np.median(fresh_ms) / np.median(cached_ms)),
+                     "same_code_object_bytes": bool(same)}
+        del p2
+        shutil.rmtree(tmp, ignore_errors=True)
+    return res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -194,6 +249,10 @@ def main():
                     help="schedule of both passes: the plan's data-movement choice per pass (auto), or forced")
     ap.add_argument("--no-side-rows", action="store_true",
                     help="skip timing the deterministic VJP, HVP and all-tangent double backward")
+    ap.add_argument("--fresh-plan", action="store_true",
+                    help="also compile the plan again in this process (empty code-object cache) and time "
+                         "its forward beside the cached plan's: through the compiler helper (the default) "
+                         "and with the compiler loaded in this process (OEQ_JIT_IN_PROCESS=1)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first copy 1 GiB device-to-device 3 times (a plain copy kernel of known size, "
                          "to scale HBM byte counters)")
@@ -285,6 +344,8 @@ def main():
     fwd_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     vjp_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
 
+    fresh = fresh_plan_check(torch, oeq, wl, plan, dev, out) if args.fresh_plan else None
+
     ab = algorithmic_bytes(wl, d.P, d.out_dim, E)
     ms_step = total / args.steps * 1e3
     step_bytes = ab["fwd"] + ab["vjp"]
@@ -326,6 +387,8 @@ def main():
     }
     if not args.no_side_rows:
         res["side_rows"] = side_rows(torch, oeq, plan, dev, N, E, ab)
+    if fresh is not None:
+        res["fresh_plan"] = fresh
     res["stream_reference"] = stream_reference(torch)
     # the dominant kernel's algorithmic rate as a fraction of this box's plain copy rate
     res["stream_reference"]["frac_of_copy"] = achieved / res["stream_reference"]["copy_GBps"]

@@ -236,6 +236,23 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
         if (dg && (st = fill_zero(p, dg, N * p->OD, s)) != OEQ_OK) return st;
         return OEQ_OK;
     }
+    if (tm == 1 && p->hvp_lds) {
+        // the HVP from Y-contracted CG rows in LDS (d_x = 0 without a Y or W tangent)
+        if (dx && (st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;
+        if (!dY && !dW && !dg) return OEQ_OK;
+        const int64_t NGB = static_cast<int64_t>(p->bwd_groups.size());
+        const bool gyp = dY && NGB > 1;
+        Workspace w;
+        if ((st = ws_bind(p, N, E, false, gyp, workspace, workspace_bytes, &w)) != OEQ_OK) return st;
+        int flags = (dW ? 1 : 0) | (dY ? 2 : 0) | (dg ? 4 : 0);
+        void *dy_target = gyp ? w.gy_part : dY;
+        int64_t gy_stride = gyp ? E * p->YD : 0;
+        int n_nodes = static_cast<int>(N);
+        void *args[] = {&rowptr, &src, &Y, &W, &g, &ggx, &dy_target, &dW, &dg, &flags, &gy_stride, &n_nodes};
+        if ((st = launch(p, "oeq_hvp_lds", static_cast<unsigned>(N * NGB), bwd_block(p), s, args)) != OEQ_OK)
+            return st;
+        return gyp ? combine_parts(p, w.gy_part, static_cast<int>(NGB), dY, E * p->YD, s) : OEQ_OK;
+    }
     // d_x = Bx(ggY,W,g) + Bx(Y,ggW,g) vanishes without a Y or W tangent
     const bool dx_live = dx && (tm & 6);
     const bool det = dx_live && mode == OEQ_BWD_DETERMINISTIC;

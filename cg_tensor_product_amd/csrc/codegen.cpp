@@ -421,6 +421,47 @@ int group_nsum(const oeq_plan &p, const std::vector<int> &paths, bool first) {
     return n;
 }
 
+// Hessian-vector product terms of one edge from its M row (in LDS), for the tangent v on
+// x: per path and m3, t[m3] = sum_m1 M[m1][m3] v[m1] (the forward of v, shared by two
+// outputs), then d_grad_out[m3] += w t[m3] and d_W += g[m3] t[m3].  The Y gradient needs
+// the uncontracted tables and is formed by dbwd_edge.
+void emit_hvp_m(std::ostringstream &o, const oeq_plan &p, const Local &L) {
+    const std::vector<MEntry> ents = m_entries(p, L);
+    const int ve = p.dtype == OEQ_F64 ? 2 : 4;
+    o << "  static __device__ __forceinline__ void hvp_m(const real_t (&v)[NX], const real_t *__restrict__ row, "
+         "const real_t (&w)[NW], const real_t (&g)[NO], real_t (&dg)[NO], real_t (&dw)[NW]) {\n";
+    o << "    const vec16_t *__restrict__ mv = reinterpret_cast<const vec16_t *>(row);\n";
+    int loaded = -1;
+    auto need = [&](size_t i) {
+        const int vi = static_cast<int>(i) / ve;
+        std::string r;
+        while (loaded < vi) {
+            ++loaded;
+            r += "    const vec16_t v" + S(loaded) + " = mv[" + S(loaded) + "];\n";
+        }
+        return r;
+    };
+    auto mref = [&](size_t i) { return "v" + S(static_cast<long long>(i) / ve) + "[" + S(static_cast<long long>(i) % ve) + "]"; };
+    size_t i = 0;
+    while (i < ents.size()) {
+        const int k = ents[i].path, m3 = ents[i].m3;
+        const Path &pa = p.paths[k];
+        const int xo = L.xoff.at(pa.i1), oo = L.ooff.at(pa.ob), wk = L.widx.at(k);
+        std::string pre = need(i);
+        std::string line = "    { real_t t = " + mref(i) + " * v[" + S(xo + ents[i].m1) + "];";
+        ++i;
+        while (i < ents.size() && ents[i].path == k && ents[i].m3 == m3) {
+            pre += need(i);
+            line += " t = fmar(" + mref(i) + ", v[" + S(xo + ents[i].m1) + "], t);";
+            ++i;
+        }
+        const std::string d = "dg[" + S(oo + m3) + "]";
+        o << pre << line << " " << d << " = fmar(w[" << wk << "], t, " << d << "); dw[" << wk << "] = fmar(g["
+          << oo + m3 << "], t, dw[" << wk << "]); }\n";
+    }
+    o << "  }\n";
+}
+
 void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int g, const std::vector<int> &paths,
                 int moff = 0, int soff = 0) {
     const Local L = make_local(p, paths, g == 0);
@@ -604,6 +645,10 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
     o << "  }\n";
     if (std::string(name) == "BG" || std::string(name) == "DG") emit_dbwd_edge(o, p, L);
     if (std::string(name) == "FG" && p.fwd_lds) emit_m_functions(o, p, L, moff);
+    if (std::string(name) == "BG" && p.hvp_lds) {
+        emit_m_functions(o, p, L, 0);
+        emit_hvp_m(o, p, L);
+    }
     o << "};\n";
 }
 
@@ -653,6 +698,12 @@ void emit_fold_x(std::ostringstream &o, const oeq_plan &p) {
 }
 
 }  // namespace
+
+int hvp_m_elems(const oeq_plan &p) {
+    int n = 0;
+    for (size_t g = 0; g < p.bwd_groups.size(); ++g) n = std::max(n, group_m_stride(p, p.bwd_groups[g]));
+    return n;
+}
 
 int fwd_m_elems(const oeq_plan &p) {
     int n = 0;
@@ -742,6 +793,10 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr bool FWD_XCD = " << (p.fwd_xcd ? "true" : "false") << ";\n";
     o << "#define M_FENCE() __builtin_amdgcn_sched_barrier(0)\n";
     o << "constexpr int FWD_MT = " << p.fwd_tile << ";\n";
+    // HVP from Y-contracted CG rows: tiles of HVP_MT edges, rows of at most HVP_M_MAX values
+    o << "constexpr bool HVP_LDS = " << (p.hvp_lds ? "true" : "false") << ";\n";
+    o << "constexpr int HVP_MT = " << p.hvp_tile << ";\n";
+    o << "constexpr int HVP_M_MAX = " << (p.hvp_lds ? hvp_m_elems(p) : 0) << ";\n";
     o << "typedef real_t vec16_t __attribute__((ext_vector_type(" << (p.dtype == OEQ_F64 ? 2 : 4) << ")));\n";
     {
         int moff = 0, soff = 0;

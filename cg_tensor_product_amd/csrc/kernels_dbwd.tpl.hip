@@ -192,3 +192,113 @@ OEQ_DBWD_KERNEL(oeq_dbwd_7_10, 7, 10, true)
 OEQ_DBWD_KERNEL(oeq_dbwd_1_2, 1, 2, true)
 OEQ_DBWD_KERNEL(oeq_dbwd_2_8, 2, 8, true)
 OEQ_DBWD_KERNEL(oeq_dbwd_4_10, 4, 10, true)
+
+// ---------------------------------------------------------------------------
+// Hessian-vector product (tangent v = gg_x only) from Y-contracted CG rows.  The
+// receiver's edges are taken in tiles of HVP_MT; for each tile the workgroup's lanes
+// build the rows M[e] = C . Y[e] in LDS (one lane per edge), then every channel lane
+// streams the tile: t = M^T v[s] per path gives d_grad_out += w t and d_W = g . t,
+// and d_Y = w (v . C g) is formed from the tables and reduced like the VJP's Y
+// gradient.  d_x is zero.  A workgroup is one (receiver, backward group), so all of
+// its waves run the same tiles and meet at the same barriers.
+// flags: bit0 d_W, bit1 d_Y, bit2 d_grad_out
+// ---------------------------------------------------------------------------
+template <int G>
+__device__ __forceinline__ void hvp_group_lds(GyStage &st, real_t *__restrict__ mt, int r, int wv, int u,
+                                              const int *__restrict__ rowptr, const int *__restrict__ src,
+                                              const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                              const real_t *__restrict__ g, const real_t *__restrict__ v,
+                                              real_t *__restrict__ dY, real_t *__restrict__ dW,
+                                              real_t *__restrict__ dg, int flags) {
+    using Gr = BG<G>;
+    const int lane = threadIdx.x & 63;
+    const bool act = (U % 64 == 0) || (u < U);
+    const int uu = act ? u : 0;
+    const bool want_dw = (flags & 1) != 0, want_dy = (flags & 2) != 0, want_dg = (flags & 4) != 0;
+    const int bi = wv * 64 + lane;  // the tile row this lane builds (when < HVP_MT)
+    real_t gv[Gr::NO];
+    Gr::load_g(g + (i64)r * OD, uu, gv);
+    if (!act) zero(gv);
+    real_t dgacc[Gr::NO];
+    zero(dgacc);
+    const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
+    if (e0 < e1) {
+        int s = uni(src[e0]);
+        real_t vv[Gr::NX], wv_[Gr::NW];
+        Gr::load_x(v + (i64)s * XD, uu, vv);
+        Gr::load_w(W + (i64)e0 * (P * U), uu, wv_);
+        real_t ynone[YD];  // the Y values are in the M rows; dbwd_edge reads none for this tangent
+        zero(ynone);
+        int tb = e0;  // first edge of the tile whose rows are in LDS
+        for (int e = e0; e < e1; ++e) {
+            if (e == tb + HVP_MT || e == e0) {
+                tb = e;
+                __syncthreads();  // the previous tile's rows are no longer read
+                if (bi < HVP_MT && e + bi < e1) {
+                    real_t yv[YD];
+                    load_y(Y, e + bi, yv);
+                    Gr::make_m(yv, mt + bi * Gr::SM);
+                }
+                __syncthreads();
+            }
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            real_t vn[Gr::NX], wn[Gr::NW];
+            Gr::load_x(v + (i64)sn * XD, uu, vn);
+            Gr::load_w(W + (i64)en * (P * U), uu, wn);
+            PIN_BWD();
+            const int j = uni((e - e0) % GY_TILE);
+            real_t dw[Gr::NW], dy[YD], dxp[Gr::NX], tnone[Gr::NW];
+            zero(dw);
+            zero(dy);
+            zero(dxp);
+            zero(tnone);
+            Gr::hvp_m(vv, mt + (e - tb) * Gr::SM, wv_, gv, dgacc, dw);
+            if (want_dy)
+                Gr::template dbwd_edge<1, false, true, false>(vv, ynone, wv_, vv, ynone, tnone, gv, false, dgacc, dw,
+                                                              dy, dxp);
+            if (want_dw && act) Gr::store_w(dW + (i64)e * (P * U), u, dw);
+            if (want_dy) {
+                gy_push(st, dY, e, j, dy, lane, wv);
+                if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, dY, e - j, j + 1);
+            }
+#pragma unroll
+            for (int k = 0; k < Gr::NX; ++k) vv[k] = vn[k];
+#pragma unroll
+            for (int k = 0; k < Gr::NW; ++k) wv_[k] = wn[k];
+        }
+    }
+    if (want_dg && act) Gr::store_out(dg + (i64)r * OD, u, dgacc);
+}
+
+template <int G>
+__device__ __forceinline__ void hvp_dispatch(GyStage &st, real_t *__restrict__ mt, int r, int grp, int wv, int u,
+                                             const int *__restrict__ rowptr, const int *__restrict__ src,
+                                             const real_t *__restrict__ Y, const real_t *__restrict__ W,
+                                             const real_t *__restrict__ g, const real_t *__restrict__ v,
+                                             real_t *__restrict__ dY, real_t *__restrict__ dW,
+                                             real_t *__restrict__ dg, int flags) {
+    if constexpr (HVP_LDS) {
+        if (grp == G) {
+            hvp_group_lds<G>(st, mt, r, wv, u, rowptr, src, Y, W, g, v, dY, dW, dg, flags);
+            return;
+        }
+        if constexpr (G + 1 < NGB) hvp_dispatch<G + 1>(st, mt, r, grp, wv, u, rowptr, src, Y, W, g, v, dY, dW, dg, flags);
+    }
+}
+
+extern "C" __global__ void __launch_bounds__(UCH * 64) BWD_OCCUPANCY
+oeq_hvp_lds(const int *__restrict__ rowptr, const int *__restrict__ src, const real_t *__restrict__ Y,
+            const real_t *__restrict__ W, const real_t *__restrict__ g, const real_t *__restrict__ v,
+            real_t *__restrict__ dY, real_t *__restrict__ dW, real_t *__restrict__ dg, int flags, i64 gy_stride,
+            int n_nodes) {
+    if constexpr (HVP_LDS) {
+        __shared__ GyStage st;
+        __shared__ __attribute__((aligned(16))) real_t mbuf[HVP_M_MAX * HVP_MT > 0 ? HVP_M_MAX * HVP_MT : 1];
+        const int r = blockIdx.x / NGB, grp = blockIdx.x - r * NGB;
+        if (r >= n_nodes) return;  // a grid larger than the groups x nodes reads nothing
+        const int wv = uni(threadIdx.x >> 6);
+        hvp_dispatch<0>(st, mbuf, r, grp, wv, wv * 64 + (threadIdx.x & 63), rowptr, src, Y, W, g, v,
+                        dY + grp * gy_stride, dW, dg, flags);
+    }
+}

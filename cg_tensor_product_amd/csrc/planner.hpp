@@ -89,6 +89,10 @@ struct oeq_plan {
     // path instead of the x-Y products plus every non-zero plus n3
     bool fwd_lds = false;
     int fwd_tile = 32;          // edges per LDS tile of M rows (capped by the LDS budget)
+    // the HVP (tangent on x only) from Y-contracted CG rows in LDS per edge tile: d_grad_out
+    // and d_W share the forward of the tangent, t = M^T v, instead of the x-Y products
+    bool hvp_lds = false;
+    int hvp_tile = 32;          // edges per HVP tile (at most one per lane of the workgroup)
     // forward workgroups of one 64-channel chunk, mapped so that each chunk stays on the
     // same XCDs (their L2 caches then hold the x rows of one chunk)
     bool fwd_xcd = false;
@@ -123,6 +127,8 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why);
 
 // Elements of one edge's Y-contracted CG rows over all forward groups (the LDS forward).
 int fwd_m_elems(const oeq_plan &p);
+// Largest M row over the backward groups (the tile-form HVP).
+int hvp_m_elems(const oeq_plan &p);
 
 // Emits the HIP source of every kernel of the plan.
 std::string emit_source(const oeq_plan &p);

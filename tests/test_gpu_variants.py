@@ -69,6 +69,10 @@ CASES = [
     ("mace_medium_fp32", {"OEQ_FWD_XCD": "1"}),
     ("wide_proxy_fp32", {"OEQ_FWD_XCD": "1", "OEQ_FWD_LDS": "1"}),
     ("mace_medium_fp64", {"OEQ_FWD_XCD": "1"}),
+    # the HVP from Y-contracted CG rows in LDS (an option): one backward group, and two
+    # groups (partial Y-gradient rows) with ragged tiles of 7 edges
+    ("mace_medium_fp32", {"OEQ_HVP_LDS": "1"}),
+    ("tiny_fp64", {"OEQ_HVP_LDS": "1", "OEQ_BWD_GROUPS": "2", "OEQ_HVP_TILE": "7"}),
     # the split double backward's accumulating forward launches in the tile form
     ("mace_medium_fp64", {"OEQ_DBWD_SPLIT": "1"}),
     ("mace_medium_fp32", {"OEQ_FWD_LDS": "1", "OEQ_DBWD_SPLIT": "2"}),
