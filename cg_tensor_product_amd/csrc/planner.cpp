@@ -97,43 +97,16 @@ int group_registers(const oeq_plan &p, const std::vector<int> &paths, bool fwd) 
     return vals * (p.dtype == OEQ_F64 ? 2 : 1) + 20;
 }
 
-// Registers of the fused all-tangent double backward for one group: g and the d_grad_out
-// accumulators, the current and next edge's x, gg_x, W, gg_W, Y, gg_Y, the per-edge
-// d_Y, d_x, d_W and the largest per-path product block.
-int dbwd_registers(const oeq_plan &p, const std::vector<int> &paths) {
-    std::set<int> xs, os;
-    int transient = 0;
-    for (int k : paths) {
-        const Path &pa = p.paths[k];
-        xs.insert(pa.i1);
-        os.insert(pa.ob);
-        transient = std::max(transient, (2 * pa.l1 + 1) * (2 * pa.l2 + 1));
-    }
-    int nx = 0, no = 0;
-    for (int i : xs) nx += 2 * p.xb[i].l + 1;
-    for (int o : os) no += 2 * p.ob[o].l + 1;
-    const int nw = static_cast<int>(paths.size());
-    const int vals = 2 * no + 5 * nx + 5 * nw + 5 * p.YD + transient;
-    return vals * (p.dtype == OEQ_F64 ? 2 : 1) + 20;
-}
-
-// The double backward's groups: split until the all-tangent kernel's estimate is under
-// budget. Measured with all three tangents (ms, 1 / 2 / 3 groups): medium fp32 1.80 / 3.01 /
-// 3.03 (estimate 316 at 1 group), medium fp64 5.91 / 4.99 / 4.99, large 6.78 / 5.30 / 4.91,
-// wide 14.84 / 10.77 / 9.79 (estimate 512 at 1 group, 317 at 2).
+// The double backward's groups: as many as the indivisible units allow (at most 16 waves
+// per workgroup). Measured with all three tangents (ms, 1 / 2 / 3 groups): large 6.78 / 5.15 /
+// 4.81, wide 14.84 / 10.50 / 9.68, medium fp64 5.91 / 4.99 (two units); the medium fp32 plan
+// runs its fused kernel on the backward groups (one group, no spill), so its split here is
+// not used.
 std::vector<std::vector<int>> choose_dbwd_groups(const oeq_plan &p) {
     const int max_g = std::max(1, 16 / p.uch);
     if (const char *e = std::getenv("OEQ_DBWD_GROUPS"))
         return partition_paths(p, false, std::max(1, std::min(std::atoi(e), max_g)));
-    std::vector<std::vector<int>> best = partition_paths(p, false, 1);
-    for (int g = 1; g <= max_g; ++g) {
-        auto cand = partition_paths(p, false, g);
-        best = cand;
-        int worst = 0;
-        for (const auto &gr : cand) worst = std::max(worst, dbwd_registers(p, gr));
-        if (worst <= 400 || static_cast<int>(cand.size()) < g) break;
-    }
-    return best;
+    return partition_paths(p, false, max_g);
 }
 
 std::vector<std::vector<int>> choose_groups(const oeq_plan &p, bool fwd) {

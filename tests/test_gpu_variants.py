@@ -53,7 +53,7 @@ CASES = [
     # double-backward path groups other than the planned ones, with each split level
     ("mace_medium_fp32", {"OEQ_DBWD_GROUPS": "2"}),
     ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "1"}),
-    ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "3", "OEQ_DBWD_SPLIT": "1"}),
+    ("mace_large_fp32", {"OEQ_DBWD_GROUPS": "2", "OEQ_DBWD_SPLIT": "1"}),
     ("mace_medium_fp64", {"OEQ_DBWD_GROUPS": "2", "OEQ_DBWD_SPLIT": "2"}),
     # forward from Y-contracted CG rows in LDS (the default for fp64 and for four or more
     # channel chunks) and the literal form: tiles of one edge, of 7 (ragged), 32, 50 and 64

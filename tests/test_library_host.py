@@ -135,8 +135,13 @@ def test_compute_argument_errors_before_any_device_work():
 def test_workspace_size_atomic(monkeypatch):
     # the receiver-stationary VJP (forced: this plan's model prefers the sender-stationary one)
     monkeypatch.setenv("OEQ_SCHEDULE", "rr")
-    # one backward path group -> no scratch in atomic mode
+    # one size serves the VJP and the double backward: the latter's two path groups (one per
+    # x block) need partial Y-gradient rows
+    assert oeq.oeq_workspace_size(oeq.Plan("8x0e+8x1o", 2, 1, "f64"), 64, 1024, "atomic") == 2 * 1024 * 9 * 8
+    # one group for both -> no scratch in atomic mode
+    monkeypatch.setenv("OEQ_DBWD_GROUPS", "1")
     assert oeq.oeq_workspace_size(oeq.Plan("8x0e+8x1o", 2, 1, "f64"), 64, 1024, "atomic") == 0
+    monkeypatch.delenv("OEQ_DBWD_GROUPS")
     # two groups -> per-group partial Y-gradient rows
     monkeypatch.setenv("OEQ_BWD_GROUPS", "2")
     p = oeq.Plan("8x0e+8x1o", 2, 1, "f64")
@@ -430,9 +435,11 @@ def test_reducible_plans_take_the_receiver_passes_only(monkeypatch):
                                           None, None, None, None, None, 0, None, 0, None) == 2
 
 
-def test_reducible_workspace_holds_the_wide_x_gradient_rows():
+def test_reducible_workspace_holds_the_wide_x_gradient_rows(monkeypatch):
     # atomic VJP of a plan with a broadcast x block: x-gradient rows of U channels in every
     # block (64 x (1 + 3) values per node) in the workspace, summed into the caller's rows
+    # (one double-backward group: no partial Y-gradient rows besides)
+    monkeypatch.setenv("OEQ_DBWD_GROUPS", "1")
     p = oeq.Plan("1x0e+64x1o", 2, 2, "f32")
     assert p.x_dim == 1 + 64 * 3
     assert oeq.oeq_workspace_size(p, 64, 1024, "atomic") == 64 * 256 * 4
