@@ -107,6 +107,9 @@ def side_rows(torch, oeq, plan, dev, N, E, ab, reps=10):
         return raw[off:off + n]
 
     wsd, wsa = ws("deterministic"), ws("atomic")
+    # the tangents of Y and W: copies of Y and W (the cost does not depend on their values, but
+    # they must be buffers of their own, or their loads would hit the cache lines of Y and W)
+    ggY, ggW = dev["Y"].clone(), dev["W"].clone()
     calls = {
         "vjp_deterministic": (ab["vjp"], lambda: oeq.oeq_tp_conv_bwd(
             plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"], mode="deterministic",
@@ -114,10 +117,9 @@ def side_rows(torch, oeq, plan, dev, N, E, ab, reps=10):
         "hvp": (ab["hvp"], lambda: oeq.oeq_tp_conv_dbwd(
             plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"], gg_x=v, out=hvp_outs,
             workspace=wsa)),
-        # the tangents of Y and W reuse Y and W themselves: the cost does not depend on their values
         "dbwd_all_tangents": (ab["dbwd"], lambda: oeq.oeq_tp_conv_dbwd(
-            plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"], gg_x=v, gg_Y=dev["Y"],
-            gg_W=dev["W"], out=outs, workspace=wsa)),
+            plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"], gg_x=v, gg_Y=ggY,
+            gg_W=ggW, out=outs, workspace=wsa)),
     }
     res = {}
     for name, (nbytes, fn) in calls.items():
@@ -131,7 +133,7 @@ def side_rows(torch, oeq, plan, dev, N, E, ab, reps=10):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         res[name] = {"ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9, "bytes": nbytes, "edges_per_s": E / (ms * 1e-3)}
-    del v, grads, outs, wsd, wsa
+    del v, grads, outs, wsd, wsa, ggY, ggW
     torch.cuda.empty_cache()
     return res
 
