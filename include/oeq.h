@@ -207,10 +207,10 @@ oeq_status oeq_tp_conv_fwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edge
  *   grad_W[e,p,u] = sum C x[s,u,m1] Y[e,m2] grad_out[r,u,m3]
  *   grad_Y[e,m2]  = sum_u sum_p sum C x[s,u,m1] W[e,p,u] grad_out[r,u,m3]
  *   grad_x[s,u,m1]= sum_{e: src[e]=s} sum_p sum C Y[e,m2] W[e,p,u] grad_out[r,u,m3]
- * Edge-stationary ("Receiver-streaming convolutions ...", opening post, backward
- * ownership): a wave owns an edge at a time, lanes span channels, grad_W is
- * written directly, grad_Y is reduced across lanes, grad_x is scattered per
- * `mode`.  Any of grad_x, grad_Y, grad_W may be NULL (not computed).
+ * Receiver-stationary and edge-streaming ("Receiver-streaming convolutions ...",
+ * opening post, backward ownership): the waves of a workgroup take one receiver's
+ * edges one at a time, lanes span channels, grad_W is written directly, grad_Y is
+ * reduced across lanes, grad_x is scattered per `mode`.  Any of grad_x, grad_Y, grad_W may be NULL (not computed).
  * When the plan's data-movement model prefers the sender-stationary VJP
  * (oeq_plan_schedule; the choice is made once, at plan creation, as the
  * maintainers' reply in "Receiver-streaming convolutions ..." proposes), the call
