@@ -793,6 +793,8 @@ std::string emit_source(const oeq_plan &p) {
     o << "constexpr bool FWD_XCD = " << (p.fwd_xcd ? "true" : "false") << ";\n";
     o << "#define M_FENCE() __builtin_amdgcn_sched_barrier(0)\n";
     o << "constexpr int FWD_MT = " << p.fwd_tile << ";\n";
+    o << "constexpr int FWD_PF = " << p.fwd_pf << ";\n";
+    o << "constexpr int BWD_PF = " << p.bwd_pf << ";\n";
     // HVP from Y-contracted CG rows: tiles of HVP_MT edges, rows of at most HVP_M_MAX values
     o << "constexpr bool HVP_LDS = " << (p.hvp_lds ? "true" : "false") << ";\n";
     o << "constexpr int HVP_MT = " << p.hvp_tile << ";\n";

@@ -65,6 +65,32 @@ __device__ __forceinline__ void fwd_group(int r, int u, const int *__restrict__ 
         edge_y<YM>(Y, e0, s, pr, yv);
         Gr::load_x(x + (i64)s * XD, uu, xv);
         Gr::load_w(W + (i64)e0 * (P * U), uu, wv);
+        if constexpr (FWD_PF >= 2) {
+            // two edges ahead: the loads of edges e+1 and e+2 are in flight while e computes
+            // (the last edges reload the row's last edge rather than read past the row)
+            const int ea = (e0 + 1 < e1) ? e0 + 1 : e0;
+            const int sa = uni(src[ea]);
+            real_t ya[YD], xa[Gr::NX], wa[Gr::NW];
+            edge_y<YM>(Y, ea, sa, pr, ya);
+            Gr::load_x(x + (i64)sa * XD, uu, xa);
+            Gr::load_w(W + (i64)ea * (P * U), uu, wa);
+            for (int e = e0; e < e1; ++e) {
+                real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
+                const int en = (e + 2 < e1) ? e + 2 : e1 - 1;
+                const int sn = uni(src[en]);
+                edge_y<YM>(Y, en, sn, pr, yn);
+                Gr::load_x(x + (i64)sn * XD, uu, xn);
+                Gr::load_w(W + (i64)en * (P * U), uu, wn);
+                PIN_FWD();
+                Gr::edge(xv, yv, wv, sum);
+#pragma unroll
+                for (int k = 0; k < YD; ++k) { yv[k] = ya[k]; ya[k] = yn[k]; }
+#pragma unroll
+                for (int k = 0; k < Gr::NX; ++k) { xv[k] = xa[k]; xa[k] = xn[k]; }
+#pragma unroll
+                for (int k = 0; k < Gr::NW; ++k) { wv[k] = wa[k]; wa[k] = wn[k]; }
+            }
+        } else
         for (int e = e0; e < e1; ++e) {
             real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
             const int en = (e + 1 < e1) ? e + 1 : e;
@@ -320,41 +346,74 @@ __device__ __forceinline__ void bwd_group(GyStage &st, int r, int wv, int u, con
     if (!act) zero(gv);  // inactive lanes contribute nothing to the lane sums
     const int e0 = uni(rowptr[r]), e1 = uni(rowptr[r + 1]);
     if (e0 >= e1) return;
-    // software pipeline: the next edge's loads are in flight while this one computes
-    int s = uni(src[e0]);
-    real_t yv[YD], xv[Gr::NX], wv_[Gr::NW];
-    load_y(Y, e0, yv);
-    Gr::load_x(x + (i64)s * XD, uu, xv);
-    Gr::load_w(W + (i64)e0 * (P * U), uu, wv_);
-    for (int e = e0; e < e1; ++e) {
-        const int en = (e + 1 < e1) ? e + 1 : e;
-        const int sn = uni(src[en]);
-        real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
-        load_y(Y, en, yn);
-        Gr::load_x(x + (i64)sn * XD, uu, xn);
-        Gr::load_w(W + (i64)en * (P * U), uu, wn);
-        // keep the next edge's loads ahead of this edge's arithmetic
-        PIN_BWD();
+    // one edge's gradients from its loaded operands
+    auto body = [&](int e, int s_, const real_t (&y_)[YD], const real_t (&x_)[Gr::NX], const real_t (&w_)[Gr::NW]) {
         const int j = uni((e - e0) % GY_TILE);
         real_t gw[Gr::NW], gy[YD], gxp[Gr::NX];
         zero(gw);
         zero(gy);
         zero(gxp);
-        Gr::template vjp<true, true, (GXMODE != 0)>(xv, yv, wv_, gv, gw, gy, gxp);
+        Gr::template vjp<true, true, (GXMODE != 0)>(x_, y_, w_, gv, gw, gy, gxp);
         if (want_gw && act) Gr::store_w(gW + (i64)e * (P * U), u, gw);
         if (want_gy) {
             gy_push(st, gY, e, j, gy, lane, wv);
             if (j == GY_TILE - 1 || e + 1 == e1) gy_flush(st, gY, e - j, j + 1);
         }
-        if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s * GXD, u, gxp);
+        if (GXMODE == 1 && act) Gr::atomic_x(gx + (i64)s_ * GXD, u, gxp);
         if (GXMODE == 2 && act) Gr::store_x(gx + (i64)e * GXD, u, gxp);
-        s = sn;
+    };
+    // software pipeline: the next edge's loads (BWD_PF = 2: the next two edges') are in
+    // flight while this one computes
+    int s = uni(src[e0]);
+    real_t yv[YD], xv[Gr::NX], wv_[Gr::NW];
+    load_y(Y, e0, yv);
+    Gr::load_x(x + (i64)s * XD, uu, xv);
+    Gr::load_w(W + (i64)e0 * (P * U), uu, wv_);
+    if constexpr (BWD_PF >= 2) {
+        // the last edges reload the row's last edge rather than read past the row
+        const int ea = (e0 + 1 < e1) ? e0 + 1 : e0;
+        int sa = uni(src[ea]);
+        real_t ya[YD], xa[Gr::NX], wa[Gr::NW];
+        load_y(Y, ea, ya);
+        Gr::load_x(x + (i64)sa * XD, uu, xa);
+        Gr::load_w(W + (i64)ea * (P * U), uu, wa);
+        for (int e = e0; e < e1; ++e) {
+            const int en = (e + 2 < e1) ? e + 2 : e1 - 1;
+            const int sn = uni(src[en]);
+            real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
+            load_y(Y, en, yn);
+            Gr::load_x(x + (i64)sn * XD, uu, xn);
+            Gr::load_w(W + (i64)en * (P * U), uu, wn);
+            PIN_BWD();
+            body(e, s, yv, xv, wv_);
+            s = sa;
+            sa = sn;
 #pragma unroll
-        for (int k = 0; k < YD; ++k) yv[k] = yn[k];
+            for (int k = 0; k < YD; ++k) { yv[k] = ya[k]; ya[k] = yn[k]; }
 #pragma unroll
-        for (int k = 0; k < Gr::NX; ++k) xv[k] = xn[k];
+            for (int k = 0; k < Gr::NX; ++k) { xv[k] = xa[k]; xa[k] = xn[k]; }
 #pragma unroll
-        for (int k = 0; k < Gr::NW; ++k) wv_[k] = wn[k];
+            for (int k = 0; k < Gr::NW; ++k) { wv_[k] = wa[k]; wa[k] = wn[k]; }
+        }
+    } else {
+        for (int e = e0; e < e1; ++e) {
+            const int en = (e + 1 < e1) ? e + 1 : e;
+            const int sn = uni(src[en]);
+            real_t yn[YD], xn[Gr::NX], wn[Gr::NW];
+            load_y(Y, en, yn);
+            Gr::load_x(x + (i64)sn * XD, uu, xn);
+            Gr::load_w(W + (i64)en * (P * U), uu, wn);
+            // keep the next edge's loads ahead of this edge's arithmetic
+            PIN_BWD();
+            body(e, s, yv, xv, wv_);
+            s = sn;
+#pragma unroll
+            for (int k = 0; k < YD; ++k) yv[k] = yn[k];
+#pragma unroll
+            for (int k = 0; k < Gr::NX; ++k) xv[k] = xn[k];
+#pragma unroll
+            for (int k = 0; k < Gr::NW; ++k) wv_[k] = wn[k];
+        }
     }
 }
 

@@ -335,6 +335,14 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         if (v >= 1) p->fwd_tile = v;
     }
     if (const char *e = std::getenv("OEQ_FWD_XCD")) p->fwd_xcd = std::atoi(e) != 0;
+    // Loads two edges ahead in the literal forward; one in the VJP. Measured on MI355X (ms,
+    // interleaved runs): forward medium fp32 0.350 -> 0.348, and 0.345 with a window of 3 to 4
+    // waves per SIMD; large 0.673 -> 0.667 (0.670 with that window); invariant 0.337 -> 0.337
+    // (0.333 with it). The VJP two edges ahead: medium 0.815 -> 0.819, large 1.80 -> 1.94,
+    // wide 3.78 -> 3.95, medium fp64 1.666 -> 1.652.
+    p->fwd_pf = 2;
+    if (const char *e = std::getenv("OEQ_FWD_PF")) p->fwd_pf = std::atoi(e) >= 2 ? 2 : 1;
+    if (const char *e = std::getenv("OEQ_BWD_PF")) p->bwd_pf = std::atoi(e) >= 2 ? 2 : 1;
     // an output channel sum adds the chunks of a receiver in the workgroup's LDS
     if (p->sum_out) p->fwd_xcd = false;
     // one lane builds one edge's rows: a tile has at most one edge per lane of a group's waves
@@ -345,6 +353,10 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
         const int row_bytes = fwd_m_elems(*p) * (p->dtype == OEQ_F64 ? 8 : 4);
         while (p->fwd_tile > 1 && p->fwd_tile * row_bytes > 81920) p->fwd_tile /= 2;
     }
+    // the window of 3 to 4 waves for the one-group fp32 literal forward (it fits 170 registers)
+    if (p->fwd_waves.first == 0 && std::getenv("OEQ_FWD_WAVES") == nullptr && !p->fwd_lds && p->fwd_pf == 2 &&
+        p->fwd_groups.size() == 1 && p->dtype == OEQ_F32)
+        p->fwd_waves = {3, 4};
     p->bwd_groups = choose_groups(*p, false);
     p->dbwd_groups = choose_dbwd_groups(*p);
     // The HVP from Y-contracted CG rows, an option (its d_grad_out store leaves out

@@ -89,6 +89,8 @@ struct oeq_plan {
     // path instead of the x-Y products plus every non-zero plus n3
     bool fwd_lds = false;
     int fwd_tile = 32;          // edges per LDS tile of M rows (capped by the LDS budget)
+    int fwd_pf = 1;             // edges the literal forward loads ahead of the one it computes
+    int bwd_pf = 1;             // the same for the VJP
     // the HVP (tangent on x only) from Y-contracted CG rows in LDS per edge tile: d_grad_out
     // and d_W share the forward of the tangent, t = M^T v, instead of the x-Y products
     bool hvp_lds = false;

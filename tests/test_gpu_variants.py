@@ -69,6 +69,10 @@ CASES = [
     ("mace_medium_fp32", {"OEQ_FWD_XCD": "1"}),
     ("wide_proxy_fp32", {"OEQ_FWD_XCD": "1", "OEQ_FWD_LDS": "1"}),
     ("mace_medium_fp64", {"OEQ_FWD_XCD": "1"}),
+    # loads one edge ahead in the forward (the default is two), two edges ahead in the VJP
+    ("mace_medium_fp32", {"OEQ_FWD_PF": "1"}),
+    ("mace_large_fp32", {"OEQ_FWD_PF": "1", "OEQ_BWD_PF": "2"}),
+    ("tiny_fp64", {"OEQ_FWD_LDS": "0", "OEQ_BWD_PF": "2"}),
     # the HVP from Y-contracted CG rows in LDS (an option): one backward group, and two
     # groups (partial Y-gradient rows) with ragged tiles of 7 edges
     ("mace_medium_fp32", {"OEQ_HVP_LDS": "1"}),
