@@ -5,7 +5,8 @@ Two calls in a row on one device, the second on a smaller graph (the shared
 device scratch keeps the first call's contents), in both x-gradient modes: the
 deterministic mode keeps its per-edge rows and sender CSR in the scratch and must
 match bit for bit; the atomic mode within the fp tolerance.  A plan whose backward
-runs in two path groups puts its partial Y-gradient rows there too.  A plan whose
+runs in two path groups puts its partial Y-gradient rows there too, and a plan with a
+one-channel x block its atomic x-gradient rows of U channels per block.  A plan whose
 kernels are not yet loaded on the device is refused (loading allocates)."""
 import numpy as np
 import pytest
@@ -27,6 +28,8 @@ def _need_gpu():
 
 
 W_ = synth.WORKLOADS
+_UVW = synth.Workload("reducible_uvw", 150, 24, synth._irr("1x0e+96x1o+96x2e"), 2, 2, "f32", "unit", 67,
+                      out_irreps=synth._irr("96x0e+1x1o+96x1e+96x2e+1x2o"))
 CASES = {
     # (larger graph, smaller graph, planner options)
     "medium_fp32": (W_["mace_medium_fp32"].scaled(n_nodes=240), W_["mace_medium_fp32"].scaled(n_nodes=90, seed=7),
@@ -35,6 +38,9 @@ CASES = {
                     {}),
     "large_two_groups": (W_["mace_large_fp32"].scaled(n_nodes=160), W_["mace_large_fp32"].scaled(n_nodes=70, seed=9),
                          {"OEQ_BWD_GROUPS": "2"}),
+    # a broadcast x block and channel sums: the atomic mode's x-gradient rows of U channels
+    # per block are in the scratch too
+    "reducible_uvw": (_UVW.scaled(n_nodes=150), _UVW.scaled(n_nodes=50, seed=10), {}),
 }
 
 
