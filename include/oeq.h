@@ -230,7 +230,8 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t n_nodes, int64_t n_edge
  * callers that cannot allocate device memory: code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation.  Its scratch (the per-edge
  * x-gradient rows and the sender CSR of DETERMINISTIC mode, the per-group partial
- * Y-gradients of a plan with several backward groups) lives in a file-scope device
+ * Y-gradients of a plan with several backward groups, the ATOMIC x-gradient rows of
+ * U channels per block of a plan with one-channel x blocks) lives in a file-scope device
  * array of 64 MiB that each device the library runs on holds until the process
  * ends; a call needing more returns OEQ_ERR_WORKSPACE with the size in
  * oeq_last_error(), before any device work.  The plan must already have run an
@@ -307,7 +308,8 @@ oeq_status oeq_sender_view(int64_t n_nodes, int64_t n_edges, const int32_t *rowp
 /* Forward, sender-stationary: out = f(x, Y, W) as oeq_tp_conv_fwd, with each
  * edge's message added into out[receiver] by floating-point atomics (so the
  * summation order varies run to run).  out is zeroed and reordered by the call
- * (two light kernels around the main one). */
+ * (two light kernels around the main one).  OEQ_ERR_UNSUPPORTED for a plan with a
+ * one-channel x or output block. */
 oeq_status oeq_tp_conv_fwd_sender(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                                   const int32_t *srowptr, const int32_t *sperm,
                                   const int32_t *sdst, const void *x, const void *Y,
@@ -317,7 +319,8 @@ oeq_status oeq_tp_conv_fwd_sender(const oeq_plan *plan, int64_t n_nodes, int64_t
  * gathered per edge; grad_W and grad_Y are per edge; grad_x of each sender is
  * accumulated in registers and stored once, without atomics, so every output is
  * bitwise repeatable.  Any gradient pointer may be NULL.  `workspace` must hold
- * oeq_workspace_size(plan, N, E, OEQ_BWD_ATOMIC) bytes when that size is not 0. */
+ * oeq_workspace_size(plan, N, E, OEQ_BWD_ATOMIC) bytes when that size is not 0.
+ * OEQ_ERR_UNSUPPORTED for a plan with a one-channel x or output block. */
 oeq_status oeq_tp_conv_bwd_sender(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                                   const int32_t *srowptr, const int32_t *sperm,
                                   const int32_t *sdst, const void *x, const void *Y,
@@ -421,7 +424,8 @@ oeq_status oeq_radial_bwd(const oeq_plan *plan, int64_t n_edges, const void *vec
  * 8, W1, W2), for a hidden width of exactly 8 (W1 [8, 8], W2 [8, P*U]).  Each lane
  * keeps its slice of W2 in registers and forms W[e] from the edge's 8 hidden
  * values.  `workspace` of oeq_radial_workspace_size(plan, E, 8) bytes holds the
- * basis and the hidden values. */
+ * basis and the hidden values.  OEQ_ERR_UNSUPPORTED for a plan with a one-channel
+ * x or output block. */
 oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                                   const int32_t *rowptr, const int32_t *src, const void *x,
                                   const void *Y, const void *vec, double r_cut, const void *W1,
@@ -435,7 +439,8 @@ oeq_status oeq_tp_conv_fwd_radial(const oeq_plan *plan, int64_t n_nodes, int64_t
  * (reduced over lanes and waves like grad_Y) and accumulates h (x) gW into a
  * per-receiver W2-gradient row; the rows are summed over receivers in order, so
  * grad_W2 and grad_W1 are bitwise repeatable.  Any output may be NULL.  Needs Y
- * degrees up to at least 2.  `workspace` of oeq_workspace_size_radial bytes. */
+ * degrees up to at least 2.  `workspace` of oeq_workspace_size_radial bytes.
+ * OEQ_ERR_UNSUPPORTED for a plan with a one-channel x or output block. */
 oeq_status oeq_workspace_size_radial(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
                                      oeq_bwd_mode mode, size_t *bytes);
 oeq_status oeq_tp_conv_bwd_radial(const oeq_plan *plan, int64_t n_nodes, int64_t n_edges,
