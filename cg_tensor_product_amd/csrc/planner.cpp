@@ -321,8 +321,9 @@ oeq_status plan_build(const oeq_tp_desc *d, oeq_plan *p, std::string *why) {
     waves("OEQ_BWD_WAVES", p->bwd_waves);
     p->fwd_groups = choose_groups(*p, true);
     // measured on MI355X (tiles of 64 edges): the tile form wins for fp64 (medium workload
-    // 0.74 against 0.76 ms) and where four or more channel chunks share each edge's rows (wide
-    // workload, U = 256: 1.49 against 1.62 ms); with two chunks in fp32 the literal form is
+    // 0.739 against 0.802 ms with the literal form loading two edges ahead) and ties where four
+    // or more channel chunks share each edge's rows (wide workload, U = 256: 1.498 against
+    // 1.489 ms; 1.62 before the two-edge pipeline); with two chunks in fp32 the literal form is
     // faster (large workload 0.67 against 0.78 ms: the tile form's 172 registers leave two
     // waves per SIMD, and the waves wait while a tile's rows are built)
     p->fwd_lds = p->dtype == OEQ_F64 || p->uch >= 4;
