@@ -270,13 +270,13 @@ def main():
     import oracle
     import synth
 
-    wl = synth.WORKLOADS[args.workload] if args.workload in synth.WORKLOADS else synth.CALIBRATION[args.workload]
-    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max)
+    wl = synth.by_name(args.workload)
+    d = oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max, y_irreps=wl.y_irreps, out_irreps=wl.out_irreps)
     inp = synth.generate(wl, d.P, d.out_dim, want=("x", "Y", "W", "g"))
     E, N = inp["E"], wl.n_nodes
     torch.cuda.set_device(0)
     # (a plan missing from the code-object cache is compiled in a child process; see Plan)
-    plan = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype)
+    plan = oeq.Plan(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.dtype, y_irreps=wl.y_irreps, out_irreps=wl.out_irreps)
     dev = {k: torch.from_numpy(inp[k]).cuda() for k in ("rowptr", "src", "x", "Y", "W", "g")}
     dt = plan.torch_dtype()
     out = torch.empty(N, plan.out_dim, dtype=dt, device="cuda")
@@ -373,6 +373,8 @@ def main():
         "config": {"workload": wl.name, "nodes": N, "edges": E, "degree": wl.degree,
                    "x_irreps": "+".join(f"{m}x{l}{'e' if p > 0 else 'o'}" for m, l, p in wl.x_irreps),
                    "y_lmax": wl.y_lmax, "paths": d.P,
+                   **({"out_irreps": "+".join(f"{m}x{l}{'e' if p > 0 else 'o'}" for m, l, p in wl.out_irreps)}
+                      if wl.out_irreps else {}),
                    "step": f"forward ({sched_f}-stationary) + VJP ("
                            + ("sender-stationary" if sched == "sender" else f"receiver-stationary, {args.mode} x-gradient")
                            + ")"},

@@ -154,7 +154,7 @@ oeq_status oeq_tp_conv_bwd(const oeq_plan *plan, int64_t N, int64_t E, const int
     }
     const bool det = gx && mode == OEQ_BWD_DETERMINISTIC;
     const bool gyp = gY && p->bwd_groups.size() > 1;
-    const bool gxe = gx && !det && needs_gxe(p);
+    const bool gxe = gx && needs_gxe(p);
     Workspace w;
     if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w, gxe)) != OEQ_OK) return st;
     int flags = (gW ? 1 : 0) | (gY ? 2 : 0);
@@ -303,9 +303,6 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
             }
         }
     }
-    // the fused passes write d_grad_out with U channels per block: a plan with one-channel
-    // output blocks takes d_grad_out from the forward kernel (its channel sum) instead
-    if (p->sum_out && level == 0) level = 1;
     // Path groups of the kernels this call launches: oeq_dbwd_<t> is built on the backward
     // groups; oeq_dbwd_<t>_d and every split pass on the double-backward groups. The grid
     // must match: a kernel maps block b to receiver b / groups.
@@ -315,7 +312,7 @@ oeq_status oeq_tp_conv_dbwd(const oeq_plan *plan, int64_t N, int64_t E, const in
     };
     const int64_t NG = level == 0 ? kernel_groups(fused) : static_cast<int64_t>(p->dbwd_groups.size());
     const bool gyp = dY && NG > 1;
-    const bool gxe = dx_live && !det && needs_gxe(p);
+    const bool gxe = dx_live && needs_gxe(p);
     Workspace w;
     if ((st = ws_bind(p, N, E, det, gyp, workspace, workspace_bytes, &w, gxe)) != OEQ_OK) return st;
     if (dx && !dx_live && (st = fill_zero(p, dx, N * p->XD, s)) != OEQ_OK) return st;

@@ -90,8 +90,8 @@ inline oeq_status untranspose(oeq_plan *p, int64_t N, void *gx, hipStream_t stre
 //   gy_part  partial Y-gradient rows of each backward path group (several groups only)
 //   h, srowptr, sperm, csr_scratch   deterministic x-gradient (per-edge rows of GXD values,
 //            sender CSR)
-//   gxe      atomic x-gradient rows of GXD values (plans with one-channel x blocks: the
-//            channels are summed into the caller's rows afterwards)
+//   gxe      x-gradient rows of GXD values (plans with one-channel x blocks: the channels
+//            are summed into the caller's rows afterwards)
 struct Workspace {
     void *gy_part = nullptr;
     void *h = nullptr;
@@ -187,7 +187,7 @@ inline oeq_status bwd_ws_bytes(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_
     }
     Workspace w;
     oeq_status st = ws_layout(p, N, E, gx && mode == OEQ_BWD_DETERMINISTIC, gY && p->bwd_groups.size() > 1, nullptr, &w,
-                              gx && mode == OEQ_BWD_ATOMIC && needs_gxe(p));
+                              gx && needs_gxe(p));
     if (st == OEQ_OK) *bytes = w.bytes;
     return st;
 }
@@ -196,8 +196,7 @@ inline oeq_status bwd_ws_bytes(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_
 // the receiver-stationary layout, or the sender view when the plan routes the VJP there.
 inline oeq_status vjp_ws_bytes(const oeq_plan *p, int64_t N, int64_t E, oeq_bwd_mode mode, size_t *bytes) {
     Workspace w;
-    oeq_status st = ws_layout(p, N, E, mode == OEQ_BWD_DETERMINISTIC, gy_groups(p) > 1, nullptr, &w,
-                              mode == OEQ_BWD_ATOMIC && needs_gxe(p));
+    oeq_status st = ws_layout(p, N, E, mode == OEQ_BWD_DETERMINISTIC, gy_groups(p) > 1, nullptr, &w, needs_gxe(p));
     if (st != OEQ_OK) return st;
     *bytes = w.bytes;
     if (bwd_by_sender(p, E)) {
@@ -228,13 +227,19 @@ inline oeq_status sender_csr_into(int64_t N, int64_t E, const int32_t *src, cons
     return OEQ_OK;
 }
 
-// x-gradient by per-edge rows (already written to w.h) summed per sender.
+inline oeq_status fold_x(oeq_plan *p, int64_t N, const void *gxe, void *gx, hipStream_t stream);
+
+// x-gradient by per-edge rows (already written to w.h) summed per sender; with one-channel
+// x blocks into the GXD-wide rows w.gxe, whose channels are then summed into gx.
 inline oeq_status det_finish(oeq_plan *p, int64_t N, const Workspace &w, void *gx, hipStream_t stream) {
     void *h = w.h;
     int32_t *srp = w.srowptr, *spm = w.sperm;
     int n = static_cast<int>(N);
-    void *args[] = {&srp, &spm, &h, &gx, &n};
-    return launch(p, "oeq_sender_sum", static_cast<unsigned>(N), 256, stream, args);
+    void *dst = needs_gxe(p) ? w.gxe : gx;
+    void *args[] = {&srp, &spm, &h, &dst, &n};
+    oeq_status st = launch(p, "oeq_sender_sum", static_cast<unsigned>(N), 256, stream, args);
+    if (st != OEQ_OK || !needs_gxe(p)) return st;
+    return fold_x(p, N, w.gxe, gx, stream);
 }
 
 // The caller's x-gradient rows from the GXD-wide rows of the atomic passes.

@@ -491,6 +491,19 @@ void emit_group(std::ostringstream &o, const oeq_plan &p, const char *name, int 
         o << "  static constexpr int NSUM = " << nsum << ", SOFF = " << soff << ";\n";
         o << "  static __device__ __forceinline__ void sum_pick(const real_t (&v)[NO], real_t (&s)[NSUM > 0 ? NSUM : 1]) {"
           << (nsum ? pick.str() : std::string(" s[0] = real_t(0);")) << " }\n";
+        // offsets of those elements in an output row (kernels that own one group per workgroup)
+        o << "  static __device__ __forceinline__ i64 sum_off_g(int j) {";
+        if (nsum) {
+            o << " switch (j) {";
+            int j = 0;
+            for (const auto &kv : L.ooff) {
+                const Block &b = p.ob[kv.first];
+                if (b.mul == p.U) continue;
+                for (int m = 0; m < 2 * b.l + 1; ++m) o << " case " << j++ << ": return " << b.row_off + m << ";";
+            }
+            o << " }";
+        }
+        o << " return 0; }\n";
     }
     // x-gradient scatter: with XT the block is addressed m-major (element m*U + u),
     // so consecutive lanes hit consecutive words; oeq_x_untranspose restores the
@@ -834,6 +847,14 @@ std::string emit_source(const oeq_plan &p) {
     } else {
         for (size_t g = 0; g < p.dbwd_groups.size(); ++g)
             emit_group(o, p, "DG", static_cast<int>(g), p.dbwd_groups[g]);
+    }
+    {
+        // one-channel output elements of the largest backward or double-backward group (the
+        // double backward sums their d_grad_out over the channels in LDS)
+        int mx = 0;
+        for (size_t g = 0; g < p.bwd_groups.size(); ++g) mx = std::max(mx, group_nsum(p, p.bwd_groups[g], g == 0));
+        for (size_t g = 0; g < p.dbwd_groups.size(); ++g) mx = std::max(mx, group_nsum(p, p.dbwd_groups[g], g == 0));
+        o << "constexpr int DBWD_NSUM_MAX = " << mx << ";\n";
     }
     emit_untranspose(o, p);
     emit_fold_x(o, p);

@@ -493,8 +493,9 @@ oeq_gy_combine(const real_t *__restrict__ part, real_t *__restrict__ gY, i64 n) 
 
 // ---------------------------------------------------------------------------
 // Deterministic x gradient: gx[s] = sum of h[e] over the sender's edges, in the
-// sender CSR's (increasing edge id) order.  The per-edge rows h carry U channels
-// in every block; a one-channel x block takes the sum of its channels per edge.
+// sender CSR's (increasing edge id) order.  Rows of GXD values (U channels in every
+// block); with one-channel x blocks the caller passes rows in the workspace and
+// oeq_fold_x then sums their channels.
 // ---------------------------------------------------------------------------
 extern "C" __global__ void __launch_bounds__(256)
 oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
@@ -502,23 +503,19 @@ oeq_sender_sum(const int *__restrict__ srowptr, const int *__restrict__ sperm,
     const int s = blockIdx.x;
     if (s >= n_nodes) return;
     const int k0 = uni(srowptr[s]), k1 = uni(srowptr[s + 1]);
-    for (i64 c = threadIdx.x; c < XD; c += 256) {
+    for (i64 c = threadIdx.x; c < GXD; c += 256) {
         real_t acc = real_t(0);
         int k = k0;
-        if constexpr (GXD == XD) {
-            // eight rows in flight, added in edge order
-            for (; k + 8 <= k1; k += 8) {
-                real_t t[8];
+        // eight rows in flight, added in edge order
+        for (; k + 8 <= k1; k += 8) {
+            real_t t[8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) t[j] = h[(i64)uni(sperm[k + j]) * XD + c];
+            for (int j = 0; j < 8; ++j) t[j] = h[(i64)uni(sperm[k + j]) * GXD + c];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc += t[j];
-            }
-            for (; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * XD + c];
-        } else {
-            for (; k < k1; ++k) acc += fold_x_elem(h + (i64)uni(sperm[k]) * GXD, (int)c);
+            for (int j = 0; j < 8; ++j) acc += t[j];
         }
-        gx[(i64)s * XD + c] = acc;
+        for (; k < k1; ++k) acc += h[(i64)uni(sperm[k]) * GXD + c];
+        gx[(i64)s * GXD + c] = acc;
     }
 }
 

@@ -107,12 +107,35 @@ __device__ __forceinline__ void dbwd_group(GyStage &st, int r, int wv, int u, co
             cur = nxt;
         }
     }
-    if constexpr ((OUT & DGO) != 0)
-    if (want_dg && act) {
-        if (acc_dg)
-            Gr::add_out(dg + (i64)r * OD, u, dgacc);
-        else
-            Gr::store_out(dg + (i64)r * OD, u, dgacc);
+    if constexpr ((OUT & DGO) != 0) {
+        if (want_dg && act) {
+            if (acc_dg)
+                Gr::add_out(dg + (i64)r * OD, u, dgacc);
+            else
+                Gr::store_out(dg + (i64)r * OD, u, dgacc);
+        }
+        // one-channel output blocks: the sum over the channels, as in the forward (each wave
+        // adds its lanes, then the chunks of the receiver are added in LDS in chunk order);
+        // want_dg is the same for every wave of the workgroup, so all meet at the barrier
+        if constexpr (Gr::NSUM > 0) {
+            if (want_dg) {
+                __shared__ real_t red[UCH * (DBWD_NSUM_MAX > 0 ? DBWD_NSUM_MAX : 1)];
+                real_t sv[Gr::NSUM];
+                Gr::sum_pick(dgacc, sv);
+#pragma unroll
+                for (int j = 0; j < Gr::NSUM; ++j) {
+                    const real_t t = wave_sum(act ? sv[j] : real_t(0));
+                    if (lane == 0) red[wv * DBWD_NSUM_MAX + j] = t;
+                }
+                __syncthreads();
+                for (int j = threadIdx.x; j < Gr::NSUM; j += blockDim.x) {
+                    real_t t = red[j];
+                    for (int c = 1; c < UCH; ++c) t += red[c * DBWD_NSUM_MAX + j];
+                    real_t *q = dg + (i64)r * OD + Gr::sum_off_g(j);
+                    *q = acc_dg ? *q + t : t;
+                }
+            }
+        }
     }
 }
 

@@ -178,11 +178,12 @@ class Desc:
     harmonics of degrees 0..y_lmax with parity (-1)^l.  Paths are
     (x block, Y block, l3, output block); with the default Y the Y block index is
     the degree.  Default paths: all triangle-allowed ones up to l3_max, one output
-    block per path, in enumeration order."""
+    block per path, in enumeration order; or, given out_irreps ((mul, l, parity), ...),
+    every enumerated path whose (l3, parity) is one of them, adding into that block."""
 
     def __init__(self, x_irreps, y_lmax: int, l3_max: int = 3,
                  paths: Optional[Sequence] = None, out_l: Optional[Sequence[int]] = None,
-                 y_irreps=None, out_mul: Optional[Sequence[int]] = None):
+                 y_irreps=None, out_mul: Optional[Sequence[int]] = None, out_irreps=None):
         self.x_irreps = tuple(tuple(t) for t in x_irreps)
         self.U = max(m for m, _, _ in self.x_irreps)
         if any(m not in (1, self.U) for m, _, _ in self.x_irreps):
@@ -195,7 +196,13 @@ class Desc:
         self.yl = [l for _, l, _ in self.y_irreps]
         self.yoff = [int(v) for v in np.cumsum([0] + [2 * l + 1 for l in self.yl])[:-1]]
         self.L = max(self.yl)
-        if paths is None:
+        if paths is None and out_irreps is not None:
+            outs = [(l, par) for _, l, par in out_irreps]
+            en = enumerate_paths(self.x_irreps, y_lmax, l3_max, y_irreps=self.y_irreps)
+            paths = [(i1, j, l3, outs.index((l3, p3))) for (i1, j, l3, p3) in en if (l3, p3) in outs]
+            out_l = [l for l, _ in outs]
+            out_mul = [m for m, _, _ in out_irreps]
+        elif paths is None:
             en = enumerate_paths(self.x_irreps, y_lmax, l3_max, y_irreps=self.y_irreps)
             paths = [(i1, j, l3, k) for k, (i1, j, l3, _) in enumerate(en)]
             out_l = [l3 for (_, _, l3, _) in en]

@@ -117,6 +117,18 @@ WORKLOADS = {
 }
 
 
+# UVW products that reduce to the channel-wise one, at the medium workload's sizes (same
+# graph and seeds): a broadcast scalar beside 128 vector channels, and outputs of which the
+# pseudotensor and scalar blocks sum the channels.
+REDUCIBLE = {
+    "uvw_bcast_medium_fp32": Workload("uvw_bcast_medium_fp32", 5000, 56, _irr("1x0e+128x1o"), 3, 3, "f32",
+                                      "inv_sqrt_paths", 2002),
+    "uvw_sum_medium_fp32": Workload("uvw_sum_medium_fp32", 5000, 56, _irr("128x0e+128x1o"), 3, 3, "f32",
+                                    "inv_sqrt_paths", 2002,
+                                    out_irreps=_irr("1x0e+128x1o+128x2e+128x3o+1x1e+1x2o+1x3e")),
+}
+
+
 # Counter calibration: the medium workload's sizes with every edge leaving node 0, so the
 # forward's HBM reads are the non-temporal W stream, Y and the CSR (x is a single cached
 # row); FETCH_SIZE of that forward checks the counter's scale for the kernels' own loads.
@@ -124,6 +136,14 @@ CALIBRATION = {
     "nt_read_calibration_fp32": Workload("nt_read_calibration_fp32", 5000, 56, _irr("128x0e+128x1o"), 3, 3,
                                          "f32", "inv_sqrt_paths", 2002, one_sender=True),
 }
+
+
+def by_name(name: str) -> Workload:
+    """A workload of WORKLOADS, REDUCIBLE or CALIBRATION."""
+    for table in (WORKLOADS, REDUCIBLE, CALIBRATION):
+        if name in table:
+            return table[name]
+    raise KeyError(name)
 
 
 # ---------------------------------------------------------------------------

@@ -23,16 +23,7 @@ def rel_l2(got, ref) -> float:
 
 
 def oracle_desc(wl: synth.Workload) -> oracle.Desc:
-    if wl.out_irreps is None:
-        return oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max, y_irreps=wl.y_irreps)
-    # given output irreps: every enumerated path whose (l3, parity) is one of them adds
-    # into that block, in enumeration order; the others are not part of the product
-    outs = [(l, par) for _, l, par in wl.out_irreps]
-    paths = [(i1, j, l3, outs.index((l3, p3)))
-             for (i1, j, l3, p3) in oracle.enumerate_paths(wl.x_irreps, wl.y_lmax, wl.l3_max, wl.y_irreps)
-             if (l3, p3) in outs]
-    return oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max, paths=paths, out_l=[l for l, _ in outs],
-                       y_irreps=wl.y_irreps, out_mul=[m for m, _, _ in wl.out_irreps])
+    return oracle.Desc(wl.x_irreps, wl.y_lmax, wl.l3_max, y_irreps=wl.y_irreps, out_irreps=wl.out_irreps)
 
 
 def inputs(wl: synth.Workload, want=("x", "Y", "W", "g")):

@@ -211,3 +211,31 @@ def test_output_blocks_without_paths_are_written_as_zero(name):
     refg = oracle.fwd(d, rp, sr, inp["v"], inp["Y"], inp["W"])
     gg = res["grad_out"].cpu().numpy()
     assert not np.isnan(gg).any() and rel_l2(gg, refg) <= RTOL[wl.dtype]
+
+
+@pytest.mark.parametrize("split", ["0", "1", "2"])
+@pytest.mark.parametrize("name", ["sum_u64_f32", "mixed_u96_f64", "sum_u256_f32"])
+def test_dbwd_split_levels_with_channel_sums(name, split):
+    """The fused double backward sums one-channel d_grad_out blocks in LDS; the split
+    passes take d_grad_out from the forward kernel.  Each level against the oracle, with
+    outputs that start as NaN."""
+    wl, d, inp, dev, plan = _case(name, {"OEQ_DBWD_SPLIT": split})
+    tx = synth.extra_normal(wl, inp["x"].shape, 0)
+    tY = synth.extra_normal(wl, inp["Y"].shape, 1)
+    tW = synth.extra_normal(wl, inp["W"].shape, 2)
+    print(f"[uvw dbwd split] {name} {split}", flush=True)
+    shapes = {"x": inp["x"].shape, "Y": inp["Y"].shape, "W": inp["W"].shape, "grad_out": inp["g"].shape}
+    for mask in (1, 7):
+        ref = oracle.dbwd(d, inp["rowptr"], inp["src"], inp["x"], inp["Y"], inp["W"], inp["g"],
+                          ggx=tx, ggY=tY if mask & 2 else None, ggW=tW if mask & 4 else None)
+        res = {k: torch.full(v, float("nan"), dtype=plan.torch_dtype(), device="cuda") for k, v in shapes.items()}
+        oeq.oeq_tp_conv_dbwd(plan, dev["rowptr"], dev["src"], dev["x"], dev["Y"], dev["W"], dev["g"],
+                             gg_x=to_dev(tx), gg_Y=to_dev(tY) if mask & 2 else None,
+                             gg_W=to_dev(tW) if mask & 4 else None, out=res)
+        torch.cuda.synchronize()
+        for k, rk in (("x", "dx"), ("Y", "dY"), ("W", "dW"), ("grad_out", "dg")):
+            got = res[k].cpu().numpy()
+            if not np.any(ref[rk]):
+                assert not got.any(), (mask, k)
+            else:
+                assert rel_l2(got, ref[rk]) <= RTOL[wl.dtype], (mask, k)

@@ -521,3 +521,12 @@ def test_mixed_multiplicities_adjoint_and_dense():
     gx, gY, gW = oracle.bwd(d, rowptr, src, x, Y, W, g)
     for a, b in ((gx, x), (gY, Y), (gW, W)):
         assert abs(np.vdot(a, b) - f) <= 1e-12 * max(1.0, abs(f))
+
+
+def test_output_irreps_collect_the_paths_of_their_irrep():
+    # 1o x (0e + 1o + 2e) up to l3 = 1: 1o x 0e -> 1o, 1o x 1o -> 0e and 1e, 1o x 2e -> 1o;
+    # given outputs 1o and 0e (one channel), the two 1o paths add into block 0, the 0e
+    # path into block 1, and the 1e path is not part of the product
+    d = oracle.Desc(((4, 1, -1),), 2, 1, out_irreps=((4, 1, -1), (1, 0, 1)))
+    assert d.paths == [(0, 0, 1, 0), (0, 1, 0, 1), (0, 2, 1, 0)]
+    assert d.out_l == [1, 0] and d.out_mul == [4, 1] and d.out_dim == 4 * 3 + 1
