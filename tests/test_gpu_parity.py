@@ -304,12 +304,14 @@ def _rel_l2_dev(got, ref, rows=1 << 14) -> float:
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32", "invariant_fp32"])
+@pytest.mark.parametrize("name", ["mace_medium_fp32", "mace_medium_fp64", "mace_large_fp32", "invariant_fp32",
+                                  "uvw_bcast_medium_fp32", "uvw_sum_medium_fp32"])
 def test_full_size_whole(name):
     """The full 5,000-node / 280,000-edge workloads in the benchmark's launch shape,
     compared on every element of every output: forward, VJP in both modes and (for
-    the large workload) the HVP."""
-    wl = W_[name]
+    the large workload) the HVP.  The two reducible-UVW workloads (a broadcast x block;
+    outputs summed over the channels) at the same sizes."""
+    wl = synth.by_name(name)
     want = ("x", "Y", "W", "g", "v") if "hvp" in wl.ops else ("x", "Y", "W", "g")
     d, inp = inputs(wl, want=want)
     print(f"[whole] {name} N={wl.n_nodes} E={inp['E']} inputs ready", flush=True)
