@@ -35,6 +35,13 @@ MUTANTS = {
                          "double gv = g[r * OD + q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m2[t] % q->n3];\n                        acc +="),
     "dbwd_term_dropped": ("if (ggY) { oracle_fwd(d, N, E, rowptr, src, x, ggY, W, rows, nrows, to); axpy(dg, to, nrows * OD); }",
                           "(void)0;"),
+    # one-channel blocks (UVW products that reduce to the channel-wise one)
+    "x_broadcast_ignored": ("double xv = x[s * XD + q->xoff + (int64_t)(u * q->xu) * q->n1 + q->m1[t]];\n                        double yv",
+                            "double xv = x[s * XD + q->xoff + (int64_t)u * q->n1 + q->m1[t]];\n                        double yv"),
+    "out_sum_first_channel_only": ("o[q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m3[t]] += q->c[t] * xv * yv * w;",
+                                   "if (q->ou || u == 0) o[q->ooff + (int64_t)(u * q->ou) * q->n3 + q->m3[t]] += q->c[t] * xv * yv * w;"),
+    "gx_broadcast_not_summed": ("gx[q->xoff + (int64_t)(u * q->xu) * q->n1 + q->m1[t]] += q->c[t] * yv * w * gv;",
+                                "if (q->xu || u == 0) gx[q->xoff + (int64_t)(u * q->xu) * q->n1 + q->m1[t]] += q->c[t] * yv * w * gv;"),
     "sender_csr_unstable": ("for (int64_t e = 0; e < E; ++e) sperm[fill[src[e]]++] = (int32_t)e;",
                             "for (int64_t e = E - 1; e >= 0; --e) sperm[fill[src[e]]++] = (int32_t)e;"),
 }
